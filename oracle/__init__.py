@@ -1,0 +1,177 @@
+"""KDA oracle -- TEST INFRASTRUCTURE, not part of the product.
+
+Plain, slow, fp64 CPU implementations of what the KDA chunked forward and the
+T=1 decode compute.  Only the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import anything from here; the product
+package never does, and nothing here imports the product package.
+
+Contents
+--------
+``recurrence``      the definition, token by token (C, fp64, threaded): see
+                    ``kda_oracle.c`` for the formula and its sources.
+``forms``           independent fp64 forms used to pin the recurrence: the naive
+                    chunked (WY) form, the short-window closed form, brute force
+                    with dense 128x128 transition matrices, and special cases.
+
+Parity status of each function is listed in ``forms``' module docstring.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+_lock = threading.Lock()
+
+_DT = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc into ``oracle/libkda_oracle.so``."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+               _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB)
+            f = lib.oracle_kda_recurrence
+            f.restype = ctypes.c_int
+            f.argtypes = [ctypes.c_int] + [ctypes.c_void_p] * 6 + [
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+            _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, min(n, 16))
+
+
+def _cpu_contig(x: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    return x.detach().to("cpu").contiguous()
+
+
+def recurrence(q, k, v, g, beta, cu_seqlens=None, scale=None, use_qk_l2norm=True,
+               initial_state=None, heads=None, threads=None, want_state=True):
+    """Token-by-token fp64 KDA recurrence.
+
+    q, k: [T, Hqk, 128]; v, g: [T, Hv, 128]; beta: [T, Hv] (logits), all one of
+    fp32/bf16/fp16 (read at their stored precision).  Dense [B, T, H, 128]
+    inputs are accepted and flattened with cu_seqlens = [0, T, 2T, ...].
+    initial_state: [N, Hv, 128(V), 128(K)] (any float dtype, widened) or None.
+    heads: optional list of value heads to compute (others are left 0).
+
+    Returns (out [T, Hv, 128] fp64 numpy, final_state [N, Hv, 128, 128] fp64
+    numpy V-first, or None).
+    """
+    q = _cpu_contig(q, "q"); k = _cpu_contig(k, "k"); v = _cpu_contig(v, "v")
+    g = _cpu_contig(g, "g"); beta = _cpu_contig(beta, "beta")
+    if q.dim() == 4:
+        B, T = q.shape[:2]
+        if cu_seqlens is not None:
+            raise ValueError("dense 4-D input takes no cu_seqlens")
+        q, k = q.reshape(B * T, *q.shape[2:]), k.reshape(B * T, *k.shape[2:])
+        v, g = v.reshape(B * T, *v.shape[2:]), g.reshape(B * T, *g.shape[2:])
+        beta = beta.reshape(B * T, beta.shape[-1])
+        cu = np.arange(B + 1, dtype=np.int64) * T
+    else:
+        if cu_seqlens is None:
+            cu = np.array([0, q.shape[0]], dtype=np.int64)
+        else:
+            cu = np.asarray(torch.as_tensor(cu_seqlens).cpu().numpy(), dtype=np.int64)
+    dt = q.dtype
+    for name, x in (("k", k), ("v", v), ("g", g), ("beta", beta)):
+        if x.dtype != dt:
+            raise TypeError(f"{name} dtype {x.dtype} != q dtype {dt}")
+    if dt not in _DT:
+        raise TypeError(f"unsupported dtype {dt}")
+    Ttot, hqk, D = q.shape
+    hv = v.shape[1]
+    if D != 128 or v.shape[2] != 128 or hv % hqk:
+        raise ValueError("bad head shapes")
+    if scale is None:
+        scale = 128 ** -0.5
+    N = len(cu) - 1
+    cu = np.ascontiguousarray(cu)
+    s0 = None
+    if initial_state is not None:
+        s0 = np.ascontiguousarray(
+            torch.as_tensor(initial_state).detach().cpu().double().numpy())
+        if s0.shape != (N, hv, 128, 128):
+            raise ValueError(f"initial_state shape {s0.shape} != {(N, hv, 128, 128)}")
+    out = np.zeros((Ttot, hv, 128), dtype=np.float64)
+    sf = np.zeros((N, hv, 128, 128), dtype=np.float64) if want_state else None
+    hs = None
+    if heads is not None:
+        hs = np.ascontiguousarray(np.asarray(list(heads), dtype=np.int32))
+
+    def ptr(t):
+        if t is None:
+            return None
+        if isinstance(t, torch.Tensor):
+            return ctypes.c_void_p(t.data_ptr())
+        return t.ctypes.data_as(ctypes.c_void_p)
+
+    lib = _load()
+    rc = lib.oracle_kda_recurrence(
+        _DT[dt], ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(cu), N, hqk, hv,
+        float(scale), int(bool(use_qk_l2norm)), ptr(s0), ptr(out), ptr(sf),
+        ptr(hs), 0 if hs is None else len(hs),
+        threads if threads else default_threads())
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out, sf
+
+
+def decode(q, k, v, g, beta, state_cache, state_indices, scale=None,
+           use_qk_l2norm=True, threads=None):
+    """One-token decode over a paged V-first state cache, as the recurrence.
+
+    q, k: [N, Hqk, 128]; v, g: [N, Hv, 128]; beta: [N, Hv];
+    state_cache: [slots, Hv, 128, 128]; state_indices: [N] (negative = skip).
+    Returns (out [N, Hv, 128] fp64, new_cache fp64 copy of the cache with the
+    touched rows replaced).  A skipped request has a zero output row and leaves
+    the cache alone.
+    """
+    idx = np.asarray(torch.as_tensor(state_indices).cpu().numpy(), dtype=np.int64)
+    cache = torch.as_tensor(state_cache).detach().cpu().double().numpy()
+    n = idx.shape[0]
+    live = np.nonzero(idx >= 0)[0]
+    out = np.zeros((n,) + tuple(v.shape[1:]), dtype=np.float64)
+    new_cache = cache.copy()
+    if live.size == 0:
+        return out, new_cache
+    sel = torch.as_tensor(live)
+    s0 = cache[idx[live]]
+    o, sf = recurrence(q[sel], k[sel], v[sel], g[sel], beta[sel],
+                       cu_seqlens=np.arange(live.size + 1, dtype=np.int64),
+                       scale=scale, use_qk_l2norm=use_qk_l2norm,
+                       initial_state=s0, threads=threads)
+    out[live] = o
+    new_cache[idx[live]] = sf
+    return out, new_cache
