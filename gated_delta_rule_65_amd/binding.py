@@ -1,0 +1,395 @@
+"""ctypes binding of libkda.so (include/kda.h).
+
+Argument marshalling only: tensors are checked for the shapes the ABI sizes
+describe (chunk_kda's checks on page "mate.kda"), outputs and the workspace are
+allocated with torch, and the call goes through the C ABI on torch's current
+stream.  Every step of the computation runs in the library's HIP kernels; there
+is no fallback of any kind, and a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+D = 128
+CHUNK = 64
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_OK, KDA_ERR_SHAPE, KDA_ERR_DTYPE, KDA_ERR_UNSUPPORTED = 0, 1, 2, 3
+KDA_ERR_WORKSPACE, KDA_ERR_HIP, KDA_ERR_ARG = 4, 5, 6
+PATH_AUTO, PATH_STAGED = 0, 1
+
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
+
+
+class KdaError(RuntimeError):
+    """The HIP runtime refused a launch, or the library is missing."""
+
+
+class ChunkArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+        ("total_tokens", ctypes.c_int64),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("hqk", ctypes.c_int32), ("hv", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("use_qk_l2norm", ctypes.c_int32),
+        ("initial_state", ctypes.c_void_p), ("final_state", ctypes.c_void_p),
+        ("state_cache", ctypes.c_void_p), ("state_indices", ctypes.c_void_p),
+        ("has_initial_state", ctypes.c_void_p), ("num_slots", ctypes.c_int32),
+        ("out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("path", ctypes.c_int32), ("groups", ctypes.c_int32),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+class WsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("chunk_offsets", "qg", "kg_t", "decay", "w", "u", "aqk", "scan", "total")
+                ] + [("max_chunks", ctypes.c_int64)]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32), ("n", ctypes.c_int32),
+        ("hqk", ctypes.c_int32), ("hv", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("use_qk_l2norm", ctypes.c_int32),
+        ("state_cache", ctypes.c_void_p), ("state_indices", ctypes.c_void_p),
+        ("num_slots", ctypes.c_int32), ("out", ctypes.c_void_p),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+_lock = threading.Lock()
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_ws_layout",
+           "kda_decode", "kda_status_str", "kda_last_error", "kda_version")
+
+
+def library_path() -> str:
+    return os.environ.get("KDA_LIBRARY", _LIB_PATH)
+
+
+def load_library():
+    """Load libkda.so once; raise KdaError if it is not built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = library_path()
+            if not os.path.exists(path):
+                raise KdaError(f"{path} is missing: build it with "
+                               "`python -m gated_delta_rule_65_amd.build`")
+            lib = ctypes.CDLL(path)
+            P = ctypes.POINTER
+            lib.kda_chunk_fwd.argtypes = [P(ChunkArgs)]
+            lib.kda_chunk_fwd.restype = ctypes.c_int
+            lib.kda_chunk_fwd_workspace_size.argtypes = [P(ChunkArgs), P(ctypes.c_size_t)]
+            lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_int
+            lib.kda_chunk_ws_layout.argtypes = [P(ChunkArgs), P(WsLayout)]
+            lib.kda_chunk_ws_layout.restype = ctypes.c_int
+            lib.kda_decode.argtypes = [P(DecodeArgs)]
+            lib.kda_decode.restype = ctypes.c_int
+            lib.kda_status_str.argtypes = [ctypes.c_int32]
+            lib.kda_status_str.restype = ctypes.c_char_p
+            lib.kda_last_error.argtypes = []
+            lib.kda_last_error.restype = ctypes.c_char_p
+            lib.kda_version.argtypes = []
+            lib.kda_version.restype = ctypes.c_char_p
+            _lib = lib
+    return _lib
+
+
+def _raise(lib, status: int):
+    msg = lib.kda_last_error().decode() or lib.kda_status_str(status).decode()
+    if status == KDA_ERR_DTYPE:
+        raise TypeError(msg)
+    if status == KDA_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    if status in (KDA_ERR_SHAPE, KDA_ERR_WORKSPACE, KDA_ERR_ARG):
+        raise ValueError(msg)
+    raise KdaError(msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    if dev.type != "cuda":
+        return None
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(cond, msg, exc=ValueError):
+    if not cond:
+        raise exc(msg)
+
+
+def _contig(name, t):
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    return t
+
+
+def _as_varlen(x, name, cu_seqlens):
+    """[B, T, H, 128] dense, or [S, H, 128] / [1, S, H, 128] with cu_seqlens."""
+    if cu_seqlens is None:
+        _need(x.dim() == 4, f"{name} must be a 4D tensor [B, T, H, 128].")
+        return x.reshape(x.shape[0] * x.shape[1], *x.shape[2:]), x.shape[0], x.shape[1]
+    if x.dim() == 3:
+        return x, 1, x.shape[0]
+    _need(x.dim() == 4 and x.shape[0] == 1,
+          f"{name} must be [S, H, 128] or [1, S, H, 128] for varlen.")
+    return x[0], 1, x.shape[1]
+
+
+def _chunk_struct(q, k, v, g, beta, out, cu, N, T, hqk, hv, scale, l2, init, fin, cache,
+                  idx, has_init, path, groups, stream):
+    a = ChunkArgs()
+    a.struct_size = ctypes.sizeof(ChunkArgs)
+    a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
+    a.dtype = _DTYPES[q.dtype]
+    a.num_seqs, a.total_tokens = N, T
+    a.cu_seqlens = _ptr(cu)
+    a.hqk, a.hv = hqk, hv
+    a.scale = scale
+    a.use_qk_l2norm = 1 if l2 else 0
+    a.initial_state, a.final_state = _ptr(init), _ptr(fin)
+    a.state_cache, a.state_indices, a.has_initial_state = _ptr(cache), _ptr(idx), _ptr(has_init)
+    a.num_slots = 0 if cache is None else cache.shape[0]
+    a.out = _ptr(out)
+    a.path, a.groups = path, groups
+    a.stream = stream
+    return a
+
+
+def _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
+                   use_qk_l2norm_in_kernel, output, final_state, state_cache, state_indices,
+                   has_initial_state):
+    varlen = cu_seqlens is not None
+    q3, B, Tq = _as_varlen(q, "q", cu_seqlens)
+    k3, _, _ = _as_varlen(k, "k", cu_seqlens)
+    v3, _, _ = _as_varlen(v, "v", cu_seqlens)
+    g3, _, _ = _as_varlen(g, "g", cu_seqlens)
+    if varlen and beta.dim() == 3:
+        _need(beta.shape[0] == 1, "beta must be [S, Hv] or [1, S, Hv] for varlen.")
+        beta = beta[0]
+    _need(q3.shape[-1] == D and k3.shape[-1] == D and v3.shape[-1] == D and g3.shape[-1] == D,
+          "chunk_kda currently requires D=128.")
+    _need(k.shape == q.shape, "k must have the same shape as q.")
+    _need(q3.shape[0] == v3.shape[0] == g3.shape[0],
+          "q, v and g must have matching [B, T] dimensions.")
+    _need(g.shape == v.shape, "g must have the same shape as v.")
+    hqk, hv = q3.shape[1], v3.shape[1]
+    _need(hv % hqk == 0, "GVA requires v/g heads to be divisible by q/k heads.")
+    T = q3.shape[0]
+    beta2 = beta.reshape(T, -1) if not varlen else beta
+    _need(tuple(beta2.shape) == (T, hv), "beta must have shape [B, T, Hv].")
+    _need(q.dtype in (torch.float32, torch.bfloat16),
+          "chunk_kda supports torch.float32 and torch.bfloat16 inputs.", TypeError)
+    for name, t in (("k", k), ("v", v), ("g", g), ("beta", beta)):
+        _need(t.dtype == q.dtype, "k, v, g and beta must have the same dtype as q.", TypeError)
+    dev = q.device
+    if varlen:
+        _need(cu_seqlens.dtype in (torch.int32, torch.int64),
+              "cu_seqlens must have dtype torch.int32 or torch.int64.", TypeError)
+        cu = cu_seqlens.to(device=dev, dtype=torch.int32).contiguous()
+        N = cu.numel() - 1
+    else:
+        cu = None
+        N = B
+    if scale is None:
+        scale = D ** -0.5
+    paged = state_cache is not None
+    init = fin = idx = hinit = None
+    if paged:
+        _need(initial_state is None and not output_final_state and final_state is None,
+              "state_cache replaces initial_state/output_final_state")
+        _need(state_indices is not None and has_initial_state is not None,
+              "state_cache needs state_indices and has_initial_state")
+        _need(state_cache.dtype == torch.float32, "state_cache must be float32", TypeError)
+        _need(state_cache.dim() == 4 and tuple(state_cache.shape[1:]) == (hv, D, D),
+              f"state_cache must be [slots, {hv}, 128, 128]")
+        _contig("state_cache", state_cache)
+        idx = state_indices.to(device=dev, dtype=torch.int32).contiguous()
+        hinit = has_initial_state.to(device=dev, dtype=torch.uint8).contiguous()
+        _need(idx.numel() == N and hinit.numel() == N,
+              "state_indices and has_initial_state need one entry per sequence")
+    else:
+        if initial_state is not None:
+            _need(initial_state.dtype == torch.float32, "initial_state must be float32",
+                  NotImplementedError)
+            _need(tuple(initial_state.shape) == (N, hv, D, D),
+                  f"initial_state must be [{N}, {hv}, 128, 128]")
+            init = _contig("initial_state", initial_state)
+        if output_final_state:
+            if final_state is None:
+                final_state = torch.empty((N, hv, D, D), device=dev, dtype=torch.float32)
+            _need(final_state.dtype == torch.float32, "final_state must be float32",
+                  NotImplementedError)
+            _need(tuple(final_state.shape) == (N, hv, D, D),
+                  f"final_state must be [{N}, {hv}, 128, 128]")
+            fin = _contig("final_state", final_state)
+    if output is None:
+        output = torch.empty_like(v)
+    _need(output.shape == v.shape or (varlen and output.shape == v3.shape),
+          "output must have the same shape as v.")
+    _need(output.dtype == q.dtype, "output must have the same dtype as q.", TypeError)
+    for name, t in (("q", q3), ("k", k3), ("v", v3), ("g", g3), ("beta", beta2),
+                    ("output", output)):
+        _contig(name, t)
+        _need(t.device == dev, f"{name} must be on {dev}")
+    return dict(q=q3, k=k3, v=v3, g=g3, beta=beta2, out=output, cu=cu, N=N, T=T, hqk=hqk,
+                hv=hv, scale=float(scale), l2=bool(use_qk_l2norm_in_kernel), init=init,
+                fin=fin, cache=state_cache if paged else None, idx=idx, has_init=hinit)
+
+
+def _run_chunk(p, path=PATH_AUTO, groups=0, workspace=None, keep=None):
+    lib = load_library()
+    dev = p["q"].device
+    a = _chunk_struct(p["q"], p["k"], p["v"], p["g"], p["beta"], p["out"], p["cu"], p["N"],
+                      p["T"], p["hqk"], p["hv"], p["scale"], p["l2"], p["init"], p["fin"],
+                      p["cache"], p["idx"], p["has_init"], path, groups, _stream(dev))
+    nbytes = ctypes.c_size_t(0)
+    st = lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(nbytes))
+    if st != KDA_OK:
+        _raise(lib, st)
+    if workspace is None:
+        workspace = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=dev)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib.kda_chunk_fwd(ctypes.byref(a))
+    if st != KDA_OK:
+        _raise(lib, st)
+    if keep is not None:
+        keep["workspace"] = workspace
+        keep["args"] = a
+    return a
+
+
+def chunk_kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False,
+              cu_seqlens=None, use_qk_l2norm_in_kernel=True, output=None, final_state=None,
+              state_cache=None, state_indices=None, has_initial_state=None, groups=0,
+              workspace=None):
+    """Chunked KDA forward (chunk_kda's argument set, plus the paged state of
+    fused_kda_chunk).  Returns out, or (out, final_state) when
+    output_final_state; in paged mode the final states land in state_cache."""
+    p = _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state,
+                       cu_seqlens, use_qk_l2norm_in_kernel, output, final_state,
+                       state_cache, state_indices, has_initial_state)
+    _run_chunk(p, groups=groups, workspace=workspace)
+    out = p["out"]
+    if output_final_state:
+        return out, p["fin"]
+    return out
+
+
+def chunk_stages(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=None,
+                 use_qk_l2norm_in_kernel=True, groups=1):
+    """Run the staged path and return its intermediates (views of the
+    workspace): chunk_offsets, qg, kg_t, decay, w, u, aqk, plus out and the
+    final state.  For tests and tools."""
+    p = _prepare_chunk(q, k, v, g, beta, scale, initial_state, True, cu_seqlens,
+                       use_qk_l2norm_in_kernel, None, None, None, None, None)
+    keep = {}
+    a = _run_chunk(p, path=PATH_STAGED, groups=groups, keep=keep)
+    lib = load_library()
+    lay = WsLayout()
+    st = lib.kda_chunk_ws_layout(ctypes.byref(a), ctypes.byref(lay))
+    if st != KDA_OK:
+        _raise(lib, st)
+    ws = keep["workspace"]
+    dt = p["q"].dtype
+    es = 4 if dt == torch.float32 else 2
+    T, H, N, mc = p["T"], p["hv"], p["N"], lay.max_chunks
+
+    def view(off, shape, dtype, esz):
+        n = 1
+        for s in shape:
+            n *= s
+        return ws[off:off + n * esz].view(dtype).view(*shape)
+
+    return dict(
+        out=p["out"], final_state=p["fin"],
+        chunk_offsets=view(lay.chunk_offsets, (N + 1,), torch.int32, 4),
+        qg=view(lay.qg, (T, H, D), dt, es),
+        kg_t=view(lay.kg_t, (mc, H, D, CHUNK), dt, es),
+        decay=view(lay.decay, (mc, H, D), torch.float32, 4),
+        w=view(lay.w, (T, H, D), dt, es),
+        u=view(lay.u, (T, H, D), dt, es),
+        aqk=view(lay.aqk, (T, H, CHUNK), dt, es),
+    )
+
+
+def kda_decode(q, k, v, g, beta, state_cache, state_indices=None, scale=None,
+               use_qk_l2norm=True, output=None):
+    """One token per request over the paged V-first fp32 state cache, updated
+    in place.  q, k: [N, Hqk, 128] or [N, 1, Hqk, 128]; v, g: [N, Hv, 128] or
+    [N, 1, Hv, 128]; beta: [N, Hv] or [N, 1, Hv]; state_cache
+    [slots, Hv, 128, 128] fp32; state_indices [N] int32/int64 (negative = skip).
+    Returns out shaped like v."""
+    shape_v = v.shape
+    if q.dim() == 4:
+        _need(q.shape[1] == 1, "kda_decode takes one token per request (T = 1)",
+              NotImplementedError)
+        q, k, v, g = q[:, 0], k[:, 0], v[:, 0], g[:, 0]
+        if beta.dim() == 3:
+            beta = beta[:, 0]
+    _need(q.dim() == 3 and q.shape[-1] == D, "q must be [N, Hqk, 128]")
+    _need(k.shape == q.shape, "k must match q")
+    n, hqk = q.shape[0], q.shape[1]
+    _need(v.dim() == 3 and v.shape[0] == n and v.shape[-1] == D, "v must be [N, Hv, 128]")
+    hv = v.shape[1]
+    _need(g.shape == v.shape, "g must have the same shape as v")
+    _need(hv % hqk == 0, f"Expected HV to be divisible by H, got HV={hv}, H={hqk}.")
+    _need(tuple(beta.shape) == (n, hv), "beta must be [N, Hv]")
+    _need(q.dtype in _DTYPES, f"unsupported dtype {q.dtype}", TypeError)
+    for name, t in (("k", k), ("v", v), ("g", g), ("beta", beta)):
+        _need(t.dtype == q.dtype, f"{name} must have q's dtype", TypeError)
+    _need(state_cache.dtype == torch.float32, "state_cache must be float32",
+          NotImplementedError)
+    _need(state_cache.dim() == 4 and tuple(state_cache.shape[1:]) == (hv, D, D),
+          "state must have shape [pool, HV, V, K]")
+    _need(state_cache.shape[0] > 0, "state pool must contain at least one slot.")
+    dev = q.device
+    idx = None
+    if state_indices is not None:
+        _need(state_indices.dim() == 1 and state_indices.shape[0] == n,
+              f"state_indices must have shape [{n}]")
+        _need(state_indices.dtype in (torch.int32, torch.int64),
+              "state_indices must have dtype torch.int32 or torch.int64", ValueError)
+        idx = state_indices.to(device=dev, dtype=torch.int32).contiguous()
+    if output is None:
+        output = torch.empty((n, hv, D), dtype=q.dtype, device=dev)
+    _need(output.numel() == n * hv * D and output.dtype == q.dtype,
+          "output must be [N, Hv, 128] of q's dtype")
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta),
+                    ("state_cache", state_cache), ("output", output)):
+        _contig(name, t)
+        _need(t.device == dev, f"{name} must be on {dev}")
+    lib = load_library()
+    a = DecodeArgs()
+    a.struct_size = ctypes.sizeof(DecodeArgs)
+    a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
+    a.dtype = _DTYPES[q.dtype]
+    a.n, a.hqk, a.hv = n, hqk, hv
+    a.scale = float(D ** -0.5 if scale is None else scale)
+    a.use_qk_l2norm = 1 if use_qk_l2norm else 0
+    a.state_cache = _ptr(state_cache)
+    a.state_indices = _ptr(idx)
+    a.num_slots = state_cache.shape[0]
+    a.out = _ptr(output)
+    a.stream = _stream(dev)
+    st = lib.kda_decode(ctypes.byref(a))
+    if st != KDA_OK:
+        _raise(lib, st)
+    return output.view(shape_v) if output.numel() == v.numel() else output

@@ -1,0 +1,229 @@
+// C-ABI entry points of the KDA library: argument checks, workspace carving,
+// launch plans.  Every check runs on the host before anything is queued; a
+// failed check returns a status and writes nothing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/kda.h"
+#include "kda_launch.hpp"
+
+#define KDA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kda_status fail(kda_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+kda_status ok() {
+  g_err[0] = '\0';
+  return KDA_OK;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t elem_size(int dtype) { return dtype == KDA_F32 ? 4 : 2; }
+
+// Shape and mode checks of the chunked forward (chunk_kda's checks, in the
+// terms of this ABI).  Pointers are checked only where the call will read or
+// write through them.
+kda_status check_chunk(const kda_chunk_args* a, bool need_ptrs) {
+  if (!a) return fail(KDA_ERR_ARG, "args is NULL");
+  if (a->struct_size != sizeof(kda_chunk_args))
+    return fail(KDA_ERR_ARG, "struct_size %zu != sizeof(kda_chunk_args) %zu",
+                a->struct_size, sizeof(kda_chunk_args));
+  if (a->dtype != KDA_F32 && a->dtype != KDA_BF16) {
+    if (a->dtype == KDA_F16)
+      return fail(KDA_ERR_DTYPE, "the chunked forward takes fp32 or bf16 inputs");
+    return fail(KDA_ERR_DTYPE, "unknown dtype %d", a->dtype);
+  }
+  if (a->num_seqs < 0) return fail(KDA_ERR_SHAPE, "num_seqs must be >= 0");
+  if (a->total_tokens < 0) return fail(KDA_ERR_SHAPE, "total_tokens must be >= 0");
+  if (a->total_tokens > (int64_t)INT32_MAX)
+    return fail(KDA_ERR_UNSUPPORTED, "total_tokens above 2^31-1");
+  if (a->hqk <= 0 || a->hv <= 0) return fail(KDA_ERR_SHAPE, "head counts must be > 0");
+  if (a->hv % a->hqk != 0)
+    return fail(KDA_ERR_SHAPE, "GVA needs hv (%d) divisible by hqk (%d)", a->hv, a->hqk);
+  if (!isfinite(a->scale)) return fail(KDA_ERR_SHAPE, "scale must be finite");
+  if (a->cu_seqlens == nullptr) {
+    if (a->num_seqs == 0 && a->total_tokens != 0)
+      return fail(KDA_ERR_SHAPE, "dense batch with no sequences but %lld tokens",
+                  (long long)a->total_tokens);
+    if (a->num_seqs > 0 && a->total_tokens % a->num_seqs != 0)
+      return fail(KDA_ERR_SHAPE, "dense batch: total_tokens %% num_seqs != 0");
+  }
+  const bool paged = a->state_cache != nullptr;
+  if (paged) {
+    if (a->initial_state || a->final_state)
+      return fail(KDA_ERR_SHAPE, "state_cache replaces initial_state/final_state");
+    if (a->num_seqs > 0 && (!a->state_indices || !a->has_initial_state))
+      return fail(KDA_ERR_SHAPE, "state_cache needs state_indices and has_initial_state");
+    if (a->num_slots <= 0) return fail(KDA_ERR_SHAPE, "num_slots must be > 0");
+  } else if (a->state_indices || a->has_initial_state) {
+    return fail(KDA_ERR_SHAPE, "state_indices/has_initial_state need a state_cache");
+  }
+  if (a->path != KDA_PATH_AUTO && a->path != KDA_PATH_STAGED)
+    return fail(KDA_ERR_UNSUPPORTED, "unknown path %d", a->path);
+  if (a->groups < 0) return fail(KDA_ERR_SHAPE, "groups must be >= 0");
+  if (a->groups > 64) return fail(KDA_ERR_UNSUPPORTED, "groups above 64");
+  if (need_ptrs && a->total_tokens > 0) {
+    if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->out)
+      return fail(KDA_ERR_ARG, "q, k, v, g, beta and out must be non-NULL");
+  }
+  return KDA_OK;
+}
+
+int64_t max_chunks_of(const kda_chunk_args* a) {
+  return a->total_tokens / KDA_CHUNK + a->num_seqs;
+}
+
+// Group count of the parallel chunk-group scan.  The scan walks each group
+// twice (pass one with 256 columns, pass two with 128) and composes the group
+// transfers in between, so it pays only when (sequence, head) units are too
+// few to fill the device and the chains are long.
+int resolve_groups(const kda_chunk_args* a) {
+  if (a->groups > 0) return a->groups;
+  return 1;
+}
+
+kda_status layout_of(const kda_chunk_args* a, kda_ws_layout* L) {
+  memset(L, 0, sizeof(*L));
+  const size_t es = elem_size(a->dtype);
+  const size_t T = (size_t)a->total_tokens, H = (size_t)a->hv;
+  const int64_t mc = max_chunks_of(a);
+  const int groups = resolve_groups(a);
+  size_t off = 0;
+  L->max_chunks = mc;
+  L->chunk_offsets = off;
+  off = align_up(off + sizeof(int32_t) * ((size_t)a->num_seqs + 1), 256);
+  L->qg = off;
+  off = align_up(off + T * H * KDA_HEAD_DIM * es, 256);
+  L->kg_t = off;
+  off = align_up(off + (size_t)mc * H * KDA_HEAD_DIM * KDA_CHUNK * es, 256);
+  L->decay = off;
+  off = align_up(off + (size_t)mc * H * KDA_HEAD_DIM * sizeof(float), 256);
+  L->w = off;
+  off = align_up(off + T * H * KDA_HEAD_DIM * es, 256);
+  L->u = off;
+  off = align_up(off + T * H * KDA_HEAD_DIM * es, 256);
+  L->aqk = off;
+  off = align_up(off + T * H * KDA_CHUNK * es, 256);
+  L->scan = off;
+  if (groups > 1) {
+    // per (group, sequence, head): transfer P, partial state B, start state
+    const size_t planes = (size_t)groups * (size_t)a->num_seqs * H;
+    off = align_up(off + planes * 3 * KDA_HEAD_DIM * KDA_HEAD_DIM * sizeof(float), 256);
+  }
+  L->total = off;
+  return KDA_OK;
+}
+
+}  // namespace
+
+KDA_API const char* kda_status_str(int32_t s) {
+  switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_SHAPE: return "inconsistent shapes or modes";
+    case KDA_ERR_DTYPE: return "unsupported dtype";
+    case KDA_ERR_UNSUPPORTED: return "unsupported request";
+    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERR_HIP: return "HIP launch failure";
+    case KDA_ERR_ARG: return "bad argument";
+    default: return "unknown status";
+  }
+}
+
+KDA_API const char* kda_last_error(void) { return g_err; }
+
+KDA_API const char* kda_version(void) { return "kda-mi355x 0.1 (gfx950)"; }
+
+KDA_API kda_status kda_chunk_fwd_workspace_size(const kda_chunk_args* a, size_t* bytes) {
+  if (!bytes) return fail(KDA_ERR_ARG, "bytes is NULL");
+  kda_status s = check_chunk(a, false);
+  if (s != KDA_OK) return s;
+  kda_ws_layout L;
+  layout_of(a, &L);
+  *bytes = L.total;
+  return ok();
+}
+
+KDA_API kda_status kda_chunk_ws_layout(const kda_chunk_args* a, kda_ws_layout* layout) {
+  if (!layout) return fail(KDA_ERR_ARG, "layout is NULL");
+  kda_status s = check_chunk(a, false);
+  if (s != KDA_OK) return s;
+  layout_of(a, layout);
+  return ok();
+}
+
+KDA_API kda_status kda_chunk_fwd(const kda_chunk_args* a) {
+  kda_status s = check_chunk(a, true);
+  if (s != KDA_OK) return s;
+  kda_ws_layout W;
+  layout_of(a, &W);
+  if (a->workspace_bytes < W.total || (W.total > 0 && a->workspace == nullptr))
+    return fail(KDA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", W.total,
+                a->workspace_bytes);
+  if (a->num_seqs == 0) return ok();
+  char* ws = (char*)a->workspace;
+  kda::ChunkLaunch L;
+  memset(&L, 0, sizeof(L));
+  L.q = a->q; L.k = a->k; L.v = a->v; L.g = a->g; L.beta = a->beta;
+  L.cu = a->cu_seqlens;
+  L.dtype = a->dtype; L.num_seqs = a->num_seqs; L.hqk = a->hqk; L.hv = a->hv;
+  L.use_l2 = a->use_qk_l2norm ? 1 : 0;
+  L.total_tokens = a->total_tokens; L.max_chunks = W.max_chunks;
+  L.scale = a->scale;
+  L.init = a->initial_state; L.fin = a->final_state;
+  L.cache = a->state_cache; L.slots = a->state_indices; L.has_init = a->has_initial_state;
+  L.num_slots = a->num_slots;
+  L.out = a->out;
+  L.chunk_offsets = (int32_t*)(ws + W.chunk_offsets);
+  L.qg = ws + W.qg; L.kg_t = ws + W.kg_t; L.decay = (float*)(ws + W.decay);
+  L.w = ws + W.w; L.u = ws + W.u; L.aqk = ws + W.aqk;
+  L.groups = resolve_groups(a);
+  L.scan = L.groups > 1 ? (float*)(ws + W.scan) : nullptr;
+  L.stream = a->stream;
+  hipError_t e = kda::launch_chunk_staged(L);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+KDA_API kda_status kda_decode(const kda_decode_args* a) {
+  if (!a) return fail(KDA_ERR_ARG, "args is NULL");
+  if (a->struct_size != sizeof(kda_decode_args))
+    return fail(KDA_ERR_ARG, "struct_size %zu != sizeof(kda_decode_args) %zu",
+                a->struct_size, sizeof(kda_decode_args));
+  if (a->dtype != KDA_F32 && a->dtype != KDA_BF16 && a->dtype != KDA_F16)
+    return fail(KDA_ERR_DTYPE, "unknown dtype %d", a->dtype);
+  if (a->n < 0) return fail(KDA_ERR_SHAPE, "n must be >= 0");
+  if (a->hqk <= 0 || a->hv <= 0) return fail(KDA_ERR_SHAPE, "head counts must be > 0");
+  if (a->hv % a->hqk != 0)
+    return fail(KDA_ERR_SHAPE, "GVA needs hv (%d) divisible by hqk (%d)", a->hv, a->hqk);
+  if (!isfinite(a->scale)) return fail(KDA_ERR_SHAPE, "scale must be finite");
+  if (a->num_slots <= 0) return fail(KDA_ERR_SHAPE, "state pool must have at least one slot");
+  if (!a->state_indices && a->num_slots < a->n)
+    return fail(KDA_ERR_SHAPE, "state pool must contain at least %d slots, got %d", a->n,
+                a->num_slots);
+  if ((size_t)a->n * (size_t)a->hv > 0x7fffffffu)
+    return fail(KDA_ERR_UNSUPPORTED, "n * hv above 2^31-1");
+  if (a->n == 0) return ok();
+  if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->out || !a->state_cache)
+    return fail(KDA_ERR_ARG, "q, k, v, g, beta, out and state_cache must be non-NULL");
+  kda::DecodeLaunch L;
+  L.q = a->q; L.k = a->k; L.v = a->v; L.g = a->g; L.beta = a->beta;
+  L.cache = a->state_cache; L.idx = a->state_indices; L.out = a->out;
+  L.dtype = a->dtype; L.n = a->n; L.hqk = a->hqk; L.hv = a->hv;
+  L.use_l2 = a->use_qk_l2norm ? 1 : 0; L.num_slots = a->num_slots; L.scale = a->scale;
+  L.stream = a->stream;
+  hipError_t e = kda::launch_decode(L);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}

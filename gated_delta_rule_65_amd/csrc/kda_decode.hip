@@ -1,0 +1,140 @@
+// One-token KDA decode over a paged, V-first fp32 state cache, in place.
+//
+// Per (request n, value head h) with slot = state_indices[n] (identity when
+// no index array is given), every state row v (one value channel; the row
+// holds S[:, v] over the 128 key channels) evolves on its own:
+//   row   <- exp(g) * row                     (decay on the key channels)
+//   u_v    = b * (v[v] - row . kn)            (delta residual)
+//   row   <- row + u_v * kn                   (rank-one write)
+//   o[v]   = scale * row . qn                 (read after the write)
+// which is gated_delta_rule_decode's in-place V-first fp32 case (page
+// "mate.kda") with the per-row solve of KdaTcVerify (page
+// "vllm.models.kimi_k3.nvidia.recoverssm.cutedsl.verify") at window 1.  A
+// negative slot produces a zero output row and no state traffic (the null
+// slot of KdaTcVerify); a slot at or past the pool size is treated the same
+// way so that a bad index can never address outside the cache.
+//
+// Mapping (HBM-bound: 64 KiB read + 64 KiB written per unit): one 256-thread
+// workgroup per unit; 16 lanes (one DPP row) own one state row, each lane
+// holding 8 key channels {4j..4j+3} and {64+4j..64+4j+3} (j = lane % 16) so
+// that each float4 access of a 16-lane group is 256 contiguous bytes.  The
+// 8 row-steps of a thread are all loaded before any arithmetic, which keeps
+// 16 KiB per wave in flight.  The two dot products per row are 16-lane DPP
+// reductions; (row . qn) after the write is formed as
+// (decayed row . qn) + u_v (kn . qn) so that one reduction pass suffices.
+#include "kda_common.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+template <typename T>
+__global__ __launch_bounds__(256) void decode_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ g, const T* __restrict__ beta, float* __restrict__ cache,
+    const int32_t* __restrict__ idx, T* __restrict__ out, int hqk, int hv, float scale,
+    int use_l2, int num_slots) {
+  const int unit = blockIdx.x;
+  const int req = unit / hv, h = unit - req * hv;
+  const int hq = h / (hv / hqk);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 15, rsub = lane >> 4;
+  T* o = out + ((size_t)req * hv + h) * D;
+  const int slot = idx ? idx[req] : req;
+  if (slot < 0 || slot >= num_slots) {
+    if (tid < D) o[tid] = from_f32<T>(0.0f);
+    return;
+  }
+  float* st = cache + ((size_t)slot * hv + h) * (size_t)(D * D);
+
+  // Issue the state loads first: rows r = 16 s + 4 wave + rsub, s = 0..7.
+  float4 hs[8][2];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int r = 16 * s + 4 * wave + rsub;
+    const float4* row = reinterpret_cast<const float4*>(st + r * D);
+    hs[s][0] = row[j];
+    hs[s][1] = row[16 + j];
+  }
+
+  const T* qp = q + ((size_t)req * hqk + hq) * D;
+  const T* kp = k + ((size_t)req * hqk + hq) * D;
+  const T* gp = g + ((size_t)req * hv + h) * D;
+  const T* vp = v + ((size_t)req * hv + h) * D;
+  float qv[8], kv[8], al[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = (e < 4) ? (4 * j + e) : (64 + 4 * j + e - 4);
+    qv[e] = to_f32(qp[c]);
+    kv[e] = to_f32(kp[c]);
+    al[e] = exp2_fast(to_f32(gp[c]) * LOG2E);
+  }
+  float vr[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) vr[s] = to_f32(vp[16 * s + 4 * wave + rsub]);
+  const float b = sigmoid(to_f32(beta[(size_t)req * hv + h]));
+
+  if (use_l2) {
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sq += qv[e] * qv[e];
+      sk += kv[e] * kv[e];
+    }
+    sq = row_sum16(sq);
+    sk = row_sum16(sk);
+    const float rq = rsqrtf(sq + L2_EPS), rk = rsqrtf(sk + L2_EPS);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qv[e] *= rq;
+      kv[e] *= rk;
+    }
+  }
+  float kq = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) kq += kv[e] * qv[e];
+  kq = row_sum16(kq);
+
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    float x[8] = {hs[s][0].x, hs[s][0].y, hs[s][0].z, hs[s][0].w,
+                  hs[s][1].x, hs[s][1].y, hs[s][1].z, hs[s][1].w};
+    float pk = 0.f, pq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] *= al[e];
+      pk += x[e] * kv[e];
+      pq += x[e] * qv[e];
+    }
+    pk = row_sum16(pk);
+    pq = row_sum16(pq);
+    const float u = b * (vr[s] - pk);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] += u * kv[e];
+    const int r = 16 * s + 4 * wave + rsub;
+    float4* row = reinterpret_cast<float4*>(st + r * D);
+    row[j] = make_float4(x[0], x[1], x[2], x[3]);
+    row[16 + j] = make_float4(x[4], x[5], x[6], x[7]);
+    if (j == 0) o[r] = from_f32<T>(scale * (pq + u * kq));
+  }
+}
+
+template <typename T>
+static hipError_t launch_decode_t(const DecodeLaunch& L) {
+  const dim3 grid((unsigned)((size_t)L.n * L.hv)), block(256);
+  hipLaunchKernelGGL(decode_kernel<T>, grid, block, 0, (hipStream_t)L.stream,
+                     (const T*)L.q, (const T*)L.k, (const T*)L.v, (const T*)L.g,
+                     (const T*)L.beta, L.cache, L.idx, (T*)L.out, L.hqk, L.hv, L.scale,
+                     L.use_l2, L.num_slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeLaunch& L) {
+  switch (L.dtype) {
+    case 0: return launch_decode_t<float>(L);
+    case 1: return launch_decode_t<bf16>(L);
+    default: return launch_decode_t<_Float16>(L);
+  }
+}
+
+}  // namespace kda

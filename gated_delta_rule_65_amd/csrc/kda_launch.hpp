@@ -1,0 +1,45 @@
+// Host-side launch descriptors between the C-ABI layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeLaunch {
+  const void *q, *k, *v, *g, *beta;
+  float* cache;
+  const int32_t* idx;
+  void* out;
+  int dtype, n, hqk, hv, use_l2, num_slots;
+  float scale;
+  void* stream;
+};
+hipError_t launch_decode(const DecodeLaunch& L);
+
+// The staged chunked forward: every buffer already carved from the workspace.
+struct ChunkLaunch {
+  const void *q, *k, *v, *g, *beta;
+  const int32_t* cu;          // [N+1] (device) or NULL for dense
+  int dtype, num_seqs, hqk, hv, use_l2;
+  int64_t total_tokens, max_chunks;
+  float scale;
+  const float* init;          // dense initial state or NULL
+  float* fin;                 // dense final state or NULL
+  float* cache;               // paged state or NULL
+  const int32_t* slots;
+  const uint8_t* has_init;
+  int num_slots;
+  void* out;
+  // workspace pieces
+  int32_t* chunk_offsets;     // [N+1]
+  void *qg, *kg_t, *w, *u, *aqk;
+  float* decay;
+  float* scan;                // group-scan planes (groups > 1)
+  int groups;
+  int max_seq_len_bound;      // upper bound of any sequence length (host-known)
+  void* stream;
+};
+hipError_t launch_chunk_staged(const ChunkLaunch& L);
+
+}  // namespace kda

@@ -1,0 +1,202 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) KDA library: the Kimi Delta Attention
+ * chunked forward and the one-token paged decode.
+ *
+ * What is computed.  For each sequence n, value head h and token t (query/key
+ * head hq = h / (Hv / Hqk): contiguous groups of Hv / Hqk value heads share one
+ * query/key head), with K = V = 128:
+ *
+ *   qn = q / sqrt(sum(q^2) + 1e-6),  kn likewise       (when use_qk_l2norm)
+ *   b  = sigmoid(beta)                                   (beta is a logit)
+ *   S  = (I - b kn kn^T) diag(exp(g)) S + b kn v^T       (S is K x V)
+ *   o  = scale * S^T qn                                  (after the write)
+ *
+ * g is a natural-log decay per key channel, expected in [-5, 0] per token
+ * (the default lower bound of the gate); results for larger |g| are
+ * unspecified.  States cross this interface "V-first": a state buffer
+ * [.., 128 (V), 128 (K)] holds S[k][v] at element [v][k].
+ *
+ * Sources (pages, by title):
+ *  - "mate.kda" (MATE 0.2.5): chunk_kda's argument set, shapes and checks
+ *    (D = 128, GVA divisibility, beta shape, dtype equality, default scale
+ *    128^-0.5, optional initial/final state, varlen cu_seqlens with B = 1);
+ *    gated_delta_rule_decode's V-first state pool [pool, HV, V, K], the in
+ *    place final state, and state_indices smaller than the pool size.
+ *  - "vllm.models.kimi_k3.amd.ops.kda_chunk": fused_kda_chunk's paged state
+ *    (state_cache / state_indices / has_initial_state replacing the initial
+ *    and final state), the caller-owned group workspace, and 64-token chunks
+ *    that restart at every sequence start.
+ *  - "vllm.models.kimi_k3.nvidia.recoverssm.cutedsl.verify" (KdaTcVerify):
+ *    the L2-norm epsilon, the sigmoid of the raw beta, and a null slot that
+ *    produces zero output without touching the state.
+ *
+ * Conventions shared by every entry point.
+ *  - Pointers marked (device) are HIP device pointers on the current device;
+ *    (host) pointers are read before the call returns.  All tensors are
+ *    dense, row-major and contiguous.
+ *  - The library allocates nothing.  Every buffer, the workspace included,
+ *    is owned by the caller and must outlive the queued work.
+ *  - Arguments are checked on the host before anything is queued.  On an
+ *    error nothing is launched, nothing is written, and a status other than
+ *    KDA_OK comes back; kda_last_error() then holds a message for the
+ *    calling thread.  Values that live in device memory (cu_seqlens,
+ *    state_indices, has_initial_state) cannot be checked without a sync and
+ *    are the caller's contract, as stated per field.
+ *  - Work is queued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    default stream).  A launch failure returns KDA_ERR_HIP.
+ *  - Outputs must not overlap inputs.  The only buffer updated in place is
+ *    the paged state cache.
+ *  - Calls are reentrant; two calls may run concurrently on different
+ *    streams as long as they share no output, cache row or workspace.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_HEAD_DIM 128   /* K = V = 128, the only head size (chunk_kda's D) */
+#define KDA_CHUNK 64       /* tokens per chunk of the chunked form */
+
+/* Element type of q, k, v, g, beta and out (one type for all of them). */
+typedef enum kda_dtype {
+  KDA_F32 = 0,   /* fp32 inputs; MFMA operands carried as split bf16 pairs */
+  KDA_BF16 = 1,  /* bf16 inputs; bf16 MFMA with fp32 accumulation */
+  KDA_F16 = 2    /* fp16 inputs (decode only) */
+} kda_dtype;
+
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_SHAPE = 1,       /* inconsistent sizes (chunk_kda raises ValueError) */
+  KDA_ERR_DTYPE = 2,       /* unsupported element type (TypeError) */
+  KDA_ERR_UNSUPPORTED = 3, /* a valid request this library does not serve */
+  KDA_ERR_WORKSPACE = 4,   /* workspace missing or too small */
+  KDA_ERR_HIP = 5,         /* the HIP runtime refused a launch */
+  KDA_ERR_ARG = 6          /* a required pointer is NULL, or a bad struct */
+} kda_status;
+
+/* Execution plan of the chunked forward. */
+typedef enum kda_path {
+  KDA_PATH_AUTO = 0,    /* the library picks */
+  KDA_PATH_STAGED = 1   /* prep -> wy -> walk, intermediates in the workspace */
+} kda_path;
+
+/*
+ * kda_chunk_args -- the chunked forward (chunk_kda's problem statement).
+ *
+ * Token layout: varlen, T_tot = total_tokens rows.  Sequence n owns rows
+ * [cu_seqlens[n], cu_seqlens[n+1]).  With cu_seqlens == NULL the batch is
+ * dense: num_seqs sequences of total_tokens / num_seqs rows each.
+ */
+typedef struct kda_chunk_args {
+  size_t struct_size;          /* = sizeof(kda_chunk_args) */
+  const void *q;               /* (device) [T_tot, Hqk, 128] dtype */
+  const void *k;               /* (device) [T_tot, Hqk, 128] dtype */
+  const void *v;               /* (device) [T_tot, Hv, 128] dtype */
+  const void *g;               /* (device) [T_tot, Hv, 128] dtype, log-decay <= 0 */
+  const void *beta;            /* (device) [T_tot, Hv] dtype, logits */
+  int32_t dtype;               /* kda_dtype: KDA_F32 or KDA_BF16 */
+  int32_t num_seqs;            /* N >= 0 */
+  int64_t total_tokens;        /* T_tot >= 0 */
+  const int32_t *cu_seqlens;   /* (device) [N+1] non-decreasing, cu[0] = 0,
+                                  cu[N] = T_tot; or NULL (dense) */
+  int32_t hqk, hv;             /* heads; hv % hqk == 0 */
+  float scale;                 /* output scale (128^-0.5 is the usual value) */
+  int32_t use_qk_l2norm;       /* 1: L2-normalise q and k in the kernels */
+  /* dense state mode (both optional, fp32, V-first) */
+  const float *initial_state;  /* (device) [N, Hv, 128, 128] or NULL (= zero) */
+  float *final_state;          /* (device) [N, Hv, 128, 128] or NULL */
+  /* paged state mode (replaces initial_state / final_state) */
+  float *state_cache;          /* (device) [num_slots, Hv, 128, 128] or NULL */
+  const int32_t *state_indices;     /* (device) [N]; row per sequence, distinct;
+                                       < 0 = no state I/O for that sequence */
+  const uint8_t *has_initial_state; /* (device) [N]; 0 = start from zero */
+  int32_t num_slots;           /* rows of state_cache (> every index used) */
+  void *out;                   /* (device) [T_tot, Hv, 128] dtype */
+  void *workspace;             /* (device) >= kda_chunk_fwd_workspace_size() */
+  size_t workspace_bytes;
+  int32_t path;                /* kda_path */
+  int32_t groups;              /* chunk groups per sequence: 0 = auto, 1 = none,
+                                  >= 2 = that many (the parallel group scan) */
+  void *stream;                /* hipStream_t or NULL */
+} kda_chunk_args;
+
+/*
+ * Workspace bytes the call described by `a` needs (0 is possible), written
+ * to *bytes.  Reads only sizes and the path/groups fields.
+ */
+kda_status kda_chunk_fwd_workspace_size(const kda_chunk_args *a, size_t *bytes);
+
+/*
+ * The chunked forward.  Writes out; writes final_state (dense mode) or the
+ * state_cache rows of the listed sequences (paged mode: read when
+ * has_initial_state[n] != 0, then overwritten with the final state).  A
+ * sequence of length 0 passes its start state through unchanged.  In paged
+ * mode a sequence with state_indices[n] < 0 gets zero output rows and no
+ * state I/O.  Chunks are 64 tokens from each sequence start; the last chunk
+ * of a sequence may be shorter.
+ */
+kda_status kda_chunk_fwd(const kda_chunk_args *a);
+
+/*
+ * Layout of the staged path's intermediates inside the workspace, for tests
+ * and tools.  Offsets are in bytes from the workspace base; "chunks" is the
+ * bound n_chunks_max = total_tokens / 64 + num_seqs used for sizing.
+ *   chunk_offsets  int32 [N + 1]: first chunk index of each sequence
+ *   qg             [T_tot, Hv, 128]  q-type: qn * exp(G) (G = in-chunk
+ *                                    cumulative log-decay, inclusive)
+ *   kg_t           [chunks, Hv, 128, 64] q-type: (kn * exp(G_last - G))^T
+ *   decay          fp32 [chunks, Hv, 128]: exp(G_last)
+ *   w, u           [T_tot, Hv, 128]  q-type: WY factors T (b kn exp(G)), T (b v)
+ *   aqk            [T_tot, Hv, 64]   q-type: sum_c qn_t kn_i exp(G_t - G_i),
+ *                                    i <= t inside the chunk, 0 above
+ * (q-type = bf16 for KDA_BF16 inputs, fp32 for KDA_F32.)
+ */
+typedef struct kda_ws_layout {
+  size_t chunk_offsets, qg, kg_t, decay, w, u, aqk, scan, total;
+  int64_t max_chunks;
+} kda_ws_layout;
+kda_status kda_chunk_ws_layout(const kda_chunk_args *a, kda_ws_layout *layout);
+
+/*
+ * kda_decode_args -- one token per request over a paged state cache, state
+ * updated in place (gated_delta_rule_decode's in-place V-first fp32 case).
+ */
+typedef struct kda_decode_args {
+  size_t struct_size;          /* = sizeof(kda_decode_args) */
+  const void *q;               /* (device) [n, Hqk, 128] dtype */
+  const void *k;               /* (device) [n, Hqk, 128] dtype */
+  const void *v;               /* (device) [n, Hv, 128] dtype */
+  const void *g;               /* (device) [n, Hv, 128] dtype, log-decay */
+  const void *beta;            /* (device) [n, Hv] dtype, logits */
+  int32_t dtype;               /* kda_dtype */
+  int32_t n;                   /* requests >= 0 */
+  int32_t hqk, hv;             /* hv % hqk == 0 */
+  float scale;
+  int32_t use_qk_l2norm;
+  float *state_cache;          /* (device) [num_slots, Hv, 128, 128] fp32 */
+  const int32_t *state_indices;  /* (device) [n], distinct where >= 0, each
+                                    < num_slots; < 0 = skip (zero output row,
+                                    no state I/O); NULL = identity (slot n) */
+  int32_t num_slots;
+  void *out;                   /* (device) [n, Hv, 128] dtype */
+  void *stream;                /* hipStream_t or NULL */
+} kda_decode_args;
+
+kda_status kda_decode(const kda_decode_args *a);
+
+/* Static text for a status code. */
+const char *kda_status_str(int32_t status);
+/* Detail of the calling thread's last failed call ("" if none). */
+const char *kda_last_error(void);
+/* Library version string. */
+const char *kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H_ */

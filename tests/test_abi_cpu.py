@@ -1,0 +1,198 @@
+"""The C ABI on the host: exports, struct agreement and every argument check.
+
+No compute call happens here: each call either queries sizes or fails its
+host-side checks before anything is queued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from gated_delta_rule_65_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load_library()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "kda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == set(B.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def chunk_args(**kw):
+    a = B.ChunkArgs()
+    a.struct_size = ctypes.sizeof(B.ChunkArgs)
+    a.dtype, a.num_seqs, a.total_tokens, a.hqk, a.hv = 1, 2, 256, 2, 4
+    a.scale, a.use_qk_l2norm = 128 ** -0.5, 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def ws_size(lib, a):
+    n = ctypes.c_size_t(0)
+    st = lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    return st, n.value
+
+
+def test_struct_size_agrees_and_workspace_is_sized(lib):
+    st, n = ws_size(lib, chunk_args())
+    assert st == B.KDA_OK and n > 0
+    bad = chunk_args()
+    bad.struct_size -= 8
+    assert ws_size(lib, bad)[0] == B.KDA_ERR_ARG
+
+
+def test_workspace_layout_is_ordered_and_covers_intermediates(lib):
+    a = chunk_args()
+    lay = B.WsLayout()
+    assert lib.kda_chunk_ws_layout(ctypes.byref(a), ctypes.byref(lay)) == B.KDA_OK
+    assert lay.max_chunks == 256 // 64 + 2
+    offs = [lay.chunk_offsets, lay.qg, lay.kg_t, lay.decay, lay.w, lay.u, lay.aqk, lay.scan]
+    assert offs == sorted(offs)
+    assert lay.qg - lay.chunk_offsets >= 4 * 3
+    assert lay.kg_t - lay.qg >= 256 * 4 * 128 * 2
+    assert lay.total >= lay.aqk + 256 * 4 * 64 * 2
+    assert all(o % 256 == 0 for o in offs)
+    # groups add the scan planes: 3 planes of 128x128 fp32 per (group, seq, head)
+    g = chunk_args(groups=4)
+    lay4 = B.WsLayout()
+    assert lib.kda_chunk_ws_layout(ctypes.byref(g), ctypes.byref(lay4)) == B.KDA_OK
+    assert lay4.total - lay4.scan >= 4 * 2 * 4 * 3 * 128 * 128 * 4
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("hv", 3, B.KDA_ERR_SHAPE),            # GVA divisibility
+    ("hqk", 0, B.KDA_ERR_SHAPE),
+    ("dtype", 2, B.KDA_ERR_DTYPE),         # fp16 chunk path not served
+    ("dtype", 9, B.KDA_ERR_DTYPE),
+    ("num_seqs", -1, B.KDA_ERR_SHAPE),
+    ("total_tokens", 255, B.KDA_ERR_SHAPE),  # dense: not a multiple of num_seqs
+    ("scale", float("inf"), B.KDA_ERR_SHAPE),
+    ("path", 7, B.KDA_ERR_UNSUPPORTED),
+    ("groups", -2, B.KDA_ERR_SHAPE),
+])
+def test_chunk_checks(lib, field, value, status):
+    a = chunk_args(**{field: value})
+    assert ws_size(lib, a)[0] == status
+    assert lib.kda_chunk_fwd(ctypes.byref(a)) == status
+    assert lib.kda_last_error().decode() != ""
+
+
+def test_chunk_state_modes_are_exclusive(lib):
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: the checks fail first
+    a = chunk_args(state_cache=fake, initial_state=fake, num_slots=4)
+    assert lib.kda_chunk_fwd(ctypes.byref(a)) == B.KDA_ERR_SHAPE
+    a = chunk_args(state_cache=fake, num_slots=4)          # no indices
+    assert lib.kda_chunk_fwd(ctypes.byref(a)) == B.KDA_ERR_SHAPE
+    a = chunk_args(state_indices=fake)                     # indices without a cache
+    assert lib.kda_chunk_fwd(ctypes.byref(a)) == B.KDA_ERR_SHAPE
+    a = chunk_args(state_cache=fake, state_indices=fake, has_initial_state=fake,
+                   num_slots=0)
+    assert lib.kda_chunk_fwd(ctypes.byref(a)) == B.KDA_ERR_SHAPE
+
+
+def test_chunk_missing_pointers_and_workspace(lib):
+    a = chunk_args()                                       # q..out NULL
+    assert lib.kda_chunk_fwd(ctypes.byref(a)) == B.KDA_ERR_ARG
+    fake = ctypes.c_void_p(0x1000)
+    a = chunk_args(q=fake, k=fake, v=fake, g=fake, beta=fake, out=fake)
+    _, need = ws_size(lib, a)
+    a.workspace, a.workspace_bytes = fake, need - 1
+    assert lib.kda_chunk_fwd(ctypes.byref(a)) == B.KDA_ERR_WORKSPACE
+    a.workspace, a.workspace_bytes = None, need
+    assert lib.kda_chunk_fwd(ctypes.byref(a)) == B.KDA_ERR_WORKSPACE
+
+
+def decode_args(**kw):
+    a = B.DecodeArgs()
+    a.struct_size = ctypes.sizeof(B.DecodeArgs)
+    a.dtype, a.n, a.hqk, a.hv, a.scale, a.use_qk_l2norm, a.num_slots = 1, 4, 2, 4, 0.1, 1, 8
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("hv", 3, B.KDA_ERR_SHAPE),
+    ("dtype", 5, B.KDA_ERR_DTYPE),
+    ("n", -1, B.KDA_ERR_SHAPE),
+    ("num_slots", 0, B.KDA_ERR_SHAPE),
+    ("num_slots", 3, B.KDA_ERR_SHAPE),      # identity map needs n slots
+    ("struct_size", 8, B.KDA_ERR_ARG),
+])
+def test_decode_checks(lib, field, value, status):
+    a = decode_args(**{field: value})
+    assert lib.kda_decode(ctypes.byref(a)) == status
+
+
+def test_decode_null_pointers_and_empty_batch(lib):
+    assert lib.kda_decode(ctypes.byref(decode_args())) == B.KDA_ERR_ARG
+    assert lib.kda_decode(ctypes.byref(decode_args(n=0))) == B.KDA_OK   # nothing queued
+    assert lib.kda_decode(None) == B.KDA_ERR_ARG
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.kda_status_str(s).decode()
+    assert b"gfx950" in lib.kda_version()
+
+
+def cpu(shape, dtype=torch.bfloat16):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def test_binding_shape_checks_raise_like_chunk_kda():
+    q = cpu((1, 64, 2, 128))
+    v = cpu((1, 64, 4, 128))
+    beta = cpu((1, 64, 4))
+    with pytest.raises(ValueError, match="D=128"):
+        B.chunk_kda(cpu((1, 64, 2, 64)), cpu((1, 64, 2, 64)), v, v, beta)
+    with pytest.raises(ValueError, match="divisible"):
+        B.chunk_kda(q, q, cpu((1, 64, 3, 128)), cpu((1, 64, 3, 128)), cpu((1, 64, 3)))
+    with pytest.raises(ValueError, match="beta"):
+        B.chunk_kda(q, q, v, v, cpu((1, 64, 2)))
+    with pytest.raises(TypeError):
+        B.chunk_kda(q.half(), q.half(), v.half(), v.half(), beta.half())
+    with pytest.raises(TypeError):
+        B.chunk_kda(q, q, v.float(), v, beta)
+    with pytest.raises(ValueError, match="4D"):
+        B.chunk_kda(q[0], q[0], v[0], v[0], beta[0])
+    cu = torch.tensor([0, 64], dtype=torch.int32)
+    with pytest.raises(ValueError, match="varlen"):
+        B.chunk_kda(torch.cat([q, q]), torch.cat([q, q]), torch.cat([v, v]),
+                    torch.cat([v, v]), torch.cat([beta, beta]), cu_seqlens=cu)
+    with pytest.raises(TypeError, match="cu_seqlens"):
+        B.chunk_kda(q, q, v, v, beta, cu_seqlens=cu.float())
+    with pytest.raises(ValueError, match="state_cache replaces"):
+        B.chunk_kda(q, q, v, v, beta, cu_seqlens=cu, state_cache=cpu((2, 4, 128, 128),
+                    torch.float32), initial_state=cpu((1, 4, 128, 128), torch.float32))
+
+
+def test_binding_decode_checks():
+    q = cpu((4, 2, 128))
+    v = cpu((4, 4, 128))
+    cache = cpu((8, 4, 128, 128), torch.float32)
+    with pytest.raises(ValueError, match="divisible"):
+        B.kda_decode(q, q, cpu((4, 3, 128)), cpu((4, 3, 128)), cpu((4, 3)), cache)
+    with pytest.raises(NotImplementedError):
+        B.kda_decode(cpu((4, 2, 2, 128)), cpu((4, 2, 2, 128)), cpu((4, 2, 4, 128)),
+                     cpu((4, 2, 4, 128)), cpu((4, 2, 4)), cache)
+    with pytest.raises(ValueError, match="pool"):
+        B.kda_decode(q, q, v, v, cpu((4, 4)), cpu((8, 4, 128, 64), torch.float32))
+    with pytest.raises(NotImplementedError):
+        B.kda_decode(q, q, v, v, cpu((4, 4)), cache.bfloat16())
