@@ -1,0 +1,323 @@
+"""Chunked forward on the GPU against the fp64 oracle.
+
+Tolerances (relative L2 over the compared tensor): <= 1e-2 for bf16 inputs,
+<= 1e-4 for fp32 inputs, for outputs and final states alike.  Stage
+intermediates (qg, kg_t, decay, w, u, aqk) are checked against the oracle's
+chunked form at the same bars.  Exactness cases (zero write strength with no
+decay, overwrite with orthonormal keys) are checked bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import forms
+from gated_delta_rule_65_amd import binding as B
+from gated_delta_rule_65_amd import inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def tol(dtype):
+    return 1e-4 if dtype == torch.float32 else 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def gpu(batch):
+    return [t.to(DEV) for t in (batch.q, batch.k, batch.v, batch.g, batch.beta)]
+
+
+def run_dense_state(batch, groups=0, l2=True):
+    """Varlen call with dense initial/final states."""
+    q, k, v, g, beta = gpu(batch)
+    init = None if batch.initial_state is None else batch.initial_state.to(DEV)
+    out, fin = B.chunk_kda(q, k, v, g, beta, scale=batch.scale, initial_state=init,
+                           output_final_state=True, cu_seqlens=batch.cu_seqlens.to(DEV),
+                           use_qk_l2norm_in_kernel=l2, groups=groups)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), fin.cpu().numpy()
+
+
+def oracle_dense(batch, heads=None, l2=True):
+    return oracle.recurrence(batch.q, batch.k, batch.v, batch.g, batch.beta,
+                             cu_seqlens=batch.cu_seqlens, scale=batch.scale,
+                             use_qk_l2norm=l2, initial_state=batch.initial_state, heads=heads)
+
+
+def f64(x):
+    return x.detach().cpu().double().numpy()
+
+
+# ------------------------------------------------------------------ workloads
+
+def test_tiny_fp32_workload():
+    """B=1, T=256, H=1, fp32, zero initial state, output + final state."""
+    b = inputs.make_workload("tiny_fp32")
+    say("tiny_fp32")
+    out, fin = run_dense_state(b)
+    o_ref, s_ref = oracle_dense(b)
+    assert rel(out, o_ref) < 1e-4
+    assert rel(fin, s_ref) < 1e-4
+
+
+CASES = [
+    # (name, lengths, hqk, hv, dtype, g_scale, init)
+    ("ragged_bf16", [1, 63, 64, 65, 200, 7], 1, 2, torch.bfloat16, 5.0, True),
+    ("ragged_fp32", [1, 63, 64, 65, 200, 7], 1, 2, torch.float32, 5.0, True),
+    ("gva_bf16", [130, 77], 2, 8, torch.bfloat16, 5.0, True),
+    ("slow_decay_bf16", [700, 300], 2, 2, torch.bfloat16, 0.5, True),
+    ("weak_decay_bf16", [1500], 1, 2, torch.bfloat16, 0.01, True),
+    ("weak_decay_fp32", [1000], 1, 1, torch.float32, 0.01, True),
+    ("no_decay_fp32", [513], 1, 1, torch.float32, 0.0, True),
+    ("zero_start_bf16", [256, 5], 1, 1, torch.bfloat16, 5.0, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_chunk_cases(case):
+    name, lengths, hqk, hv, dt, gs, init = case
+    b = inputs.make_chunk(lengths, hqk, hv, dtype=dt, g_scale=gs, seed=len(name), init=init)
+    say("case", name, lengths, hqk, hv, dt, gs)
+    out, fin = run_dense_state(b)
+    o_ref, s_ref = oracle_dense(b)
+    assert rel(out, o_ref) < tol(dt), rel(out, o_ref)
+    assert rel(fin, s_ref) < tol(dt), rel(fin, s_ref)
+
+
+def test_no_l2norm_custom_scale():
+    b = inputs.make_chunk([100, 40], 1, 2, dtype=torch.float32, seed=4, init=True)
+    b.q = b.q * 0.05
+    b.k = b.k * 0.05   # un-normalised keys must keep the delta rule contractive
+    b.scale = 0.7
+    say("no_l2norm")
+    out, fin = run_dense_state(b, l2=False)
+    o_ref, s_ref = oracle_dense(b, l2=False)
+    assert rel(out, o_ref) < 1e-4 and rel(fin, s_ref) < 1e-4
+
+
+def test_dense_4d_input_matches_varlen():
+    b = inputs.make_chunk([96, 96], 2, 2, seed=8, init=True)
+    q, k, v, g, beta = gpu(b)
+    out4, fin4 = B.chunk_kda(q.view(2, 96, 2, 128), k.view(2, 96, 2, 128),
+                             v.view(2, 96, 2, 128), g.view(2, 96, 2, 128),
+                             beta.view(2, 96, 2), scale=b.scale,
+                             initial_state=b.initial_state.to(DEV), output_final_state=True)
+    out, fin = B.chunk_kda(q, k, v, g, beta, scale=b.scale,
+                           initial_state=b.initial_state.to(DEV), output_final_state=True,
+                           cu_seqlens=b.cu_seqlens.to(DEV))
+    assert torch.equal(out4.view_as(out), out) and torch.equal(fin4, fin)
+
+
+# ------------------------------------------------------- stage intermediates
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_stage_intermediates_match_chunked_form(dt):
+    lengths = [70, 1, 128, 33]
+    b = inputs.make_chunk(lengths, 1, 2, dtype=dt, seed=12, init=True)
+    say("stages", dt)
+    q, k, v, g, beta = gpu(b)
+    st = B.chunk_stages(q, k, v, g, beta, cu_seqlens=b.cu_seqlens.to(DEV), scale=b.scale,
+                        initial_state=b.initial_state.to(DEV))
+    torch.cuda.synchronize()
+    o_ref, s_ref, inter = forms.chunked(f64(b.q), f64(b.k), f64(b.v), f64(b.g), f64(b.beta),
+                                        b.cu_seqlens.numpy(), b.scale, True,
+                                        f64(b.initial_state), C=64, intermediates=True)
+    offs = st["chunk_offsets"].cpu().numpy()
+    expect = np.concatenate([[0], np.cumsum([(x + 63) // 64 for x in lengths])])
+    assert np.array_equal(offs, expect)
+    nch = int(offs[-1])
+    t_ = tol(dt)
+    for key in ("qg", "w", "u"):
+        assert rel(st[key].float().cpu().numpy(), inter[key]) < t_, key
+    assert rel(st["aqk"].float().cpu().numpy(), inter["aqk"]) < t_
+    assert rel(st["decay"][:nch].cpu().numpy(), inter["d"]) < t_
+    # kg_t: chunk-major and transposed; rows past a short chunk are zero
+    kgt = st["kg_t"][:nch].float().cpu().numpy()
+    ref = np.zeros_like(kgt)
+    cu = b.cu_seqlens.tolist()
+    ci = 0
+    for n in range(len(lengths)):
+        for s in range(cu[n], cu[n + 1], 64):
+            e = min(s + 64, cu[n + 1])
+            ref[ci, :, :, :e - s] = inter["kg"][s:e].transpose(1, 2, 0)
+            ci += 1
+    assert rel(kgt, ref) < t_
+    assert rel(st["out"].float().cpu().numpy(), o_ref) < t_
+    assert rel(st["final_state"].cpu().numpy(), s_ref) < t_
+
+
+# ------------------------------------------------------------- exactness cases
+
+def test_zero_write_strength_no_decay_keeps_state_bitwise():
+    """b = 0 (logit -1e4 -> sigmoid 0) and g = 0: the state passes through
+    bit for bit and the output is the frozen-state read-out."""
+    b = inputs.make_chunk([150, 64], 1, 2, dtype=torch.bfloat16, seed=2, init=True)
+    b.beta.fill_(-1e4)
+    b.g.zero_()
+    say("b=0,g=0")
+    out, fin = run_dense_state(b)
+    assert np.array_equal(fin, b.initial_state.numpy())
+    o_ref, _ = forms.closed_b0(f64(b.q), f64(b.g), b.cu_seqlens.numpy(), b.scale,
+                               f64(b.initial_state), 2)
+    assert rel(out, o_ref) < 1e-2
+
+
+def test_zero_write_strength_with_decay_closed_form():
+    b = inputs.make_chunk([300], 1, 1, dtype=torch.float32, g_scale=0.05, seed=3, init=True)
+    b.beta.fill_(-1e4)
+    say("b=0 decay")
+    out, fin = run_dense_state(b)
+    o_ref, s_ref = forms.closed_b0(f64(b.q), f64(b.g), b.cu_seqlens.numpy(), b.scale,
+                                   f64(b.initial_state), 1)
+    assert rel(out, o_ref) < 1e-4 and rel(fin, s_ref) < 1e-4
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_exact_overwrite_with_orthonormal_keys(dt):
+    """b = 1 (logit 40), g = 0, distinct basis keys, q = k, scale 1, no norm,
+    zero start: every product is x1 or +0, so o_t = v_t and row pi(t) of the
+    state equals v_t exactly.  The fp32 path carries MFMA operands as a
+    hi + lo bf16 pair, so its values are drawn on the bf16 grid (lo = 0)."""
+    T, hv = 128, 2
+    gen = torch.Generator().manual_seed(5)
+    perm = torch.randperm(128, generator=gen)[:T]
+    k = torch.zeros(T, 1, 128, dtype=dt)
+    k[torch.arange(T), 0, perm] = 1
+    v = torch.randn(T, hv, 128, generator=gen).to(torch.bfloat16).to(dt)
+    g = torch.zeros(T, hv, 128, dtype=dt)
+    beta = torch.full((T, hv), 40.0, dtype=dt)
+    cu = torch.tensor([0, T], dtype=torch.int32, device=DEV)
+    say("overwrite", dt)
+    out, fin = B.chunk_kda(k.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), beta.to(DEV), scale=1.0,
+                           output_final_state=True, cu_seqlens=cu,
+                           use_qk_l2norm_in_kernel=False)
+    assert torch.equal(out.cpu(), v)
+    fin = fin.cpu()
+    for t in range(T):
+        assert torch.equal(fin[0, :, :, perm[t]], v[t].float())
+
+
+# ------------------------------------------------------------------ paged state
+
+def test_paged_state_equals_dense_and_leaves_other_rows():
+    lengths = [90, 0, 64, 131]
+    b = inputs.make_chunk(lengths, 2, 4, dtype=torch.bfloat16, seed=21, paged_slots=9)
+    b.has_initial_state = torch.tensor([1, 1, 0, 1], dtype=torch.uint8)
+    say("paged")
+    q, k, v, g, beta = gpu(b)
+    cache = b.state_cache.to(DEV)
+    out = B.chunk_kda(q, k, v, g, beta, scale=b.scale, cu_seqlens=b.cu_seqlens.to(DEV),
+                      state_cache=cache, state_indices=b.state_indices.to(DEV),
+                      has_initial_state=b.has_initial_state.to(DEV))
+    torch.cuda.synchronize()
+    idx = b.state_indices.long()
+    s0 = b.state_cache[idx].clone()
+    s0[2] = 0.0
+    o_ref, s_ref = oracle.recurrence(b.q, b.k, b.v, b.g, b.beta, cu_seqlens=b.cu_seqlens,
+                                     scale=b.scale, initial_state=s0)
+    assert rel(out.float().cpu().numpy(), o_ref) < 1e-2
+    got = cache.cpu()
+    assert rel(got[idx].numpy(), s_ref) < 1e-2
+    # the zero-length sequence passes its row through bit for bit
+    assert torch.equal(got[idx[1]], b.state_cache[idx[1]])
+    others = torch.ones(9, dtype=torch.bool)
+    others[idx] = False
+    assert torch.equal(got[others], b.state_cache[others])
+
+
+def test_paged_null_slot_gives_zero_rows_and_no_state_io():
+    lengths = [40, 70]
+    b = inputs.make_chunk(lengths, 1, 2, dtype=torch.bfloat16, seed=22, paged_slots=4)
+    b.state_indices = torch.tensor([-1, 2], dtype=torch.int32)
+    say("null slot")
+    q, k, v, g, beta = gpu(b)
+    cache = b.state_cache.to(DEV)
+    out = B.chunk_kda(q, k, v, g, beta, scale=b.scale, cu_seqlens=b.cu_seqlens.to(DEV),
+                      state_cache=cache, state_indices=b.state_indices.to(DEV),
+                      has_initial_state=b.has_initial_state.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.all(out[:40].cpu() == 0)
+    got = cache.cpu()
+    for r in (0, 1, 3):
+        assert torch.equal(got[r], b.state_cache[r])
+    sl = slice(40, 110)
+    o_ref, s_ref = oracle.recurrence(b.q[sl], b.k[sl], b.v[sl], b.g[sl], b.beta[sl],
+                                     scale=b.scale, initial_state=b.state_cache[2:3])
+    assert rel(out[40:].float().cpu().numpy(), o_ref) < 1e-2
+    assert rel(got[2].numpy(), s_ref[0]) < 1e-2
+
+
+def test_empty_batch_and_all_empty_sequences():
+    b = inputs.make_chunk([0, 0], 1, 1, seed=1, init=True)
+    q, k, v, g, beta = gpu(b)
+    init = b.initial_state.to(DEV)
+    out, fin = B.chunk_kda(q, k, v, g, beta, initial_state=init, output_final_state=True,
+                           cu_seqlens=b.cu_seqlens.to(DEV))
+    torch.cuda.synchronize()
+    assert out.numel() == 0 and torch.equal(fin, init)
+
+
+def test_deterministic():
+    b = inputs.make_chunk([300, 77], 2, 4, seed=31, init=True)
+    r1 = run_dense_state(b)
+    r2 = run_dense_state(b)
+    assert np.array_equal(r1[0], r2[0]) and np.array_equal(r1[1], r2[1])
+
+
+# --------------------------------------------------------------- full workloads
+
+def test_dense_prefill_workload():
+    """B=4, T=4096, H=16, bf16, fp32 initial state: every output and state."""
+    b = inputs.make_workload("dense_prefill")
+    say("dense_prefill")
+    out, fin = run_dense_state(b)
+    o_ref, s_ref = oracle_dense(b)
+    e_o, e_s = rel(out, o_ref), rel(fin, s_ref)
+    say("  rel out", e_o, "state", e_s)
+    assert e_o < 1e-2 and e_s < 1e-2
+
+
+def test_varlen_gva_paged_workload():
+    """24 log-uniform sequences (S = 32768), Hqk=8, Hv=32, paged cache [64,...]."""
+    b = inputs.make_workload("varlen_gva_paged")
+    say("varlen_gva_paged", b.meta["lengths"])
+    q, k, v, g, beta = gpu(b)
+    cache = b.state_cache.to(DEV)
+    out = B.chunk_kda(q, k, v, g, beta, scale=b.scale, cu_seqlens=b.cu_seqlens.to(DEV),
+                      state_cache=cache, state_indices=b.state_indices.to(DEV),
+                      has_initial_state=b.has_initial_state.to(DEV))
+    torch.cuda.synchronize()
+    idx = b.state_indices.long()
+    o_ref, s_ref = oracle.recurrence(b.q, b.k, b.v, b.g, b.beta, cu_seqlens=b.cu_seqlens,
+                                     scale=b.scale, initial_state=b.state_cache[idx])
+    got = cache.cpu()
+    e_o, e_s = rel(out.float().cpu().numpy(), o_ref), rel(got[idx].numpy(), s_ref)
+    say("  rel out", e_o, "state", e_s)
+    assert e_o < 1e-2 and e_s < 1e-2
+    others = torch.ones(64, dtype=torch.bool)
+    others[idx] = False
+    assert torch.equal(got[others], b.state_cache[others])
+
+
+def test_long_single_workload_sampled_heads():
+    """B=1, T=131072, H=32, slow decay: outputs and final states of 8 of the
+    32 heads (heads are independent, so the sample is exact, not approximate)."""
+    b = inputs.make_workload("long_single")
+    heads = [0, 5, 9, 14, 18, 23, 27, 31]
+    say("long_single")
+    out, fin = run_dense_state(b)
+    o_ref, s_ref = oracle_dense(b, heads=heads)
+    e_o = rel(out[:, heads], o_ref[:, heads])
+    e_s = rel(fin[:, heads], s_ref[:, heads])
+    say("  rel out", e_o, "state", e_s)
+    assert e_o < 1e-2 and e_s < 1e-2
