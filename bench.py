@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Throughput of the KDA hot path on one MI355X.
+
+One step = one chunked forward over the dense-prefill workload (B=4, T=4096,
+Hqk=Hv=16, D=128, bf16, fp32 initial and final state) followed by one paged
+decode over the decode workload (256 requests x 32 heads, fp32 cache
+[1024, 32, 128, 128]), inputs resident in HBM.  W untimed warm-up steps, then K
+timed steps bracketed by device synchronisation.  Per-kernel times come from
+HIP events recorded by the library at its stage boundaries on the launch
+stream; the decode is bracketed by events on the same stream.
+
+Printed: one JSON line.  ``value`` is chunk-forward tokens/s (tokens of the
+prefill batch / mean chunk-forward time); ``ms_per_step`` is the wall time of a
+whole step (chunk forward + decode).  ``roofline`` describes the kernel that
+takes the most time in a step; ``kernels`` lists all of them.
+``cpu_baseline`` times the fp64 CPU oracle on the host (rank 0, N=1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("chunk_kda fwd tokens/s + TFLOP/s (% bf16 MFMA peak); "
+          "decode state GB/s (% HBM)")
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+K = V = 128
+C = 64
+
+
+# ------------------------------------------------------------ work accounting
+
+def wy_flops(L: int) -> float:
+    """Triangle-aware WY work of one chunk of L tokens for one value head:
+    A_kk (strictly lower) + A_qk (lower) + the unit-lower inverse + w and u."""
+    return K * L * (L - 1) + K * L * (L + 1) + L ** 3 / 3 + (K + V) * L * (L - 1)
+
+
+def walk_flops(L: int) -> float:
+    """Walk work of one chunk: w S, qg S, kg^T U (2 L K V each), A_qk U
+    (lower), and the diagonal decay of S."""
+    return V * L * (L + 1) + 6 * L * K * V + K * V
+
+
+def chunk_lengths(lengths):
+    out = []
+    for n in lengths:
+        out += [C] * (n // C) + ([n % C] if n % C else [])
+    return out
+
+
+def chunk_work(lengths, hqk, hv, es, state_in, state_out):
+    """Algorithmic flops and bytes per kernel for one chunked forward."""
+    T = sum(lengths)
+    chunks = chunk_lengths(lengths)
+    nch = len(chunks)
+    N = len(lengths)
+    prep_b = (2 * T * hqk + T * hv) * 128 * es + T * hv * 128 * es + nch * hv * 128 * (64 * es + 4)
+    wy_b = (2 * T * hqk + 2 * T * hv) * 128 * es + T * hv * es + T * hv * (2 * 128 + 64) * es
+    walk_b = (T * hv * (3 * 128 + 64) * es + nch * hv * 128 * (64 * es + 4)
+              + T * hv * 128 * es + (state_in + state_out) * N * hv * 128 * 128 * 4)
+    return dict(
+        tokens=T,
+        prep=dict(bytes=prep_b, flops=0.0),
+        wy=dict(bytes=wy_b, flops=hv * sum(wy_flops(L) for L in chunks)),
+        walk=dict(bytes=walk_b, flops=hv * sum(walk_flops(L) for L in chunks)),
+        table=dict(bytes=4 * (2 * N + 1), flops=0.0),
+    )
+
+
+def decode_work(n, hqk, hv, es):
+    state = n * hv * 128 * 128 * 4 * 2
+    io = n * (2 * hqk * 128 + 2 * hv * 128 + hv + hv * 128) * es + n * 4
+    return dict(bytes=state + io, state_bytes=state)
+
+
+# ------------------------------------------------------------------ HIP events
+
+class HipEvents:
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def record(self, e, stream):
+        if self.lib.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(a),
+                                        ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+# ------------------------------------------------------------------- helpers
+
+def source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_65_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str):
+    """Counter-derived HBM bytes per launch (profiles/traffic.json), or None
+    when absent or taken from a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    rec = t.get("kernels", {}).get(kernel)
+    if not rec or rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(batch_cpu, lengths, dec_cpu):
+    """The fp64 oracle on the host: the whole prefill batch (all sequences and
+    heads), then the whole decode batch."""
+    import oracle
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.recurrence(batch_cpu.q, batch_cpu.k, batch_cpu.v, batch_cpu.g, batch_cpu.beta,
+                      cu_seqlens=batch_cpu.cu_seqlens, scale=batch_cpu.scale,
+                      initial_state=batch_cpu.initial_state, threads=threads)
+    t_chunk = time.perf_counter() - t0
+    return dict(value=sum(lengths) / t_chunk, unit="tokens/s", cores=threads,
+                kind="oracle",
+                sample=(f"whole prefill batch ({len(lengths)} x {lengths[0]} tokens, "
+                        f"{batch_cpu.v.shape[1]} heads), fp64 token recurrence, "
+                        f"{t_chunk:.2f} s on {cpu_model()}"))
+
+
+# ---------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--groups", type=int, default=0, help="chunk groups (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by head or sequence with no communication; see the "
+              "design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_65_amd import binding as B
+    from gated_delta_rule_65_amd import inputs
+
+    B.load_library()   # raises if the HIP library is not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ev = HipEvents()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    # inputs resident in HBM
+    wl = inputs.WORKLOADS["dense_prefill"]
+    lengths = [wl["T"]] * wl["B"]
+    cb = inputs.make_workload("dense_prefill", device=dev)
+    hqk, hv = wl["hqk"], wl["hv"]
+    T = sum(lengths)
+    q4 = cb.q.view(wl["B"], wl["T"], hqk, 128)
+    k4 = cb.k.view(wl["B"], wl["T"], hqk, 128)
+    v4 = cb.v.view(wl["B"], wl["T"], hv, 128)
+    g4 = cb.g.view(wl["B"], wl["T"], hv, 128)
+    b4 = cb.beta.view(wl["B"], wl["T"], hv)
+    out = torch.empty_like(v4)
+    fin = torch.empty((wl["B"], hv, 128, 128), device=dev, dtype=torch.float32)
+    dwl = inputs.WORKLOADS["decode_paged"]
+    db = inputs.make_workload("decode_paged", device=dev)
+    dout = torch.empty_like(db.v)
+    # one workspace, sized once
+    p = B._prepare_chunk(q4, k4, v4, g4, b4, cb.scale, cb.initial_state, True, None, True,
+                         out, fin, None, None, None)
+    nbytes = ctypes.c_size_t(0)
+    a = B._chunk_struct(p["q"], p["k"], p["v"], p["g"], p["beta"], p["out"], None, p["N"],
+                        p["T"], hqk, hv, p["scale"], True, p["init"], p["fin"], None, None,
+                        None, 0, args.groups, ctypes.c_void_p(stream))
+    B.load_library().kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(nbytes))
+    ws = torch.empty(nbytes.value, dtype=torch.uint8, device=dev)
+
+    nev = B.NUM_STAGE_EVENTS
+    ev_sets = [[ev.create() for _ in range(nev)] for _ in range(args.steps)]
+    dec_ev = [(ev.create(), ev.create()) for _ in range(args.steps)]
+
+    def step(i=None):
+        B.chunk_kda(q4, k4, v4, g4, b4, scale=cb.scale, initial_state=cb.initial_state,
+                    output_final_state=True, output=out, final_state=fin,
+                    groups=args.groups, workspace=ws,
+                    stage_events=None if i is None else ev_sets[i])
+        if not args.no_decode:
+            if i is not None:
+                ev.record(dec_ev[i][0], stream)
+            B.kda_decode(db.q, db.k, db.v, db.g, db.beta, db.state_cache, db.state_indices,
+                         scale=db.scale, output=dout)
+            if i is not None:
+                ev.record(dec_ev[i][1], stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    names = ["table", "prep", "wy", "walk", "compose", "pass2"]
+    per = {n: [] for n in names}
+    chunk_ms, dec_ms = [], []
+    for i in range(args.steps):
+        e = ev_sets[i]
+        for j, n in enumerate(names):
+            per[n].append(ev.ms(e[j], e[j + 1]))
+        chunk_ms.append(ev.ms(e[0], e[nev - 1]))
+        if not args.no_decode:
+            dec_ms.append(ev.ms(*dec_ev[i]))
+    mean = lambda xs: sum(xs) / max(len(xs), 1)
+    t_chunk = mean(chunk_ms) / 1e3
+    work = chunk_work(lengths, hqk, hv, 2, True, True)
+    flops = work["wy"]["flops"] + work["walk"]["flops"]
+
+    kernels = {}
+    for n, bound in (("prep", "hbm"), ("wy", "mfma"), ("walk", "mfma")):
+        ms = mean(per[n])
+        if ms <= 0:
+            continue
+        s = ms / 1e3
+        gbs = work[n]["bytes"] / s / 1e9
+        tfl = work[n]["flops"] / s / 1e12
+        kernels[n] = dict(ms=round(ms, 4), bound=bound, gb_s=round(gbs, 1),
+                          tflops=round(tfl, 2),
+                          frac=round((gbs / PEAK_HBM_GBS) if bound == "hbm"
+                                     else (tfl / PEAK_BF16_TFLOPS), 4))
+    dec = None
+    if not args.no_decode:
+        dw = decode_work(dwl["N"], dwl["hqk"], dwl["hv"], 2)
+        s = mean(dec_ms) / 1e3
+        gbs = dw["bytes"] / s / 1e9
+        kernels["decode"] = dict(ms=round(s * 1e3, 4), bound="hbm", gb_s=round(gbs, 1),
+                                 frac=round(gbs / PEAK_HBM_GBS, 4))
+        dec = dict(ms=round(s * 1e3, 4), gb_s=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4),
+                   state_gb_s=round(dw["state_bytes"] / s / 1e9, 1),
+                   workload=f"{dwl['N']} requests x {dwl['hv']} heads, cache "
+                            f"[{dwl['slots']}, {dwl['hv']}, 128, 128] fp32")
+
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    kd = kernels[dom]
+    kname = {"prep": "prep_kernel", "wy": "wy_kernel", "walk": "walk_kernel",
+             "decode": "decode_kernel"}[dom]
+    if kd["bound"] == "hbm":
+        wb = work[dom]["bytes"] if dom != "decode" else decode_work(
+            dwl["N"], dwl["hqk"], dwl["hv"], 2)["bytes"]
+        roof = dict(bound="hbm", achieved=kd["gb_s"], peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=kd["frac"], kernel=kname, algorithmic_bytes=wb)
+    else:
+        roof = dict(bound="mfma", achieved=kd["tflops"], peak=PEAK_BF16_TFLOPS,
+                    unit="TFLOP/s", frac=kd["frac"], kernel=kname,
+                    algorithmic_flops=work[dom]["flops"])
+    roof["traffic"] = load_traffic(kname)
+    roof["launch_ms"] = kd["ms"]
+
+    res = dict(
+        metric=METRIC, value=round(T / t_chunk, 1), unit="tokens/s", n_gpus=1,
+        steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(wall / args.steps * 1e3, 4), higher_is_better=True,
+        scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+        config=dict(workload="dense_prefill", B=wl["B"], T=wl["T"], hqk=hqk, hv=hv,
+                    head_dim=128, chunk=64, state="fp32 initial+final",
+                    groups=args.groups, decode=None if dec is None else dec["workload"]),
+        chunk_ms=round(t_chunk * 1e3, 4),
+        tflops=round(flops / t_chunk / 1e12, 2),
+        mfma_frac=round(flops / t_chunk / 1e12 / PEAK_BF16_TFLOPS, 4),
+        decode=dec, kernels=kernels, roofline=roof,
+    )
+    if not args.no_cpu_baseline:
+        cpu = inputs.Batch(cb.q.cpu(), cb.k.cpu(), cb.v.cpu(), cb.g.cpu(), cb.beta.cpu(),
+                           cb.cu_seqlens.cpu(), cb.scale, initial_state=cb.initial_state.cpu())
+        res["cpu_baseline"] = cpu_baseline(cpu, lengths, None)
+    else:
+        res["cpu_baseline"] = None
+    for es in ev_sets:
+        for e in es:
+            ev.destroy(e)
+    for a_, b_ in dec_ev:
+        ev.destroy(a_)
+        ev.destroy(b_)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

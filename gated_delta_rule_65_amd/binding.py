@@ -46,8 +46,12 @@ class ChunkArgs(ctypes.Structure):
         ("out", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("path", ctypes.c_int32), ("groups", ctypes.c_int32),
+        ("stage_events", ctypes.c_void_p), ("num_stage_events", ctypes.c_int32),
         ("stream", ctypes.c_void_p),
     ]
+
+
+NUM_STAGE_EVENTS = 7
 
 
 class WsLayout(ctypes.Structure):
@@ -253,7 +257,7 @@ def _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state, c
                 fin=fin, cache=state_cache if paged else None, idx=idx, has_init=hinit)
 
 
-def _run_chunk(p, path=PATH_AUTO, groups=0, workspace=None, keep=None):
+def _run_chunk(p, path=PATH_AUTO, groups=0, workspace=None, keep=None, events=None):
     lib = load_library()
     dev = p["q"].device
     a = _chunk_struct(p["q"], p["k"], p["v"], p["g"], p["beta"], p["out"], p["cu"], p["N"],
@@ -267,6 +271,10 @@ def _run_chunk(p, path=PATH_AUTO, groups=0, workspace=None, keep=None):
         workspace = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=dev)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = workspace.numel() * workspace.element_size()
+    if events is not None:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        a.stage_events = ctypes.cast(arr, ctypes.c_void_p)
+        a.num_stage_events = len(events)
     st = lib.kda_chunk_fwd(ctypes.byref(a))
     if st != KDA_OK:
         _raise(lib, st)
@@ -279,14 +287,16 @@ def _run_chunk(p, path=PATH_AUTO, groups=0, workspace=None, keep=None):
 def chunk_kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False,
               cu_seqlens=None, use_qk_l2norm_in_kernel=True, output=None, final_state=None,
               state_cache=None, state_indices=None, has_initial_state=None, groups=0,
-              workspace=None):
+              workspace=None, stage_events=None):
     """Chunked KDA forward (chunk_kda's argument set, plus the paged state of
     fused_kda_chunk).  Returns out, or (out, final_state) when
-    output_final_state; in paged mode the final states land in state_cache."""
+    output_final_state; in paged mode the final states land in state_cache.
+    stage_events: optional list of up to 7 hipEvent_t handles (ints) recorded
+    at the stage boundaries (profiling)."""
     p = _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state,
                        cu_seqlens, use_qk_l2norm_in_kernel, output, final_state,
                        state_cache, state_indices, has_initial_state)
-    _run_chunk(p, groups=groups, workspace=workspace)
+    _run_chunk(p, groups=groups, workspace=workspace, events=stage_events)
     out = p["out"]
     if output_final_state:
         return out, p["fin"]

@@ -74,6 +74,8 @@ kda_status check_chunk(const kda_chunk_args* a, bool need_ptrs) {
     return fail(KDA_ERR_UNSUPPORTED, "unknown path %d", a->path);
   if (a->groups < 0) return fail(KDA_ERR_SHAPE, "groups must be >= 0");
   if (a->groups > 64) return fail(KDA_ERR_UNSUPPORTED, "groups above 64");
+  if (a->stage_events && (a->num_stage_events < 0 || a->num_stage_events > KDA_NUM_EVENTS))
+    return fail(KDA_ERR_ARG, "num_stage_events must be in [0, %d]", KDA_NUM_EVENTS);
   if (need_ptrs && a->total_tokens > 0) {
     if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->out)
       return fail(KDA_ERR_ARG, "q, k, v, g, beta and out must be non-NULL");
@@ -188,6 +190,8 @@ KDA_API kda_status kda_chunk_fwd(const kda_chunk_args* a) {
   L.chunk_offsets = (int32_t*)(ws + W.chunk_offsets);
   L.qg = ws + W.qg; L.kg_t = ws + W.kg_t; L.decay = (float*)(ws + W.decay);
   L.w = ws + W.w; L.u = ws + W.u; L.aqk = ws + W.aqk;
+  L.events = a->stage_events;
+  L.num_events = a->stage_events ? a->num_stage_events : 0;
   L.groups = resolve_groups(a);
   L.scan = L.groups > 1 ? (float*)(ws + W.scan) : nullptr;
   L.stream = a->stream;

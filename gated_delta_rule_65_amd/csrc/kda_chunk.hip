@@ -703,24 +703,34 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(
 
 // --------------------------------------------------------------------- launch
 
+static void mark(const ChunkLaunch& L, int i) {
+  if (i < L.num_events && L.events[i]) (void)hipEventRecord((hipEvent_t)L.events[i], (hipStream_t)L.stream);
+}
+
 template <typename E>
 static hipError_t launch_staged_t(const ChunkLaunch& L) {
   hipStream_t st = (hipStream_t)L.stream;
+  mark(L, 0);
   const int N = L.num_seqs;
   const int T = (int)L.total_tokens;
   const int dense_len = L.cu ? 0 : (N > 0 ? T / N : 0);
   hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(1024), 0, st, L.cu, N, dense_len, T,
                      L.chunk_offsets);
+  mark(L, 1);
   if (L.max_chunks > 0 && T > 0) {
     hipLaunchKernelGGL(prep_kernel<E>, dim3((unsigned)L.max_chunks, L.hqk), dim3(256), 0, st,
                        (const E*)L.q, (const E*)L.k, (const E*)L.g, L.cu, dense_len, T,
                        L.chunk_offsets, N, L.hqk, L.hv, L.use_l2, (E*)L.qg, (E*)L.kg_t,
                        L.decay);
+    mark(L, 2);
     hipLaunchKernelGGL(wy_kernel<E>, dim3((unsigned)L.max_chunks, L.hv), dim3(256), 0, st,
                        (const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.g,
                        (const E*)L.beta, L.cu, dense_len, T, L.chunk_offsets, N, L.hqk, L.hv,
                        L.use_l2, (E*)L.w, (E*)L.u, (E*)L.aqk);
+  } else {
+    mark(L, 2);
   }
+  mark(L, 3);
   constexpr int NW = 4;
   const int nvb = D / (16 * NW);
   const int units = N * L.hv;
@@ -730,6 +740,9 @@ static hipError_t launch_staged_t(const ChunkLaunch& L) {
                      (const E*)L.aqk, L.cu, dense_len, T, L.chunk_offsets, N, L.hv, L.scale,
                      L.init, L.fin, L.cache, L.slots, L.has_init, L.num_slots, (E*)L.out, nvb,
                      units, (int)L.max_chunks);
+  mark(L, 4);
+  mark(L, 5);
+  mark(L, 6);
   return hipGetLastError();
 }
 

@@ -37,7 +37,8 @@ struct ChunkLaunch {
   float* decay;
   float* scan;                // group-scan planes (groups > 1)
   int groups;
-  int max_seq_len_bound;      // upper bound of any sequence length (host-known)
+  void** events;              // optional stage events (KDA_EV_*), may be NULL
+  int num_events;
   void* stream;
 };
 hipError_t launch_chunk_staged(const ChunkLaunch& L);

@@ -122,8 +122,27 @@ typedef struct kda_chunk_args {
   int32_t path;                /* kda_path */
   int32_t groups;              /* chunk groups per sequence: 0 = auto, 1 = none,
                                   >= 2 = that many (the parallel group scan) */
+  void **stage_events;         /* optional hipEvent_t[num_stage_events], recorded
+                                  on `stream` at the stage boundaries below
+                                  (profiling); NULL = none.  The caller owns them. */
+  int32_t num_stage_events;
   void *stream;                /* hipStream_t or NULL */
 } kda_chunk_args;
+
+/* Stage boundaries of kda_chunk_fwd (indices into stage_events).  Event i is
+ * recorded when stage i ends; KDA_EV_BEGIN precedes the first kernel.  With
+ * groups > 1 the walk runs as pass one, compose and pass two; with groups == 1
+ * the compose and pass-two events are recorded right after the walk. */
+enum {
+  KDA_EV_BEGIN = 0,    /* before the chunk table */
+  KDA_EV_TABLE = 1,    /* chunk table built */
+  KDA_EV_PREP = 2,     /* prep done (qg, kg_t, decay) */
+  KDA_EV_WY = 3,       /* WY done (w, u, aqk) */
+  KDA_EV_WALK = 4,     /* walk (or group pass one) done */
+  KDA_EV_COMPOSE = 5,  /* group transfers composed */
+  KDA_EV_PASS2 = 6,    /* group pass two done */
+  KDA_NUM_EVENTS = 7
+};
 
 /*
  * Workspace bytes the call described by `a` needs (0 is possible), written
