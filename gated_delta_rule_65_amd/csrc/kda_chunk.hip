@@ -130,53 +130,60 @@ __device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
 }
 
 // A 64 x 128 token tile of q and k (L2-normalised when asked) into fp32 LDS.
-// Thread mapping: 16 lanes (one DPP row) per token row, 8 channels per lane.
-template <typename E, int SK>
-__device__ __forceinline__ void load_qk_tile(const E* src, int stride_t, int L, int use_l2,
-                                             float (*dst)[SK]) {
+// Thread mapping: 16 lanes (one DPP row) per token row, 8 channels per lane;
+// all four row loads are issued before the first reduction.
+template <typename E>
+__device__ __forceinline__ void load_rows4(const E* src, int stride_t, int L, float (&x)[4][8]) {
   const int tid = threadIdx.x, rg = tid >> 4, j = tid & 15;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int t = rg + 16 * it;
-    float x[8];
     if (t < L) {
-      load8(src + (size_t)t * stride_t + 8 * j, x);
+      load8(src + (size_t)t * stride_t + 8 * j, x[it]);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      for (int e = 0; e < 8; ++e) x[it][e] = 0.f;
     }
-    if (use_l2) {
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s += x[e] * x[e];
-      s = row_sum16(s);
-      const float r = rsqrtf(s + L2_EPS);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] *= r;
-    }
-    *reinterpret_cast<float4*>(&dst[t][8 * j]) = make_float4(x[0], x[1], x[2], x[3]);
-    *reinterpret_cast<float4*>(&dst[t][8 * j + 4]) = make_float4(x[4], x[5], x[6], x[7]);
   }
 }
 
-// g tile (x log2 e) into LDS, then the inclusive cumulative sum over tokens
-// per channel.  Rows past L hold g = 0, so G stays at G_{L-1} there.
-template <typename E, int SK>
-__device__ __forceinline__ void load_gate_cumsum(const E* src, int stride_t, int L,
-                                                 float (*sG)[SK]) {
+__device__ __forceinline__ void l2norm_rows4(float (&x)[4][8]) {
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += x[it][e] * x[it][e];
+    s = row_sum16(s);
+    const float r = rsqrtf(s + L2_EPS);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[it][e] *= r;
+  }
+}
+
+template <int SK>
+__device__ __forceinline__ void rows4_to_lds(const float (&x)[4][8], float (*dst)[SK]) {
   const int tid = threadIdx.x, rg = tid >> 4, j = tid & 15;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int t = rg + 16 * it;
-    float x[8];
-    if (t < L) {
-      load8(src + (size_t)t * stride_t + 8 * j, x);
-    } else {
+    *reinterpret_cast<float4*>(&dst[t][8 * j]) =
+        make_float4(x[it][0], x[it][1], x[it][2], x[it][3]);
+    *reinterpret_cast<float4*>(&dst[t][8 * j + 4]) =
+        make_float4(x[it][4], x[it][5], x[it][6], x[it][7]);
+  }
+}
+
+// g rows (already in registers, x log2 e applied here) into LDS, then the
+// inclusive cumulative sum over tokens per channel.  Rows past L hold g = 0,
+// so G stays at G_{L-1} there.
+template <int SK>
+__device__ __forceinline__ void gate_cumsum(const float (&x)[4][8], float (*sG)[SK]) {
+  const int tid = threadIdx.x, rg = tid >> 4, j = tid & 15;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
-    }
+  for (int it = 0; it < 4; ++it) {
+    const int t = rg + 16 * it;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sG[t][8 * j + e] = x[e] * LOG2E;
+    for (int e = 0; e < 8; ++e) sG[t][8 * j + e] = x[it][e] * LOG2E;
   }
   __syncthreads();
   const int c = tid & 127, half = tid >> 7;  // 256 threads: two halves of 32 tokens
@@ -218,36 +225,25 @@ __global__ __launch_bounds__(256) void prep_kernel(const E* __restrict__ q,
   const int tid = threadIdx.x, rg = tid >> 4, j = tid & 15;
   const int L = p.L;
 
-  // q rows stay in registers, k rows go to LDS (kg is written transposed)
-  float qn[4][8];
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int t = rg + 16 * it;
-    float x[8];
-    if (t < L) {
-      load8(q + ((size_t)(p.t0 + t) * hqk + hq) * D + 8 * j, x);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
-    }
-    if (use_l2) {
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s += x[e] * x[e];
-      s = row_sum16(s);
-      const float r = rsqrtf(s + L2_EPS);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] *= r;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qn[it][e] = x[e];
+  // q rows stay in registers, k rows go to LDS (kg is written transposed);
+  // the first head's g rows are fetched together with q and k.
+  float qn[4][8], kx[4][8], gx[4][8];
+  load_rows4(q + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, qn);
+  load_rows4(k + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, kx);
+  load_rows4(g + ((size_t)p.t0 * hv + hq * grp) * D, hv * D, L, gx);
+  if (use_l2) {
+    l2norm_rows4(qn);
+    l2norm_rows4(kx);
   }
-  load_qk_tile<E, SK>(k + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, use_l2, sK);
+  rows4_to_lds<SK>(kx, sK);
 
   for (int gi = 0; gi < grp; ++gi) {
     const int h = hq * grp + gi;
-    __syncthreads();
-    load_gate_cumsum<E, SK>(g + ((size_t)p.t0 * hv + h) * D, hv * D, L, sG);
+    if (gi > 0) {
+      __syncthreads();
+      load_rows4(g + ((size_t)p.t0 * hv + h) * D, hv * D, L, gx);
+    }
+    gate_cumsum<SK>(gx, sG);
     // qg = qn 2^G, token-major
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -352,10 +348,21 @@ __global__ __launch_bounds__(256) void wy_kernel(
   const int l16 = lane & 15, gq = lane >> 4;
   const int L = p.L;
 
-  load_qk_tile<E, SK>(q + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, use_l2, sQ);
-  load_qk_tile<E, SK>(k + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, use_l2, sK);
-  if (tid < C) sB[tid] = (tid < L) ? sigmoid(to_f32(beta[(size_t)(p.t0 + tid) * hv + h])) : 0.f;
-  load_gate_cumsum<E, SK>(g + ((size_t)p.t0 * hv + h) * D, hv * D, L, sG);
+  {
+    float qx[4][8], kx[4][8], gx[4][8];
+    load_rows4(q + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, qx);
+    load_rows4(k + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, kx);
+    load_rows4(g + ((size_t)p.t0 * hv + h) * D, hv * D, L, gx);
+    const float braw = (tid < L) ? to_f32(beta[(size_t)(p.t0 + tid) * hv + h]) : 0.f;
+    if (use_l2) {
+      l2norm_rows4(qx);
+      l2norm_rows4(kx);
+    }
+    rows4_to_lds<SK>(qx, sQ);
+    rows4_to_lds<SK>(kx, sK);
+    if (tid < C) sB[tid] = (tid < L) ? sigmoid(braw) : 0.f;
+    gate_cumsum<SK>(gx, sG);
+  }
 
   // ---- couplings A_kk (to LDS) and A_qk (to memory), transposed tiles:
   //      rows i (A operand R), columns t (B operand L).
@@ -418,6 +425,9 @@ __global__ __launch_bounds__(256) void wy_kernel(
   }
   __syncthreads();
 
+  float vx[4][8];
+  load_rows4(v + ((size_t)p.t0 * hv + h) * D, hv * D, L, vx);
+
   // ---- T = (I + A_kk)^-1: diagonal 16x16 blocks by substitution (one wave
   //      each, one lane per column), then the off-diagonal blocks by levels.
   if (lane < 16) {
@@ -450,23 +460,9 @@ __global__ __launch_bounds__(256) void wy_kernel(
   __syncthreads();
   if (wave == 0) wy_offdiag_t<SA>(3, 0, sT, sX[0], lane);
 
-  // ---- v into the q slot (q is no longer needed)
-  {
-    const int rg = tid >> 4, j = tid & 15;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int t = rg + 16 * it;
-      float x[8];
-      if (t < L) {
-        load8(v + ((size_t)(p.t0 + t) * hv + h) * D + 8 * j, x);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.f;
-      }
-      *reinterpret_cast<float4*>(&sQ[t][8 * j]) = make_float4(x[0], x[1], x[2], x[3]);
-      *reinterpret_cast<float4*>(&sQ[t][8 * j + 4]) = make_float4(x[4], x[5], x[6], x[7]);
-    }
-  }
+  // ---- v into the q slot (q is no longer needed; its loads were issued
+  //      before the inversion)
+  rows4_to_lds<SK>(vx, sQ);
   __syncthreads();
 
   // ---- w^T = (b kn 2^G)^T T^T and u^T = (b v)^T T^T: rows c (A operand),
@@ -526,20 +522,44 @@ __global__ __launch_bounds__(256) void wy_kernel(
 
 // ----------------------------------------------------------------------- walk
 
-// Cooperative copy of a rows x COLS tile (row stride gstride elements) into LDS
-// rows of stride LS, zero-filling rows >= valid.  16-byte pieces.
-template <typename E, int ROWS, int COLS, int LS, int NT>
-__device__ __forceinline__ void tile_to_lds(E* lds, const E* src, size_t gstride, int valid) {
-  constexpr int EPP = 16 / (int)sizeof(E);
-  constexpr int PPR = COLS / EPP;
-  constexpr int PIECES = ROWS * PPR;
-  for (int pc = threadIdx.x; pc < PIECES; pc += NT) {
-    const int r = pc / PPR, cc = (pc - r * PPR) * EPP;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (r < valid) val = *reinterpret_cast<const uint4*>(src + (size_t)r * gstride + cc);
-    *reinterpret_cast<uint4*>(lds + r * LS + cc) = val;
+// Register stage of a ROWS x COLS tile: each thread holds PER 16-byte pieces.
+// load() only issues global loads (rows >= valid read as zero); store()
+// writes them to LDS rows of stride LS.
+template <typename E, int ROWS, int COLS, int NT>
+struct TileReg {
+  static constexpr int EPP = 16 / (int)sizeof(E);
+  static constexpr int PPR = COLS / EPP;
+  static constexpr int PIECES = ROWS * PPR;
+  static constexpr int PER = (PIECES + NT - 1) / NT;
+  uint4 v[PER];
+  __device__ __forceinline__ void load(const E* src, size_t gstride, int valid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int pc = (int)threadIdx.x + i * NT;
+      const int r = pc / PPR, cc = (pc - r * PPR) * EPP;
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (pc < PIECES && r < valid)
+        v[i] = *reinterpret_cast<const uint4*>(src + (size_t)r * gstride + cc);
+    }
   }
-}
+  template <int LS>
+  __device__ __forceinline__ void store(E* lds) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int pc = (int)threadIdx.x + i * NT;
+      if (pc < PIECES) {
+        const int r = pc / PPR, cc = (pc - r * PPR) * EPP;
+        E* dst = lds + r * LS + cc;
+        if ((LS * sizeof(E)) % 16 == 0) {
+          *reinterpret_cast<uint4*>(dst) = v[i];
+        } else {  // rows only 8-byte aligned
+          reinterpret_cast<uint2*>(dst)[0] = make_uint2(v[i].x, v[i].y);
+          reinterpret_cast<uint2*>(dst)[1] = make_uint2(v[i].z, v[i].w);
+        }
+      }
+    }
+  }
+};
 
 // The inter-chunk walk fused with the output projection.  One workgroup of NW
 // waves per (sequence, value head, block of 16 NW value channels); each wave
@@ -558,7 +578,11 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(
   constexpr bool SPLIT = std::is_same<E, float>::value;
   constexpr int NT = 64 * NW;
   constexpr int BV = 16 * NW;
-  constexpr int PAD = SPLIT ? 4 : 8;
+  // Row strides (elements) of the LDS tiles.  A fragment read has 16 lanes
+  // take 8 (bf16) or 16 (fp32) bytes from 16 consecutive rows at one column;
+  // a stride of 4 elements past a 128-byte multiple puts those rows on
+  // disjoint banks.
+  constexpr int PAD = 4;
   constexpr int S128 = D + PAD, S64 = C + PAD, SU = BV + PAD;
   __shared__ E sW[C * S128];
   __shared__ E sQg[C * S128];
@@ -613,20 +637,44 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(
   }
 
   const int c_first = offs[n];
-  const int nch = offs[n + 1] - c_first;
-  for (int jc = 0; jc < nch; ++jc) {
+  // a malformed cu_seqlens could claim chunks past the bound; never read them
+  const int nch = max(0, min(offs[n + 1], max_chunks) - c_first);
+
+  // K-side tiles of a chunk travel through registers: with bf16 operands the
+  // next chunk's loads are issued before this chunk's products, so their
+  // latency hides behind the MFMA work.
+  constexpr bool PREFETCH = !SPLIT;
+  TileReg<E, C, D, NT> rW, rQ;
+  TileReg<E, C, C, NT> rA;
+  TileReg<E, C, BV, NT> rU;
+  TileReg<E, D, C, NT> rK;
+  float rd = 0.f;
+  auto fetch = [&](int jc) {
     const int c = c_first + jc;
-    if (c >= max_chunks) break;  // only a malformed cu_seqlens gets here
     const int t0 = sp.bos + C * jc;
     const int L = min(C, sp.eos - t0);
+    rW.load(w + ((size_t)t0 * hv + h) * D, (size_t)hv * D, L);
+    rQ.load(qg + ((size_t)t0 * hv + h) * D, (size_t)hv * D, L);
+    rA.load(aqk + ((size_t)t0 * hv + h) * C, (size_t)hv * C, L);
+    rU.load(u + ((size_t)t0 * hv + h) * D + v0, (size_t)hv * D, L);
+    rK.load(kg_t + ((size_t)c * hv + h) * D * C, C, D);
+    if (tid < D) rd = decay[((size_t)c * hv + h) * D + tid];
+  };
+  if (PREFETCH && nch > 0) fetch(0);
+
+  for (int jc = 0; jc < nch; ++jc) {
+    const int t0 = sp.bos + C * jc;
+    const int L = min(C, sp.eos - t0);
+    if (!PREFETCH) fetch(jc);
     __syncthreads();
-    tile_to_lds<E, C, D, S128, NT>(sW, w + ((size_t)t0 * hv + h) * D, (size_t)hv * D, L);
-    tile_to_lds<E, C, D, S128, NT>(sQg, qg + ((size_t)t0 * hv + h) * D, (size_t)hv * D, L);
-    tile_to_lds<E, C, C, S64, NT>(sAq, aqk + ((size_t)t0 * hv + h) * C, (size_t)hv * C, L);
-    tile_to_lds<E, C, BV, SU, NT>(sU, u + ((size_t)t0 * hv + h) * D + v0, (size_t)hv * D, L);
-    tile_to_lds<E, D, C, S64, NT>(sKg, kg_t + ((size_t)c * hv + h) * D * C, C, D);
-    for (int i = tid; i < D; i += NT) sD[i] = decay[((size_t)c * hv + h) * D + i];
+    rW.template store<S128>(sW);
+    rQ.template store<S128>(sQg);
+    rA.template store<S64>(sAq);
+    rU.template store<SU>(sU);
+    rK.template store<S64>(sKg);
+    if (tid < D) sD[tid] = rd;
     __syncthreads();
+    if (PREFETCH && jc + 1 < nch) fetch(jc + 1);
 
     // the state as an MFMA operand (K = key channel, in perm32 order)
     Frag<SPLIT> Hf[4];
