@@ -56,7 +56,8 @@ NUM_STAGE_EVENTS = 7
 
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("chunk_offsets", "qg", "kg_t", "decay", "w", "u", "aqk", "scan", "total")
+                ("chunk_offsets", "zero", "table", "qg", "kg_t", "decay", "w", "u", "aqk", "scan",
+                 "total")
                 ] + [("max_chunks", ctypes.c_int64)]
 
 
@@ -305,9 +306,10 @@ def chunk_kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_sta
 
 def chunk_stages(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=None,
                  use_qk_l2norm_in_kernel=True, groups=1):
-    """Run the staged path and return its intermediates (views of the
-    workspace): chunk_offsets, qg, kg_t, decay, w, u, aqk, plus out and the
-    final state.  For tests and tools."""
+    """Run the staged path and return its intermediates as raw views of the
+    workspace (layouts and the packed fragment order as kda.h documents them):
+    chunk_offsets, qg, kg_t, decay, w, u_t, aqk, plus out and the final
+    state.  For tests and tools."""
     p = _prepare_chunk(q, k, v, g, beta, scale, initial_state, True, cu_seqlens,
                        use_qk_l2norm_in_kernel, None, None, None, None, None)
     keep = {}
@@ -335,7 +337,7 @@ def chunk_stages(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=No
         kg_t=view(lay.kg_t, (mc, H, D, CHUNK), dt, es),
         decay=view(lay.decay, (mc, H, D), torch.float32, 4),
         w=view(lay.w, (T, H, D), dt, es),
-        u=view(lay.u, (T, H, D), dt, es),
+        u_t=view(lay.u, (mc, H, D, CHUNK), dt, es),
         aqk=view(lay.aqk, (T, H, CHUNK), dt, es),
     )
 

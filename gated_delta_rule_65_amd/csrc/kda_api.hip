@@ -106,6 +106,10 @@ kda_status layout_of(const kda_chunk_args* a, kda_ws_layout* L) {
   L->max_chunks = mc;
   L->chunk_offsets = off;
   off = align_up(off + sizeof(int32_t) * ((size_t)a->num_seqs + 1), 256);
+  L->zero = off;
+  off = align_up(off + 1024, 256);
+  L->table = off;
+  off = align_up(off + 16 * (size_t)mc, 256);
   L->qg = off;
   off = align_up(off + T * H * KDA_HEAD_DIM * es, 256);
   L->kg_t = off;
@@ -115,7 +119,7 @@ kda_status layout_of(const kda_chunk_args* a, kda_ws_layout* L) {
   L->w = off;
   off = align_up(off + T * H * KDA_HEAD_DIM * es, 256);
   L->u = off;
-  off = align_up(off + T * H * KDA_HEAD_DIM * es, 256);
+  off = align_up(off + (size_t)mc * H * KDA_HEAD_DIM * KDA_CHUNK * es, 256);
   L->aqk = off;
   off = align_up(off + T * H * KDA_CHUNK * es, 256);
   L->scan = off;
@@ -188,6 +192,8 @@ KDA_API kda_status kda_chunk_fwd(const kda_chunk_args* a) {
   L.num_slots = a->num_slots;
   L.out = a->out;
   L.chunk_offsets = (int32_t*)(ws + W.chunk_offsets);
+  L.zero = ws + W.zero;
+  L.table = ws + W.table;
   L.qg = ws + W.qg; L.kg_t = ws + W.kg_t; L.decay = (float*)(ws + W.decay);
   L.w = ws + W.w; L.u = ws + W.u; L.aqk = ws + W.aqk;
   L.events = a->stage_events;

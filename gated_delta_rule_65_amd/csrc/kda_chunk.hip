@@ -28,6 +28,7 @@
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 #include "kda_mfma.hpp"
+#include "kda_tiles.hpp"
 
 namespace kda {
 
@@ -47,12 +48,17 @@ __device__ __forceinline__ SeqSpan seq_span(const int32_t* cu, int n, int dense_
   return {b, e};
 }
 
-// offs[n] = first chunk of sequence n; offs[N] = number of chunks.
+// offs[n] = first chunk of sequence n; offs[N] = number of chunks; and the
+// chunk records table[c] = (sequence, first token, length, 0) for every c below
+// max_chunks (length 0 past the last chunk), so a kernel finds its chunk with
+// one 16-byte load.
 __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* cu, int N,
                                                              int dense_len, int T,
-                                                             int32_t* offs) {
+                                                             int32_t* offs, int4* table,
+                                                             int max_chunks, uint4* zero) {
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x;
+  if (tid < 64) zero[tid] = make_uint4(0, 0, 0, 0);  // the zero page the walk DMAs from
   const int per = (N + 1023) / 1024;
   const int s0 = min(N, tid * per), s1 = min(N, s0 + per);
   int sum = 0;
@@ -72,30 +78,23 @@ __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* cu, 
   for (int n = s0; n < s1; ++n) {
     offs[n] = run;
     const SeqSpan s = seq_span(cu, n, dense_len, T);
-    run += (s.eos - s.bos + C - 1) / C;
+    for (int t0 = s.bos; t0 < s.eos; t0 += C, ++run)
+      if (run < max_chunks) table[run] = make_int4(n, t0, min(C, s.eos - t0), 0);
   }
-  if (tid == 1023) offs[N] = part[1023];
+  const int total = part[1023];
+  if (tid == 1023) offs[N] = total;
+  for (int c = total + tid; c < max_chunks; c += 1024) table[c] = make_int4(0, 0, 0, 0);
 }
 
 struct ChunkPos {
   int n, t0, L;
 };
 
-// Chunk c -> (sequence, first token, length) by binary search of offs.
-__device__ __forceinline__ bool locate_chunk(int c, const int32_t* offs, int N,
-                                             const int32_t* cu, int dense_len, int T,
-                                             ChunkPos& p) {
-  if (c >= offs[N]) return false;
-  int lo = 0, hi = N - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (offs[mid] <= c) lo = mid;
-    else hi = mid - 1;
-  }
-  const SeqSpan s = seq_span(cu, lo, dense_len, T);
-  p.n = lo;
-  p.t0 = s.bos + C * (c - offs[lo]);
-  p.L = min(C, s.eos - p.t0);
+__device__ __forceinline__ bool locate_chunk(int c, const int4* table, ChunkPos& p) {
+  const int4 e = table[c];
+  p.n = e.x;
+  p.t0 = e.y;
+  p.L = e.z;
   return p.L > 0;
 }
 
@@ -116,34 +115,24 @@ __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
   x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
-__device__ __forceinline__ void store8(bf16* p, const float (&x)[8]) {
-  uint4 u;
-  u.x = (uint32_t)bf16_bits(x[0]) | ((uint32_t)bf16_bits(x[1]) << 16);
-  u.y = (uint32_t)bf16_bits(x[2]) | ((uint32_t)bf16_bits(x[3]) << 16);
-  u.z = (uint32_t)bf16_bits(x[4]) | ((uint32_t)bf16_bits(x[5]) << 16);
-  u.w = (uint32_t)bf16_bits(x[6]) | ((uint32_t)bf16_bits(x[7]) << 16);
-  *reinterpret_cast<uint4*>(p) = u;
-}
-__device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
-  *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
-  *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
-}
-
 // A 64 x 128 token tile of q and k (L2-normalised when asked) into fp32 LDS.
 // Thread mapping: 16 lanes (one DPP row) per token row, 8 channels per lane;
 // all four row loads are issued before the first reduction.
 template <typename E>
 __device__ __forceinline__ void load_rows4(const E* src, int stride_t, int L, float (&x)[4][8]) {
+  // Rows past L re-read row L - 1 (always in bounds, L >= 1) and are zeroed
+  // afterwards, so the four loads go out back to back with no branch.
   const int tid = threadIdx.x, rg = tid >> 4, j = tid & 15;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int t = rg + 16 * it;
-    if (t < L) {
-      load8(src + (size_t)t * stride_t + 8 * j, x[it]);
-    } else {
+    const int t = min(rg + 16 * it, L - 1);
+    load8(src + (size_t)t * stride_t + 8 * j, x[it]);
+  }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[it][e] = 0.f;
-    }
+  for (int it = 0; it < 4; ++it) {
+    const bool live = rg + 16 * it < L;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[it][e] = live ? x[it][e] : 0.f;
   }
 }
 
@@ -160,19 +149,6 @@ __device__ __forceinline__ void l2norm_rows4(float (&x)[4][8]) {
   }
 }
 
-template <int SK>
-__device__ __forceinline__ void rows4_to_lds(const float (&x)[4][8], float (*dst)[SK]) {
-  const int tid = threadIdx.x, rg = tid >> 4, j = tid & 15;
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int t = rg + 16 * it;
-    *reinterpret_cast<float4*>(&dst[t][8 * j]) =
-        make_float4(x[it][0], x[it][1], x[it][2], x[it][3]);
-    *reinterpret_cast<float4*>(&dst[t][8 * j + 4]) =
-        make_float4(x[it][4], x[it][5], x[it][6], x[it][7]);
-  }
-}
-
 // g rows (already in registers, x log2 e applied here) into LDS, then the
 // inclusive cumulative sum over tokens per channel.  Rows past L hold g = 0,
 // so G stays at G_{L-1} there.
@@ -185,7 +161,7 @@ __device__ __forceinline__ void gate_cumsum(const float (&x)[4][8], float (*sG)[
 #pragma unroll
     for (int e = 0; e < 8; ++e) sG[t][8 * j + e] = x[it][e] * LOG2E;
   }
-  __syncthreads();
+  lds_barrier();
   const int c = tid & 127, half = tid >> 7;  // 256 threads: two halves of 32 tokens
   float run = 0.f;
 #pragma unroll 8
@@ -193,106 +169,118 @@ __device__ __forceinline__ void gate_cumsum(const float (&x)[4][8], float (*sG)[
     run += sG[32 * half + tt][c];
     sG[32 * half + tt][c] = run;
   }
-  __syncthreads();
+  lds_barrier();
   if (half == 1) {
     const float base = sG[31][c];
 #pragma unroll 8
     for (int tt = 0; tt < 32; ++tt) sG[32 + tt][c] += base;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // ----------------------------------------------------------------------- prep
 
+// LDS element type of the staged operand tiles: bf16 inputs keep bf16 tiles,
+// fp32 inputs keep fp32 tiles (their MFMA operands are split hi + lo).
+template <typename E> struct TileT;
+template <> struct TileT<bf16> { using T = bf16; };
+template <> struct TileT<float> { using T = float; };
+
+__device__ __forceinline__ void st_elem(bf16* p, float x) { p->x = bf16_bits(x); }
+__device__ __forceinline__ void st_elem(float* p, float x) { *p = x; }
+__device__ __forceinline__ float ld_elem(const bf16* p) { return to_f32(*p); }
+__device__ __forceinline__ float ld_elem(const float* p) { return *p; }
+
 // One workgroup per (chunk, query/key head); loops over the value heads of the
-// GVA group.  Streaming: reads q, k, g once, writes qg, kg_t, decay.
+// GVA group.  Streaming: reads q, k, g once and writes qg (token-major, key
+// channel packed), kg_t (chunk-major, token packed) and decay.  The LDS G tile
+// doubles as the transpose buffer of kg.
 template <typename E>
 __global__ __launch_bounds__(256) void prep_kernel(const E* __restrict__ q,
                                                    const E* __restrict__ k,
                                                    const E* __restrict__ g,
-                                                   const int32_t* __restrict__ cu,
-                                                   int dense_len, int T,
-                                                   const int32_t* __restrict__ offs, int N,
+                                                   const int4* __restrict__ table,
                                                    int hqk, int hv, int use_l2,
                                                    E* __restrict__ qg, E* __restrict__ kg_t,
                                                    float* __restrict__ decay) {
   constexpr int SK = D + 4;
-  __shared__ float sK[C][SK];
   __shared__ float sG[C][SK];
+  E* sKg = reinterpret_cast<E*>(&sG[0][0]);   // kg tile [64][SKG] after G is consumed
+  constexpr int SKG = sizeof(E) == 4 ? D + 4 : D + 8;  // must fit in the G tile
   ChunkPos p;
-  if (!locate_chunk(blockIdx.x, offs, N, cu, dense_len, T, p)) return;
+  if (!locate_chunk(blockIdx.x, table, p)) return;
   const int c = blockIdx.x, hq = blockIdx.y, grp = hv / hqk;
   const int tid = threadIdx.x, rg = tid >> 4, j = tid & 15;
   const int L = p.L;
 
-  // q rows stay in registers, k rows go to LDS (kg is written transposed);
-  // the first head's g rows are fetched together with q and k.
-  float qn[4][8], kx[4][8], gx[4][8];
+  float qn[4][8], kn[4][8], gx[4][8];
   load_rows4(q + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, qn);
-  load_rows4(k + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, kx);
+  load_rows4(k + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, kn);
   load_rows4(g + ((size_t)p.t0 * hv + hq * grp) * D, hv * D, L, gx);
   if (use_l2) {
     l2norm_rows4(qn);
-    l2norm_rows4(kx);
+    l2norm_rows4(kn);
   }
-  rows4_to_lds<SK>(kx, sK);
+  const int cb = 32 * (j >> 2), run0 = cb + pack32(8 * (j & 3)), run1 = cb + pack32(8 * (j & 3) + 4);
 
   for (int gi = 0; gi < grp; ++gi) {
     const int h = hq * grp + gi;
     if (gi > 0) {
-      __syncthreads();
+      lds_barrier();
       load_rows4(g + ((size_t)p.t0 * hv + h) * D, hv * D, L, gx);
     }
     gate_cumsum<SK>(gx, sG);
-    // qg = qn 2^G, token-major
+    float G[4][8], Gl[8];
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) G[it][e] = sG[rg + 16 * it][8 * j + e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) Gl[e] = sG[L - 1][8 * j + e];
+    lds_barrier();  // G consumed; the tile now holds kg
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int t = rg + 16 * it;
+      float xq[8], xk[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        xq[e] = qn[it][e] * exp2_fast(G[it][e]);
+        xk[e] = kn[it][e] * exp2_fast(Gl[e] - G[it][e]);
+        st_elem(sKg + t * SKG + 8 * j + e, xk[e]);
+      }
       if (t < L) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = qn[it][e] * exp2_fast(sG[t][8 * j + e]);
-        store8(qg + ((size_t)(p.t0 + t) * hv + h) * D + 8 * j, x);
+        E* dst = qg + ((size_t)(p.t0 + t) * hv + h) * D;
+        store4(dst + run0, xq[0], xq[1], xq[2], xq[3]);
+        store4(dst + run1, xq[4], xq[5], xq[6], xq[7]);
       }
     }
-    // kg_t[c][h][kk][t] = kn_t[kk] 2^(G_last - G_t), zero past L
+    if (rg == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        decay[((size_t)c * hv + h) * D + 8 * j + e] = exp2_fast(Gl[e]);
+    }
+    lds_barrier();
+    // kg_t[c][h][kk][packed t]: thread -> key channel kk, one 32-token block
     {
-      const int kk = tid >> 1, th = (tid & 1) * 32;
-      const float glast = sG[L - 1][kk];
-      E* dst = kg_t + (((size_t)c * hv + h) * D + kk) * C + th;
+      const int kk = tid >> 1, tb = 32 * (tid & 1);
+      E* dst = kg_t + (((size_t)c * hv + h) * D + kk) * C + tb;
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        float x[8];
+      for (int m4 = 0; m4 < 8; ++m4) {
+        float x[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int t = th + 8 * blk + e;
-          x[e] = (t < L) ? sK[t][kk] * exp2_fast(glast - sG[t][kk]) : 0.f;
-        }
-        store8(dst + 8 * blk, x);
+        for (int r = 0; r < 4; ++r) x[r] = ld_elem(sKg + (tb + unpack32(4 * m4 + r)) * SKG + kk);
+        store4(dst + 4 * m4, x[0], x[1], x[2], x[3]);
       }
     }
-    if (tid < D) decay[((size_t)c * hv + h) * D + tid] = exp2_fast(sG[L - 1][tid]);
   }
 }
 
 // ------------------------------------------------------------------------- WY
 
-// (row block a, column block b) pairs of the lower 64x64 couplings per wave,
-// and the strictly upper blocks of A_qk each wave writes as zeros.
-__constant__ int8_t kWyPairs[4][3][2] = {{{3, 3}, {3, 2}, {3, 1}},
-                                         {{3, 0}, {2, 2}, {2, 1}},
-                                         {{2, 0}, {1, 1}, {-1, -1}},
-                                         {{1, 0}, {0, 0}, {-1, -1}}};
-__constant__ int8_t kWyZero[4][3][2] = {{{-1, -1}, {-1, -1}, {-1, -1}},
-                                        {{-1, -1}, {-1, -1}, {-1, -1}},
-                                        {{0, 1}, {0, 2}, {0, 3}},
-                                        {{1, 2}, {1, 3}, {2, 3}}};
-
 // X = sum_{c in [b, a)} A_ac T_cb into scratch (one 16x16 block per wave).
-template <int SA>
-__device__ __forceinline__ void wy_offdiag_x(int a, int b, const float (*sA)[SA],
-                                             const float (*sT)[SA], float (*sX)[17],
-                                             int lane) {
+template <int SA, int STT>
+__device__ __forceinline__ void wy_offdiag_x(int a, int b, const float* sA, const float* sT,
+                                             float (*sX)[17], int lane) {
   const int col = lane & 15, rq = lane >> 4;
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
@@ -300,111 +288,176 @@ __device__ __forceinline__ void wy_offdiag_x(int a, int b, const float (*sA)[SA]
     float acc = 0.f;
     for (int cb = b; cb < a; ++cb) {
 #pragma unroll
-      for (int m = 0; m < 16; ++m) acc += sA[16 * a + row][16 * cb + m] * sT[16 * cb + m][16 * b + col];
+      for (int m = 0; m < 16; ++m)
+        acc += sA[(16 * a + row) * SA + 16 * cb + m] * sT[(16 * cb + m) * STT + 16 * b + col];
     }
     sX[row][col] = acc;
   }
 }
 
 // T_ab = -T_aa X.
-template <int SA>
-__device__ __forceinline__ void wy_offdiag_t(int a, int b, float (*sT)[SA],
-                                             const float (*sX)[17], int lane) {
+template <int STT>
+__device__ __forceinline__ void wy_offdiag_t(int a, int b, float* sT, const float (*sX)[17],
+                                             int lane) {
   const int col = lane & 15, rq = lane >> 4;
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const int row = 4 * rq + rr;
     float acc = 0.f;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) acc += sT[16 * a + row][16 * a + m] * sX[m][col];
-    sT[16 * a + row][16 * b + col] = -acc;
+    for (int m = 0; m < 16; ++m) acc += sT[(16 * a + row) * STT + 16 * a + m] * sX[m][col];
+    sT[(16 * a + row) * STT + 16 * b + col] = -acc;
   }
 }
 
-// One workgroup (4 waves) per (chunk, value head): couplings on MFMA, the
-// unit-lower inverse by blocked forward substitution in LDS (fp32), then
-// w = T (b kn 2^G) and u = T (b v) on MFMA.
+// 8 consecutive elements of an LDS tile row as floats.
+__device__ __forceinline__ void row8(const bf16* p, float (&x)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(wv[i] << 16);
+    x[2 * i + 1] = __uint_as_float(wv[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void row8(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// Fragment straight from 8 consecutive elements of a bf16 / fp32 LDS row.
+__device__ __forceinline__ FragB frag_row(const bf16* p) {
+  return FragB{__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p))};
+}
+__device__ __forceinline__ FragS frag_row(const float* p) {
+  float x[8];
+  row8(p, x);
+  return make_frag<true>(x);
+}
+
+// One workgroup (4 waves) per (chunk, value head).
+//   phase 0: q, k normalised; G = log2(e) cumsum(g); block-referenced operand
+//            tiles QL = qn 2^(G - G_m), KL = kn 2^(G - G_m), KR = kn 2^(G_m - G)
+//            (m = token 16 a + 7 of the row's 16-token block a) and the
+//            reference rows GM[a] = G_{16 a + 7}.
+//   phase 1: A_kk (to LDS, fp32) and A_qk (to memory) on MFMA:
+//            A[t][i] = L_a[t] . KR[i] 2^(GM[a] - GM[b]) for t in block a, i in b.
+//   phase 2: T = (I + A_kk)^-1 in fp32 by blocked forward substitution.
+//   phase 3: w = T (b KL 2^GM) and u = T (b v) on MFMA.
 template <typename E>
 __global__ __launch_bounds__(256) void wy_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
-    const E* __restrict__ g, const E* __restrict__ beta, const int32_t* __restrict__ cu,
-    int dense_len, int T, const int32_t* __restrict__ offs, int N, int hqk, int hv,
-    int use_l2, E* __restrict__ w_out, E* __restrict__ u_out, E* __restrict__ aqk) {
+    const E* __restrict__ g, const E* __restrict__ beta, const int4* __restrict__ table,
+    int hqk, int hv, int use_l2, E* __restrict__ w_out, E* __restrict__ u_t,
+    E* __restrict__ aqk) {
   constexpr bool SPLIT = std::is_same<E, float>::value;
-  constexpr int SK = D + 4;
-  constexpr int SA = C + 4;
-  __shared__ float sQ[C][SK];  // q, later v
-  __shared__ float sK[C][SK];
-  __shared__ float sG[C][SK];
-  __shared__ float sA[C][SA];
-  __shared__ float sT[C][SA];
-  __shared__ float sB[C];
-  __shared__ float sX[4][16][17];
+  using TE = typename TileT<E>::T;
+  constexpr int ST = D + (SPLIT ? 4 : 8);        // operand tile row stride (elements)
+  constexpr int TILE = C * ST * (int)sizeof(TE);  // bytes of one 64 x 128 operand tile
+  constexpr int SG = D + 4;                       // G tile row stride (fp32)
+  constexpr int SA = C + 4;                       // A_kk / T row stride (fp32)
+  constexpr int AB = C * SA * 4;
+  // regions: R0 = QL | X scratch | V ; R1 = KL ; R2 = KR | T ; R3 = A ; G spans R2..
+  constexpr int R0 = 0, R1 = R0 + TILE, R2 = R1 + TILE;
+  constexpr int R2SZ = TILE > AB ? TILE : AB;
+  constexpr int R3 = R2 + R2SZ;
+  constexpr int RGM = R3 + AB;
+  constexpr int RB = RGM + 4 * D * 4;
+  constexpr int BYTES = RB + C * 4;
+  static_assert(C * SG * 4 <= R2SZ + AB, "G tile must fit in R2 + R3");
+  __shared__ __attribute__((aligned(16))) char smem[BYTES];
+  TE* QL = reinterpret_cast<TE*>(smem + R0);
+  TE* KL = reinterpret_cast<TE*>(smem + R1);
+  TE* KR = reinterpret_cast<TE*>(smem + R2);
+  float* sTt = reinterpret_cast<float*>(smem + R2);
+  float (*sG)[SG] = reinterpret_cast<float (*)[SG]>(smem + R2);
+  float* sA = reinterpret_cast<float*>(smem + R3);
+  float* GM = reinterpret_cast<float*>(smem + RGM);
+  float* sB = reinterpret_cast<float*>(smem + RB);
+  float (*sX)[16][17] = reinterpret_cast<float (*)[16][17]>(smem + R0);
+  TE* sV = reinterpret_cast<TE*>(smem + R0);
 
   ChunkPos p;
-  if (!locate_chunk(blockIdx.x, offs, N, cu, dense_len, T, p)) return;
-  const int h = blockIdx.y, hq = h / (hv / hqk);
+  if (!locate_chunk(blockIdx.x, table, p)) return;
+  const int c = blockIdx.x, h = blockIdx.y, hq = h / (hv / hqk);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, gq = lane >> 4;
+  const int rg = tid >> 4, j = tid & 15;
   const int L = p.L;
 
+  // ---- phase 0
   {
     float qx[4][8], kx[4][8], gx[4][8];
     load_rows4(q + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, qx);
     load_rows4(k + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, kx);
     load_rows4(g + ((size_t)p.t0 * hv + h) * D, hv * D, L, gx);
-    const float braw = (tid < L) ? to_f32(beta[(size_t)(p.t0 + tid) * hv + h]) : 0.f;
+    const float braw = to_f32(beta[(size_t)(p.t0 + min(tid, L - 1)) * hv + h]);
     if (use_l2) {
       l2norm_rows4(qx);
       l2norm_rows4(kx);
     }
-    rows4_to_lds<SK>(qx, sQ);
-    rows4_to_lds<SK>(kx, sK);
-    if (tid < C) sB[tid] = (tid < L) ? sigmoid(braw) : 0.f;
-    gate_cumsum<SK>(gx, sG);
-  }
-
-  // ---- couplings A_kk (to LDS) and A_qk (to memory), transposed tiles:
-  //      rows i (A operand R), columns t (B operand L).
-  {
-    int cur_a = -1;
-    Frag<SPLIT> Lk[4], Lq[4];
-    for (int pi = 0; pi < 3; ++pi) {
-      const int a = kWyPairs[wave][pi][0], b = kWyPairs[wave][pi][1];
-      if (a < 0) break;
-      const int ma = 16 * a + 7;
-      if (a != cur_a) {
-        cur_a = a;
-        const int t = 16 * a + l16;
+    gate_cumsum<SG>(gx, sG);
+    // my rows t = rg + 16 it lie in block it; its reference row is 16 it + 7
+    float G[4][8], Gm[4][8];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          float lk[8], lq[8];
+    for (int it = 0; it < 4; ++it) {
 #pragma unroll
-          for (int jj = 0; jj < 8; ++jj) {
-            const int c = 32 * s + 8 * gq + jj;
-            const float e = exp2_fast(sG[t][c] - sG[ma][c]);
-            lk[jj] = sK[t][c] * e;
-            lq[jj] = sQ[t][c] * e;
-          }
-          Lk[s] = make_frag<SPLIT>(lk);
-          Lq[s] = make_frag<SPLIT>(lq);
-        }
+      for (int e = 0; e < 8; ++e) {
+        G[it][e] = sG[rg + 16 * it][8 * j + e];
+        Gm[it][e] = sG[16 * it + 7][8 * j + e];
       }
-      f32x4_t acck = {0.f, 0.f, 0.f, 0.f}, accq = {0.f, 0.f, 0.f, 0.f};
+    }
+    lds_barrier();  // G consumed; R2/R3 are free
+    if (rg == 7) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) GM[it * D + 8 * j + e] = G[it][e];
+    }
+    if (tid < C) sB[tid] = (tid < L) ? sigmoid(braw) : 0.f;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int t = rg + 16 * it;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float up = exp2_fast(G[it][e] - Gm[it][e]);
+        const float dn = exp2_fast(Gm[it][e] - G[it][e]);
+        st_elem(QL + t * ST + 8 * j + e, qx[it][e] * up);
+        st_elem(KL + t * ST + 8 * j + e, kx[it][e] * up);
+        st_elem(KR + t * ST + 8 * j + e, kx[it][e] * dn);
+      }
+    }
+  }
+  lds_barrier();
+
+  // ---- phase 1: couplings, transposed tiles (rows i from KR, columns t from L).
+  //      Each wave takes a fixed set of (row block a, column block b) pairs
+  //      and writes the strictly upper blocks of A_qk as zeros.
+  {
+    auto pair = [&](const int a, const int b) {
+      const int t = 16 * a + l16;
       const int i = 16 * b + l16;
+      f32x4_t acck = {0.f, 0.f, 0.f, 0.f}, accq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        float r[8];
+        const int c0 = 32 * s + 8 * gq;
+        const Frag<SPLIT> Lk = frag_row(KL + t * ST + c0);
+        const Frag<SPLIT> Lq = frag_row(QL + t * ST + c0);
+        Frag<SPLIT> R;
+        if (a == b) {
+          R = frag_row(KR + i * ST + c0);
+        } else {
+          float x[8];
+          row8(KR + i * ST + c0, x);
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int c = 32 * s + 8 * gq + jj;
-          r[jj] = sK[i][c] * exp2_fast(sG[ma][c] - sG[i][c]);
+          for (int e = 0; e < 8; ++e) x[e] *= exp2_fast(GM[a * D + c0 + e] - GM[b * D + c0 + e]);
+          R = make_frag<SPLIT>(x);
         }
-        const Frag<SPLIT> R = make_frag<SPLIT>(r);
-        mma(acck, R, Lk[s]);
-        mma(accq, R, Lq[s]);
+        mma(acck, R, Lk);
+        mma(accq, R, Lq);
       }
-      const int t = 16 * a + l16;
       const int i0 = 16 * b + 4 * gq;
       float ak[4], aq[4];
 #pragma unroll
@@ -412,184 +465,171 @@ __global__ __launch_bounds__(256) void wy_kernel(
         ak[r] = (i0 + r < t) ? acck[r] * sB[t] : 0.f;
         aq[r] = (i0 + r <= t) ? accq[r] : 0.f;
       }
-      store4(&sA[t][i0], ak[0], ak[1], ak[2], ak[3]);
-      if (t < L) store4(aqk + ((size_t)(p.t0 + t) * hv + h) * C + i0, aq[0], aq[1], aq[2], aq[3]);
-    }
-#pragma unroll
-    for (int zi = 0; zi < 3; ++zi) {
-      const int a = kWyZero[wave][zi][0], b = kWyZero[wave][zi][1];
-      if (a < 0) break;
+      store4(sA + t * SA + i0, ak[0], ak[1], ak[2], ak[3]);
+      if (t < L)
+        store4(aqk + ((size_t)(p.t0 + t) * hv + h) * C + packed_index(i0), aq[0], aq[1], aq[2],
+               aq[3]);
+    };
+    auto zero = [&](const int a, const int b) {
       const int t = 16 * a + l16;
-      if (t < L) store4(aqk + ((size_t)(p.t0 + t) * hv + h) * C + 16 * b + 4 * gq, 0.f, 0.f, 0.f, 0.f);
+      if (t < L)
+        store4(aqk + ((size_t)(p.t0 + t) * hv + h) * C + packed_index(16 * b + 4 * gq), 0.f,
+               0.f, 0.f, 0.f);
+    };
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    if (wu == 0) {
+      pair(3, 3); pair(3, 2); pair(3, 1);
+    } else if (wu == 1) {
+      pair(3, 0); pair(2, 2); pair(2, 1);
+    } else if (wu == 2) {
+      pair(2, 0); pair(1, 1); zero(0, 1); zero(0, 2); zero(0, 3);
+    } else {
+      pair(1, 0); pair(0, 0); zero(1, 2); zero(1, 3); zero(2, 3);
     }
   }
-  __syncthreads();
-
+  // v rows are fetched now; they land during the inversion
   float vx[4][8];
   load_rows4(v + ((size_t)p.t0 * hv + h) * D, hv * D, L, vx);
+  lds_barrier();
 
-  // ---- T = (I + A_kk)^-1: diagonal 16x16 blocks by substitution (one wave
-  //      each, one lane per column), then the off-diagonal blocks by levels.
+  // ---- phase 2: T = (I + A_kk)^-1 (KR is dead: T takes its place)
   if (lane < 16) {
+    // lane = column of the diagonal block; row r + 1 of A is read while row r
+    // is substituted (every lane reads the same row: LDS broadcast)
     const int a = wave;
+    const float* arow = sA + 16 * a * SA + 16 * a;
     float x[16];
+    float4 cur[4], nxt[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) cur[q4] = *reinterpret_cast<const float4*>(arow + 4 * q4);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
+      if (r < 15) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          nxt[q4] = *reinterpret_cast<const float4*>(arow + (r + 1) * SA + 4 * q4);
+      }
+      const float av[16] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w, cur[1].x, cur[1].y,
+                            cur[1].z, cur[1].w, cur[2].x, cur[2].y, cur[2].z, cur[2].w,
+                            cur[3].x, cur[3].y, cur[3].z, cur[3].w};
       float val = (r == lane) ? 1.f : 0.f;
 #pragma unroll
-      for (int ii = 0; ii < r; ++ii) val -= sA[16 * a + r][16 * a + ii] * x[ii];
+      for (int ii = 0; ii < r; ++ii) val -= av[ii] * x[ii];
       x[r] = val;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) cur[q4] = nxt[q4];
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sT[16 * a + r][16 * a + lane] = x[r];
+    for (int r = 0; r < 16; ++r) sTt[(16 * a + r) * SA + 16 * a + lane] = x[r];
   }
   for (int idx = tid; idx < C * C; idx += 256) {
     const int t = idx >> 6, i = idx & 63;
-    if ((i >> 4) > (t >> 4)) sT[t][i] = 0.f;
+    if ((i >> 4) > (t >> 4)) sTt[t * SA + i] = 0.f;
   }
-  __syncthreads();
-  if (wave < 3) wy_offdiag_x<SA>(wave + 1, wave, sA, sT, sX[wave], lane);
-  __syncthreads();
-  if (wave < 3) wy_offdiag_t<SA>(wave + 1, wave, sT, sX[wave], lane);
-  __syncthreads();
-  if (wave < 2) wy_offdiag_x<SA>(wave + 2, wave, sA, sT, sX[wave], lane);
-  __syncthreads();
-  if (wave < 2) wy_offdiag_t<SA>(wave + 2, wave, sT, sX[wave], lane);
-  __syncthreads();
-  if (wave == 0) wy_offdiag_x<SA>(3, 0, sA, sT, sX[0], lane);
-  __syncthreads();
-  if (wave == 0) wy_offdiag_t<SA>(3, 0, sT, sX[0], lane);
+  lds_barrier();
+  if (wave < 3) wy_offdiag_x<SA, SA>(wave + 1, wave, sA, sTt, sX[wave], lane);
+  lds_barrier();
+  if (wave < 3) wy_offdiag_t<SA>(wave + 1, wave, sTt, sX[wave], lane);
+  lds_barrier();
+  if (wave < 2) wy_offdiag_x<SA, SA>(wave + 2, wave, sA, sTt, sX[wave], lane);
+  lds_barrier();
+  if (wave < 2) wy_offdiag_t<SA>(wave + 2, wave, sTt, sX[wave], lane);
+  lds_barrier();
+  if (wave == 0) wy_offdiag_x<SA, SA>(3, 0, sA, sTt, sX[0], lane);
+  lds_barrier();
+  if (wave == 0) wy_offdiag_t<SA>(3, 0, sTt, sX[0], lane);
+  lds_barrier();
+  // v tile into R0 (the X scratch is dead)
+#pragma unroll
+  for (int it = 0; it < 4; ++it)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st_elem(sV + (rg + 16 * it) * ST + 8 * j + e, vx[it][e]);
+  lds_barrier();
 
-  // ---- v into the q slot (q is no longer needed; its loads were issued
-  //      before the inversion)
-  rows4_to_lds<SK>(vx, sQ);
-  __syncthreads();
-
-  // ---- w^T = (b kn 2^G)^T T^T and u^T = (b v)^T T^T: rows c (A operand),
-  //      columns t (B operand = T^T), K = i; T is lower, so tiles of t < 32
-  //      need only i < 32.
-  {
-    Frag<SPLIT> Tf[4][2];
+  // ---- phase 3
+  Frag<SPLIT> Tf[4][2];  // T rows t = 16 ta + l16, K = i = 32 s + 8 gq + jj
 #pragma unroll
-    for (int ta = 0; ta < 4; ++ta) {
+  for (int ta = 0; ta < 4; ++ta)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if (s == 1 && ta < 2) continue;
-        const int t = 16 * ta + l16;
-        float x[8];
+    for (int s = 0; s < 2; ++s) {
+      if (s == 1 && ta < 2) continue;
+      float x[8];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) x[jj] = sT[t][32 * s + 8 * gq + jj];
-        Tf[ta][s] = make_frag<SPLIT>(x);
-      }
+      for (int jj = 0; jj < 8; ++jj) x[jj] = sTt[(16 * ta + l16) * SA + 32 * s + 8 * gq + jj];
+      Tf[ta][s] = make_frag<SPLIT>(x);
     }
 #pragma unroll
-    for (int cbi = 0; cbi < 2; ++cbi) {
-      const int cb = 2 * wave + cbi;
-      const int c = 16 * cb + l16;
-      Frag<SPLIT> Yk[2], Yv[2];
+  for (int cbi = 0; cbi < 2; ++cbi) {
+    const int cb = 2 * wave + cbi;
+    const int cc = 16 * cb + l16;  // key channel (w) / value channel (u) of this lane
+    Frag<SPLIT> Yk[2], Yv[2];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        float yk[8], yv[8];
+    for (int s = 0; s < 2; ++s) {
+      float yk[8], yv[8];
+      const int blk = 2 * s + (gq >> 1);  // 16-token block of i = 32 s + 8 gq + jj
+      const float gm = exp2_fast(GM[blk * D + cc]);
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int i = 32 * s + 8 * gq + jj;
-          const float bi = sB[i];
-          yk[jj] = bi * sK[i][c] * exp2_fast(sG[i][c]);
-          yv[jj] = bi * sQ[i][c];
-        }
-        Yk[s] = make_frag<SPLIT>(yk);
-        Yv[s] = make_frag<SPLIT>(yv);
+      for (int jj = 0; jj < 8; ++jj) {
+        const int i = 32 * s + 8 * gq + jj;
+        const float bi = sB[i];
+        yk[jj] = bi * ld_elem(KL + i * ST + cc) * gm;
+        yv[jj] = bi * ld_elem(sV + i * ST + cc);
       }
+      Yk[s] = make_frag<SPLIT>(yk);
+      Yv[s] = make_frag<SPLIT>(yv);
+    }
 #pragma unroll
-      for (int ta = 0; ta < 4; ++ta) {
-        f32x4_t aw = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
-        mma(aw, Yk[0], Tf[ta][0]);
-        mma(au, Yv[0], Tf[ta][0]);
-        if (ta >= 2) {
-          mma(aw, Yk[1], Tf[ta][1]);
-          mma(au, Yv[1], Tf[ta][1]);
-        }
-        const int t = 16 * ta + l16;
-        if (t < L) {
-          const size_t o = ((size_t)(p.t0 + t) * hv + h) * D + 16 * cb + 4 * gq;
-          store4(w_out + o, aw[0], aw[1], aw[2], aw[3]);
-          store4(u_out + o, au[0], au[1], au[2], au[3]);
-        }
+    for (int ta = 0; ta < 4; ++ta) {
+      f32x4_t aw = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+      mma(aw, Yk[0], Tf[ta][0]);   // w^T: rows key channel, cols t
+      mma(au, Tf[ta][0], Yv[0]);   // u:   rows t, cols value channel
+      if (ta >= 2) {
+        mma(aw, Yk[1], Tf[ta][1]);
+        mma(au, Tf[ta][1], Yv[1]);
       }
+      const int t = 16 * ta + l16;
+      if (t < L) {
+        E* dst = w_out + ((size_t)(p.t0 + t) * hv + h) * D + packed_index(16 * cb + 4 * gq);
+        store4(dst, aw[0], aw[1], aw[2], aw[3]);
+      }
+      // u_t[c][h][v][packed t]: rows t = 16 ta + 4 gq + r of column cc (zero past L)
+      E* du = u_t + (((size_t)c * hv + h) * D + cc) * C + packed_index(16 * ta + 4 * gq);
+      store4(du, au[0], au[1], au[2], au[3]);
     }
   }
 }
 
 // ----------------------------------------------------------------------- walk
 
-// Register stage of a ROWS x COLS tile: each thread holds PER 16-byte pieces.
-// load() only issues global loads (rows >= valid read as zero); store()
-// writes them to LDS rows of stride LS.
-template <typename E, int ROWS, int COLS, int NT>
-struct TileReg {
-  static constexpr int EPP = 16 / (int)sizeof(E);
-  static constexpr int PPR = COLS / EPP;
-  static constexpr int PIECES = ROWS * PPR;
-  static constexpr int PER = (PIECES + NT - 1) / NT;
-  uint4 v[PER];
-  __device__ __forceinline__ void load(const E* src, size_t gstride, int valid) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int pc = (int)threadIdx.x + i * NT;
-      const int r = pc / PPR, cc = (pc - r * PPR) * EPP;
-      v[i] = make_uint4(0, 0, 0, 0);
-      if (pc < PIECES && r < valid)
-        v[i] = *reinterpret_cast<const uint4*>(src + (size_t)r * gstride + cc);
-    }
-  }
-  template <int LS>
-  __device__ __forceinline__ void store(E* lds) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int pc = (int)threadIdx.x + i * NT;
-      if (pc < PIECES) {
-        const int r = pc / PPR, cc = (pc - r * PPR) * EPP;
-        E* dst = lds + r * LS + cc;
-        if ((LS * sizeof(E)) % 16 == 0) {
-          *reinterpret_cast<uint4*>(dst) = v[i];
-        } else {  // rows only 8-byte aligned
-          reinterpret_cast<uint2*>(dst)[0] = make_uint2(v[i].x, v[i].y);
-          reinterpret_cast<uint2*>(dst)[1] = make_uint2(v[i].z, v[i].w);
-        }
-      }
-    }
-  }
-};
-
 // The inter-chunk walk fused with the output projection.  One workgroup of NW
 // waves per (sequence, value head, block of 16 NW value channels); each wave
 // owns 16 value channels and keeps its 128 x 16 slice of the state in MFMA
-// accumulators (fp32) for the whole sequence.  Per chunk, all waves share the
-// K-side operands (w, qg, kg_t, aqk, decay) staged once in LDS.
+// accumulators (fp32) for the whole sequence.  The K-side tiles of a chunk
+// (w, qg, aqk, kg_t, the block's u_t rows, decay) arrive by LDS DMA into a
+// two-stage ring (one stage for fp32 operands), so the next chunk's tiles
+// stream in while this chunk's products run.
 template <typename E, int NW>
 __global__ __launch_bounds__(64 * NW) void walk_kernel(
     const E* __restrict__ qg, const E* __restrict__ kg_t, const float* __restrict__ decay,
-    const E* __restrict__ w, const E* __restrict__ u, const E* __restrict__ aqk,
+    const E* __restrict__ w, const E* __restrict__ u_t, const E* __restrict__ aqk,
     const int32_t* __restrict__ cu, int dense_len, int T, const int32_t* __restrict__ offs,
     int N, int hv, float scale, const float* __restrict__ init, float* __restrict__ fin,
     float* __restrict__ cache, const int32_t* __restrict__ slots,
     const uint8_t* __restrict__ has_init, int num_slots, E* __restrict__ out, int nvb,
-    int units, int max_chunks) {
+    int units, int max_chunks, const uint4* __restrict__ zero) {
   constexpr bool SPLIT = std::is_same<E, float>::value;
+  constexpr int STAGES = SPLIT ? 1 : 2;
   constexpr int NT = 64 * NW;
   constexpr int BV = 16 * NW;
-  // Row strides (elements) of the LDS tiles.  A fragment read has 16 lanes
-  // take 8 (bf16) or 16 (fp32) bytes from 16 consecutive rows at one column;
-  // a stride of 4 elements past a 128-byte multiple puts those rows on
-  // disjoint banks.
-  constexpr int PAD = 4;
-  constexpr int S128 = D + PAD, S64 = C + PAD, SU = BV + PAD;
-  __shared__ E sW[C * S128];
-  __shared__ E sQg[C * S128];
-  __shared__ E sKg[D * S64];
-  __shared__ E sAq[C * S64];
-  __shared__ E sU[C * SU];
-  __shared__ float sD[D];
+  constexpr int EPP = 16 / (int)sizeof(E);  // elements per 16-byte piece
+  constexpr int P128 = D / EPP, P64 = C / EPP;
+  constexpr int OFF_W = 0, OFF_Q = OFF_W + C * P128, OFF_A = OFF_Q + C * P128;
+  constexpr int OFF_K = OFF_A + C * P64, OFF_U = OFF_K + D * P64, OFF_D = OFF_U + BV * P64;
+  constexpr int STAGE = OFF_D + 64;
+  // two distinct arrays (not one indexed ring) so that the compiler can tell
+  // the stage being filled from the stage being read
+  __shared__ uint4 smemA[STAGE];
+  __shared__ uint4 smemB[STAGES == 2 ? STAGE : 1];
 
   // The nvb blocks of one (sequence, head) get ids with equal id % 8, so they
   // land on one XCD and share its L2 for the K-side tiles.
@@ -598,10 +638,12 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(
   const int vb = rem >> 3, unit = blk * 8 + (rem & 7);
   if (unit >= units) return;
   const int n = unit / hv, h = unit - n * hv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, gq = lane >> 4;
   const int v0 = vb * BV;                  // first value channel of the block
-  const int vcol = v0 + 16 * wave + l16;   // this lane's C-tile column
+  const int vl = 16 * wave + l16;          // this lane's C-tile column inside the block
+  const int vcol = v0 + vl;
   const SeqSpan sp = seq_span(cu, n, dense_len, T);
 
   const float* src = nullptr;
@@ -640,43 +682,56 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(
   // a malformed cu_seqlens could claim chunks past the bound; never read them
   const int nch = max(0, min(offs[n + 1], max_chunks) - c_first);
 
-  // K-side tiles of a chunk travel through registers: with bf16 operands the
-  // next chunk's loads are issued before this chunk's products, so their
-  // latency hides behind the MFMA work.
-  constexpr bool PREFETCH = !SPLIT;
-  TileReg<E, C, D, NT> rW, rQ;
-  TileReg<E, C, C, NT> rA;
-  TileReg<E, C, BV, NT> rU;
-  TileReg<E, D, C, NT> rK;
-  float rd = 0.f;
-  auto fetch = [&](int jc) {
+  // K-side tiles of chunk jc into a stage, in two parts: w and qg (needed
+  // first), then aqk, kg_t, the block's u_t rows and decay.
+  auto issue_wq = [&](int jc, uint4* base) {
+    const int t0 = sp.bos + C * jc;
+    const int L = min(C, sp.eos - t0);
+    const size_t rowb = (size_t)hv * D * sizeof(E);
+    dma_tile<C, P128, NW, true>(base + OFF_W, w + ((size_t)t0 * hv + h) * D, rowb, L, zero,
+                                wave, lane);
+    dma_tile<C, P128, NW, true>(base + OFF_Q, qg + ((size_t)t0 * hv + h) * D, rowb, L, zero,
+                                wave, lane);
+  };
+  auto issue_rest = [&](int jc, uint4* base) {
     const int c = c_first + jc;
     const int t0 = sp.bos + C * jc;
     const int L = min(C, sp.eos - t0);
-    rW.load(w + ((size_t)t0 * hv + h) * D, (size_t)hv * D, L);
-    rQ.load(qg + ((size_t)t0 * hv + h) * D, (size_t)hv * D, L);
-    rA.load(aqk + ((size_t)t0 * hv + h) * C, (size_t)hv * C, L);
-    rU.load(u + ((size_t)t0 * hv + h) * D + v0, (size_t)hv * D, L);
-    rK.load(kg_t + ((size_t)c * hv + h) * D * C, C, D);
-    if (tid < D) rd = decay[((size_t)c * hv + h) * D + tid];
+    dma_tile<C, P64, NW, true>(base + OFF_A, aqk + ((size_t)t0 * hv + h) * C,
+                               (size_t)hv * C * sizeof(E), L, zero, wave, lane);
+    dma_tile<D, P64, NW, false>(base + OFF_K, kg_t + ((size_t)c * hv + h) * D * C,
+                                C * sizeof(E), D, zero, wave, lane);
+    dma_tile<BV, P64, NW, false>(base + OFF_U, u_t + (((size_t)c * hv + h) * D + v0) * C,
+                                 C * sizeof(E), BV, zero, wave, lane);
+    if (wave == NW - 1) {
+      // decay: 32 pieces, lanes 32..63 fill the pad from the zero page
+      const char* gp = lane < 32 ? (const char*)(decay + ((size_t)c * hv + h) * D) + 16 * lane
+                                 : (const char*)zero;
+      __builtin_amdgcn_global_load_lds(gp, (lds_vptr)(base + OFF_D), 16, 0, 0);
+    }
   };
-  if (PREFETCH && nch > 0) fetch(0);
+  auto issue = [&](int jc, uint4* base) {
+    issue_wq(jc, base);
+    issue_rest(jc, base);
+  };
+  if (nch > 0) issue(0, smemA);
 
-  for (int jc = 0; jc < nch; ++jc) {
+  auto body = [&](int jc, uint4* cur, uint4* nxt) {
     const int t0 = sp.bos + C * jc;
     const int L = min(C, sp.eos - t0);
-    if (!PREFETCH) fetch(jc);
-    __syncthreads();
-    rW.template store<S128>(sW);
-    rQ.template store<S128>(sQg);
-    rA.template store<S64>(sAq);
-    rU.template store<SU>(sU);
-    rK.template store<S64>(sKg);
-    if (tid < D) sD[tid] = rd;
-    __syncthreads();
-    if (PREFETCH && jc + 1 < nch) fetch(jc + 1);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA of chunk jc has landed
+    lds_barrier();                // ... and every other wave's
+    const bool more = STAGES == 2 && jc + 1 < nch;
+    if (SPLIT && more) issue_wq(jc + 1, nxt);
+    const uint4* stg = cur;
+    const uint4* tW = stg + OFF_W;
+    const uint4* tQ = stg + OFF_Q;
+    const uint4* tA = stg + OFF_A;
+    const uint4* tK = stg + OFF_K;
+    const uint4* tU = stg + OFF_U;
+    const float* sD = reinterpret_cast<const float*>(stg + OFF_D);
 
-    // the state as an MFMA operand (K = key channel, in perm32 order)
+    // the state as an MFMA operand (K = key channel, perm32 order)
     Frag<SPLIT> Hf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -684,62 +739,155 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(
                     S[2 * s + 1][0], S[2 * s + 1][1], S[2 * s + 1][2], S[2 * s + 1][3]};
       Hf[s] = make_frag<SPLIT>(x);
     }
-    // HW = w S (rows t, cols v) and O^T = (qg S)^T (rows v, cols t)
+    // u values of this lane's column, read early
+    float uv[2][8];
+    unit_vals<P64>(tU, vl, gq, SPLIT, uv[0]);
+    unit_vals<P64>(tU, vl, 4 + gq, SPLIT, uv[1]);
+
+    // HW = w S (rows t, cols v) and O^T = (qg S)^T (rows v, cols t); the
+    // fragments of K step s + 1 are read while step s multiplies.
     f32x4_t HW[4], O[4];
 #pragma unroll
     for (int ta = 0; ta < 4; ++ta) {
       HW[ta] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       O[ta] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    if constexpr (!SPLIT) {
+      FragB fw[2][4], fq[2][4];
+      auto load_k = [&](int s, int buf) {
+#pragma unroll
+        for (int ta = 0; ta < 4; ++ta) {
+          fw[buf][ta] = frag_bf16<P128>(tW, 16 * ta + l16, 4 * s + gq);
+          fq[buf][ta] = frag_bf16<P128>(tQ, 16 * ta + l16, 4 * s + gq);
+        }
+      };
+      // The next chunk's w / qg DMA (2 x WQ_PER wave instructions) is spread
+      // over the K steps, so the wave keeps issuing products while the memory
+      // pipeline takes it.
+      constexpr int WQ_PER = C * P128 / 64 / NW;
+      const int tn = sp.bos + C * (jc + 1);
+      const int Ln = min(C, sp.eos - tn);
+      const size_t rowb = (size_t)hv * D * sizeof(E);
+      const E* wsrc = w + ((size_t)tn * hv + h) * D;
+      const E* qsrc = qg + ((size_t)tn * hv + h) * D;
+      load_k(0, 0);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const E* wr = sW + (16 * ta + l16) * S128 + 32 * s + 4 * gq;
-        mma(HW[ta], frag_from(wr, wr + 16), Hf[s]);
-        const E* qr = sQg + (16 * ta + l16) * S128 + 32 * s + 4 * gq;
-        mma(O[ta], Hf[s], frag_from(qr, qr + 16));
+        if (s < 3) load_k(s + 1, (s + 1) & 1);
+        if (more) {
+#pragma unroll
+          for (int m = 0; m < 2 * WQ_PER / 4; ++m) {
+            const int mm = (2 * WQ_PER / 4) * s + m;
+            if (mm < WQ_PER)
+              dma_one<C, P128, NW, true>(mm, nxt + OFF_W, wsrc, rowb, Ln, zero, wave, lane);
+            else
+              dma_one<C, P128, NW, true>(mm - WQ_PER, nxt + OFF_Q, qsrc, rowb, Ln, zero, wave,
+                                         lane);
+          }
+        }
+#pragma unroll
+        for (int ta = 0; ta < 4; ++ta) {
+          mma(HW[ta], fw[s & 1][ta], Hf[s]);
+          mma(O[ta], Hf[s], fq[s & 1][ta]);
+        }
       }
+      // Pin the schedule: the 8 fragment reads of a K step go out while the
+      // 8 products of the previous step run.
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS read
+#pragma unroll
+      for (int i = 0; i < 24; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int ta = 0; ta < 4; ++ta) {
+          mma(HW[ta], frag_f32<P128>(tW, 16 * ta + l16, 4 * s + gq), Hf[s]);
+          mma(O[ta], Hf[s], frag_f32<P128>(tQ, 16 * ta + l16, 4 * s + gq));
+        }
     }
-    // U = u - w S   (C layout: col v, rows t = 16 ta + 4 gq + r)
+    if (more) issue_rest(jc + 1, nxt);
+    // U = u - w S  (C layout: col v, rows t = 16 ta + 4 gq + r)
     Frag<SPLIT> Uf[2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       float x[8];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int ta = 2 * s2 + half;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * ta + 4 * gq + r;
-          x[4 * half + r] = to_f32(sU[t * SU + 16 * wave + l16]) - HW[ta][r];
-        }
+      for (int r = 0; r < 4; ++r) {
+        x[r] = uv[s2][r] - HW[2 * s2][r];
+        x[4 + r] = uv[s2][4 + r] - HW[2 * s2 + 1][r];
       }
       Uf[s2] = make_frag<SPLIT>(x);
     }
-    // O^T += U^T A_qk^T  (A_qk lower: t < 32 needs i < 32 only)
+    if constexpr (!SPLIT) {
+      // A_qk fragments (A_qk lower: t < 32 needs i < 32 only), kg^T fragments
+      FragB fa[4][2], fk[8][2];
+#pragma unroll
+      for (int ta = 0; ta < 4; ++ta)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+          if (!(s2 == 1 && ta < 2)) fa[ta][s2] = frag_bf16<P64>(tA, 16 * ta + l16, 4 * s2 + gq);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) fk[kb][s2] = frag_bf16<P64>(tK, 16 * kb + l16, 4 * s2 + gq);
+      // O^T += U^T A_qk^T
+#pragma unroll
+      for (int ta = 0; ta < 4; ++ta) {
+        mma(O[ta], Uf[0], fa[ta][0]);
+        if (ta >= 2) mma(O[ta], Uf[1], fa[ta][1]);
+      }
+#pragma unroll
+      for (int kb = 4; kb < 8; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) fk[kb][s2] = frag_bf16<P64>(tK, 16 * kb + l16, 4 * s2 + gq);
+      // S <- diag(d) S + kg^T U   (rows k, cols v, K = t)
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        const float4 d4 = *reinterpret_cast<const float4*>(sD + 16 * kb + 4 * gq);
+        S[kb][0] *= d4.x;
+        S[kb][1] *= d4.y;
+        S[kb][2] *= d4.z;
+        S[kb][3] *= d4.w;
+        mma(S[kb], fk[kb][0], Uf[0]);
+        mma(S[kb], fk[kb][1], Uf[1]);
+      }
+    } else {
+#pragma unroll
+      for (int ta = 0; ta < 4; ++ta) {
+        mma(O[ta], Uf[0], frag_f32<P64>(tA, 16 * ta + l16, gq));
+        if (ta >= 2) mma(O[ta], Uf[1], frag_f32<P64>(tA, 16 * ta + l16, 4 + gq));
+      }
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        const float4 d4 = *reinterpret_cast<const float4*>(sD + 16 * kb + 4 * gq);
+        S[kb][0] *= d4.x;
+        S[kb][1] *= d4.y;
+        S[kb][2] *= d4.z;
+        S[kb][3] *= d4.w;
+        mma(S[kb], frag_f32<P64>(tK, 16 * kb + l16, gq), Uf[0]);
+        mma(S[kb], frag_f32<P64>(tK, 16 * kb + l16, 4 + gq), Uf[1]);
+      }
+    }
 #pragma unroll
     for (int ta = 0; ta < 4; ++ta) {
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        if (s2 == 1 && ta < 2) continue;
-        const E* ar = sAq + (16 * ta + l16) * S64 + 32 * s2 + 4 * gq;
-        mma(O[ta], Uf[s2], frag_from(ar, ar + 16));
-      }
       const int t = 16 * ta + l16;
       if (t < L) {
         E* op = out + ((size_t)(t0 + t) * hv + h) * D + v0 + 16 * wave + 4 * gq;
         store4(op, scale * O[ta][0], scale * O[ta][1], scale * O[ta][2], scale * O[ta][3]);
       }
     }
-    // S <- diag(d) S + kg^T U   (rows k, cols v, K = t)
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[kb][r] *= sD[16 * kb + 4 * gq + r];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const E* kr = sKg + (16 * kb + l16) * S64 + 32 * s2 + 4 * gq;
-        mma(S[kb], frag_from(kr, kr + 16), Uf[s2]);
-      }
+    if (STAGES == 1 && jc + 1 < nch) {
+      lds_barrier();  // everyone is done with the single stage
+      issue(jc + 1, cur);
     }
+  };
+  for (int jc = 0; jc < nch; jc += 2) {
+    body(jc, smemA, smemB);
+    if (jc + 1 < nch) body(jc + 1, STAGES == 2 ? smemB : smemA, smemA);
   }
   if (dst) {
 #pragma unroll
@@ -763,31 +911,43 @@ static hipError_t launch_staged_t(const ChunkLaunch& L) {
   const int T = (int)L.total_tokens;
   const int dense_len = L.cu ? 0 : (N > 0 ? T / N : 0);
   hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(1024), 0, st, L.cu, N, dense_len, T,
-                     L.chunk_offsets);
+                     L.chunk_offsets, (int4*)L.table, (int)L.max_chunks, (uint4*)L.zero);
   mark(L, 1);
   if (L.max_chunks > 0 && T > 0) {
     hipLaunchKernelGGL(prep_kernel<E>, dim3((unsigned)L.max_chunks, L.hqk), dim3(256), 0, st,
-                       (const E*)L.q, (const E*)L.k, (const E*)L.g, L.cu, dense_len, T,
-                       L.chunk_offsets, N, L.hqk, L.hv, L.use_l2, (E*)L.qg, (E*)L.kg_t,
-                       L.decay);
+                       (const E*)L.q, (const E*)L.k, (const E*)L.g, (const int4*)L.table,
+                       L.hqk, L.hv, L.use_l2, (E*)L.qg, (E*)L.kg_t, L.decay);
     mark(L, 2);
     hipLaunchKernelGGL(wy_kernel<E>, dim3((unsigned)L.max_chunks, L.hv), dim3(256), 0, st,
                        (const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.g,
-                       (const E*)L.beta, L.cu, dense_len, T, L.chunk_offsets, N, L.hqk, L.hv,
-                       L.use_l2, (E*)L.w, (E*)L.u, (E*)L.aqk);
+                       (const E*)L.beta, (const int4*)L.table, L.hqk, L.hv, L.use_l2,
+                       (E*)L.w, (E*)L.u, (E*)L.aqk);
   } else {
     mark(L, 2);
   }
   mark(L, 3);
-  constexpr int NW = 4;
-  const int nvb = D / (16 * NW);
+  // Few (sequence, head) units: split the value channels over more
+  // workgroups (4 blocks of 32) so the walk reaches more CUs.
   const int units = N * L.hv;
-  const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * nvb);
-  hipLaunchKernelGGL((walk_kernel<E, NW>), dim3(grid), dim3(64 * NW), 0, st, (const E*)L.qg,
-                     (const E*)L.kg_t, L.decay, (const E*)L.w, (const E*)L.u,
-                     (const E*)L.aqk, L.cu, dense_len, T, L.chunk_offsets, N, L.hv, L.scale,
-                     L.init, L.fin, L.cache, L.slots, L.has_init, L.num_slots, (E*)L.out, nvb,
-                     units, (int)L.max_chunks);
+  if (units >= 128) {
+    constexpr int NW = 4;
+    const int nvb = D / (16 * NW);
+    const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * nvb);
+    hipLaunchKernelGGL((walk_kernel<E, NW>), dim3(grid), dim3(64 * NW), 0, st, (const E*)L.qg,
+                       (const E*)L.kg_t, L.decay, (const E*)L.w, (const E*)L.u,
+                       (const E*)L.aqk, L.cu, dense_len, T, L.chunk_offsets, N, L.hv, L.scale,
+                       L.init, L.fin, L.cache, L.slots, L.has_init, L.num_slots, (E*)L.out,
+                       nvb, units, (int)L.max_chunks, (const uint4*)L.zero);
+  } else {
+    constexpr int NW = 2;
+    const int nvb = D / (16 * NW);
+    const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * nvb);
+    hipLaunchKernelGGL((walk_kernel<E, NW>), dim3(grid), dim3(64 * NW), 0, st, (const E*)L.qg,
+                       (const E*)L.kg_t, L.decay, (const E*)L.w, (const E*)L.u,
+                       (const E*)L.aqk, L.cu, dense_len, T, L.chunk_offsets, N, L.hv, L.scale,
+                       L.init, L.fin, L.cache, L.slots, L.has_init, L.num_slots, (E*)L.out,
+                       nvb, units, (int)L.max_chunks, (const uint4*)L.zero);
+  }
   mark(L, 4);
   mark(L, 5);
   mark(L, 6);

@@ -21,12 +21,9 @@ __device__ __forceinline__ float to_f32(bf16 v) {
 }
 __device__ __forceinline__ float to_f32(_Float16 v) { return (float)v; }
 
-// fp32 -> bf16 with round-to-nearest-even (NaN kept quiet).
+// fp32 -> bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32; NaN stays NaN).
 __device__ __forceinline__ uint16_t bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 template <typename T> __device__ __forceinline__ T from_f32(float f);
@@ -43,6 +40,17 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float sigmoid(float x) {
   return 1.0f / (1.0f + exp2_fast(-x * LOG2E));
+}
+
+// Workgroup barrier that orders LDS only.  __syncthreads() is a full
+// release/acquire fence and so also waits for every global load still in
+// flight; this one waits for LDS traffic alone, so prefetches issued before it
+// keep streaming across it.  (LDS DMA writes are covered by an explicit vmcnt
+// wait before the barrier.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Cross-lane moves inside a 16-lane DPP row.

@@ -33,9 +33,11 @@ struct ChunkLaunch {
   void* out;
   // workspace pieces
   int32_t* chunk_offsets;     // [N+1]
+  void* table;                // int4 [max_chunks]: (sequence, first token, length, 0)
   void *qg, *kg_t, *w, *u, *aqk;
   float* decay;
   float* scan;                // group-scan planes (groups > 1)
+  void* zero;                 // 1 KiB zero page (written by the chunk-table kernel)
   int groups;
   void** events;              // optional stage events (KDA_EV_*), may be NULL
   int num_events;

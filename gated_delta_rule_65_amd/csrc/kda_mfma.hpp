@@ -99,10 +99,8 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
   *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
 __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
-  uint2 u;
-  u.x = (uint32_t)bf16_bits(a) | ((uint32_t)bf16_bits(b) << 16);
-  u.y = (uint32_t)bf16_bits(c) | ((uint32_t)bf16_bits(d) << 16);
-  *reinterpret_cast<uint2*>(p) = u;
+  const bf16x4_t v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+  *reinterpret_cast<bf16x4_t*>(p) = v;
 }
 
 }  // namespace kda

@@ -164,19 +164,26 @@ kda_status kda_chunk_fwd(const kda_chunk_args *a);
 /*
  * Layout of the staged path's intermediates inside the workspace, for tests
  * and tools.  Offsets are in bytes from the workspace base; "chunks" is the
- * bound n_chunks_max = total_tokens / 64 + num_seqs used for sizing.
+ * bound n_chunks_max = total_tokens / 64 + num_seqs used for sizing.  G is the
+ * inclusive in-chunk cumulative log-decay, b = sigmoid(beta).
  *   chunk_offsets  int32 [N + 1]: first chunk index of each sequence
- *   qg             [T_tot, Hv, 128]  q-type: qn * exp(G) (G = in-chunk
- *                                    cumulative log-decay, inclusive)
- *   kg_t           [chunks, Hv, 128, 64] q-type: (kn * exp(G_last - G))^T
+ *   zero           1 KiB of zeros (source of the rows past a short chunk)
+ *   table          int32x4 [chunks]: (sequence, first token, length, 0) per
+ *                  chunk, length 0 past the last chunk
+ *   qg             [T_tot, Hv, 128]  qn * exp(G)                        (P)
+ *   kg_t           [chunks, Hv, 128, 64]  (kn * exp(G_last - G))^T      (P)
  *   decay          fp32 [chunks, Hv, 128]: exp(G_last)
- *   w, u           [T_tot, Hv, 128]  q-type: WY factors T (b kn exp(G)), T (b v)
- *   aqk            [T_tot, Hv, 64]   q-type: sum_c qn_t kn_i exp(G_t - G_i),
- *                                    i <= t inside the chunk, 0 above
- * (q-type = bf16 for KDA_BF16 inputs, fp32 for KDA_F32.)
+ *   w              [T_tot, Hv, 128]  T (b kn exp(G)), T = (I + A_kk)^-1  (P)
+ *   u              [chunks, Hv, 128 (v), 64 (t)]  (T (b v))^T           (P)
+ *   aqk            [T_tot, Hv, 64]   sum_c qn_t kn_i exp(G_t - G_i), i <= t
+ *                                    inside the chunk, 0 above         (P)
+ * (P): the last axis is stored in MFMA fragment order: inside each block of
+ * 32 elements, position 8 g + j holds element 4 g + j for j < 4 and
+ * 16 + 4 g + (j - 4) for j >= 4.  Token axes of a short chunk are zero past
+ * its length.  Element type: bf16 for KDA_BF16 inputs, fp32 for KDA_F32.
  */
 typedef struct kda_ws_layout {
-  size_t chunk_offsets, qg, kg_t, decay, w, u, aqk, scan, total;
+  size_t chunk_offsets, zero, table, qg, kg_t, decay, w, u, aqk, scan, total;
   int64_t max_chunks;
 } kda_ws_layout;
 kda_status kda_chunk_ws_layout(const kda_chunk_args *a, kda_ws_layout *layout);

@@ -62,9 +62,11 @@ def test_workspace_layout_is_ordered_and_covers_intermediates(lib):
     lay = B.WsLayout()
     assert lib.kda_chunk_ws_layout(ctypes.byref(a), ctypes.byref(lay)) == B.KDA_OK
     assert lay.max_chunks == 256 // 64 + 2
-    offs = [lay.chunk_offsets, lay.qg, lay.kg_t, lay.decay, lay.w, lay.u, lay.aqk, lay.scan]
+    offs = [lay.chunk_offsets, lay.zero, lay.table, lay.qg, lay.kg_t, lay.decay, lay.w, lay.u,
+            lay.aqk, lay.scan]
     assert offs == sorted(offs)
-    assert lay.qg - lay.chunk_offsets >= 4 * 3
+    assert lay.zero - lay.chunk_offsets >= 4 * 3 and lay.table - lay.zero >= 1024
+    assert lay.qg - lay.table >= 16 * lay.max_chunks
     assert lay.kg_t - lay.qg >= 256 * 4 * 128 * 2
     assert lay.total >= lay.aqk + 256 * 4 * 64 * 2
     assert all(o % 256 == 0 for o in offs)

@@ -120,6 +120,23 @@ def test_dense_4d_input_matches_varlen():
 
 # ------------------------------------------------------- stage intermediates
 
+def packed_to_logical(n):
+    """Index array: logical element x of an axis of length n (a multiple of
+    32) sits at packed position idx[x] (the fragment order kda.h states)."""
+    idx = np.zeros(n, dtype=np.int64)
+    for blk in range(0, n, 32):
+        for gq in range(4):
+            for j in range(8):
+                x = 4 * gq + j if j < 4 else 16 + 4 * gq + (j - 4)
+                idx[blk + x] = blk + 8 * gq + j
+    return idx
+
+
+def test_packed_order_is_a_permutation():
+    for n in (32, 64, 128):
+        assert sorted(packed_to_logical(n).tolist()) == list(range(n))
+
+
 @pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
 def test_stage_intermediates_match_chunked_form(dt):
     lengths = [70, 1, 128, 33]
@@ -137,21 +154,27 @@ def test_stage_intermediates_match_chunked_form(dt):
     assert np.array_equal(offs, expect)
     nch = int(offs[-1])
     t_ = tol(dt)
-    for key in ("qg", "w", "u"):
-        assert rel(st[key].float().cpu().numpy(), inter[key]) < t_, key
-    assert rel(st["aqk"].float().cpu().numpy(), inter["aqk"]) < t_
+    p128, p64 = packed_to_logical(128), packed_to_logical(64)
+    for key in ("qg", "w"):
+        got = st[key].float().cpu().numpy()[..., p128]
+        assert rel(got, inter[key]) < t_, key
+    assert rel(st["aqk"].float().cpu().numpy()[..., p64], inter["aqk"]) < t_
     assert rel(st["decay"][:nch].cpu().numpy(), inter["d"]) < t_
-    # kg_t: chunk-major and transposed; rows past a short chunk are zero
-    kgt = st["kg_t"][:nch].float().cpu().numpy()
-    ref = np.zeros_like(kgt)
+    # kg_t and u_t: chunk-major and transposed; tokens past a short chunk are zero
+    kgt = st["kg_t"][:nch].float().cpu().numpy()[..., p64]
+    ut = st["u_t"][:nch].float().cpu().numpy()[..., p64]
+    ref_k = np.zeros_like(kgt)
+    ref_u = np.zeros_like(ut)
     cu = b.cu_seqlens.tolist()
     ci = 0
     for n in range(len(lengths)):
         for s in range(cu[n], cu[n + 1], 64):
             e = min(s + 64, cu[n + 1])
-            ref[ci, :, :, :e - s] = inter["kg"][s:e].transpose(1, 2, 0)
+            ref_k[ci, :, :, :e - s] = inter["kg"][s:e].transpose(1, 2, 0)
+            ref_u[ci, :, :, :e - s] = inter["u"][s:e].transpose(1, 2, 0)
             ci += 1
-    assert rel(kgt, ref) < t_
+    assert rel(kgt, ref_k) < t_
+    assert rel(ut, ref_u) < t_
     assert rel(st["out"].float().cpu().numpy(), o_ref) < t_
     assert rel(st["final_state"].cpu().numpy(), s_ref) < t_
 
