@@ -177,6 +177,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--groups", type=int, default=0, help="chunk groups (0 = auto)")
+    ap.add_argument("--walk-waves", type=int, default=0,
+                    help="waves per walk workgroup: 0 = auto, 2, 4 or 8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     args = ap.parse_args()
@@ -218,7 +220,7 @@ def main():
     nbytes = ctypes.c_size_t(0)
     a = B._chunk_struct(p["q"], p["k"], p["v"], p["g"], p["beta"], p["out"], None, p["N"],
                         p["T"], hqk, hv, p["scale"], True, p["init"], p["fin"], None, None,
-                        None, 0, args.groups, ctypes.c_void_p(stream))
+                        None, 0, args.groups, ctypes.c_void_p(stream), args.walk_waves)
     B.load_library().kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(nbytes))
     ws = torch.empty(nbytes.value, dtype=torch.uint8, device=dev)
 
@@ -229,7 +231,7 @@ def main():
     def step(i=None):
         B.chunk_kda(q4, k4, v4, g4, b4, scale=cb.scale, initial_state=cb.initial_state,
                     output_final_state=True, output=out, final_state=fin,
-                    groups=args.groups, workspace=ws,
+                    groups=args.groups, walk_waves=args.walk_waves, workspace=ws,
                     stage_events=None if i is None else ev_sets[i])
         if not args.no_decode:
             if i is not None:

@@ -46,6 +46,7 @@ class ChunkArgs(ctypes.Structure):
         ("out", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("path", ctypes.c_int32), ("groups", ctypes.c_int32),
+        ("walk_waves", ctypes.c_int32),
         ("stage_events", ctypes.c_void_p), ("num_stage_events", ctypes.c_int32),
         ("stream", ctypes.c_void_p),
     ]
@@ -58,7 +59,8 @@ class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("chunk_offsets", "zero", "table", "qg", "kg_t", "decay", "w", "u", "aqk", "scan",
                  "total")
-                ] + [("max_chunks", ctypes.c_int64)]
+                ] + [("max_chunks", ctypes.c_int64), ("groups", ctypes.c_int32),
+                     ("walk_waves", ctypes.c_int32)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -158,7 +160,7 @@ def _as_varlen(x, name, cu_seqlens):
 
 
 def _chunk_struct(q, k, v, g, beta, out, cu, N, T, hqk, hv, scale, l2, init, fin, cache,
-                  idx, has_init, path, groups, stream):
+                  idx, has_init, path, groups, stream, walk_waves=0):
     a = ChunkArgs()
     a.struct_size = ctypes.sizeof(ChunkArgs)
     a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
@@ -172,7 +174,7 @@ def _chunk_struct(q, k, v, g, beta, out, cu, N, T, hqk, hv, scale, l2, init, fin
     a.state_cache, a.state_indices, a.has_initial_state = _ptr(cache), _ptr(idx), _ptr(has_init)
     a.num_slots = 0 if cache is None else cache.shape[0]
     a.out = _ptr(out)
-    a.path, a.groups = path, groups
+    a.path, a.groups, a.walk_waves = path, groups, walk_waves
     a.stream = stream
     return a
 
@@ -258,12 +260,14 @@ def _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state, c
                 fin=fin, cache=state_cache if paged else None, idx=idx, has_init=hinit)
 
 
-def _run_chunk(p, path=PATH_AUTO, groups=0, workspace=None, keep=None, events=None):
+def _run_chunk(p, path=PATH_AUTO, groups=0, workspace=None, keep=None, events=None,
+               walk_waves=0):
     lib = load_library()
     dev = p["q"].device
     a = _chunk_struct(p["q"], p["k"], p["v"], p["g"], p["beta"], p["out"], p["cu"], p["N"],
                       p["T"], p["hqk"], p["hv"], p["scale"], p["l2"], p["init"], p["fin"],
-                      p["cache"], p["idx"], p["has_init"], path, groups, _stream(dev))
+                      p["cache"], p["idx"], p["has_init"], path, groups, _stream(dev),
+                      walk_waves)
     nbytes = ctypes.c_size_t(0)
     st = lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(nbytes))
     if st != KDA_OK:
@@ -288,16 +292,19 @@ def _run_chunk(p, path=PATH_AUTO, groups=0, workspace=None, keep=None, events=No
 def chunk_kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False,
               cu_seqlens=None, use_qk_l2norm_in_kernel=True, output=None, final_state=None,
               state_cache=None, state_indices=None, has_initial_state=None, groups=0,
-              workspace=None, stage_events=None):
+              workspace=None, stage_events=None, walk_waves=0):
     """Chunked KDA forward (chunk_kda's argument set, plus the paged state of
     fused_kda_chunk).  Returns out, or (out, final_state) when
     output_final_state; in paged mode the final states land in state_cache.
     stage_events: optional list of up to 7 hipEvent_t handles (ints) recorded
-    at the stage boundaries (profiling)."""
+    at the stage boundaries (profiling).  groups / walk_waves: 0 lets the
+    planner choose; otherwise they fix the walk's launch shape (tuning only,
+    the result is the same up to rounding order)."""
     p = _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state,
                        cu_seqlens, use_qk_l2norm_in_kernel, output, final_state,
                        state_cache, state_indices, has_initial_state)
-    _run_chunk(p, groups=groups, workspace=workspace, events=stage_events)
+    _run_chunk(p, groups=groups, workspace=workspace, events=stage_events,
+               walk_waves=walk_waves)
     out = p["out"]
     if output_final_state:
         return out, p["fin"]
@@ -405,3 +412,21 @@ def kda_decode(q, k, v, g, beta, state_cache, state_indices=None, scale=None,
     if st != KDA_OK:
         _raise(lib, st)
     return output.view(shape_v) if output.numel() == v.numel() else output
+
+
+def chunk_plan(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_state=False,
+               groups=0, walk_waves=0):
+    """The walk's launch plan (groups, walk_waves) that chunk_kda takes for
+    these arguments.  Host-side only: nothing runs on the device."""
+    p = _prepare_chunk(q, k, v, g, beta, None, initial_state, output_final_state, cu_seqlens,
+                       True, None, None, None, None, None)
+    a = _chunk_struct(p["q"], p["k"], p["v"], p["g"], p["beta"], p["out"], p["cu"], p["N"],
+                      p["T"], p["hqk"], p["hv"], p["scale"], True, p["init"], p["fin"], None,
+                      None, None, PATH_AUTO, groups, None, walk_waves)
+    lay = WsLayout()
+    lib = load_library()
+    st = lib.kda_chunk_ws_layout(ctypes.byref(a), ctypes.byref(lay))
+    if st != KDA_OK:
+        _raise(lib, st)
+    return lay.groups, lay.walk_waves
+

@@ -2,6 +2,8 @@
 // launch plans.  Every check runs on the host before anything is queued; a
 // failed check returns a status and writes nothing.
 #include <math.h>
+
+#include <cmath>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -74,6 +76,8 @@ kda_status check_chunk(const kda_chunk_args* a, bool need_ptrs) {
     return fail(KDA_ERR_UNSUPPORTED, "unknown path %d", a->path);
   if (a->groups < 0) return fail(KDA_ERR_SHAPE, "groups must be >= 0");
   if (a->groups > 64) return fail(KDA_ERR_UNSUPPORTED, "groups above 64");
+  if (a->walk_waves != 0 && a->walk_waves != 2 && a->walk_waves != 4 && a->walk_waves != 8)
+    return fail(KDA_ERR_ARG, "walk_waves must be 0, 2, 4 or 8");
   if (a->stage_events && (a->num_stage_events < 0 || a->num_stage_events > KDA_NUM_EVENTS))
     return fail(KDA_ERR_ARG, "num_stage_events must be in [0, %d]", KDA_NUM_EVENTS);
   if (need_ptrs && a->total_tokens > 0) {
@@ -87,13 +91,51 @@ int64_t max_chunks_of(const kda_chunk_args* a) {
   return a->total_tokens / KDA_CHUNK + a->num_seqs;
 }
 
-// Group count of the parallel chunk-group scan.  The scan walks each group
-// twice (pass one with 256 columns, pass two with 128) and composes the group
-// transfers in between, so it pays only when (sequence, head) units are too
-// few to fill the device and the chains are long.
-int resolve_groups(const kda_chunk_args* a) {
-  if (a->groups > 0) return a->groups;
-  return 1;
+// Launch plan of the walk: chunk groups G and waves per walk workgroup (each
+// wave owns 16 state columns, so a (sequence, head) spreads over 8 / waves
+// workgroups).  The walk is a chain over a sequence's chunks whose length sets
+// its time; one walk workgroup is resident per CU (its LDS ring fills most of
+// the CU).  Cost in chunk-steps: waves of resident workgroups times chain
+// length, with the group scan paying pass one (2x the columns, no outputs),
+// G compose steps and pass two over chains G times shorter.
+struct WalkPlan {
+  int groups, waves;
+};
+
+WalkPlan plan_walk(const kda_chunk_args* a) {
+  const int cap = 256;  // resident walk workgroups
+  const int N = a->num_seqs > 0 ? a->num_seqs : 1;
+  const int64_t units = (int64_t)N * a->hv;
+  const double nc = (double)max_chunks_of(a) / N;  // chunks per sequence (mean bound)
+  const int waves_opts[3] = {2, 4, 8};
+  // time of one chunk step of a workgroup, by waves (measured on MI355X: the
+  // step is latency-bound, so wider workgroups take longer per step)
+  const double step_cost[3] = {1.0, 1.12, 1.55};
+  WalkPlan best = {1, 2};
+  double best_cost = 1e300;
+  for (int wi = 0; wi < 3; ++wi) {
+    const int nw = waves_opts[wi], nvb = 8 / nw;
+    if (a->walk_waves > 0 && nw != a->walk_waves) continue;
+    for (int G = 1; G <= 64; G *= 2) {
+      if (a->groups > 0 && G != a->groups) continue;
+      double cost;
+      if (G == 1) {
+        cost = std::ceil((double)(units * nvb) / cap) * nc * step_cost[wi];
+      } else {
+        const double cpg = std::ceil(nc / G);
+        const double r1 = std::ceil((double)(units * G * 2 * nvb) / cap);
+        const double r2 = std::ceil((double)(units * G * nvb) / cap);
+        cost = (0.8 * r1 + r2) * cpg * step_cost[wi] + G;
+      }
+      if (cost < best_cost * 0.999) {
+        best_cost = cost;
+        best = {G, nw};
+      }
+    }
+  }
+  if (a->groups > 0 && best.groups != a->groups)  // G not a power of 2
+    best = {a->groups, a->walk_waves > 0 ? a->walk_waves : 2};
+  return best;
 }
 
 kda_status layout_of(const kda_chunk_args* a, kda_ws_layout* L) {
@@ -101,9 +143,12 @@ kda_status layout_of(const kda_chunk_args* a, kda_ws_layout* L) {
   const size_t es = elem_size(a->dtype);
   const size_t T = (size_t)a->total_tokens, H = (size_t)a->hv;
   const int64_t mc = max_chunks_of(a);
-  const int groups = resolve_groups(a);
+  const WalkPlan plan = plan_walk(a);
+  const int groups = plan.groups;
   size_t off = 0;
   L->max_chunks = mc;
+  L->groups = plan.groups;
+  L->walk_waves = plan.waves;
   L->chunk_offsets = off;
   off = align_up(off + sizeof(int32_t) * ((size_t)a->num_seqs + 1), 256);
   L->zero = off;
@@ -198,7 +243,8 @@ KDA_API kda_status kda_chunk_fwd(const kda_chunk_args* a) {
   L.w = ws + W.w; L.u = ws + W.u; L.aqk = ws + W.aqk;
   L.events = a->stage_events;
   L.num_events = a->stage_events ? a->num_stage_events : 0;
-  L.groups = resolve_groups(a);
+  L.groups = W.groups;
+  L.walk_waves = W.walk_waves;
   L.scan = L.groups > 1 ? (float*)(ws + W.scan) : nullptr;
   L.stream = a->stream;
   hipError_t e = kda::launch_chunk_staged(L);

@@ -601,24 +601,55 @@ __global__ __launch_bounds__(256) void wy_kernel(
 
 // ----------------------------------------------------------------------- walk
 
+// Arguments of the walk kernels (one struct so the three modes share them).
+template <typename E>
+struct WalkArgs {
+  const E *qg, *kg_t, *w, *u_t, *aqk;
+  const float* decay;
+  const int32_t* cu;
+  int dense_len, T;
+  const int32_t* offs;
+  int N, hv;
+  float scale;
+  const float* init;
+  float* fin;
+  float* cache;
+  const int32_t* slots;
+  const uint8_t* has_init;
+  int num_slots;
+  E* out;
+  int nvb, units, max_chunks, groups;
+  float* scan;  // group planes (g, n, h): P [k][j], B [v][k], H_in [v][k]
+  const uint4* zero;
+};
+
+constexpr size_t PLANE = (size_t)D * D;
+__device__ __forceinline__ float* scan_plane(float* scan, int g, int n, int h, int N, int hv,
+                                             int which) {
+  return scan + ((((size_t)g * N + n) * hv + h) * 3 + which) * PLANE;
+}
+
 // The inter-chunk walk fused with the output projection.  One workgroup of NW
-// waves per (sequence, value head, block of 16 NW value channels); each wave
-// owns 16 value channels and keeps its 128 x 16 slice of the state in MFMA
-// accumulators (fp32) for the whole sequence.  The K-side tiles of a chunk
-// (w, qg, aqk, kg_t, the block's u_t rows, decay) arrive by LDS DMA into a
+// waves per (sequence, value head [, chunk group], block of 16 NW columns);
+// each wave owns 16 columns of the state and keeps its 128 x 16 slice in MFMA
+// accumulators (fp32) through the chunks.  The K-side tiles of a chunk (w,
+// qg, aqk, kg_t, the block's u_t rows, decay) arrive by LDS DMA into a
 // two-stage ring (one stage for fp32 operands), so the next chunk's tiles
 // stream in while this chunk's products run.
-template <typename E, int NW>
-__global__ __launch_bounds__(64 * NW) void walk_kernel(
-    const E* __restrict__ qg, const E* __restrict__ kg_t, const float* __restrict__ decay,
-    const E* __restrict__ w, const E* __restrict__ u_t, const E* __restrict__ aqk,
-    const int32_t* __restrict__ cu, int dense_len, int T, const int32_t* __restrict__ offs,
-    int N, int hv, float scale, const float* __restrict__ init, float* __restrict__ fin,
-    float* __restrict__ cache, const int32_t* __restrict__ slots,
-    const uint8_t* __restrict__ has_init, int num_slots, E* __restrict__ out, int nvb,
-    int units, int max_chunks, const uint4* __restrict__ zero) {
+//
+// MODE 0: the whole sequence, outputs and final state.
+// MODE 1: group pass one.  Group g of the sequence's chunks is walked from
+//         zero; the first nvb column blocks are the 128 value columns (with
+//         u: the group's partial state B_g), the next nvb blocks are 128
+//         transfer columns started at the identity with u = 0 (the group
+//         transfer P_g = prod_c (diag(d_c) - kg_c^T w_c)).  No outputs.
+// MODE 2: group pass two.  Group g is walked from its composed start state
+//         H_in(g); outputs for its tokens, the final state from the last group.
+template <typename E, int NW, int MODE>
+__global__ __launch_bounds__(64 * NW) void walk_kernel(const WalkArgs<E> a) {
   constexpr bool SPLIT = std::is_same<E, float>::value;
   constexpr int STAGES = SPLIT ? 1 : 2;
+  constexpr bool OUT = MODE != 1;
   constexpr int NT = 64 * NW;
   constexpr int BV = 16 * NW;
   constexpr int EPP = 16 / (int)sizeof(E);  // elements per 16-byte piece
@@ -631,46 +662,73 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(
   __shared__ uint4 smemA[STAGE];
   __shared__ uint4 smemB[STAGES == 2 ? STAGE : 1];
 
-  // The nvb blocks of one (sequence, head) get ids with equal id % 8, so they
-  // land on one XCD and share its L2 for the K-side tiles.
+  // The column blocks of one (sequence, head, group) get ids with equal
+  // id % 8, so they land on one XCD and share its L2 for the K-side tiles.
+  const int G = MODE == 0 ? 1 : a.groups;
+  const int ncb = MODE == 1 ? 2 * a.nvb : a.nvb;
   const int id = blockIdx.x;
-  const int blk = id / (8 * nvb), rem = id - blk * 8 * nvb;
-  const int vb = rem >> 3, unit = blk * 8 + (rem & 7);
-  if (unit >= units) return;
+  const int blk = id / (8 * ncb), rem = id - blk * 8 * ncb;
+  const int cb = rem >> 3, ug = blk * 8 + (rem & 7);
+  if (ug >= a.units * G) return;
+  const int unit = ug / G, g = ug - unit * G;
+  const int hv = a.hv;
   const int n = unit / hv, h = unit - n * hv;
+  const bool tcols = MODE == 1 && cb >= a.nvb;  // transfer columns of pass one
+  const int vb = tcols ? cb - a.nvb : cb;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, gq = lane >> 4;
-  const int v0 = vb * BV;                  // first value channel of the block
+  const int v0 = vb * BV;                  // first column of the block
   const int vl = 16 * wave + l16;          // this lane's C-tile column inside the block
   const int vcol = v0 + vl;
-  const SeqSpan sp = seq_span(cu, n, dense_len, T);
+  const SeqSpan sp = seq_span(a.cu, n, a.dense_len, a.T);
 
-  const float* src = nullptr;
-  float* dst = nullptr;
-  if (cache) {
-    const int slot = slots[n];
-    if (slot < 0 || slot >= num_slots) {
+  // this workgroup's chunks: group g of the sequence's chunk chain
+  const int c_first = a.offs[n];
+  // a malformed cu_seqlens could claim chunks past the bound; never read them
+  const int nch_all = max(0, min(a.offs[n + 1], a.max_chunks) - c_first);
+  const int cpg = (nch_all + G - 1) / G;
+  const int jc0 = min(nch_all, g * cpg), jc1 = min(nch_all, jc0 + cpg);
+
+  float* row = nullptr;  // paged cache row of this (sequence, head)
+  if (a.cache) {
+    const int slot = a.slots[n];
+    if (slot < 0 || slot >= a.num_slots) {
       // null slot: zero output rows, no state traffic
-      for (int idx = tid; idx < (sp.eos - sp.bos) * BV; idx += NT) {
-        const int t = idx / BV, vv = idx - t * BV;
-        out[((size_t)(sp.bos + t) * hv + h) * D + v0 + vv] = from_f32<E>(0.f);
+      if (OUT) {
+        const int tb = sp.bos + C * jc0, te = min(sp.eos, sp.bos + C * jc1);
+        for (int idx = tid; idx < (te - tb) * BV; idx += NT) {
+          const int t = idx / BV, vv = idx - t * BV;
+          a.out[((size_t)(tb + t) * hv + h) * D + v0 + vv] = from_f32<E>(0.f);
+        }
       }
       return;
     }
-    float* row = cache + ((size_t)slot * hv + h) * (size_t)(D * D);
-    dst = row;
-    if (has_init[n]) src = row;
+    row = a.cache + ((size_t)slot * hv + h) * PLANE;
+  }
+  const float* src = nullptr;
+  float* dst = nullptr;
+  if (MODE == 0) {
+    src = a.cache ? (a.has_init[n] ? row : nullptr)
+                  : (a.init ? a.init + ((size_t)n * hv + h) * PLANE : nullptr);
+    dst = a.cache ? row : (a.fin ? a.fin + ((size_t)n * hv + h) * PLANE : nullptr);
+  } else if (MODE == 1) {
+    dst = scan_plane(a.scan, g, n, h, a.N, hv, tcols ? 0 : 1);
   } else {
-    if (init) src = init + ((size_t)n * hv + h) * (size_t)(D * D);
-    if (fin) dst = fin + ((size_t)n * hv + h) * (size_t)(D * D);
+    src = scan_plane(a.scan, g, n, h, a.N, hv, 2);
+    if (g == G - 1)
+      dst = a.cache ? row : (a.fin ? a.fin + ((size_t)n * hv + h) * PLANE : nullptr);
   }
 
-  // state slice: S[kb][r] = S[k = 16 kb + 4 gq + r][v = vcol]  (V-first row vcol)
+  // state slice: S[kb][r] = S[k = 16 kb + 4 gq + r][column vcol]  (V-first row vcol)
   f32x4_t S[8];
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb) {
-    if (src) {
+    if (tcols) {
+      const int k0 = 16 * kb + 4 * gq;
+      S[kb] = f32x4_t{k0 == vcol ? 1.f : 0.f, k0 + 1 == vcol ? 1.f : 0.f,
+                      k0 + 2 == vcol ? 1.f : 0.f, k0 + 3 == vcol ? 1.f : 0.f};
+    } else if (src) {
       const float4 x = *reinterpret_cast<const float4*>(src + (size_t)vcol * D + 16 * kb + 4 * gq);
       S[kb] = f32x4_t{x.x, x.y, x.z, x.w};
     } else {
@@ -678,58 +736,56 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(
     }
   }
 
-  const int c_first = offs[n];
-  // a malformed cu_seqlens could claim chunks past the bound; never read them
-  const int nch = max(0, min(offs[n + 1], max_chunks) - c_first);
-
-  // K-side tiles of chunk jc into a stage, in two parts: w and qg (needed
-  // first), then aqk, kg_t, the block's u_t rows and decay.
+  const uint4* zero = a.zero;
+  // K-side tiles of chunk jc into a stage, in two parts: w (and qg), then
+  // aqk, kg_t, the block's u_t rows and decay.
   auto issue_wq = [&](int jc, uint4* base) {
     const int t0 = sp.bos + C * jc;
     const int L = min(C, sp.eos - t0);
     const size_t rowb = (size_t)hv * D * sizeof(E);
-    dma_tile<C, P128, NW, true>(base + OFF_W, w + ((size_t)t0 * hv + h) * D, rowb, L, zero,
+    dma_tile<C, P128, NW, true>(base + OFF_W, a.w + ((size_t)t0 * hv + h) * D, rowb, L, zero,
                                 wave, lane);
-    dma_tile<C, P128, NW, true>(base + OFF_Q, qg + ((size_t)t0 * hv + h) * D, rowb, L, zero,
-                                wave, lane);
+    if (OUT)
+      dma_tile<C, P128, NW, true>(base + OFF_Q, a.qg + ((size_t)t0 * hv + h) * D, rowb, L, zero,
+                                  wave, lane);
   };
   auto issue_rest = [&](int jc, uint4* base) {
     const int c = c_first + jc;
     const int t0 = sp.bos + C * jc;
     const int L = min(C, sp.eos - t0);
-    dma_tile<C, P64, NW, true>(base + OFF_A, aqk + ((size_t)t0 * hv + h) * C,
-                               (size_t)hv * C * sizeof(E), L, zero, wave, lane);
-    dma_tile<D, P64, NW, false>(base + OFF_K, kg_t + ((size_t)c * hv + h) * D * C,
+    if (OUT)
+      dma_tile<C, P64, NW, true>(base + OFF_A, a.aqk + ((size_t)t0 * hv + h) * C,
+                                 (size_t)hv * C * sizeof(E), L, zero, wave, lane);
+    dma_tile<D, P64, NW, false>(base + OFF_K, a.kg_t + ((size_t)c * hv + h) * D * C,
                                 C * sizeof(E), D, zero, wave, lane);
-    dma_tile<BV, P64, NW, false>(base + OFF_U, u_t + (((size_t)c * hv + h) * D + v0) * C,
-                                 C * sizeof(E), BV, zero, wave, lane);
+    if (!tcols)
+      dma_tile<BV, P64, NW, false>(base + OFF_U, a.u_t + (((size_t)c * hv + h) * D + v0) * C,
+                                   C * sizeof(E), BV, zero, wave, lane);
     if (wave == NW - 1) {
       // decay: 32 pieces, lanes 32..63 fill the pad from the zero page
-      const char* gp = lane < 32 ? (const char*)(decay + ((size_t)c * hv + h) * D) + 16 * lane
+      const char* gp = lane < 32 ? (const char*)(a.decay + ((size_t)c * hv + h) * D) + 16 * lane
                                  : (const char*)zero;
       __builtin_amdgcn_global_load_lds(gp, (lds_vptr)(base + OFF_D), 16, 0, 0);
     }
   };
-  auto issue = [&](int jc, uint4* base) {
-    issue_wq(jc, base);
-    issue_rest(jc, base);
-  };
-  if (nch > 0) issue(0, smemA);
+  if (jc0 < jc1) {
+    issue_wq(jc0, smemA);
+    issue_rest(jc0, smemA);
+  }
 
   auto body = [&](int jc, uint4* cur, uint4* nxt) {
     const int t0 = sp.bos + C * jc;
     const int L = min(C, sp.eos - t0);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA of chunk jc has landed
-    lds_barrier();                // ... and every other wave's
-    const bool more = STAGES == 2 && jc + 1 < nch;
+    lds_barrier();                  // ... and every other wave's
+    const bool more = STAGES == 2 && jc + 1 < jc1;
     if (SPLIT && more) issue_wq(jc + 1, nxt);
-    const uint4* stg = cur;
-    const uint4* tW = stg + OFF_W;
-    const uint4* tQ = stg + OFF_Q;
-    const uint4* tA = stg + OFF_A;
-    const uint4* tK = stg + OFF_K;
-    const uint4* tU = stg + OFF_U;
-    const float* sD = reinterpret_cast<const float*>(stg + OFF_D);
+    const uint4* tW = cur + OFF_W;
+    const uint4* tQ = cur + OFF_Q;
+    const uint4* tA = cur + OFF_A;
+    const uint4* tK = cur + OFF_K;
+    const uint4* tU = cur + OFF_U;
+    const float* sD = reinterpret_cast<const float*>(cur + OFF_D);
 
     // the state as an MFMA operand (K = key channel, perm32 order)
     Frag<SPLIT> Hf[4];
@@ -739,13 +795,17 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(
                     S[2 * s + 1][0], S[2 * s + 1][1], S[2 * s + 1][2], S[2 * s + 1][3]};
       Hf[s] = make_frag<SPLIT>(x);
     }
-    // u values of this lane's column, read early
+    // u values of this lane's column (zero for transfer columns)
     float uv[2][8];
-    unit_vals<P64>(tU, vl, gq, SPLIT, uv[0]);
-    unit_vals<P64>(tU, vl, 4 + gq, SPLIT, uv[1]);
+    if (!tcols) {
+      unit_vals<P64>(tU, vl, gq, SPLIT, uv[0]);
+      unit_vals<P64>(tU, vl, 4 + gq, SPLIT, uv[1]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) uv[0][e] = uv[1][e] = 0.f;
+    }
 
-    // HW = w S (rows t, cols v) and O^T = (qg S)^T (rows v, cols t); the
-    // fragments of K step s + 1 are read while step s multiplies.
+    // HW = w S (rows t, cols v) and O^T = (qg S)^T (rows v, cols t)
     f32x4_t HW[4], O[4];
 #pragma unroll
     for (int ta = 0; ta < 4; ++ta) {
@@ -758,29 +818,29 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(
 #pragma unroll
         for (int ta = 0; ta < 4; ++ta) {
           fw[buf][ta] = frag_bf16<P128>(tW, 16 * ta + l16, 4 * s + gq);
-          fq[buf][ta] = frag_bf16<P128>(tQ, 16 * ta + l16, 4 * s + gq);
+          if (OUT) fq[buf][ta] = frag_bf16<P128>(tQ, 16 * ta + l16, 4 * s + gq);
         }
       };
-      // The next chunk's w / qg DMA (2 x WQ_PER wave instructions) is spread
-      // over the K steps, so the wave keeps issuing products while the memory
-      // pipeline takes it.
+      // The next chunk's w / qg DMA is spread over the K steps, so the wave
+      // keeps issuing products while the memory pipeline takes it.
       constexpr int WQ_PER = C * P128 / 64 / NW;
+      constexpr int NDMA = OUT ? 2 * WQ_PER : WQ_PER;
       const int tn = sp.bos + C * (jc + 1);
       const int Ln = min(C, sp.eos - tn);
       const size_t rowb = (size_t)hv * D * sizeof(E);
-      const E* wsrc = w + ((size_t)tn * hv + h) * D;
-      const E* qsrc = qg + ((size_t)tn * hv + h) * D;
+      const E* wsrc = a.w + ((size_t)tn * hv + h) * D;
+      const E* qsrc = a.qg + ((size_t)tn * hv + h) * D;
       load_k(0, 0);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         if (s < 3) load_k(s + 1, (s + 1) & 1);
         if (more) {
 #pragma unroll
-          for (int m = 0; m < 2 * WQ_PER / 4; ++m) {
-            const int mm = (2 * WQ_PER / 4) * s + m;
+          for (int m = 0; m < (NDMA + 3) / 4; ++m) {
+            const int mm = ((NDMA + 3) / 4) * s + m;
             if (mm < WQ_PER)
               dma_one<C, P128, NW, true>(mm, nxt + OFF_W, wsrc, rowb, Ln, zero, wave, lane);
-            else
+            else if (mm < NDMA)
               dma_one<C, P128, NW, true>(mm - WQ_PER, nxt + OFF_Q, qsrc, rowb, Ln, zero, wave,
                                          lane);
           }
@@ -788,25 +848,26 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(
 #pragma unroll
         for (int ta = 0; ta < 4; ++ta) {
           mma(HW[ta], fw[s & 1][ta], Hf[s]);
-          mma(O[ta], Hf[s], fq[s & 1][ta]);
+          if (OUT) mma(O[ta], Hf[s], fq[s & 1][ta]);
         }
       }
-      // Pin the schedule: the 8 fragment reads of a K step go out while the
-      // 8 products of the previous step run.
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS read
+      // Pin the schedule: the fragment reads of a K step go out while the
+      // products of the previous step run.
+      constexpr int NF = OUT ? 8 : 4;
+      __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);  // DS read
 #pragma unroll
-      for (int i = 0; i < 24; ++i) {
+      for (int i = 0; i < 3 * NF; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NF, 0);
     } else {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int ta = 0; ta < 4; ++ta) {
           mma(HW[ta], frag_f32<P128>(tW, 16 * ta + l16, 4 * s + gq), Hf[s]);
-          mma(O[ta], Hf[s], frag_f32<P128>(tQ, 16 * ta + l16, 4 * s + gq));
+          if (OUT) mma(O[ta], Hf[s], frag_f32<P128>(tQ, 16 * ta + l16, 4 * s + gq));
         }
     }
     if (more) issue_rest(jc + 1, nxt);
@@ -825,20 +886,24 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(
     if constexpr (!SPLIT) {
       // A_qk fragments (A_qk lower: t < 32 needs i < 32 only), kg^T fragments
       FragB fa[4][2], fk[8][2];
+      if (OUT) {
 #pragma unroll
-      for (int ta = 0; ta < 4; ++ta)
+        for (int ta = 0; ta < 4; ++ta)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-          if (!(s2 == 1 && ta < 2)) fa[ta][s2] = frag_bf16<P64>(tA, 16 * ta + l16, 4 * s2 + gq);
+          for (int s2 = 0; s2 < 2; ++s2)
+            if (!(s2 == 1 && ta < 2)) fa[ta][s2] = frag_bf16<P64>(tA, 16 * ta + l16, 4 * s2 + gq);
+      }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) fk[kb][s2] = frag_bf16<P64>(tK, 16 * kb + l16, 4 * s2 + gq);
       // O^T += U^T A_qk^T
+      if (OUT) {
 #pragma unroll
-      for (int ta = 0; ta < 4; ++ta) {
-        mma(O[ta], Uf[0], fa[ta][0]);
-        if (ta >= 2) mma(O[ta], Uf[1], fa[ta][1]);
+        for (int ta = 0; ta < 4; ++ta) {
+          mma(O[ta], Uf[0], fa[ta][0]);
+          if (ta >= 2) mma(O[ta], Uf[1], fa[ta][1]);
+        }
       }
 #pragma unroll
       for (int kb = 4; kb < 8; ++kb)
@@ -856,10 +921,12 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(
         mma(S[kb], fk[kb][1], Uf[1]);
       }
     } else {
+      if (OUT) {
 #pragma unroll
-      for (int ta = 0; ta < 4; ++ta) {
-        mma(O[ta], Uf[0], frag_f32<P64>(tA, 16 * ta + l16, gq));
-        if (ta >= 2) mma(O[ta], Uf[1], frag_f32<P64>(tA, 16 * ta + l16, 4 + gq));
+        for (int ta = 0; ta < 4; ++ta) {
+          mma(O[ta], Uf[0], frag_f32<P64>(tA, 16 * ta + l16, gq));
+          if (ta >= 2) mma(O[ta], Uf[1], frag_f32<P64>(tA, 16 * ta + l16, 4 + gq));
+        }
       }
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
@@ -872,28 +939,104 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(
         mma(S[kb], frag_f32<P64>(tK, 16 * kb + l16, 4 + gq), Uf[1]);
       }
     }
+    if (OUT) {
 #pragma unroll
-    for (int ta = 0; ta < 4; ++ta) {
-      const int t = 16 * ta + l16;
-      if (t < L) {
-        E* op = out + ((size_t)(t0 + t) * hv + h) * D + v0 + 16 * wave + 4 * gq;
-        store4(op, scale * O[ta][0], scale * O[ta][1], scale * O[ta][2], scale * O[ta][3]);
+      for (int ta = 0; ta < 4; ++ta) {
+        const int t = 16 * ta + l16;
+        if (t < L) {
+          E* op = a.out + ((size_t)(t0 + t) * hv + h) * D + v0 + 16 * wave + 4 * gq;
+          store4(op, a.scale * O[ta][0], a.scale * O[ta][1], a.scale * O[ta][2],
+                 a.scale * O[ta][3]);
+        }
       }
     }
-    if (STAGES == 1 && jc + 1 < nch) {
+    if (STAGES == 1 && jc + 1 < jc1) {
       lds_barrier();  // everyone is done with the single stage
-      issue(jc + 1, cur);
+      issue_wq(jc + 1, cur);
+      issue_rest(jc + 1, cur);
     }
   };
-  for (int jc = 0; jc < nch; jc += 2) {
+  for (int jc = jc0; jc < jc1; jc += 2) {
     body(jc, smemA, smemB);
-    if (jc + 1 < nch) body(jc + 1, STAGES == 2 ? smemB : smemA, smemA);
+    if (jc + 1 < jc1) body(jc + 1, STAGES == 2 ? smemB : smemA, smemA);
   }
   if (dst) {
+    if (tcols) {
+      // transfer P[k][j] row-major, j = this lane's column
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(size_t)(16 * kb + 4 * gq + r) * D + vcol] = S[kb][r];
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+        *reinterpret_cast<float4*>(dst + (size_t)vcol * D + 16 * kb + 4 * gq) =
+            make_float4(S[kb][0], S[kb][1], S[kb][2], S[kb][3]);
+    }
+  }
+}
+
+// ------------------------------------------------------------ group compose
+
+// H_in(0) = S0 and H_in(g+1) = H_in(g) P_g + B_g (V-first: row v of H is
+// column v of S, so S_in(g+1) = P_g S_in(g) + B_g).  The rows of H are
+// independent, so each one-wave workgroup carries 16 rows (v) through all
+// groups of one (sequence, head).  P_g S is formed on MFMA with fp32
+// operands split into hi + lo bf16 pairs (three products), keeping the
+// composition close to fp32 however many groups there are.
+template <typename E>
+__global__ __launch_bounds__(64) void compose_kernel(const WalkArgs<E> a) {
+  const int unit = blockIdx.x >> 3, rb = blockIdx.x & 7;
+  if (unit >= a.units) return;
+  const int hv = a.hv;
+  const int n = unit / hv, h = unit - n * hv;
+  const int lane = threadIdx.x, l16 = lane & 15, gq = lane >> 4;
+  const int vcol = 16 * rb + l16;
+  const int G = a.groups;
+  const float* src = nullptr;
+  if (a.cache) {
+    const int slot = a.slots[n];
+    if (slot < 0 || slot >= a.num_slots) return;
+    if (a.has_init[n]) src = a.cache + ((size_t)slot * hv + h) * PLANE;
+  } else if (a.init) {
+    src = a.init + ((size_t)n * hv + h) * PLANE;
+  }
+  f32x4_t S[8];
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) {
+    if (src) {
+      const float4 x = *reinterpret_cast<const float4*>(src + (size_t)vcol * D + 16 * kb + 4 * gq);
+      S[kb] = f32x4_t{x.x, x.y, x.z, x.w};
+    } else {
+      S[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  for (int g = 0; g < G; ++g) {
+    float* hin = scan_plane(a.scan, g, n, h, a.N, hv, 2);
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb)
-      *reinterpret_cast<float4*>(dst + (size_t)vcol * D + 16 * kb + 4 * gq) =
+      *reinterpret_cast<float4*>(hin + (size_t)vcol * D + 16 * kb + 4 * gq) =
           make_float4(S[kb][0], S[kb][1], S[kb][2], S[kb][3]);
+    if (g == G - 1) break;
+    const float* P = scan_plane(a.scan, g, n, h, a.N, hv, 0);
+    const float* Bp = scan_plane(a.scan, g, n, h, a.N, hv, 1);
+    FragS Hf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float x[8] = {S[2 * s][0], S[2 * s][1], S[2 * s][2], S[2 * s][3],
+                    S[2 * s + 1][0], S[2 * s + 1][1], S[2 * s + 1][2], S[2 * s + 1][3]};
+      Hf[s] = make_frag<true>(x);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      const float4 b4 = *reinterpret_cast<const float4*>(Bp + (size_t)vcol * D + 16 * kb + 4 * gq);
+      f32x4_t acc = {b4.x, b4.y, b4.z, b4.w};
+      const float* prow = P + (size_t)(16 * kb + l16) * D;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        mma(acc, frag_from(prow + 32 * s + 4 * gq, prow + 32 * s + 16 + 4 * gq), Hf[s]);
+      S[kb] = acc;
+    }
   }
 }
 
@@ -901,6 +1044,29 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(
 
 static void mark(const ChunkLaunch& L, int i) {
   if (i < L.num_events && L.events[i]) (void)hipEventRecord((hipEvent_t)L.events[i], (hipStream_t)L.stream);
+}
+
+template <typename E, int NW>
+static void launch_walk(const ChunkLaunch& L, const WalkArgs<E>& wa) {
+  hipStream_t st = (hipStream_t)L.stream;
+  const int nvb = wa.nvb, units = wa.units, G = wa.groups;
+  if (G <= 1) {
+    const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * nvb);
+    hipLaunchKernelGGL((walk_kernel<E, NW, 0>), dim3(grid), dim3(64 * NW), 0, st, wa);
+    mark(L, 4);
+    mark(L, 5);
+    mark(L, 6);
+    return;
+  }
+  const int ug = units * G;
+  hipLaunchKernelGGL((walk_kernel<E, NW, 1>), dim3((unsigned)(((ug + 7) / 8) * 8 * 2 * nvb)),
+                     dim3(64 * NW), 0, st, wa);
+  mark(L, 4);
+  hipLaunchKernelGGL((compose_kernel<E>), dim3((unsigned)(units * 8)), dim3(64), 0, st, wa);
+  mark(L, 5);
+  hipLaunchKernelGGL((walk_kernel<E, NW, 2>), dim3((unsigned)(((ug + 7) / 8) * 8 * nvb)),
+                     dim3(64 * NW), 0, st, wa);
+  mark(L, 6);
 }
 
 template <typename E>
@@ -926,36 +1092,25 @@ static hipError_t launch_staged_t(const ChunkLaunch& L) {
     mark(L, 2);
   }
   mark(L, 3);
-  // Few (sequence, head) units: split the value channels over more
-  // workgroups (4 blocks of 32) so the walk reaches more CUs.
-  const int units = N * L.hv;
-  if (units >= 128) {
-    constexpr int NW = 4;
-    const int nvb = D / (16 * NW);
-    const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * nvb);
-    hipLaunchKernelGGL((walk_kernel<E, NW>), dim3(grid), dim3(64 * NW), 0, st, (const E*)L.qg,
-                       (const E*)L.kg_t, L.decay, (const E*)L.w, (const E*)L.u,
-                       (const E*)L.aqk, L.cu, dense_len, T, L.chunk_offsets, N, L.hv, L.scale,
-                       L.init, L.fin, L.cache, L.slots, L.has_init, L.num_slots, (E*)L.out,
-                       nvb, units, (int)L.max_chunks, (const uint4*)L.zero);
-  } else {
-    constexpr int NW = 2;
-    const int nvb = D / (16 * NW);
-    const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * nvb);
-    hipLaunchKernelGGL((walk_kernel<E, NW>), dim3(grid), dim3(64 * NW), 0, st, (const E*)L.qg,
-                       (const E*)L.kg_t, L.decay, (const E*)L.w, (const E*)L.u,
-                       (const E*)L.aqk, L.cu, dense_len, T, L.chunk_offsets, N, L.hv, L.scale,
-                       L.init, L.fin, L.cache, L.slots, L.has_init, L.num_slots, (E*)L.out,
-                       nvb, units, (int)L.max_chunks, (const uint4*)L.zero);
+  WalkArgs<E> wa;
+  wa.qg = (const E*)L.qg; wa.kg_t = (const E*)L.kg_t; wa.w = (const E*)L.w;
+  wa.u_t = (const E*)L.u; wa.aqk = (const E*)L.aqk; wa.decay = L.decay;
+  wa.cu = L.cu; wa.dense_len = dense_len; wa.T = T; wa.offs = L.chunk_offsets;
+  wa.N = N; wa.hv = L.hv; wa.scale = L.scale;
+  wa.init = L.init; wa.fin = L.fin; wa.cache = L.cache; wa.slots = L.slots;
+  wa.has_init = L.has_init; wa.num_slots = L.num_slots; wa.out = (E*)L.out;
+  wa.units = N * L.hv; wa.max_chunks = (int)L.max_chunks; wa.groups = L.groups;
+  wa.scan = L.scan; wa.zero = (const uint4*)L.zero;
+  wa.nvb = D / (16 * L.walk_waves);
+  switch (L.walk_waves) {
+    case 8: launch_walk<E, 8>(L, wa); break;
+    case 4: launch_walk<E, 4>(L, wa); break;
+    default: launch_walk<E, 2>(L, wa); break;
   }
-  mark(L, 4);
-  mark(L, 5);
-  mark(L, 6);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_staged(const ChunkLaunch& L) {
-  if (L.groups > 1) return hipErrorNotSupported;
   return L.dtype == 0 ? launch_staged_t<float>(L) : launch_staged_t<bf16>(L);
 }
 

@@ -38,7 +38,8 @@ struct ChunkLaunch {
   float* decay;
   float* scan;                // group-scan planes (groups > 1)
   void* zero;                 // 1 KiB zero page (written by the chunk-table kernel)
-  int groups;
+  int groups;                 // chunk groups per sequence (1 = plain walk)
+  int walk_waves;             // waves per walk workgroup: 2, 4 or 8 (16 columns each)
   void** events;              // optional stage events (KDA_EV_*), may be NULL
   int num_events;
   void* stream;

@@ -122,6 +122,8 @@ typedef struct kda_chunk_args {
   int32_t path;                /* kda_path */
   int32_t groups;              /* chunk groups per sequence: 0 = auto, 1 = none,
                                   >= 2 = that many (the parallel group scan) */
+  int32_t walk_waves;          /* waves per walk workgroup: 0 = auto, else 2, 4
+                                  or 8 (a tuning knob; results do not change) */
   void **stage_events;         /* optional hipEvent_t[num_stage_events], recorded
                                   on `stream` at the stage boundaries below
                                   (profiling); NULL = none.  The caller owns them. */
@@ -177,6 +179,12 @@ kda_status kda_chunk_fwd(const kda_chunk_args *a);
  *   u              [chunks, Hv, 128 (v), 64 (t)]  (T (b v))^T           (P)
  *   aqk            [T_tot, Hv, 64]   sum_c qn_t kn_i exp(G_t - G_i), i <= t
  *                                    inside the chunk, 0 above         (P)
+ *   scan           fp32 [G, N, Hv, 3, 128, 128] when the walk runs as a
+ *                  group scan (G = groups > 1), else empty: per chunk group,
+ *                  the transfer (plane 0, [k][j]), the partial state from zero
+ *                  and the group's start state (planes 1 and 2, [v][k])
+ * groups and walk_waves report the launch plan that kda_chunk_fwd takes for
+ * these arguments (the chosen values when the arguments leave them at 0).
  * (P): the last axis is stored in MFMA fragment order: inside each block of
  * 32 elements, position 8 g + j holds element 4 g + j for j < 4 and
  * 16 + 4 g + (j - 4) for j >= 4.  Token axes of a short chunk are zero past
@@ -185,6 +193,7 @@ kda_status kda_chunk_fwd(const kda_chunk_args *a);
 typedef struct kda_ws_layout {
   size_t chunk_offsets, zero, table, qg, kg_t, decay, w, u, aqk, scan, total;
   int64_t max_chunks;
+  int32_t groups, walk_waves;
 } kda_ws_layout;
 kda_status kda_chunk_ws_layout(const kda_chunk_args *a, kda_ws_layout *layout);
 

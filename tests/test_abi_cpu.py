@@ -87,6 +87,8 @@ def test_workspace_layout_is_ordered_and_covers_intermediates(lib):
     ("scale", float("inf"), B.KDA_ERR_SHAPE),
     ("path", 7, B.KDA_ERR_UNSUPPORTED),
     ("groups", -2, B.KDA_ERR_SHAPE),
+    ("groups", 65, B.KDA_ERR_UNSUPPORTED),
+    ("walk_waves", 3, B.KDA_ERR_ARG),
 ])
 def test_chunk_checks(lib, field, value, status):
     a = chunk_args(**{field: value})
@@ -198,3 +200,19 @@ def test_binding_decode_checks():
         B.kda_decode(q, q, v, v, cpu((4, 4)), cpu((8, 4, 128, 64), torch.float32))
     with pytest.raises(NotImplementedError):
         B.kda_decode(q, q, v, v, cpu((4, 4)), cache.bfloat16())
+
+
+def test_planner_picks_groups_only_for_long_chains(lib):
+    """Workspace grows by the scan planes exactly when the planner groups."""
+    def total(**kw):
+        a = chunk_args(**kw)
+        lay = B.WsLayout()
+        assert lib.kda_chunk_ws_layout(ctypes.byref(a), ctypes.byref(lay)) == B.KDA_OK
+        return lay.total - lay.scan
+    # 4 x 4096 tokens over 16 heads: 256 two-wave workgroups of 64-chunk
+    # chains fill the device -> no scan
+    assert total(num_seqs=4, total_tokens=4 * 4096, hqk=16, hv=16) == 0
+    # one 131072-token sequence over 32 heads: 2048-chunk chains -> scan planes
+    assert total(num_seqs=1, total_tokens=131072, hqk=32, hv=32) > 0
+    # explicit groups always reserve their planes
+    assert total(num_seqs=2, total_tokens=256, groups=4) == 4 * 2 * 4 * 3 * 128 * 128 * 4

@@ -37,13 +37,14 @@ def gpu(batch):
     return [t.to(DEV) for t in (batch.q, batch.k, batch.v, batch.g, batch.beta)]
 
 
-def run_dense_state(batch, groups=0, l2=True):
+def run_dense_state(batch, groups=0, l2=True, walk_waves=0):
     """Varlen call with dense initial/final states."""
     q, k, v, g, beta = gpu(batch)
     init = None if batch.initial_state is None else batch.initial_state.to(DEV)
     out, fin = B.chunk_kda(q, k, v, g, beta, scale=batch.scale, initial_state=init,
                            output_final_state=True, cu_seqlens=batch.cu_seqlens.to(DEV),
-                           use_qk_l2norm_in_kernel=l2, groups=groups)
+                           use_qk_l2norm_in_kernel=l2, groups=groups,
+                           walk_waves=walk_waves)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), fin.cpu().numpy()
 
@@ -344,3 +345,85 @@ def test_long_single_workload_sampled_heads():
     e_s = rel(fin[:, heads], s_ref[:, heads])
     say("  rel out", e_o, "state", e_s)
     assert e_o < 1e-2 and e_s < 1e-2
+
+
+# ------------------------------------------------------------- group scan
+
+SCAN_CASES = [
+    # (name, lengths, hqk, hv, dtype, g_scale)
+    ("weak_bf16", [2500], 1, 2, torch.bfloat16, 0.01),
+    ("slow_bf16", [3000], 2, 2, torch.bfloat16, 0.5),
+    ("nodecay_fp32", [1100], 1, 1, torch.float32, 0.0),
+    ("varlen_bf16", [1300, 70, 1, 640, 200], 1, 2, torch.bfloat16, 0.05),
+]
+
+
+@pytest.mark.parametrize("groups,waves", [(2, 2), (4, 4), (8, 8), (3, 2), (1, 4), (1, 8)])
+@pytest.mark.parametrize("case", SCAN_CASES, ids=[c[0] for c in SCAN_CASES])
+def test_group_scan_matches_oracle_and_plain_walk(case, groups, waves):
+    """The chunk-group scan (pass one, compose, pass two) against the oracle,
+    and against the plain walk (G = 1) on the same inputs.  Weak or no decay
+    keeps the carried state visible in every output."""
+    name, lengths, hqk, hv, dt, gs = case
+    b = inputs.make_chunk(lengths, hqk, hv, dtype=dt, g_scale=gs, seed=40 + len(name), init=True)
+    say("scan", name, groups, waves)
+    o1, s1 = run_dense_state(b, groups=1, walk_waves=2)
+    og, sg = run_dense_state(b, groups=groups, walk_waves=waves)
+    o_ref, s_ref = oracle_dense(b)
+    t_ = tol(dt)
+    assert rel(og, o_ref) < t_, rel(og, o_ref)
+    assert rel(sg, s_ref) < t_, rel(sg, s_ref)
+    # the scan reorders the same products; it must agree with the plain walk
+    # well inside the oracle tolerance
+    assert rel(og, o1) < t_ / 2 and rel(sg, s1) < t_ / 2
+
+
+def test_group_scan_more_groups_than_chunks():
+    b = inputs.make_chunk([100, 30], 1, 1, dtype=torch.float32, g_scale=0.1, seed=77, init=True)
+    o, s = run_dense_state(b, groups=16)
+    o_ref, s_ref = oracle_dense(b)
+    assert rel(o, o_ref) < 1e-4 and rel(s, s_ref) < 1e-4
+
+
+def test_group_scan_paged_with_null_slot():
+    lengths = [900, 500, 64]
+    b = inputs.make_chunk(lengths, 1, 2, dtype=torch.bfloat16, g_scale=0.05, seed=78,
+                          paged_slots=6)
+    b.state_indices = torch.tensor([4, -1, 1], dtype=torch.int32)
+    b.has_initial_state = torch.tensor([1, 1, 0], dtype=torch.uint8)
+    q, k, v, g, beta = gpu(b)
+    cache = b.state_cache.to(DEV)
+    out = B.chunk_kda(q, k, v, g, beta, scale=b.scale, cu_seqlens=b.cu_seqlens.to(DEV),
+                      state_cache=cache, state_indices=b.state_indices.to(DEV),
+                      has_initial_state=b.has_initial_state.to(DEV), groups=4)
+    torch.cuda.synchronize()
+    cu = b.cu_seqlens.tolist()
+    assert torch.all(out[cu[1]:cu[2]].cpu() == 0)
+    got = cache.cpu()
+    for n, slot, start in ((0, 4, b.state_cache[4]), (2, 1, torch.zeros(2, 128, 128))):
+        sl = slice(cu[n], cu[n + 1])
+        o_ref, s_ref = oracle.recurrence(b.q[sl], b.k[sl], b.v[sl], b.g[sl], b.beta[sl],
+                                         scale=b.scale, initial_state=start[None])
+        assert rel(out[sl].float().cpu().numpy(), o_ref) < 1e-2
+        assert rel(got[slot].numpy(), s_ref[0]) < 1e-2
+    for r in (0, 2, 3, 5):
+        assert torch.equal(got[r], b.state_cache[r])
+
+
+def test_auto_plan_uses_groups_for_long_single_sequence():
+    """The planner takes the group scan for one long sequence over few heads
+    (and the result still matches the plain walk)."""
+    b = inputs.make_chunk([16384], 2, 2, dtype=torch.bfloat16, g_scale=0.5, seed=79, init=True)
+    q, k, v, g, beta = gpu(b)
+    G, W = B.chunk_plan(q, k, v, g, beta, cu_seqlens=b.cu_seqlens.to(DEV),
+                        initial_state=b.initial_state.to(DEV), output_final_state=True)
+    assert G > 1 and W in (2, 4, 8)
+    out_auto, fin_auto = B.chunk_kda(q, k, v, g, beta, scale=b.scale,
+                                     initial_state=b.initial_state.to(DEV),
+                                     output_final_state=True, cu_seqlens=b.cu_seqlens.to(DEV))
+    out1, fin1 = B.chunk_kda(q, k, v, g, beta, scale=b.scale,
+                             initial_state=b.initial_state.to(DEV), output_final_state=True,
+                             cu_seqlens=b.cu_seqlens.to(DEV), groups=1)
+    torch.cuda.synchronize()
+    assert rel(out_auto.float().cpu().numpy(), out1.float().cpu().numpy()) < 5e-3
+    assert rel(fin_auto.cpu().numpy(), fin1.cpu().numpy()) < 5e-3
