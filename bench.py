@@ -68,9 +68,13 @@ def chunk_work(lengths, hqk, hv, es, state_in, state_out):
     wy_b = (2 * T * hqk + 2 * T * hv) * 128 * es + T * hv * es + T * hv * (2 * 128 + 64) * es
     walk_b = (T * hv * (3 * 128 + 64) * es + nch * hv * 128 * (64 * es + 4)
               + T * hv * 128 * es + (state_in + state_out) * N * hv * 128 * 128 * 4)
+    # prep folded into WY: the inputs once, all six intermediates out
+    intra_b = ((2 * T * hqk + 2 * T * hv) * 128 * es + T * hv * es
+               + T * hv * (3 * 128 + 64) * es + nch * hv * 128 * (2 * 64 * es + 4))
     return dict(
         tokens=T,
         prep=dict(bytes=prep_b, flops=0.0),
+        intra=dict(bytes=intra_b, flops=hv * sum(wy_flops(L) for L in chunks)),
         wy=dict(bytes=wy_b, flops=hv * sum(wy_flops(L) for L in chunks)),
         walk=dict(bytes=walk_b, flops=hv * sum(walk_flops(L) for L in chunks)),
         table=dict(bytes=4 * (2 * N + 1), flops=0.0),
@@ -179,6 +183,8 @@ def main():
     ap.add_argument("--groups", type=int, default=0, help="chunk groups (0 = auto)")
     ap.add_argument("--walk-waves", type=int, default=0,
                     help="waves per walk workgroup: 0 = auto, 2, 4 or 8")
+    ap.add_argument("--path", choices=["auto", "staged", "fused"], default="auto",
+                    help="chunk path: prep as its own kernel (staged) or folded into WY")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     args = ap.parse_args()
@@ -228,27 +234,58 @@ def main():
     ev_sets = [[ev.create() for _ in range(nev)] for _ in range(args.steps)]
     dec_ev = [(ev.create(), ev.create()) for _ in range(args.steps)]
 
-    def step(i=None):
+    path = {"auto": B.PATH_AUTO, "staged": B.PATH_STAGED, "fused": B.PATH_FUSED}[args.path]
+
+    def chunk(evs=None):
         B.chunk_kda(q4, k4, v4, g4, b4, scale=cb.scale, initial_state=cb.initial_state,
                     output_final_state=True, output=out, final_state=fin,
                     groups=args.groups, walk_waves=args.walk_waves, workspace=ws,
-                    stage_events=None if i is None else ev_sets[i])
+                    stage_events=evs, path=path)
+
+    def decode():
+        B.kda_decode(db.q, db.k, db.v, db.g, db.beta, db.state_cache, db.state_indices,
+                     scale=db.scale, output=dout)
+
+    def step():
+        chunk()
         if not args.no_decode:
-            if i is not None:
-                ev.record(dec_ev[i][0], stream)
-            B.kda_decode(db.q, db.k, db.v, db.g, db.beta, db.state_cache, db.state_indices,
-                         scale=db.scale, output=dout)
-            if i is not None:
-                ev.record(dec_ev[i][1], stream)
+            decode()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # the timed region: exactly `steps` whole steps, nothing else on the stream
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # Breakdowns, after the timed region.  An event record between kernels
+    # costs a few microseconds, so the chunk and decode times come from runs
+    # bracketed by one event pair each, and the per-kernel times from a run
+    # with the library's stage events.
+    def bracketed(fn):
+        a_, b_ = ev.create(), ev.create()
+        ev.record(a_, stream)
+        for _ in range(args.steps):
+            fn()
+        ev.record(b_, stream)
+        torch.cuda.synchronize()
+        ms = ev.ms(a_, b_) / args.steps
+        ev.destroy(a_)
+        ev.destroy(b_)
+        return ms
+
+    chunk_only_ms = bracketed(chunk)
+    dec_only_ms = None if args.no_decode else bracketed(decode)
+    for i in range(args.steps):
+        chunk(ev_sets[i])
+        if not args.no_decode:
+            ev.record(dec_ev[i][0], stream)
+            decode()
+            ev.record(dec_ev[i][1], stream)
+    torch.cuda.synchronize()
 
     names = ["table", "prep", "wy", "walk", "compose", "pass2"]
     per = {n: [] for n in names}
@@ -261,26 +298,36 @@ def main():
         if not args.no_decode:
             dec_ms.append(ev.ms(*dec_ev[i]))
     mean = lambda xs: sum(xs) / max(len(xs), 1)
-    t_chunk = mean(chunk_ms) / 1e3
+    t_chunk = chunk_only_ms / 1e3
     work = chunk_work(lengths, hqk, hv, 2, True, True)
     flops = work["wy"]["flops"] + work["walk"]["flops"]
 
+    # the fused path records an empty prep stage: its WY kernel carries prep
+    fused = args.path != "staged"
     kernels = {}
-    for n, bound in (("prep", "hbm"), ("wy", "mfma"), ("walk", "mfma")):
+    stages = (("wy", "intra", "mfma"),) if fused else (("prep", "prep", "hbm"),
+                                                      ("wy", "wy", "mfma"))
+    for n, wk, bound in stages + (("walk", "walk", "mfma"),):
         ms = mean(per[n])
         if ms <= 0:
             continue
         s = ms / 1e3
-        gbs = work[n]["bytes"] / s / 1e9
-        tfl = work[n]["flops"] / s / 1e12
+        gbs = work[wk]["bytes"] / s / 1e9
+        tfl = work[wk]["flops"] / s / 1e12
         kernels[n] = dict(ms=round(ms, 4), bound=bound, gb_s=round(gbs, 1),
-                          tflops=round(tfl, 2),
+                          tflops=round(tfl, 2), hbm_frac=round(gbs / PEAK_HBM_GBS, 4),
                           frac=round((gbs / PEAK_HBM_GBS) if bound == "hbm"
                                      else (tfl / PEAK_BF16_TFLOPS), 4))
+        if n == "wy" and fused:
+            kernels[n]["note"] = "prep folded in (reads q, k, v, g, beta; writes all intermediates)"
+    for n in ("compose", "pass2"):
+        ms = mean(per[n])
+        if ms > 0.003:
+            kernels[n] = dict(ms=round(ms, 4))
     dec = None
     if not args.no_decode:
         dw = decode_work(dwl["N"], dwl["hqk"], dwl["hv"], 2)
-        s = mean(dec_ms) / 1e3
+        s = dec_only_ms / 1e3
         gbs = dw["bytes"] / s / 1e9
         kernels["decode"] = dict(ms=round(s * 1e3, 4), bound="hbm", gb_s=round(gbs, 1),
                                  frac=round(gbs / PEAK_HBM_GBS, 4))
@@ -293,27 +340,34 @@ def main():
     kd = kernels[dom]
     kname = {"prep": "prep_kernel", "wy": "wy_kernel", "walk": "walk_kernel",
              "decode": "decode_kernel"}[dom]
+    wkey = "intra" if (dom == "wy" and fused) else dom
     if kd["bound"] == "hbm":
-        wb = work[dom]["bytes"] if dom != "decode" else decode_work(
+        wb = work[wkey]["bytes"] if dom != "decode" else decode_work(
             dwl["N"], dwl["hqk"], dwl["hv"], 2)["bytes"]
         roof = dict(bound="hbm", achieved=kd["gb_s"], peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=kd["frac"], kernel=kname, algorithmic_bytes=wb)
     else:
         roof = dict(bound="mfma", achieved=kd["tflops"], peak=PEAK_BF16_TFLOPS,
                     unit="TFLOP/s", frac=kd["frac"], kernel=kname,
-                    algorithmic_flops=work[dom]["flops"])
+                    algorithmic_flops=work[wkey]["flops"])
     roof["traffic"] = load_traffic(kname)
     roof["launch_ms"] = kd["ms"]
 
+    n_dec = 0 if args.no_decode else dwl["N"]
+    step_s = wall / args.steps
     res = dict(
-        metric=METRIC, value=round(T / t_chunk, 1), unit="tokens/s", n_gpus=1,
+        metric=METRIC, value=round((T + n_dec) / step_s, 1), unit="tokens/s", n_gpus=1,
         steps=args.steps, warmup=args.warmup,
         ms_per_step=round(wall / args.steps * 1e3, 4), higher_is_better=True,
         scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
         config=dict(workload="dense_prefill", B=wl["B"], T=wl["T"], hqk=hqk, hv=hv,
                     head_dim=128, chunk=64, state="fp32 initial+final",
-                    groups=args.groups, decode=None if dec is None else dec["workload"]),
+                    groups=args.groups, walk_waves=args.walk_waves,
+                    path="fused" if fused else "staged",
+                    decode=None if dec is None else dec["workload"],
+                    value_counts=f"{T} prefill + {n_dec} decode tokens per step"),
         chunk_ms=round(t_chunk * 1e3, 4),
+        chunk_tokens_per_s=round(T / t_chunk, 1),
         tflops=round(flops / t_chunk / 1e12, 2),
         mfma_frac=round(flops / t_chunk / 1e12 / PEAK_BF16_TFLOPS, 4),
         decode=dec, kernels=kernels, roofline=roof,

@@ -21,7 +21,7 @@ _LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_OK, KDA_ERR_SHAPE, KDA_ERR_DTYPE, KDA_ERR_UNSUPPORTED = 0, 1, 2, 3
 KDA_ERR_WORKSPACE, KDA_ERR_HIP, KDA_ERR_ARG = 4, 5, 6
-PATH_AUTO, PATH_STAGED = 0, 1
+PATH_AUTO, PATH_STAGED, PATH_FUSED = 0, 1, 2
 
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 
@@ -292,18 +292,19 @@ def _run_chunk(p, path=PATH_AUTO, groups=0, workspace=None, keep=None, events=No
 def chunk_kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False,
               cu_seqlens=None, use_qk_l2norm_in_kernel=True, output=None, final_state=None,
               state_cache=None, state_indices=None, has_initial_state=None, groups=0,
-              workspace=None, stage_events=None, walk_waves=0):
+              workspace=None, stage_events=None, walk_waves=0, path=PATH_AUTO):
     """Chunked KDA forward (chunk_kda's argument set, plus the paged state of
     fused_kda_chunk).  Returns out, or (out, final_state) when
     output_final_state; in paged mode the final states land in state_cache.
     stage_events: optional list of up to 7 hipEvent_t handles (ints) recorded
     at the stage boundaries (profiling).  groups / walk_waves: 0 lets the
     planner choose; otherwise they fix the walk's launch shape (tuning only,
-    the result is the same up to rounding order)."""
+    the result is the same up to rounding order).  path: PATH_AUTO,
+    PATH_STAGED (prep as its own kernel) or PATH_FUSED."""
     p = _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state,
                        cu_seqlens, use_qk_l2norm_in_kernel, output, final_state,
                        state_cache, state_indices, has_initial_state)
-    _run_chunk(p, groups=groups, workspace=workspace, events=stage_events,
+    _run_chunk(p, path=path, groups=groups, workspace=workspace, events=stage_events,
                walk_waves=walk_waves)
     out = p["out"]
     if output_final_state:
@@ -312,15 +313,16 @@ def chunk_kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_sta
 
 
 def chunk_stages(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=None,
-                 use_qk_l2norm_in_kernel=True, groups=1):
-    """Run the staged path and return its intermediates as raw views of the
+                 use_qk_l2norm_in_kernel=True, groups=1, path=PATH_STAGED):
+    """Run the chunk path (PATH_STAGED: prep as its own kernel; PATH_FUSED:
+    prep folded into WY) and return its intermediates as raw views of the
     workspace (layouts and the packed fragment order as kda.h documents them):
     chunk_offsets, qg, kg_t, decay, w, u_t, aqk, plus out and the final
     state.  For tests and tools."""
     p = _prepare_chunk(q, k, v, g, beta, scale, initial_state, True, cu_seqlens,
                        use_qk_l2norm_in_kernel, None, None, None, None, None)
     keep = {}
-    a = _run_chunk(p, path=PATH_STAGED, groups=groups, keep=keep)
+    a = _run_chunk(p, path=path, groups=groups, keep=keep)
     lib = load_library()
     lay = WsLayout()
     st = lib.kda_chunk_ws_layout(ctypes.byref(a), ctypes.byref(lay))

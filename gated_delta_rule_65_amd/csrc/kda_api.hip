@@ -72,7 +72,7 @@ kda_status check_chunk(const kda_chunk_args* a, bool need_ptrs) {
   } else if (a->state_indices || a->has_initial_state) {
     return fail(KDA_ERR_SHAPE, "state_indices/has_initial_state need a state_cache");
   }
-  if (a->path != KDA_PATH_AUTO && a->path != KDA_PATH_STAGED)
+  if (a->path != KDA_PATH_AUTO && a->path != KDA_PATH_STAGED && a->path != KDA_PATH_FUSED)
     return fail(KDA_ERR_UNSUPPORTED, "unknown path %d", a->path);
   if (a->groups < 0) return fail(KDA_ERR_SHAPE, "groups must be >= 0");
   if (a->groups > 64) return fail(KDA_ERR_UNSUPPORTED, "groups above 64");
@@ -243,6 +243,7 @@ KDA_API kda_status kda_chunk_fwd(const kda_chunk_args* a) {
   L.w = ws + W.w; L.u = ws + W.u; L.aqk = ws + W.aqk;
   L.events = a->stage_events;
   L.num_events = a->stage_events ? a->num_stage_events : 0;
+  L.fuse_prep = a->path == KDA_PATH_STAGED ? 0 : 1;
   L.groups = W.groups;
   L.walk_waves = W.walk_waves;
   L.scan = L.groups > 1 ? (float*)(ws + W.scan) : nullptr;

@@ -136,6 +136,24 @@ __device__ __forceinline__ void load_rows4(const E* src, int stride_t, int L, fl
   }
 }
 
+// The same tile with each thread holding four consecutive tokens: rows
+// 4 rg + it, so wave w holds the 16-token block w.
+template <typename E>
+__device__ __forceinline__ void load_rows4c(const E* src, int stride_t, int L, float (&x)[4][8]) {
+  const int tid = threadIdx.x, rg = tid >> 4, j = tid & 15;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int t = min(4 * rg + it, L - 1);
+    load8(src + (size_t)t * stride_t + 8 * j, x[it]);
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const bool live = 4 * rg + it < L;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[it][e] = live ? x[it][e] : 0.f;
+  }
+}
+
 __device__ __forceinline__ void l2norm_rows4(float (&x)[4][8]) {
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
@@ -277,37 +295,32 @@ __global__ __launch_bounds__(256) void prep_kernel(const E* __restrict__ q,
 
 // ------------------------------------------------------------------------- WY
 
-// X = sum_{c in [b, a)} A_ac T_cb into scratch (one 16x16 block per wave).
-template <int SA, int STT>
-__device__ __forceinline__ void wy_offdiag_x(int a, int b, const float* sA, const float* sT,
-                                             float (*sX)[17], int lane) {
-  const int col = lane & 15, rq = lane >> 4;
+// One off-diagonal block of T = (I + A)^-1 (A strictly lower, 16 x 16 blocks,
+// fp32 row-major with row stride SA), on fp32 MFMA (16x16x4, exact products):
+//   X = sum_{c = b}^{a-1} A_ac T_cb,   T_ab = -T_aa X.
+// Operand layouts of v_mfma_f32_16x16x4_f32: A lane l holds [row l % 16][k =
+// l / 16], B lane l holds [k = l / 16][col l % 16], C lane l holds [rows
+// 4 (l / 16) + r][col l % 16].  X stays in registers: at step s of the second
+// product lane group g takes k = 4 g + s, which is exactly C element r = s.
+template <int SA>
+__device__ __forceinline__ void wy_offdiag(int a, int b, const float* sA, float* sT, int lane) {
+  const int l16 = lane & 15, gq = lane >> 4;
+  f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+  for (int cb = b; cb < a; ++cb) {
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int row = 4 * rq + rr;
-    float acc = 0.f;
-    for (int cb = b; cb < a; ++cb) {
-#pragma unroll
-      for (int m = 0; m < 16; ++m)
-        acc += sA[(16 * a + row) * SA + 16 * cb + m] * sT[(16 * cb + m) * STT + 16 * b + col];
+    for (int s = 0; s < 4; ++s) {
+      const int kk = 16 * cb + 4 * s + gq;
+      x = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * a + l16) * SA + kk],
+                                               sT[kk * SA + 16 * b + l16], x, 0, 0, 0);
     }
-    sX[row][col] = acc;
   }
-}
-
-// T_ab = -T_aa X.
-template <int STT>
-__device__ __forceinline__ void wy_offdiag_t(int a, int b, float* sT, const float (*sX)[17],
-                                             int lane) {
-  const int col = lane & 15, rq = lane >> 4;
+  f32x4_t y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int row = 4 * rq + rr;
-    float acc = 0.f;
+  for (int s = 0; s < 4; ++s)
+    y = __builtin_amdgcn_mfma_f32_16x16x4f32(sT[(16 * a + l16) * SA + 16 * a + 4 * gq + s], x[s],
+                                             y, 0, 0, 0);
 #pragma unroll
-    for (int m = 0; m < 16; ++m) acc += sT[(16 * a + row) * STT + 16 * a + m] * sX[m][col];
-    sT[(16 * a + row) * STT + 16 * b + col] = -acc;
-  }
+  for (int r = 0; r < 4; ++r) sT[(16 * a + 4 * gq + r) * SA + 16 * b + l16] = -y[r];
 }
 
 // 8 consecutive elements of an LDS tile row as floats.
@@ -338,7 +351,9 @@ __device__ __forceinline__ FragS frag_row(const float* p) {
 }
 
 // One workgroup (4 waves) per (chunk, value head).
-//   phase 0: q, k normalised; G = log2(e) cumsum(g); block-referenced operand
+//   phase 0: q, k normalised; G = log2(e) cumsum(g) (in registers: wave w
+//            holds the 16-token block w, four consecutive tokens per thread);
+//            block-referenced operand
 //            tiles QL = qn 2^(G - G_m), KL = kn 2^(G - G_m), KR = kn 2^(G_m - G)
 //            (m = token 16 a + 7 of the row's 16-token block a) and the
 //            reference rows GM[a] = G_{16 a + 7}.
@@ -346,37 +361,38 @@ __device__ __forceinline__ FragS frag_row(const float* p) {
 //            A[t][i] = L_a[t] . KR[i] 2^(GM[a] - GM[b]) for t in block a, i in b.
 //   phase 2: T = (I + A_kk)^-1 in fp32 by blocked forward substitution.
 //   phase 3: w = T (b KL 2^GM) and u = T (b v) on MFMA.
-template <typename E>
+//
+// With PREP the kernel also writes the prep outputs (qg, kg_t, decay), so the
+// inputs are read from HBM once for the whole intra-chunk stage.
+template <typename E, bool PREP>
 __global__ __launch_bounds__(256) void wy_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ g, const E* __restrict__ beta, const int4* __restrict__ table,
     int hqk, int hv, int use_l2, E* __restrict__ w_out, E* __restrict__ u_t,
-    E* __restrict__ aqk) {
+    E* __restrict__ aqk, E* __restrict__ qg, E* __restrict__ kg_t, float* __restrict__ decay) {
   constexpr bool SPLIT = std::is_same<E, float>::value;
   using TE = typename TileT<E>::T;
   constexpr int ST = D + (SPLIT ? 4 : 8);        // operand tile row stride (elements)
   constexpr int TILE = C * ST * (int)sizeof(TE);  // bytes of one 64 x 128 operand tile
-  constexpr int SG = D + 4;                       // G tile row stride (fp32)
   constexpr int SA = C + 4;                       // A_kk / T row stride (fp32)
   constexpr int AB = C * SA * 4;
-  // regions: R0 = QL | X scratch | V ; R1 = KL ; R2 = KR | T ; R3 = A ; G spans R2..
+  // regions: R0 = QL | V ; R1 = KL ; R2 = KR | T ; R3 = A
   constexpr int R0 = 0, R1 = R0 + TILE, R2 = R1 + TILE;
   constexpr int R2SZ = TILE > AB ? TILE : AB;
   constexpr int R3 = R2 + R2SZ;
   constexpr int RGM = R3 + AB;
   constexpr int RB = RGM + 4 * D * 4;
-  constexpr int BYTES = RB + C * 4;
-  static_assert(C * SG * 4 <= R2SZ + AB, "G tile must fit in R2 + R3");
+  constexpr int RWT = RB + C * 4;   // per-wave gate totals [4][D]
+  constexpr int BYTES = RWT + 4 * D * 4;
   __shared__ __attribute__((aligned(16))) char smem[BYTES];
   TE* QL = reinterpret_cast<TE*>(smem + R0);
   TE* KL = reinterpret_cast<TE*>(smem + R1);
   TE* KR = reinterpret_cast<TE*>(smem + R2);
   float* sTt = reinterpret_cast<float*>(smem + R2);
-  float (*sG)[SG] = reinterpret_cast<float (*)[SG]>(smem + R2);
   float* sA = reinterpret_cast<float*>(smem + R3);
+  float* sWt = reinterpret_cast<float*>(smem + RWT);
   float* GM = reinterpret_cast<float*>(smem + RGM);
   float* sB = reinterpret_cast<float*>(smem + RB);
-  float (*sX)[16][17] = reinterpret_cast<float (*)[16][17]>(smem + R0);
   TE* sV = reinterpret_cast<TE*>(smem + R0);
 
   ChunkPos p;
@@ -389,44 +405,100 @@ __global__ __launch_bounds__(256) void wy_kernel(
 
   // ---- phase 0
   {
-    float qx[4][8], kx[4][8], gx[4][8];
-    load_rows4(q + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, qx);
-    load_rows4(k + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, kx);
-    load_rows4(g + ((size_t)p.t0 * hv + h) * D, hv * D, L, gx);
+    float qx[4][8], kx[4][8], G[4][8];
+    load_rows4c(q + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, qx);
+    load_rows4c(k + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, kx);
+    load_rows4c(g + ((size_t)p.t0 * hv + h) * D, hv * D, L, G);
     const float braw = to_f32(beta[(size_t)(p.t0 + min(tid, L - 1)) * hv + h]);
     if (use_l2) {
       l2norm_rows4(qx);
       l2norm_rows4(kx);
     }
-    gate_cumsum<SG>(gx, sG);
-    // my rows t = rg + 16 it lie in block it; its reference row is 16 it + 7
-    float G[4][8], Gm[4][8];
+    // G: inclusive cumsum over tokens (rows past L hold g = 0, so G stays at
+    // G_{L-1} there).  In-thread over the 4 tokens, across the 4 row groups
+    // of the wave by shuffles, across waves through LDS.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int r4 = lane >> 4;
+    float excl[8];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int e = 0; e < 8; ++e) {
+      float run = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        G[it][e] = sG[rg + 16 * it][8 * j + e];
-        Gm[it][e] = sG[16 * it + 7][8 * j + e];
+      for (int it = 0; it < 4; ++it) {
+        run += G[it][e] * LOG2E;
+        G[it][e] = run;
       }
+      float x = run, y;
+      y = __shfl_up(x, 16);
+      x += r4 >= 1 ? y : 0.f;
+      y = __shfl_up(x, 32);
+      x += r4 >= 2 ? y : 0.f;
+      excl[e] = x - run;
+      if (r4 == 3) sWt[wv * D + 8 * j + e] = x;
     }
-    lds_barrier();  // G consumed; R2/R3 are free
-    if (rg == 7) {
+    lds_barrier();
+    float Gl[8], Gm[8];
 #pragma unroll
-      for (int it = 0; it < 4; ++it)
+    for (int e = 0; e < 8; ++e) {
+      float before = 0.f, all = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) GM[it * D + 8 * j + e] = G[it][e];
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const float x = sWt[w2 * D + 8 * j + e];
+        before += w2 < wv ? x : 0.f;
+        all += x;
+      }
+      Gl[e] = all;  // G at the last token of the chunk
+#pragma unroll
+      for (int it = 0; it < 4; ++it) G[it][e] += excl[e] + before;
+      // reference token 16 wv + 7 of this wave's block: row group 1, it = 3
+      Gm[e] = __shfl(G[3][e], 16 + j);
+    }
+    if (r4 == 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) GM[wv * D + 8 * j + e] = G[3][e];
     }
     if (tid < C) sB[tid] = (tid < L) ? sigmoid(braw) : 0.f;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int t = rg + 16 * it;
+      const int t = 4 * rg + it;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float up = exp2_fast(G[it][e] - Gm[it][e]);
-        const float dn = exp2_fast(Gm[it][e] - G[it][e]);
+        const float up = exp2_fast(G[it][e] - Gm[e]);
+        const float dn = exp2_fast(Gm[e] - G[it][e]);
         st_elem(QL + t * ST + 8 * j + e, qx[it][e] * up);
         st_elem(KL + t * ST + 8 * j + e, kx[it][e] * up);
         st_elem(KR + t * ST + 8 * j + e, kx[it][e] * dn);
+      }
+    }
+    if (PREP) {
+      // qg = qn 2^G (token-major, channel packed)
+      const int cb = 32 * (j >> 2);
+      const int run0 = cb + pack32(8 * (j & 3)), run1 = cb + pack32(8 * (j & 3) + 4);
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int t = 4 * rg + it;
+        float xq[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xq[e] = qx[it][e] * exp2_fast(G[it][e]);
+        if (t < L) {
+          E* dst = qg + ((size_t)(p.t0 + t) * hv + h) * D;
+          store4(dst + run0, xq[0], xq[1], xq[2], xq[3]);
+          store4(dst + run1, xq[4], xq[5], xq[6], xq[7]);
+        }
+      }
+      // kg_t[c][h][kk][packed t] = kn 2^(G_last - G): this thread's 4
+      // consecutive tokens are 4 consecutive packed positions (zero past L)
+      E* kdst = kg_t + ((size_t)c * hv + h) * D * C + packed_index(4 * rg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float xk[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) xk[it] = kx[it][e] * exp2_fast(Gl[e] - G[it][e]);
+        store4(kdst + (size_t)(8 * j + e) * C, xk[0], xk[1], xk[2], xk[3]);
+      }
+      if (tid < 16) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) decay[((size_t)c * hv + h) * D + 8 * j + e] = exp2_fast(Gl[e]);
       }
     }
   }
@@ -527,19 +599,17 @@ __global__ __launch_bounds__(256) void wy_kernel(
     if ((i >> 4) > (t >> 4)) sTt[t * SA + i] = 0.f;
   }
   lds_barrier();
-  if (wave < 3) wy_offdiag_x<SA, SA>(wave + 1, wave, sA, sTt, sX[wave], lane);
-  lds_barrier();
-  if (wave < 3) wy_offdiag_t<SA>(wave + 1, wave, sTt, sX[wave], lane);
-  lds_barrier();
-  if (wave < 2) wy_offdiag_x<SA, SA>(wave + 2, wave, sA, sTt, sX[wave], lane);
-  lds_barrier();
-  if (wave < 2) wy_offdiag_t<SA>(wave + 2, wave, sTt, sX[wave], lane);
-  lds_barrier();
-  if (wave == 0) wy_offdiag_x<SA, SA>(3, 0, sA, sTt, sX[0], lane);
-  lds_barrier();
-  if (wave == 0) wy_offdiag_t<SA>(3, 0, sTt, sX[0], lane);
-  lds_barrier();
-  // v tile into R0 (the X scratch is dead)
+  {
+    // levels a - b = 1, 2, 3 of the off-diagonal blocks, one block per wave
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    if (wu < 3) wy_offdiag<SA>(wu + 1, wu, sA, sTt, lane);
+    lds_barrier();
+    if (wu < 2) wy_offdiag<SA>(wu + 2, wu, sA, sTt, lane);
+    lds_barrier();
+    if (wu == 0) wy_offdiag<SA>(3, 0, sA, sTt, lane);
+    lds_barrier();
+  }
+  // v tile into R0
 #pragma unroll
   for (int it = 0; it < 4; ++it)
 #pragma unroll
@@ -1080,14 +1150,22 @@ static hipError_t launch_staged_t(const ChunkLaunch& L) {
                      L.chunk_offsets, (int4*)L.table, (int)L.max_chunks, (uint4*)L.zero);
   mark(L, 1);
   if (L.max_chunks > 0 && T > 0) {
-    hipLaunchKernelGGL(prep_kernel<E>, dim3((unsigned)L.max_chunks, L.hqk), dim3(256), 0, st,
-                       (const E*)L.q, (const E*)L.k, (const E*)L.g, (const int4*)L.table,
-                       L.hqk, L.hv, L.use_l2, (E*)L.qg, (E*)L.kg_t, L.decay);
+    if (!L.fuse_prep)
+      hipLaunchKernelGGL(prep_kernel<E>, dim3((unsigned)L.max_chunks, L.hqk), dim3(256), 0, st,
+                         (const E*)L.q, (const E*)L.k, (const E*)L.g, (const int4*)L.table,
+                         L.hqk, L.hv, L.use_l2, (E*)L.qg, (E*)L.kg_t, L.decay);
     mark(L, 2);
-    hipLaunchKernelGGL(wy_kernel<E>, dim3((unsigned)L.max_chunks, L.hv), dim3(256), 0, st,
-                       (const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.g,
-                       (const E*)L.beta, (const int4*)L.table, L.hqk, L.hv, L.use_l2,
-                       (E*)L.w, (E*)L.u, (E*)L.aqk);
+    const dim3 grid((unsigned)L.max_chunks, L.hv);
+    if (L.fuse_prep)
+      hipLaunchKernelGGL((wy_kernel<E, true>), grid, dim3(256), 0, st, (const E*)L.q,
+                         (const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta,
+                         (const int4*)L.table, L.hqk, L.hv, L.use_l2, (E*)L.w, (E*)L.u,
+                         (E*)L.aqk, (E*)L.qg, (E*)L.kg_t, L.decay);
+    else
+      hipLaunchKernelGGL((wy_kernel<E, false>), grid, dim3(256), 0, st, (const E*)L.q,
+                         (const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta,
+                         (const int4*)L.table, L.hqk, L.hv, L.use_l2, (E*)L.w, (E*)L.u,
+                         (E*)L.aqk, (E*)nullptr, (E*)nullptr, (float*)nullptr);
   } else {
     mark(L, 2);
   }

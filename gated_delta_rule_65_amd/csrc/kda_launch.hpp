@@ -40,6 +40,7 @@ struct ChunkLaunch {
   void* zero;                 // 1 KiB zero page (written by the chunk-table kernel)
   int groups;                 // chunk groups per sequence (1 = plain walk)
   int walk_waves;             // waves per walk workgroup: 2, 4 or 8 (16 columns each)
+  int fuse_prep;              // 1: the WY kernel also writes qg, kg_t and decay
   void** events;              // optional stage events (KDA_EV_*), may be NULL
   int num_events;
   void* stream;

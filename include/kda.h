@@ -81,8 +81,10 @@ typedef enum kda_status {
 
 /* Execution plan of the chunked forward. */
 typedef enum kda_path {
-  KDA_PATH_AUTO = 0,    /* the library picks */
-  KDA_PATH_STAGED = 1   /* prep -> wy -> walk, intermediates in the workspace */
+  KDA_PATH_AUTO = 0,    /* the library picks (KDA_PATH_FUSED) */
+  KDA_PATH_STAGED = 1,  /* prep -> wy -> walk, intermediates in the workspace */
+  KDA_PATH_FUSED = 2    /* prep folded into the WY kernel (one pass over q, k,
+                           g) -> walk; same intermediates, same results */
 } kda_path;
 
 /*
