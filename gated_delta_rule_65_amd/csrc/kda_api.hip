@@ -152,7 +152,7 @@ kda_status layout_of(const kda_chunk_args* a, kda_ws_layout* L) {
   L->chunk_offsets = off;
   off = align_up(off + sizeof(int32_t) * ((size_t)a->num_seqs + 1), 256);
   L->zero = off;
-  off = align_up(off + 1024, 256);
+  off = align_up(off + 1024 + 256, 256);  // zero page, then the WY work counter
   L->table = off;
   off = align_up(off + 16 * (size_t)mc, 256);
   L->qg = off;

@@ -23,6 +23,7 @@
 // For i in an earlier block both factors are <= 1; inside block a both
 // exponents stay within 8 steps (<= 58 in log2 units), which fp32 and bf16
 // hold.  Products for i > t may be large but finite and are masked away.
+#include <algorithm>
 #include <type_traits>
 
 #include "kda_common.hpp"
@@ -58,7 +59,8 @@ __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* cu, 
                                                              int max_chunks, uint4* zero) {
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x;
-  if (tid < 64) zero[tid] = make_uint4(0, 0, 0, 0);  // the zero page the walk DMAs from
+  if (tid < 65) zero[tid] = make_uint4(0, 0, 0, 0);  // the zero page the walk DMAs from,
+                                                     // then the WY work counter
   const int per = (N + 1023) / 1024;
   const int s0 = min(N, tid * per), s1 = min(N, s0 + per);
   int sum = 0;
@@ -350,66 +352,216 @@ __device__ __forceinline__ FragS frag_row(const float* p) {
   return make_frag<true>(x);
 }
 
+// A q / k / v / g row tile: thread (rg, j) takes rows t = 4 rg + it (so
+// wave w holds the 16-token block w) and channels 8 j .. 8 j + 7, kept
+// undecoded (their bits) so that a tile can be fetched one work item ahead
+// and decoded when its turn comes.
+template <typename E> struct RawRows;
+template <> struct RawRows<bf16> { uint4 r[4]; };
+template <> struct RawRows<float> { float4 r[4][2]; };
+__device__ __forceinline__ void raw_row(const bf16* p, RawRows<bf16>& x, int it) {
+  x.r[it] = *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void raw_row(const float* p, RawRows<float>& x, int it) {
+  x.r[it][0] = reinterpret_cast<const float4*>(p)[0];
+  x.r[it][1] = reinterpret_cast<const float4*>(p)[1];
+}
+__device__ __forceinline__ void raw_vals(const RawRows<bf16>& x, int it, float* o) {
+  const uint32_t w[4] = {x.r[it].x, x.r[it].y, x.r[it].z, x.r[it].w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    o[2 * d] = __uint_as_float(w[d] << 16);
+    o[2 * d + 1] = __uint_as_float(w[d] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void raw_vals(const RawRows<float>& x, int it, float* o) {
+  const float4 a = x.r[it][0], b = x.r[it][1];
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+  o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+template <typename E>
+__device__ __forceinline__ void raw_load(const E* src, int stride_t, int L, RawRows<E>& x,
+                                         int tid) {
+  const int rg = tid >> 4, j = tid & 15;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int t = min(4 * rg + it, L - 1);  // rows past L re-read row L - 1 ...
+    raw_row(src + (size_t)t * stride_t + 8 * j, x, it);
+  }
+}
+template <typename E>
+__device__ __forceinline__ void raw_decode(const RawRows<E>& x, int L, float (&out)[4][8],
+                                           int tid) {
+  const int rg = tid >> 4;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    raw_vals(x, it, out[it]);
+    const bool live = 4 * rg + it < L;  // ... and are zeroed here
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[it][e] = live ? out[it][e] : 0.f;
+  }
+}
+// Channel e (0..7) of the 4 rows of a raw tile as 4 consecutive values.
+__device__ __forceinline__ bf16x4_t raw_column(const RawRows<bf16>& x, int e) {
+  uint32_t b[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const uint32_t w[4] = {x.r[it].x, x.r[it].y, x.r[it].z, x.r[it].w};
+    b[it] = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu);
+  }
+  return __builtin_bit_cast(bf16x4_t, make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16)));
+}
+__device__ __forceinline__ float4 raw_column(const RawRows<float>& x, int e) {
+  float c[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    float o[8];
+    raw_vals(x, it, o);
+    c[it] = o[e];
+  }
+  return make_float4(c[0], c[1], c[2], c[3]);
+}
+// Four values of one channel (4 consecutive tokens) in the tile element type.
+template <typename E> struct Col4;
+template <> struct Col4<bf16> { using T = bf16x4_t; };
+template <> struct Col4<float> { using T = float4; };
+__device__ __forceinline__ void col4(bf16x4_t& d, float a, float b, float c, float e) {
+  d = bf16x4_t{(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)e};
+}
+__device__ __forceinline__ void col4(float4& d, float a, float b, float c, float e) {
+  d = make_float4(a, b, c, e);
+}
+
+// 16-byte store of 8 values (bf16: one piece; fp32: two).
+__device__ __forceinline__ void store8(bf16* p, const float (&x)[8]) {
+  *reinterpret_cast<bf16x8_t*>(p) = pack8(x);
+}
+__device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+}
+
+// Transposed operand tile [128 rows][64 tokens] (rows: key positions or value
+// channels), 16-byte pieces XOR-swizzled with (r ^ (r >> 3)) & 7 so that the
+// 8-token-per-row writes of the phase-0 layout (rows 8 j + e) and the
+// fragment reads (rows 16 cb + l16) both spread over the banks.
+template <typename TE>
+__device__ __forceinline__ int tslot(int r, int piece) {
+  constexpr int PT = C * (int)sizeof(TE) / 16;  // pieces per row
+  return r * PT + (piece ^ ((r ^ (r >> 3)) & 7));
+}
+
+// 8 consecutive tokens (two 16-byte pieces from `piece`) of row r of an fp32
+// transposed tile.
+__device__ __forceinline__ void unit_vals_t(const uint4* tile, int r, int piece, float (&x)[8]) {
+  const float4 a = __builtin_bit_cast(float4, tile[tslot<float>(r, piece)]);
+  const float4 b = __builtin_bit_cast(float4, tile[tslot<float>(r, piece + 1)]);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
 // One workgroup (4 waves) per (chunk, value head).
-//   phase 0: q, k normalised; G = log2(e) cumsum(g) (in registers: wave w
-//            holds the 16-token block w, four consecutive tokens per thread);
-//            block-referenced operand
-//            tiles QL = qn 2^(G - G_m), KL = kn 2^(G - G_m), KR = kn 2^(G_m - G)
-//            (m = token 16 a + 7 of the row's 16-token block a) and the
-//            reference rows GM[a] = G_{16 a + 7}.
+//   phase 0: q, k normalised; G = log2(e) cumsum(g) in registers (a wave
+//            holds one 16-token block, four consecutive tokens and eight
+//            consecutive channels per thread); block-referenced operand tiles
+//            QL = qn 2^(G - G_m), KL = kn 2^(G - G_m), KR = kn 2^(G_m - G)
+//            (m = token 16 a + 7 of the row's block a); the decay factors
+//            between block references E_ab = 2^(G_ma - G_mb), b < a.
 //   phase 1: A_kk (to LDS, fp32) and A_qk (to memory) on MFMA:
-//            A[t][i] = L_a[t] . KR[i] 2^(GM[a] - GM[b]) for t in block a, i in b.
+//            A[t][i] = L_a[t] . KR_b[i] E_ab for t in block a, i in b.
+//            Then kn 2^G and v are laid down transposed (token-contiguous).
+//   Channel order inside the kernel is natural; the fragment order of the
+//   outputs (qg, w) is applied when they are stored.
 //   phase 2: T = (I + A_kk)^-1 in fp32 by blocked forward substitution.
-//   phase 3: w = T (b KL 2^GM) and u = T (b v) on MFMA.
+//   phase 3: with T' = T diag(b): w = T' (kn 2^G) and u = T' v on MFMA.
 //
 // With PREP the kernel also writes the prep outputs (qg, kg_t, decay), so the
 // inputs are read from HBM once for the whole intra-chunk stage.
 template <typename E, bool PREP>
-__global__ __launch_bounds__(256) void wy_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void wy_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ g, const E* __restrict__ beta, const int4* __restrict__ table,
     int hqk, int hv, int use_l2, E* __restrict__ w_out, E* __restrict__ u_t,
-    E* __restrict__ aqk, E* __restrict__ qg, E* __restrict__ kg_t, float* __restrict__ decay) {
+    E* __restrict__ aqk, E* __restrict__ qg, E* __restrict__ kg_t, float* __restrict__ decay,
+    int items, int* __restrict__ counter) {
   constexpr bool SPLIT = std::is_same<E, float>::value;
   using TE = typename TileT<E>::T;
-  constexpr int ST = D + (SPLIT ? 4 : 8);        // operand tile row stride (elements)
-  constexpr int TILE = C * ST * (int)sizeof(TE);  // bytes of one 64 x 128 operand tile
+  constexpr int ST = D + (SPLIT ? 4 : 8);        // row stride of the [64 t][128] tiles
+  constexpr int TILE = C * ST * (int)sizeof(TE);
+  constexpr int TTILE = D * C * (int)sizeof(TE);  // transposed [128][64 t] tile
   constexpr int SA = C + 4;                       // A_kk / T row stride (fp32)
   constexpr int AB = C * SA * 4;
-  // regions: R0 = QL | V ; R1 = KL ; R2 = KR | T ; R3 = A
-  constexpr int R0 = 0, R1 = R0 + TILE, R2 = R1 + TILE;
+  // regions: R0 = QL | (kn 2^G)^T ; R1 = KL | v^T ; R2 = KR | T ; R3 = A
+  constexpr int R0SZ = TILE > TTILE ? TILE : TTILE;
   constexpr int R2SZ = TILE > AB ? TILE : AB;
-  constexpr int R3 = R2 + R2SZ;
-  constexpr int RGM = R3 + AB;
-  constexpr int RB = RGM + 4 * D * 4;
-  constexpr int RWT = RB + C * 4;   // per-wave gate totals [4][D]
-  constexpr int BYTES = RWT + 4 * D * 4;
+  constexpr int R0 = 0, R1 = R0 + R0SZ, R2 = R1 + R0SZ, R3 = R2 + R2SZ;
+  constexpr int RE = R3 + AB;          // E_ab [6][128] fp32
+  constexpr int RP = RE + 6 * D * 4;   // per-wave inclusive sums at token 16 w + 7
+  constexpr int RWT = RP + 4 * D * 4;  // per-wave gate totals
+  constexpr int RB = RWT + 4 * D * 4;  // b [64]
+  constexpr int BYTES = RB + C * 4;
   __shared__ __attribute__((aligned(16))) char smem[BYTES];
   TE* QL = reinterpret_cast<TE*>(smem + R0);
   TE* KL = reinterpret_cast<TE*>(smem + R1);
   TE* KR = reinterpret_cast<TE*>(smem + R2);
+  uint4* KGt = reinterpret_cast<uint4*>(smem + R0);
+  uint4* Vt = reinterpret_cast<uint4*>(smem + R1);
   float* sTt = reinterpret_cast<float*>(smem + R2);
   float* sA = reinterpret_cast<float*>(smem + R3);
+  float* sE = reinterpret_cast<float*>(smem + RE);
+  float* sP = reinterpret_cast<float*>(smem + RP);
   float* sWt = reinterpret_cast<float*>(smem + RWT);
-  float* GM = reinterpret_cast<float*>(smem + RGM);
   float* sB = reinterpret_cast<float*>(smem + RB);
-  TE* sV = reinterpret_cast<TE*>(smem + R0);
 
+  const int grp = hv / hqk;
+
+  // Persistent: work item = (chunk, value head), chunk-major.  A workgroup
+  // starts with item blockIdx.x and claims each following item from a
+  // counter (zeroed by the chunk-table kernel) while it works on the current
+  // one, so fast workgroups take more items.  The raw q, k, g rows and beta
+  // of the next item are fetched during this item's phases 1-3.  Items past
+  // the last chunk end the loop (their records have length 0, and every
+  // later claim is past it too).
+  __shared__ int s_next;
+  int item = blockIdx.x;
   ChunkPos p;
-  if (!locate_chunk(blockIdx.x, table, p)) return;
-  const int c = blockIdx.x, h = blockIdx.y, hq = h / (hv / hqk);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  bool ok = item < items && locate_chunk(item / hv, table, p);
+  RawRows<E> rq, rk, rgt;
+  E rb;
+  auto prefetch = [&](int it_, const ChunkPos& pp, int tid) {
+    const int h_ = it_ % hv, hq_ = h_ / grp;
+    raw_load(q + ((size_t)pp.t0 * hqk + hq_) * D, hqk * D, pp.L, rq, tid);
+    raw_load(k + ((size_t)pp.t0 * hqk + hq_) * D, hqk * D, pp.L, rk, tid);
+    raw_load(g + ((size_t)pp.t0 * hv + h_) * D, hv * D, pp.L, rgt, tid);
+    rb = beta[(size_t)(pp.t0 + min(tid, pp.L - 1)) * hv + h_];
+  };
+  if (ok) prefetch(item, p, (int)threadIdx.x);
+
+  while (ok) {
+  // Lane-derived indices are rebuilt from an opaque copy of the thread id in
+  // every iteration: hoisted out of the loop, the many per-lane LDS addresses
+  // derived from them would stay live across the whole loop.
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int l16 = lane & 15, gq = lane >> 4;
-  const int rg = tid >> 4, j = tid & 15;
+  const int rg = tid >> 4, j = tid & 15, r4 = lane >> 4;
+  const int c = item / hv, h = item - c * hv;
   const int L = p.L;
+  int claim = 0;
+  if (tid == 0) claim = atomicAdd(counter, 1);  // the next item; published below
+
+  // kn 2^G for phase 3, kept (per channel, 4 tokens) across phase 1
+  typename Col4<E>::T kgp[8];
 
   // ---- phase 0
   {
     float qx[4][8], kx[4][8], G[4][8];
-    load_rows4c(q + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, qx);
-    load_rows4c(k + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, kx);
-    load_rows4c(g + ((size_t)p.t0 * hv + h) * D, hv * D, L, G);
-    const float braw = to_f32(beta[(size_t)(p.t0 + min(tid, L - 1)) * hv + h]);
+    raw_decode(rq, L, qx, tid);
+    raw_decode(rk, L, kx, tid);
+    raw_decode(rgt, L, G, tid);
+    const float braw = to_f32(rb);
     if (use_l2) {
       l2norm_rows4(qx);
       l2norm_rows4(kx);
@@ -417,8 +569,6 @@ __global__ __launch_bounds__(256) void wy_kernel(
     // G: inclusive cumsum over tokens (rows past L hold g = 0, so G stays at
     // G_{L-1} there).  In-thread over the 4 tokens, across the 4 row groups
     // of the wave by shuffles, across waves through LDS.
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const int r4 = lane >> 4;
     float excl[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -434,7 +584,8 @@ __global__ __launch_bounds__(256) void wy_kernel(
       y = __shfl_up(x, 32);
       x += r4 >= 2 ? y : 0.f;
       excl[e] = x - run;
-      if (r4 == 3) sWt[wv * D + 8 * j + e] = x;
+      if (r4 == 1) sP[wv * D + 8 * j + e] = x;   // through token 16 w + 7
+      if (r4 == 3) sWt[wv * D + 8 * j + e] = x;  // the whole block
     }
     lds_barrier();
     float Gl[8], Gm[8];
@@ -453,56 +604,74 @@ __global__ __launch_bounds__(256) void wy_kernel(
       // reference token 16 wv + 7 of this wave's block: row group 1, it = 3
       Gm[e] = __shfl(G[3][e], 16 + j);
     }
-    if (r4 == 1) {
+    // E_ab = 2^(G_ma - G_mb) for the 6 pairs b < a (pair index a (a - 1) / 2 + b)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) GM[wv * D + 8 * j + e] = G[3][e];
+    for (int m = 0; m < 3; ++m) {
+      const int idx = tid + 256 * m, pi = idx >> 7, ch = idx & (D - 1);
+      const int a = pi < 1 ? 1 : (pi < 3 ? 2 : 3), b = pi - a * (a - 1) / 2;
+      float ga = sP[a * D + ch], gb = sP[b * D + ch];
+#pragma unroll
+      for (int w2 = 0; w2 < 3; ++w2) {
+        ga += w2 < a ? sWt[w2 * D + ch] : 0.f;
+        gb += w2 < b ? sWt[w2 * D + ch] : 0.f;
+      }
+      sE[idx] = exp2_fast(ga - gb);
     }
     if (tid < C) sB[tid] = (tid < L) ? sigmoid(braw) : 0.f;
+    float pm[8], pl[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pm[e] = exp2_fast(Gm[e]);          // 2^G = 2^(G - G_m) 2^G_m
+      pl[e] = exp2_fast(Gl[e] - Gm[e]);  // 2^(G_last - G) = 2^(G_m - G) 2^(G_last - G_m)
+    }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int t = 4 * rg + it;
+      float xq[8], xl[8], xr[8], xg[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float up = exp2_fast(G[it][e] - Gm[e]);
         const float dn = exp2_fast(Gm[e] - G[it][e]);
-        st_elem(QL + t * ST + 8 * j + e, qx[it][e] * up);
-        st_elem(KL + t * ST + 8 * j + e, kx[it][e] * up);
-        st_elem(KR + t * ST + 8 * j + e, kx[it][e] * dn);
+        xq[e] = qx[it][e] * up;
+        xl[e] = kx[it][e] * up;
+        xr[e] = kx[it][e] * dn;
+        G[it][e] = xl[e] * pm[e];    // kn 2^G (G is dead from here)
+        xg[e] = xq[e] * pm[e];       // qn 2^G
+        kx[it][e] = xr[e] * pl[e];   // kn 2^(G_last - G)
+      }
+      store8(QL + t * ST + 8 * j, xq);
+      store8(KL + t * ST + 8 * j, xl);
+      store8(KR + t * ST + 8 * j, xr);
+      if (PREP && t < L) {
+        // qg in fragment order: channels 8 j .. 8 j + 3 and 8 j + 4 .. 8 j + 7
+        // are two runs of 4 consecutive packed positions
+        E* dst = qg + ((size_t)(p.t0 + t) * hv + h) * D + 32 * (j >> 2);
+        store4(dst + pack32(8 * (j & 3)), xg[0], xg[1], xg[2], xg[3]);
+        store4(dst + pack32(8 * (j & 3) + 4), xg[4], xg[5], xg[6], xg[7]);
       }
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) col4(kgp[e], G[0][e], G[1][e], G[2][e], G[3][e]);
     if (PREP) {
-      // qg = qn 2^G (token-major, channel packed)
-      const int cb = 32 * (j >> 2);
-      const int run0 = cb + pack32(8 * (j & 3)), run1 = cb + pack32(8 * (j & 3) + 4);
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int t = 4 * rg + it;
-        float xq[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xq[e] = qx[it][e] * exp2_fast(G[it][e]);
-        if (t < L) {
-          E* dst = qg + ((size_t)(p.t0 + t) * hv + h) * D;
-          store4(dst + run0, xq[0], xq[1], xq[2], xq[3]);
-          store4(dst + run1, xq[4], xq[5], xq[6], xq[7]);
-        }
-      }
-      // kg_t[c][h][kk][packed t] = kn 2^(G_last - G): this thread's 4
-      // consecutive tokens are 4 consecutive packed positions (zero past L)
+      // kg_t[c][h][key channel][packed t]: this thread's 4 consecutive tokens
+      // are 4 consecutive packed positions (zero past L)
       E* kdst = kg_t + ((size_t)c * hv + h) * D * C + packed_index(4 * rg);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float xk[4];
-#pragma unroll
-        for (int it = 0; it < 4; ++it) xk[it] = kx[it][e] * exp2_fast(Gl[e] - G[it][e]);
-        store4(kdst + (size_t)(8 * j + e) * C, xk[0], xk[1], xk[2], xk[3]);
-      }
+      for (int e = 0; e < 8; ++e)
+        store4(kdst + (size_t)(8 * j + e) * C, kx[0][e], kx[1][e], kx[2][e], kx[3][e]);
       if (tid < 16) {
+        float dv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) decay[((size_t)c * hv + h) * D + 8 * j + e] = exp2_fast(Gl[e]);
+        for (int e = 0; e < 8; ++e) dv[e] = exp2_fast(Gl[e]);
+        store8(decay + ((size_t)c * hv + h) * D + 8 * j, dv);
       }
     }
   }
+  if (tid == 0) s_next = claim + (int)gridDim.x;
   lds_barrier();
+  const int nitem = s_next;
+  ChunkPos np;
+  const bool nok = nitem < items && locate_chunk(nitem / hv, table, np);
 
   // ---- phase 1: couplings, transposed tiles (rows i from KR, columns t from L).
   //      Each wave takes a fixed set of (row block a, column block b) pairs
@@ -511,6 +680,7 @@ __global__ __launch_bounds__(256) void wy_kernel(
     auto pair = [&](const int a, const int b) {
       const int t = 16 * a + l16;
       const int i = 16 * b + l16;
+      const float* eab = sE + (a * (a - 1) / 2 + b) * D;
       f32x4_t acck = {0.f, 0.f, 0.f, 0.f}, accq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -521,10 +691,11 @@ __global__ __launch_bounds__(256) void wy_kernel(
         if (a == b) {
           R = frag_row(KR + i * ST + c0);
         } else {
-          float x[8];
+          float x[8], ef[8];
           row8(KR + i * ST + c0, x);
+          row8(eab + c0, ef);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] *= exp2_fast(GM[a * D + c0 + e] - GM[b * D + c0 + e]);
+          for (int e = 0; e < 8; ++e) x[e] *= ef[e];
           R = make_frag<SPLIT>(x);
         }
         mma(acck, R, Lk);
@@ -548,21 +719,37 @@ __global__ __launch_bounds__(256) void wy_kernel(
         store4(aqk + ((size_t)(p.t0 + t) * hv + h) * C + packed_index(16 * b + 4 * gq), 0.f,
                0.f, 0.f, 0.f);
     };
-    const int wu = __builtin_amdgcn_readfirstlane(wave);
-    if (wu == 0) {
+    if (wv == 0) {
       pair(3, 3); pair(3, 2); pair(3, 1);
-    } else if (wu == 1) {
+    } else if (wv == 1) {
       pair(3, 0); pair(2, 2); pair(2, 1);
-    } else if (wu == 2) {
+    } else if (wv == 2) {
       pair(2, 0); pair(1, 1); zero(0, 1); zero(0, 2); zero(0, 3);
     } else {
       pair(1, 0); pair(0, 0); zero(1, 2); zero(1, 3); zero(2, 3);
     }
   }
-  // v rows are fetched now; they land during the inversion
-  float vx[4][8];
-  load_rows4(v + ((size_t)p.t0 * hv + h) * D, hv * D, L, vx);
+  // v rows (fragment-order channels) are fetched now; they land during the
+  // products above
+  // (rows past L are not zeroed: they meet b = 0 columns of T')
+  RawRows<E> rv;
+  raw_load(v + ((size_t)p.t0 * hv + h) * D, hv * D, L, rv, tid);
+  if (nok) prefetch(nitem, np, tid);  // after v, so waiting for v leaves these in flight
   lds_barrier();
+  // (kn 2^G)^T into R0 and v^T into R1 (rows: channels 8 j + e), each
+  // thread's 4 consecutive tokens as one run
+  {
+    constexpr int EPP = 16 / (int)sizeof(TE);
+    const int piece = (4 * rg) / EPP, sub = (4 * rg) % EPP;
+    using C4 = typename Col4<E>::T;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = 8 * j + e;
+      *reinterpret_cast<C4*>(reinterpret_cast<TE*>(KGt + tslot<TE>(r, piece)) + sub) = kgp[e];
+      *reinterpret_cast<C4*>(reinterpret_cast<TE*>(Vt + tslot<TE>(r, piece)) + sub) =
+          raw_column(rv, e);
+    }
+  }
 
   // ---- phase 2: T = (I + A_kk)^-1 (KR is dead: T takes its place)
   if (lane < 16) {
@@ -599,54 +786,46 @@ __global__ __launch_bounds__(256) void wy_kernel(
     if ((i >> 4) > (t >> 4)) sTt[t * SA + i] = 0.f;
   }
   lds_barrier();
-  {
-    // levels a - b = 1, 2, 3 of the off-diagonal blocks, one block per wave
-    const int wu = __builtin_amdgcn_readfirstlane(wave);
-    if (wu < 3) wy_offdiag<SA>(wu + 1, wu, sA, sTt, lane);
-    lds_barrier();
-    if (wu < 2) wy_offdiag<SA>(wu + 2, wu, sA, sTt, lane);
-    lds_barrier();
-    if (wu == 0) wy_offdiag<SA>(3, 0, sA, sTt, lane);
-    lds_barrier();
-  }
-  // v tile into R0
-#pragma unroll
-  for (int it = 0; it < 4; ++it)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st_elem(sV + (rg + 16 * it) * ST + 8 * j + e, vx[it][e]);
+  // levels a - b = 1, 2, 3 of the off-diagonal blocks, one block per wave
+  if (wv < 3) wy_offdiag<SA>(wv + 1, wv, sA, sTt, lane);
+  lds_barrier();
+  if (wv < 2) wy_offdiag<SA>(wv + 2, wv, sA, sTt, lane);
+  lds_barrier();
+  if (wv == 0) wy_offdiag<SA>(3, 0, sA, sTt, lane);
   lds_barrier();
 
-  // ---- phase 3
-  Frag<SPLIT> Tf[4][2];  // T rows t = 16 ta + l16, K = i = 32 s + 8 gq + jj
+  // ---- phase 3: T' = T diag(b); w^T = (kn 2^G)^T T'^T and u = T' v
+  Frag<SPLIT> Tf[4][2];  // T' rows t = 16 ta + l16, K = i = 32 s + 8 gq + jj
 #pragma unroll
   for (int ta = 0; ta < 4; ++ta)
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      if (s == 1 && ta < 2) continue;
-      float x[8];
+      if (s == 1 && ta < 2) continue;  // T' is lower triangular
+      const int i0 = 32 * s + 8 * gq;
+      float x[8], bb[8];
+      row8(sTt + (16 * ta + l16) * SA + i0, x);
+      row8(sB + i0, bb);
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) x[jj] = sTt[(16 * ta + l16) * SA + 32 * s + 8 * gq + jj];
+      for (int jj = 0; jj < 8; ++jj) x[jj] *= bb[jj];
       Tf[ta][s] = make_frag<SPLIT>(x);
     }
 #pragma unroll
   for (int cbi = 0; cbi < 2; ++cbi) {
-    const int cb = 2 * wave + cbi;
-    const int cc = 16 * cb + l16;  // key channel (w) / value channel (u) of this lane
+    const int cb = 2 * wv + cbi;
+    const int row = 16 * cb + l16;  // key channel (w) / value channel (u) of this lane
     Frag<SPLIT> Yk[2], Yv[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      float yk[8], yv[8];
-      const int blk = 2 * s + (gq >> 1);  // 16-token block of i = 32 s + 8 gq + jj
-      const float gm = exp2_fast(GM[blk * D + cc]);
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int i = 32 * s + 8 * gq + jj;
-        const float bi = sB[i];
-        yk[jj] = bi * ld_elem(KL + i * ST + cc) * gm;
-        yv[jj] = bi * ld_elem(sV + i * ST + cc);
+      if constexpr (SPLIT) {
+        float xk[8], xv[8];
+        unit_vals_t(KGt, row, 8 * s + 2 * gq, xk);
+        unit_vals_t(Vt, row, 8 * s + 2 * gq, xv);
+        Yk[s] = make_frag<true>(xk);
+        Yv[s] = make_frag<true>(xv);
+      } else {
+        Yk[s] = FragB{__builtin_bit_cast(bf16x8_t, KGt[tslot<TE>(row, 4 * s + gq)])};
+        Yv[s] = FragB{__builtin_bit_cast(bf16x8_t, Vt[tslot<TE>(row, 4 * s + gq)])};
       }
-      Yk[s] = make_frag<SPLIT>(yk);
-      Yv[s] = make_frag<SPLIT>(yv);
     }
 #pragma unroll
     for (int ta = 0; ta < 4; ++ta) {
@@ -658,14 +837,18 @@ __global__ __launch_bounds__(256) void wy_kernel(
         mma(au, Tf[ta][1], Yv[1]);
       }
       const int t = 16 * ta + l16;
-      if (t < L) {
-        E* dst = w_out + ((size_t)(p.t0 + t) * hv + h) * D + packed_index(16 * cb + 4 * gq);
-        store4(dst, aw[0], aw[1], aw[2], aw[3]);
-      }
-      // u_t[c][h][v][packed t]: rows t = 16 ta + 4 gq + r of column cc (zero past L)
-      E* du = u_t + (((size_t)c * hv + h) * D + cc) * C + packed_index(16 * ta + 4 * gq);
+      if (t < L)
+        store4(w_out + ((size_t)(p.t0 + t) * hv + h) * D + packed_index(16 * cb + 4 * gq), aw[0],
+               aw[1], aw[2], aw[3]);
+      // u_t[c][h][v][packed t]: rows t = 16 ta + 4 gq + r of column `row` (zero past L)
+      E* du = u_t + (((size_t)c * hv + h) * D + row) * C + packed_index(16 * ta + 4 * gq);
       store4(du, au[0], au[1], au[2], au[3]);
     }
+  }
+  lds_barrier();  // the next item rewrites every region
+  item = nitem;
+  p = np;
+  ok = nok;
   }
 }
 
@@ -1112,6 +1295,19 @@ __global__ __launch_bounds__(64) void compose_kernel(const WalkArgs<E> a) {
 
 // --------------------------------------------------------------------- launch
 
+// Compute units of the current device (cached per device).
+static int cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
+
 static void mark(const ChunkLaunch& L, int i) {
   if (i < L.num_events && L.events[i]) (void)hipEventRecord((hipEvent_t)L.events[i], (hipStream_t)L.stream);
 }
@@ -1155,17 +1351,23 @@ static hipError_t launch_staged_t(const ChunkLaunch& L) {
                          (const E*)L.q, (const E*)L.k, (const E*)L.g, (const int4*)L.table,
                          L.hqk, L.hv, L.use_l2, (E*)L.qg, (E*)L.kg_t, L.decay);
     mark(L, 2);
-    const dim3 grid((unsigned)L.max_chunks, L.hv);
+    // persistent WY grid: the resident workgroups (LDS allows two per CU for
+    // bf16 tiles, one for fp32)
+    const int items = (int)L.max_chunks * L.hv;
+    const int resident = cu_count() * (std::is_same<E, float>::value ? 1 : 2);
+    const dim3 grid((unsigned)std::max(1, std::min(items, resident)));
+    int* wy_counter = reinterpret_cast<int*>((char*)L.zero + 1024);
     if (L.fuse_prep)
       hipLaunchKernelGGL((wy_kernel<E, true>), grid, dim3(256), 0, st, (const E*)L.q,
                          (const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta,
                          (const int4*)L.table, L.hqk, L.hv, L.use_l2, (E*)L.w, (E*)L.u,
-                         (E*)L.aqk, (E*)L.qg, (E*)L.kg_t, L.decay);
+                         (E*)L.aqk, (E*)L.qg, (E*)L.kg_t, L.decay, items, wy_counter);
     else
       hipLaunchKernelGGL((wy_kernel<E, false>), grid, dim3(256), 0, st, (const E*)L.q,
                          (const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta,
                          (const int4*)L.table, L.hqk, L.hv, L.use_l2, (E*)L.w, (E*)L.u,
-                         (E*)L.aqk, (E*)nullptr, (E*)nullptr, (float*)nullptr);
+                         (E*)L.aqk, (E*)nullptr, (E*)nullptr, (float*)nullptr, items,
+                         wy_counter);
   } else {
     mark(L, 2);
   }

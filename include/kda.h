@@ -171,7 +171,8 @@ kda_status kda_chunk_fwd(const kda_chunk_args *a);
  * bound n_chunks_max = total_tokens / 64 + num_seqs used for sizing.  G is the
  * inclusive in-chunk cumulative log-decay, b = sigmoid(beta).
  *   chunk_offsets  int32 [N + 1]: first chunk index of each sequence
- *   zero           1 KiB of zeros (source of the rows past a short chunk)
+ *   zero           1 KiB of zeros (source of the rows past a short chunk),
+ *                  then a work counter of the WY kernel (int32)
  *   table          int32x4 [chunks]: (sequence, first token, length, 0) per
  *                  chunk, length 0 past the last chunk
  *   qg             [T_tot, Hv, 128]  qn * exp(G)                        (P)
