@@ -5,15 +5,19 @@ One step = one chunked forward over the dense-prefill workload (B=4, T=4096,
 Hqk=Hv=16, D=128, bf16, fp32 initial and final state) followed by one paged
 decode over the decode workload (256 requests x 32 heads, fp32 cache
 [1024, 32, 128, 128]), inputs resident in HBM.  W untimed warm-up steps, then K
-timed steps bracketed by device synchronisation.  Per-kernel times come from
-HIP events recorded by the library at its stage boundaries on the launch
-stream; the decode is bracketed by events on the same stream.
+timed steps bracketed by device synchronisation, with two HIP events per step
+on the library's stream (chunk start, decode start) for the launch durations
+of the two calls.  The per-kernel breakdown of the chunk forward comes from a
+separate pass with the library's stage events.
 
-Printed: one JSON line.  ``value`` is chunk-forward tokens/s (tokens of the
-prefill batch / mean chunk-forward time); ``ms_per_step`` is the wall time of a
-whole step (chunk forward + decode).  ``roofline`` describes the kernel that
-takes the most time in a step; ``kernels`` lists all of them.
-``cpu_baseline`` times the fp64 CPU oracle on the host (rank 0, N=1 only).
+Printed: one JSON line.  ``value`` is whole-step throughput: the tokens of a
+step (16384 prefill + 256 decode) over the mean wall time of a timed step.
+``chunk_tokens_per_s`` is the chunk forward alone.  ``roofline`` describes the
+kernel that takes the most time in a step (HBM traffic from rocprofv3 byte
+counters scaled by a plain copy kernel, when recorded for the current kernel
+sources); ``kernels`` lists all of them.  ``cpu_baseline`` times the fp64 CPU
+oracle on the host.  ``--copy-calibration`` adds the reference copy kernel
+after the timed region.
 """
 from __future__ import annotations
 
@@ -70,7 +74,7 @@ def chunk_work(lengths, hqk, hv, es, state_in, state_out):
               + T * hv * 128 * es + (state_in + state_out) * N * hv * 128 * 128 * 4)
     # prep folded into WY: the inputs once, all six intermediates out
     intra_b = ((2 * T * hqk + 2 * T * hv) * 128 * es + T * hv * es
-               + T * hv * (3 * 128 + 64) * es + nch * hv * 128 * (2 * 64 * es + 4))
+               + T * hv * (2 * 128 + 64) * es + nch * hv * 128 * (2 * 64 * es + 4))
     return dict(
         tokens=T,
         prep=dict(bytes=prep_b, flops=0.0),
@@ -175,6 +179,22 @@ def cpu_baseline(batch_cpu, lengths, dec_cpu):
 
 # ---------------------------------------------------------------------- main
 
+CAL_BYTES = 256 << 20  # bytes read (and written) by one calibration copy
+
+
+def copy_calibration(dev):
+    """A plain copy kernel of known size (fp32 x * 1.0 into another buffer),
+    launched three times, for scaling FETCH_SIZE / WRITE_SIZE readings."""
+    import torch
+    src = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    return dict(kernel="elementwise mul (copy)", bytes_read=CAL_BYTES, bytes_written=CAL_BYTES,
+                launches=3)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,6 +207,12 @@ def main():
                     help="chunk path: prep as its own kernel (staged) or folded into WY")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-back-to-back", action="store_true",
+                    help="also time decode launched back to back (after the timed region)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, run a plain elementwise copy of "
+                         f"{CAL_BYTES >> 20} MiB (reads and writes that many bytes) three "
+                         "times: the reference kernel for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -232,7 +258,6 @@ def main():
 
     nev = B.NUM_STAGE_EVENTS
     ev_sets = [[ev.create() for _ in range(nev)] for _ in range(args.steps)]
-    dec_ev = [(ev.create(), ev.create()) for _ in range(args.steps)]
 
     path = {"auto": B.PATH_AUTO, "staged": B.PATH_STAGED, "fused": B.PATH_FUSED}[args.path]
 
@@ -254,51 +279,55 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # the timed region: exactly `steps` whole steps, nothing else on the stream
+    # The timed region: exactly `steps` whole steps.  Two events per step on
+    # the library's stream (chunk start, decode start; the next step's chunk
+    # start closes the decode) give the launch durations of the two calls.
+    tev = [ev.create() for _ in range(2 * args.steps + 1)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step()
+        ev.record(tev[2 * i], stream)
+        chunk()
+        if not args.no_decode:
+            ev.record(tev[2 * i + 1], stream)
+            decode()
+    ev.record(tev[2 * args.steps], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if args.no_decode:
+        chunk_ms = [ev.ms(tev[2 * i], tev[2 * i + 2]) for i in range(args.steps)]
+        dec_ms = []
+    else:
+        chunk_ms = [ev.ms(tev[2 * i], tev[2 * i + 1]) for i in range(args.steps)]
+        dec_ms = [ev.ms(tev[2 * i + 1], tev[2 * i + 2]) for i in range(args.steps)]
+    for e in tev:
+        ev.destroy(e)
 
-    # Breakdowns, after the timed region.  An event record between kernels
-    # costs a few microseconds, so the chunk and decode times come from runs
-    # bracketed by one event pair each, and the per-kernel times from a run
-    # with the library's stage events.
-    def bracketed(fn):
+    # After the timed region: the per-kernel breakdown from the library's
+    # stage events, and decode launched back to back (each launch then also
+    # waits out the write-back of the previous one's state rows).
+    for i in range(args.steps):
+        chunk(ev_sets[i])
+    torch.cuda.synchronize()
+    dec_b2b_ms = None
+    if args.decode_back_to_back and not args.no_decode:
         a_, b_ = ev.create(), ev.create()
         ev.record(a_, stream)
         for _ in range(args.steps):
-            fn()
+            decode()
         ev.record(b_, stream)
         torch.cuda.synchronize()
-        ms = ev.ms(a_, b_) / args.steps
+        dec_b2b_ms = ev.ms(a_, b_) / args.steps
         ev.destroy(a_)
         ev.destroy(b_)
-        return ms
-
-    chunk_only_ms = bracketed(chunk)
-    dec_only_ms = None if args.no_decode else bracketed(decode)
-    for i in range(args.steps):
-        chunk(ev_sets[i])
-        if not args.no_decode:
-            ev.record(dec_ev[i][0], stream)
-            decode()
-            ev.record(dec_ev[i][1], stream)
-    torch.cuda.synchronize()
 
     names = ["table", "prep", "wy", "walk", "compose", "pass2"]
     per = {n: [] for n in names}
-    chunk_ms, dec_ms = [], []
     for i in range(args.steps):
         e = ev_sets[i]
         for j, n in enumerate(names):
             per[n].append(ev.ms(e[j], e[j + 1]))
-        chunk_ms.append(ev.ms(e[0], e[nev - 1]))
-        if not args.no_decode:
-            dec_ms.append(ev.ms(*dec_ev[i]))
     mean = lambda xs: sum(xs) / max(len(xs), 1)
-    t_chunk = chunk_only_ms / 1e3
+    t_chunk = mean(chunk_ms) / 1e3
     work = chunk_work(lengths, hqk, hv, 2, True, True)
     flops = work["wy"]["flops"] + work["walk"]["flops"]
 
@@ -327,12 +356,15 @@ def main():
     dec = None
     if not args.no_decode:
         dw = decode_work(dwl["N"], dwl["hqk"], dwl["hv"], 2)
-        s = dec_only_ms / 1e3
+        s = mean(dec_ms) / 1e3
         gbs = dw["bytes"] / s / 1e9
         kernels["decode"] = dict(ms=round(s * 1e3, 4), bound="hbm", gb_s=round(gbs, 1),
                                  frac=round(gbs / PEAK_HBM_GBS, 4))
         dec = dict(ms=round(s * 1e3, 4), gb_s=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4),
                    state_gb_s=round(dw["state_bytes"] / s / 1e9, 1),
+                   back_to_back_ms=None if dec_b2b_ms is None else round(dec_b2b_ms, 4),
+                   back_to_back_gb_s=None if dec_b2b_ms is None else
+                   round(dw["bytes"] / (dec_b2b_ms / 1e3) / 1e9, 1),
                    workload=f"{dwl['N']} requests x {dwl['hv']} heads, cache "
                             f"[{dwl['slots']}, {dwl['hv']}, 128, 128] fp32")
 
@@ -372,6 +404,8 @@ def main():
         mfma_frac=round(flops / t_chunk / 1e12 / PEAK_BF16_TFLOPS, 4),
         decode=dec, kernels=kernels, roofline=roof,
     )
+    if args.copy_calibration:
+        res["copy_calibration"] = copy_calibration(dev)
     if not args.no_cpu_baseline:
         cpu = inputs.Batch(cb.q.cpu(), cb.k.cpu(), cb.v.cpu(), cb.g.cpu(), cb.beta.cpu(),
                            cb.cu_seqlens.cpu(), cb.scale, initial_state=cb.initial_state.cpu())
@@ -381,9 +415,6 @@ def main():
     for es in ev_sets:
         for e in es:
             ev.destroy(e)
-    for a_, b_ in dec_ev:
-        ev.destroy(a_)
-        ev.destroy(b_)
     print(json.dumps(res))
 
 
