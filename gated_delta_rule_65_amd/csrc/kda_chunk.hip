@@ -1032,7 +1032,6 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(const WalkArgs<E> a) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA of chunk jc has landed
     lds_barrier();                  // ... and every other wave's
     const bool more = STAGES == 2 && jc + 1 < jc1;
-    if (SPLIT && more) issue_wq(jc + 1, nxt);
     const uint4* tW = cur + OFF_W;
     const uint4* tQ = cur + OFF_Q;
     const uint4* tA = cur + OFF_A;
@@ -1137,8 +1136,12 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(const WalkArgs<E> a) {
       Uf[s2] = make_frag<SPLIT>(x);
     }
     if constexpr (!SPLIT) {
-      // A_qk fragments (A_qk lower: t < 32 needs i < 32 only), kg^T fragments
+      // Every A_qk and kg^T fragment and the decay of this lane's state rows
+      // are read up front (A_qk is lower: t < 32 needs i < 32 only); the
+      // schedule is pinned so the reads go out together and the products
+      // follow as they land, instead of each product waiting on its own read.
       FragB fa[4][2], fk[8][2];
+      float4 dk[8];
       if (OUT) {
 #pragma unroll
         for (int ta = 0; ta < 4; ++ta)
@@ -1147,9 +1150,11 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(const WalkArgs<E> a) {
             if (!(s2 == 1 && ta < 2)) fa[ta][s2] = frag_bf16<P64>(tA, 16 * ta + l16, 4 * s2 + gq);
       }
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 8; ++kb) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) fk[kb][s2] = frag_bf16<P64>(tK, 16 * kb + l16, 4 * s2 + gq);
+        dk[kb] = *reinterpret_cast<const float4*>(sD + 16 * kb + 4 * gq);
+      }
       // O^T += U^T A_qk^T
       if (OUT) {
 #pragma unroll
@@ -1158,20 +1163,23 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(const WalkArgs<E> a) {
           if (ta >= 2) mma(O[ta], Uf[1], fa[ta][1]);
         }
       }
-#pragma unroll
-      for (int kb = 4; kb < 8; ++kb)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) fk[kb][s2] = frag_bf16<P64>(tK, 16 * kb + l16, 4 * s2 + gq);
       // S <- diag(d) S + kg^T U   (rows k, cols v, K = t)
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
-        const float4 d4 = *reinterpret_cast<const float4*>(sD + 16 * kb + 4 * gq);
-        S[kb][0] *= d4.x;
-        S[kb][1] *= d4.y;
-        S[kb][2] *= d4.z;
-        S[kb][3] *= d4.w;
+        S[kb][0] *= dk[kb].x;
+        S[kb][1] *= dk[kb].y;
+        S[kb][2] *= dk[kb].z;
+        S[kb][3] *= dk[kb].w;
         mma(S[kb], fk[kb][0], Uf[0]);
         mma(S[kb], fk[kb][1], Uf[1]);
+      }
+      constexpr int NFA = OUT ? 6 : 0;
+      __builtin_amdgcn_sched_group_barrier(0x100, NFA + 24, 0);  // DS reads
+      if (OUT) __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);  // A_qk U
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // decay
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // kg^T U
       }
     } else {
       if (OUT) {
@@ -1193,14 +1201,20 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(const WalkArgs<E> a) {
       }
     }
     if (OUT) {
+      // rows t = 16 ta + l16 of this lane's 4 output columns
+      E* op = a.out + ((size_t)(t0 + l16) * hv + h) * D + v0 + 16 * wave + 4 * gq;
+      const size_t tstep = (size_t)16 * hv * D;
+      if (L == C) {
 #pragma unroll
-      for (int ta = 0; ta < 4; ++ta) {
-        const int t = 16 * ta + l16;
-        if (t < L) {
-          E* op = a.out + ((size_t)(t0 + t) * hv + h) * D + v0 + 16 * wave + 4 * gq;
-          store4(op, a.scale * O[ta][0], a.scale * O[ta][1], a.scale * O[ta][2],
+        for (int ta = 0; ta < 4; ++ta)
+          store4(op + ta * tstep, a.scale * O[ta][0], a.scale * O[ta][1], a.scale * O[ta][2],
                  a.scale * O[ta][3]);
-        }
+      } else {
+#pragma unroll
+        for (int ta = 0; ta < 4; ++ta)
+          if (16 * ta + l16 < L)
+            store4(op + ta * tstep, a.scale * O[ta][0], a.scale * O[ta][1], a.scale * O[ta][2],
+                   a.scale * O[ta][3]);
       }
     }
     if (STAGES == 1 && jc + 1 < jc1) {
