@@ -58,6 +58,13 @@ def _load():
                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                 ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                 ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+            f = lib.oracle_kda_recurrence_gated
+            f.restype = ctypes.c_int
+            f.argtypes = [ctypes.c_int] + [ctypes.c_void_p] * 6 + [
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double,
+                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
             _lib = lib
     return _lib
 
@@ -77,8 +84,13 @@ def _cpu_contig(x: torch.Tensor, name: str) -> torch.Tensor:
 
 
 def recurrence(q, k, v, g, beta, cu_seqlens=None, scale=None, use_qk_l2norm=True,
-               initial_state=None, heads=None, threads=None, want_state=True):
+               initial_state=None, heads=None, threads=None, want_state=True,
+               A_log=None, dt_bias=None, lower_bound=-5.0):
     """Token-by-token fp64 KDA recurrence.
+
+    With A_log [Hv] and dt_bias [Hv, 128] (both or neither, any float dtype,
+    widened exactly) g is a raw gate and the step log-decay is
+    lower_bound * sigmoid(exp(A_log[h]) * (g + dt_bias[h, c])).
 
     q, k: [T, Hqk, 128]; v, g: [T, Hv, 128]; beta: [T, Hv] (logits), all one of
     fp32/bf16/fp16 (read at their stored precision).  Dense [B, T, H, 128]
@@ -137,11 +149,19 @@ def recurrence(q, k, v, g, beta, cu_seqlens=None, scale=None, use_qk_l2norm=True
             return ctypes.c_void_p(t.data_ptr())
         return t.ctypes.data_as(ctypes.c_void_p)
 
+    if (A_log is None) != (dt_bias is None):
+        raise ValueError("A_log and dt_bias must be given together")
+    al = db = None
+    if A_log is not None:
+        al = np.ascontiguousarray(torch.as_tensor(A_log).detach().cpu().double().numpy())
+        db = np.ascontiguousarray(torch.as_tensor(dt_bias).detach().cpu().double().numpy())
+        if al.shape != (hv,) or db.shape != (hv, 128):
+            raise ValueError("A_log must be [Hv] and dt_bias [Hv, 128]")
     lib = _load()
-    rc = lib.oracle_kda_recurrence(
+    rc = lib.oracle_kda_recurrence_gated(
         _DT[dt], ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(cu), N, hqk, hv,
-        float(scale), int(bool(use_qk_l2norm)), ptr(s0), ptr(out), ptr(sf),
-        ptr(hs), 0 if hs is None else len(hs),
+        float(scale), int(bool(use_qk_l2norm)), ptr(al), ptr(db), float(lower_bound),
+        ptr(s0), ptr(out), ptr(sf), ptr(hs), 0 if hs is None else len(hs),
         threads if threads else default_threads())
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
@@ -149,7 +169,7 @@ def recurrence(q, k, v, g, beta, cu_seqlens=None, scale=None, use_qk_l2norm=True
 
 
 def decode(q, k, v, g, beta, state_cache, state_indices, scale=None,
-           use_qk_l2norm=True, threads=None):
+           use_qk_l2norm=True, threads=None, A_log=None, dt_bias=None, lower_bound=-5.0):
     """One-token decode over a paged V-first state cache, as the recurrence.
 
     q, k: [N, Hqk, 128]; v, g: [N, Hv, 128]; beta: [N, Hv];
@@ -171,7 +191,8 @@ def decode(q, k, v, g, beta, state_cache, state_indices, scale=None,
     o, sf = recurrence(q[sel], k[sel], v[sel], g[sel], beta[sel],
                        cu_seqlens=np.arange(live.size + 1, dtype=np.int64),
                        scale=scale, use_qk_l2norm=use_qk_l2norm,
-                       initial_state=s0, threads=threads)
+                       initial_state=s0, threads=threads, A_log=A_log, dt_bias=dt_bias,
+                       lower_bound=lower_bound)
     out[live] = o
     new_cache[idx[live]] = sf
     return out, new_cache

@@ -32,6 +32,13 @@
  * The head map hq = h / (Hv / Hqk) (contiguous groups of value heads share a
  * query/key head) is a reading: the pages only require divisibility.
  *
+ * Gate parameters (optional): with a per-head A_log and a per-(head, channel)
+ * dt_bias, the g input is a raw gate and the log-decay of a step is
+ *   lower_bound * sigmoid(exp(A_log[h]) * (g + dt_bias[h][c]))
+ * (the activation of KdaTcVerify on page
+ * "vllm.models.kimi_k3.nvidia.recoverssm.cutedsl.verify"; chunk_kda of page
+ * "mate.kda" takes A_log, dt_bias and lower_bound = -5 by default).
+ *
  * Inputs are read at their stored precision (fp32, bf16 or fp16) and widened
  * to fp64 exactly; nothing is rounded before the outputs leave in fp64.
  * Work is spread over (sequence, value head) units with POSIX threads.
@@ -80,6 +87,8 @@ typedef struct {
   const int64_t *cu;
   int num_seqs, hqk, hv, use_l2norm;
   double scale;
+  const double *a_log, *dt_bias; /* gate parameters, or NULL */
+  double lower_bound;
   const double *s0;
   double *out, *s_final;
   const int *heads;
@@ -109,7 +118,11 @@ static void run_unit(job_t *J, int n, int h) {
     for (int c = 0; c < KD; ++c) {
       qn[c] = load_elem(J->q, J->dtype, qoff + c);
       kn[c] = load_elem(J->k, J->dtype, qoff + c);
-      alpha[c] = exp(load_elem(J->g, J->dtype, voff + c));
+      double gl = load_elem(J->g, J->dtype, voff + c);
+      if (J->a_log)
+        gl = J->lower_bound /
+             (1.0 + exp(-exp(J->a_log[h]) * (gl + J->dt_bias[(int64_t)h * KD + c])));
+      alpha[c] = exp(gl);
       sq += qn[c] * qn[c];
       sk += kn[c] * kn[c];
     }
@@ -176,12 +189,14 @@ static void *worker(void *arg) {
  * are.  s0 may be NULL (zero start); s_final may be NULL.
  * Returns 0 on success, -1 on a bad argument.
  */
-int oracle_kda_recurrence(int dtype, const void *q, const void *k, const void *v,
-                          const void *g, const void *beta, const int64_t *cu,
-                          int num_seqs, int hqk, int hv, double scale,
-                          int use_l2norm, const double *s0, double *out,
-                          double *s_final, const int *heads, int n_heads,
-                          int n_threads) {
+int oracle_kda_recurrence_gated(int dtype, const void *q, const void *k, const void *v,
+                                const void *g, const void *beta, const int64_t *cu,
+                                int num_seqs, int hqk, int hv, double scale,
+                                int use_l2norm, const double *a_log,
+                                const double *dt_bias, double lower_bound,
+                                const double *s0, double *out, double *s_final,
+                                const int *heads, int n_heads, int n_threads) {
+  if ((a_log == NULL) != (dt_bias == NULL)) return -1;
   if (hqk <= 0 || hv <= 0 || hv % hqk != 0 || num_seqs < 0 || dtype < 0 || dtype > 2)
     return -1;
   if (heads) {
@@ -192,6 +207,7 @@ int oracle_kda_recurrence(int dtype, const void *q, const void *k, const void *v
   J.dtype = dtype; J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta;
   J.cu = cu; J.num_seqs = num_seqs; J.hqk = hqk; J.hv = hv;
   J.use_l2norm = use_l2norm; J.scale = scale; J.s0 = s0; J.out = out;
+  J.a_log = a_log; J.dt_bias = dt_bias; J.lower_bound = lower_bound;
   J.s_final = s_final; J.heads = heads; J.n_heads = n_heads; J.next_unit = 0;
   pthread_mutex_init(&J.lock, NULL);
   if (n_threads < 1) n_threads = 1;
@@ -201,4 +217,16 @@ int oracle_kda_recurrence(int dtype, const void *q, const void *k, const void *v
   for (int i = 0; i < n_threads; ++i) pthread_join(th[i], NULL);
   pthread_mutex_destroy(&J.lock);
   return 0;
+}
+
+/* The recurrence with g taken as the log-decay itself. */
+int oracle_kda_recurrence(int dtype, const void *q, const void *k, const void *v,
+                          const void *g, const void *beta, const int64_t *cu,
+                          int num_seqs, int hqk, int hv, double scale,
+                          int use_l2norm, const double *s0, double *out,
+                          double *s_final, const int *heads, int n_heads,
+                          int n_threads) {
+  return oracle_kda_recurrence_gated(dtype, q, k, v, g, beta, cu, num_seqs, hqk, hv, scale,
+                                     use_l2norm, NULL, NULL, 0.0, s0, out, s_final, heads,
+                                     n_heads, n_threads);
 }

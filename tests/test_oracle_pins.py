@@ -246,3 +246,108 @@ def test_workload_recipes_are_seeded():
     gen = torch.Generator().manual_seed(1)
     L = inputs.varlen_lengths(gen, 32768, 24, 64, 8192)
     assert sum(L) == 32768 and min(L) >= 64 and max(L) <= 8192
+
+
+# --------------------------------------------------------- gate parameters
+#
+# With A_log [Hv] and dt_bias [Hv, 128] the g input is a raw gate and the step
+# log-decay is lower_bound * sigmoid(exp(A_log[h]) * (g + dt_bias[h, c]))
+# (KdaTcVerify page; chunk_kda of mate.kda takes the three parameters).  The
+# pins below fix that form through limits and invariances, each against a run
+# of the plain recurrence (g = the log-decay) on constant or shifted inputs.
+
+def gate_batch(seed, dtype=torch.float32, hv=2):
+    b = small_batch([40, 25], 1, hv, seed, dtype=dtype)
+    gen = torch.Generator().manual_seed(seed + 100)
+    b.g = torch.randn(b.g.shape, generator=gen).to(dtype)  # raw gate ~ N(0, 1)
+    a_log = torch.rand(hv, generator=gen, dtype=torch.float64) * 2 - 1
+    dt_bias = torch.randn(hv, 128, generator=gen, dtype=torch.float64)
+    return b, a_log, dt_bias
+
+
+def with_g(b, g):
+    c = inputs.Batch(b.q, b.k, b.v, g.to(b.q.dtype), b.beta, b.cu_seqlens, b.scale,
+                     initial_state=b.initial_state)
+    return c
+
+
+def test_gate_zero_lower_bound_means_no_decay():
+    b, al, db = gate_batch(1)
+    o, s = run_R(b, A_log=al, dt_bias=db, lower_bound=0.0)
+    o0, s0 = run_R(with_g(b, torch.zeros_like(b.g)))
+    assert rel(o, o0) < 1e-13 and rel(s, s0) < 1e-13
+
+
+def test_gate_saturates_to_lower_bound_and_zero_per_channel():
+    """dt_bias = +60 drives the sigmoid to 1 (g = lower_bound), -60 to 0 (g = 0);
+    alternating channels pin the channel index and the sign inside."""
+    b, al, _ = gate_batch(2)
+    db = torch.full((2, 128), 60.0, dtype=torch.float64)
+    db[:, 1::2] = -60.0
+    o, s = run_R(b, A_log=al, dt_bias=db, lower_bound=-5.0)
+    g = torch.zeros_like(b.g, dtype=torch.float32)
+    g[..., 0::2] = -5.0
+    o1, s1 = run_R(with_g(b, g))
+    assert rel(o, o1) < 1e-7 and rel(s, s1) < 1e-7
+
+
+def test_gate_vanishing_a_gives_half_lower_bound():
+    """A_log = -60: the raw gate is scaled by e^-60, the sigmoid sits at 1/2."""
+    b, _, db = gate_batch(3)
+    al = torch.full((2,), -60.0, dtype=torch.float64)
+    o, s = run_R(b, A_log=al, dt_bias=db, lower_bound=-3.0)
+    o1, s1 = run_R(with_g(b, torch.full_like(b.g, -1.5, dtype=torch.float32)))
+    assert rel(o, o1) < 1e-12 and rel(s, s1) < 1e-12
+
+
+def test_gate_per_head_parameters():
+    """Head 0 saturated (g = lower_bound), head 1 at a -> 0 (g = lower_bound / 2):
+    a swapped head index of A_log or dt_bias fails."""
+    b, _, _ = gate_batch(4)
+    al = torch.tensor([0.0, -60.0], dtype=torch.float64)
+    db = torch.zeros((2, 128), dtype=torch.float64)
+    db[0] = 60.0
+    o, s = run_R(b, A_log=al, dt_bias=db, lower_bound=-4.0)
+    g = torch.empty_like(b.g, dtype=torch.float32)
+    g[:, 0] = -4.0
+    g[:, 1] = -2.0
+    o1, s1 = run_R(with_g(b, g))
+    assert rel(o, o1) < 1e-7 and rel(s, s1) < 1e-7
+
+
+def test_gate_bias_shift_invariance():
+    """(g + d, dt_bias - d) gives the same decay: dt_bias adds to the raw gate
+    inside the scaled sigmoid.  d = 0.5 keeps the fp32 sums exact enough."""
+    b, al, db = gate_batch(5)
+    o, s = run_R(b, A_log=al, dt_bias=db, lower_bound=-5.0)
+    o1, s1 = run_R(with_g(b, b.g.double() + 0.5), A_log=al, dt_bias=db - 0.5,
+                   lower_bound=-5.0)
+    assert rel(o, o1) < 1e-6 and rel(s, s1) < 1e-6
+
+
+def test_gate_scale_invariance():
+    """(A_log + ln 2, g / 2, dt_bias / 2) gives the same decay: exp(A_log)
+    multiplies the biased gate.  Halving is exact in binary."""
+    b, al, db = gate_batch(6)
+    o, s = run_R(b, A_log=al, dt_bias=db, lower_bound=-5.0)
+    o1, s1 = run_R(with_g(b, b.g.double() / 2), A_log=al + np.log(2.0), dt_bias=db / 2,
+                   lower_bound=-5.0)
+    assert rel(o, o1) < 1e-12 and rel(s, s1) < 1e-12
+
+
+def test_gate_default_draw_special_case():
+    """A_log = 0, dt_bias = 0, lower_bound = -5 turns a raw N(0, 1) gate into
+    the workloads' g = -5 sigmoid(N(0, 1)): the oracle on the raw draw matches
+    the oracle on the workload recipe's g (both in fp32 storage)."""
+    b, _, _ = gate_batch(7)
+    o, s = run_R(b, A_log=torch.zeros(2, dtype=torch.float64),
+                 dt_bias=torch.zeros(2, 128, dtype=torch.float64), lower_bound=-5.0)
+    g = (torch.sigmoid(b.g.float()) * -5.0)  # the recipe's transform (inputs.py)
+    o1, s1 = run_R(with_g(b, g))
+    assert rel(o, o1) < 1e-6 and rel(s, s1) < 1e-6
+
+
+def test_gate_requires_both_parameters():
+    b, al, _ = gate_batch(8)
+    with pytest.raises(ValueError):
+        run_R(b, A_log=al)
