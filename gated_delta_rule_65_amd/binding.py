@@ -49,6 +49,8 @@ class ChunkArgs(ctypes.Structure):
         ("walk_waves", ctypes.c_int32),
         ("stage_events", ctypes.c_void_p), ("num_stage_events", ctypes.c_int32),
         ("stream", ctypes.c_void_p),
+        ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+        ("dt_bias_dtype", ctypes.c_int32), ("lower_bound", ctypes.c_float),
     ]
 
 
@@ -74,6 +76,8 @@ class DecodeArgs(ctypes.Structure):
         ("state_cache", ctypes.c_void_p), ("state_indices", ctypes.c_void_p),
         ("num_slots", ctypes.c_int32), ("out", ctypes.c_void_p),
         ("stream", ctypes.c_void_p),
+        ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+        ("dt_bias_dtype", ctypes.c_int32), ("lower_bound", ctypes.c_float),
     ]
 
 
@@ -137,6 +141,29 @@ def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
+def _gate(A_log, dt_bias, lower_bound, hv, dev):
+    """Checked gate parameters (chunk_kda's A_log / dt_bias / lower_bound):
+    (A_log, dt_bias, dt_bias dtype code, lower_bound), or Nones."""
+    if A_log is None and dt_bias is None:
+        return None, None, 0, float(lower_bound)
+    _need(A_log is not None and dt_bias is not None,
+          "A_log and dt_bias must be provided together.")
+    _need(A_log.dtype == torch.float32, "A_log must be float32", TypeError)
+    _need(dt_bias.dtype in (torch.float32, torch.bfloat16),
+          "dt_bias must be float32 or bfloat16", TypeError)
+    _need(tuple(A_log.shape) == (hv,), f"A_log must have shape [{hv}]")
+    _need(tuple(dt_bias.shape) == (hv, D), f"dt_bias must have shape [{hv}, {D}]")
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
+        _contig(name, t)
+        _need(t.device == dev, f"{name} must be on {dev}")
+    return A_log, dt_bias, _DTYPES[dt_bias.dtype], float(lower_bound)
+
+
+def _set_gate(a, gate):
+    al, db, code, lb = gate
+    a.A_log, a.dt_bias, a.dt_bias_dtype, a.lower_bound = _ptr(al), _ptr(db), code, lb
+
+
 def _need(cond, msg, exc=ValueError):
     if not cond:
         raise exc(msg)
@@ -160,7 +187,7 @@ def _as_varlen(x, name, cu_seqlens):
 
 
 def _chunk_struct(q, k, v, g, beta, out, cu, N, T, hqk, hv, scale, l2, init, fin, cache,
-                  idx, has_init, path, groups, stream, walk_waves=0):
+                  idx, has_init, path, groups, stream, walk_waves=0, gate=None):
     a = ChunkArgs()
     a.struct_size = ctypes.sizeof(ChunkArgs)
     a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
@@ -176,6 +203,7 @@ def _chunk_struct(q, k, v, g, beta, out, cu, N, T, hqk, hv, scale, l2, init, fin
     a.out = _ptr(out)
     a.path, a.groups, a.walk_waves = path, groups, walk_waves
     a.stream = stream
+    _set_gate(a, gate if gate is not None else (None, None, 0, -5.0))
     return a
 
 
@@ -261,13 +289,13 @@ def _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state, c
 
 
 def _run_chunk(p, path=PATH_AUTO, groups=0, workspace=None, keep=None, events=None,
-               walk_waves=0):
+               walk_waves=0, gate=None):
     lib = load_library()
     dev = p["q"].device
     a = _chunk_struct(p["q"], p["k"], p["v"], p["g"], p["beta"], p["out"], p["cu"], p["N"],
                       p["T"], p["hqk"], p["hv"], p["scale"], p["l2"], p["init"], p["fin"],
                       p["cache"], p["idx"], p["has_init"], path, groups, _stream(dev),
-                      walk_waves)
+                      walk_waves, gate)
     nbytes = ctypes.c_size_t(0)
     st = lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(nbytes))
     if st != KDA_OK:
@@ -292,7 +320,8 @@ def _run_chunk(p, path=PATH_AUTO, groups=0, workspace=None, keep=None, events=No
 def chunk_kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False,
               cu_seqlens=None, use_qk_l2norm_in_kernel=True, output=None, final_state=None,
               state_cache=None, state_indices=None, has_initial_state=None, groups=0,
-              workspace=None, stage_events=None, walk_waves=0, path=PATH_AUTO):
+              workspace=None, stage_events=None, walk_waves=0, path=PATH_AUTO,
+              A_log=None, dt_bias=None, lower_bound=-5.0):
     """Chunked KDA forward (chunk_kda's argument set, plus the paged state of
     fused_kda_chunk).  Returns out, or (out, final_state) when
     output_final_state; in paged mode the final states land in state_cache.
@@ -300,12 +329,15 @@ def chunk_kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_sta
     at the stage boundaries (profiling).  groups / walk_waves: 0 lets the
     planner choose; otherwise they fix the walk's launch shape (tuning only,
     the result is the same up to rounding order).  path: PATH_AUTO,
-    PATH_STAGED (prep as its own kernel) or PATH_FUSED."""
+    PATH_STAGED (prep as its own kernel) or PATH_FUSED.  A_log [Hv] fp32 and
+    dt_bias [Hv, 128] fp32/bf16 (both or neither) make g a raw gate with
+    log-decay lower_bound * sigmoid(exp(A_log) * (g + dt_bias))."""
     p = _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state,
                        cu_seqlens, use_qk_l2norm_in_kernel, output, final_state,
                        state_cache, state_indices, has_initial_state)
+    gate = _gate(A_log, dt_bias, lower_bound, p["hv"], p["q"].device)
     _run_chunk(p, path=path, groups=groups, workspace=workspace, events=stage_events,
-               walk_waves=walk_waves)
+               walk_waves=walk_waves, gate=gate)
     out = p["out"]
     if output_final_state:
         return out, p["fin"]
@@ -352,11 +384,12 @@ def chunk_stages(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=No
 
 
 def kda_decode(q, k, v, g, beta, state_cache, state_indices=None, scale=None,
-               use_qk_l2norm=True, output=None):
+               use_qk_l2norm=True, output=None, A_log=None, dt_bias=None, lower_bound=-5.0):
     """One token per request over the paged V-first fp32 state cache, updated
     in place.  q, k: [N, Hqk, 128] or [N, 1, Hqk, 128]; v, g: [N, Hv, 128] or
     [N, 1, Hv, 128]; beta: [N, Hv] or [N, 1, Hv]; state_cache
     [slots, Hv, 128, 128] fp32; state_indices [N] int32/int64 (negative = skip).
+    With A_log / dt_bias, g is a raw gate (the form chunk_kda takes).
     Returns out shaped like v."""
     shape_v = v.shape
     if q.dim() == 4:
@@ -410,6 +443,7 @@ def kda_decode(q, k, v, g, beta, state_cache, state_indices=None, scale=None,
     a.num_slots = state_cache.shape[0]
     a.out = _ptr(output)
     a.stream = _stream(dev)
+    _set_gate(a, _gate(A_log, dt_bias, lower_bound, hv, dev))
     st = lib.kda_decode(ctypes.byref(a))
     if st != KDA_OK:
         _raise(lib, st)

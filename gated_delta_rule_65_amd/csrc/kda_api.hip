@@ -34,6 +34,29 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 size_t elem_size(int dtype) { return dtype == KDA_F32 ? 4 : 2; }
 
+// Gate parameters: both or neither; dt_bias fp32 or bf16; lower_bound in
+// [-10, 0] (per-step log-decays beyond -10 would leave the exponent range
+// the chunk tiles are built for).
+kda_status check_gate(const float* a_log, const void* dt_bias, int32_t dt_dtype, float lb) {
+  if ((a_log == nullptr) != (dt_bias == nullptr))
+    return fail(KDA_ERR_SHAPE, "A_log and dt_bias must be provided together");
+  if (!a_log) return KDA_OK;
+  if (dt_dtype != KDA_F32 && dt_dtype != KDA_BF16)
+    return fail(KDA_ERR_DTYPE, "dt_bias must be fp32 or bf16");
+  if (!(lb >= -10.0f && lb <= 0.0f))
+    return fail(KDA_ERR_UNSUPPORTED, "lower_bound must lie in [-10, 0]");
+  return KDA_OK;
+}
+
+kda::GateArgs gate_of(const float* a_log, const void* dt_bias, int32_t dt_dtype, float lb) {
+  kda::GateArgs g;
+  g.a_log = a_log;
+  g.bias = dt_bias;
+  g.bias_bf16 = dt_dtype == KDA_BF16 ? 1 : 0;
+  g.lower_bound = lb;
+  return g;
+}
+
 // Shape and mode checks of the chunked forward (chunk_kda's checks, in the
 // terms of this ABI).  Pointers are checked only where the call will read or
 // write through them.
@@ -78,6 +101,10 @@ kda_status check_chunk(const kda_chunk_args* a, bool need_ptrs) {
   if (a->groups > 64) return fail(KDA_ERR_UNSUPPORTED, "groups above 64");
   if (a->walk_waves != 0 && a->walk_waves != 2 && a->walk_waves != 4 && a->walk_waves != 8)
     return fail(KDA_ERR_ARG, "walk_waves must be 0, 2, 4 or 8");
+  {
+    const kda_status gs = check_gate(a->A_log, a->dt_bias, a->dt_bias_dtype, a->lower_bound);
+    if (gs != KDA_OK) return gs;
+  }
   if (a->stage_events && (a->num_stage_events < 0 || a->num_stage_events > KDA_NUM_EVENTS))
     return fail(KDA_ERR_ARG, "num_stage_events must be in [0, %d]", KDA_NUM_EVENTS);
   if (need_ptrs && a->total_tokens > 0) {
@@ -244,6 +271,7 @@ KDA_API kda_status kda_chunk_fwd(const kda_chunk_args* a) {
   L.events = a->stage_events;
   L.num_events = a->stage_events ? a->num_stage_events : 0;
   L.fuse_prep = a->path == KDA_PATH_STAGED ? 0 : 1;
+  L.gate = gate_of(a->A_log, a->dt_bias, a->dt_bias_dtype, a->lower_bound);
   L.groups = W.groups;
   L.walk_waves = W.walk_waves;
   L.scan = L.groups > 1 ? (float*)(ws + W.scan) : nullptr;
@@ -271,6 +299,10 @@ KDA_API kda_status kda_decode(const kda_decode_args* a) {
                 a->num_slots);
   if ((size_t)a->n * (size_t)a->hv > 0x7fffffffu)
     return fail(KDA_ERR_UNSUPPORTED, "n * hv above 2^31-1");
+  {
+    const kda_status gs = check_gate(a->A_log, a->dt_bias, a->dt_bias_dtype, a->lower_bound);
+    if (gs != KDA_OK) return gs;
+  }
   if (a->n == 0) return ok();
   if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->out || !a->state_cache)
     return fail(KDA_ERR_ARG, "q, k, v, g, beta, out and state_cache must be non-NULL");
@@ -280,6 +312,7 @@ KDA_API kda_status kda_decode(const kda_decode_args* a) {
   L.dtype = a->dtype; L.n = a->n; L.hqk = a->hqk; L.hv = a->hv;
   L.use_l2 = a->use_qk_l2norm ? 1 : 0; L.num_slots = a->num_slots; L.scale = a->scale;
   L.stream = a->stream;
+  L.gate = gate_of(a->A_log, a->dt_bias, a->dt_bias_dtype, a->lower_bound);
   hipError_t e = kda::launch_decode(L);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();

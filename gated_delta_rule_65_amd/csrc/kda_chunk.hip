@@ -222,7 +222,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const E* __restrict__ q,
                                                    const int4* __restrict__ table,
                                                    int hqk, int hv, int use_l2,
                                                    E* __restrict__ qg, E* __restrict__ kg_t,
-                                                   float* __restrict__ decay) {
+                                                   float* __restrict__ decay,
+                                                   const GateArgs ga) {
   constexpr int SK = D + 4;
   __shared__ float sG[C][SK];
   E* sKg = reinterpret_cast<E*>(&sG[0][0]);   // kg tile [64][SKG] after G is consumed
@@ -248,6 +249,17 @@ __global__ __launch_bounds__(256) void prep_kernel(const E* __restrict__ q,
     if (gi > 0) {
       lds_barrier();
       load_rows4(g + ((size_t)p.t0 * hv + h) * D, hv * D, L, gx);
+    }
+    if (ga.a_log) {
+      // raw gate -> log-decay; rows past L stay 0
+      const float a = exp2_fast(ga.a_log[h] * LOG2E);
+      float bias[8];
+      gate_bias8(ga, h, 8 * j, bias);
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          gx[it][e] = rg + 16 * it < L ? gate_apply(gx[it][e], a, bias[e], ga.lower_bound) : 0.f;
     }
     gate_cumsum<SK>(gx, sG);
     float G[4][8], Gl[8];
@@ -483,7 +495,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     const E* __restrict__ g, const E* __restrict__ beta, const int4* __restrict__ table,
     int hqk, int hv, int use_l2, E* __restrict__ w_out, E* __restrict__ u_t,
     E* __restrict__ aqk, E* __restrict__ qg, E* __restrict__ kg_t, float* __restrict__ decay,
-    int items, int* __restrict__ counter) {
+    int items, int* __restrict__ counter, const GateArgs ga) {
   constexpr bool SPLIT = std::is_same<E, float>::value;
   using TE = typename TileT<E>::T;
   constexpr int ST = D + (SPLIT ? 4 : 8);        // row stride of the [64 t][128] tiles
@@ -528,12 +540,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   bool ok = item < items && locate_chunk(item / hv, table, p);
   RawRows<E> rq, rk, rgt;
   E rb;
+  float gA = 0.f, gB[8];  // gate parameters of the item's head (with A_log)
   auto prefetch = [&](int it_, const ChunkPos& pp, int tid) {
     const int h_ = it_ % hv, hq_ = h_ / grp;
     raw_load(q + ((size_t)pp.t0 * hqk + hq_) * D, hqk * D, pp.L, rq, tid);
     raw_load(k + ((size_t)pp.t0 * hqk + hq_) * D, hqk * D, pp.L, rk, tid);
     raw_load(g + ((size_t)pp.t0 * hv + h_) * D, hv * D, pp.L, rgt, tid);
     rb = beta[(size_t)(pp.t0 + min(tid, pp.L - 1)) * hv + h_];
+    if (ga.a_log) {
+      gA = ga.a_log[h_];
+      gate_bias8(ga, h_, 8 * (tid & 15), gB);
+    }
   };
   if (ok) prefetch(item, p, (int)threadIdx.x);
 
@@ -561,6 +578,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     raw_decode(rq, L, qx, tid);
     raw_decode(rk, L, kx, tid);
     raw_decode(rgt, L, G, tid);
+    if (ga.a_log) {
+      // raw gate -> log-decay; rows past L stay 0
+      const float a = exp2_fast(gA * LOG2E);
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          G[it][e] = 4 * rg + it < L ? gate_apply(G[it][e], a, gB[e], ga.lower_bound) : 0.f;
+    }
     const float braw = to_f32(rb);
     if (use_l2) {
       l2norm_rows4(qx);
@@ -1363,7 +1389,7 @@ static hipError_t launch_staged_t(const ChunkLaunch& L) {
     if (!L.fuse_prep)
       hipLaunchKernelGGL(prep_kernel<E>, dim3((unsigned)L.max_chunks, L.hqk), dim3(256), 0, st,
                          (const E*)L.q, (const E*)L.k, (const E*)L.g, (const int4*)L.table,
-                         L.hqk, L.hv, L.use_l2, (E*)L.qg, (E*)L.kg_t, L.decay);
+                         L.hqk, L.hv, L.use_l2, (E*)L.qg, (E*)L.kg_t, L.decay, L.gate);
     mark(L, 2);
     // persistent WY grid: the resident workgroups (LDS allows two per CU for
     // bf16 tiles, one for fp32)
@@ -1375,13 +1401,14 @@ static hipError_t launch_staged_t(const ChunkLaunch& L) {
       hipLaunchKernelGGL((wy_kernel<E, true>), grid, dim3(256), 0, st, (const E*)L.q,
                          (const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta,
                          (const int4*)L.table, L.hqk, L.hv, L.use_l2, (E*)L.w, (E*)L.u,
-                         (E*)L.aqk, (E*)L.qg, (E*)L.kg_t, L.decay, items, wy_counter);
+                         (E*)L.aqk, (E*)L.qg, (E*)L.kg_t, L.decay, items, wy_counter,
+                         L.gate);
     else
       hipLaunchKernelGGL((wy_kernel<E, false>), grid, dim3(256), 0, st, (const E*)L.q,
                          (const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta,
                          (const int4*)L.table, L.hqk, L.hv, L.use_l2, (E*)L.w, (E*)L.u,
                          (E*)L.aqk, (E*)nullptr, (E*)nullptr, (float*)nullptr, items,
-                         wy_counter);
+                         wy_counter, L.gate);
   } else {
     mark(L, 2);
   }

@@ -42,6 +42,41 @@ __device__ __forceinline__ float sigmoid(float x) {
   return 1.0f / (1.0f + exp2_fast(-x * LOG2E));
 }
 
+// Optional gate parameters (the raw gate g becomes the log-decay
+// lower_bound * sigmoid(a (g + bias)), a = exp(A_log[h])).
+struct GateArgs {
+  const float* a_log;  // [Hv] or NULL
+  const void* bias;    // [Hv, 128] fp32 or bf16
+  int bias_bf16;
+  float lower_bound;
+};
+__device__ __forceinline__ float gate_bias(const GateArgs& ga, int h, int c) {
+  const size_t i = (size_t)h * D + c;
+  return ga.bias_bf16 ? to_f32(reinterpret_cast<const bf16*>(ga.bias)[i])
+                      : reinterpret_cast<const float*>(ga.bias)[i];
+}
+// The 8 biases of channels c0 .. c0 + 7 (c0 a multiple of 8).
+__device__ __forceinline__ void gate_bias8(const GateArgs& ga, int h, int c0, float (&b)[8]) {
+  const size_t i = (size_t)h * D + c0;
+  if (ga.bias_bf16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16*>(ga.bias) + i);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      b[2 * d] = __uint_as_float(w[d] << 16);
+      b[2 * d + 1] = __uint_as_float(w[d] & 0xffff0000u);
+    }
+  } else {
+    const float4 x = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(ga.bias) + i)[0];
+    const float4 y = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(ga.bias) + i)[1];
+    b[0] = x.x; b[1] = x.y; b[2] = x.z; b[3] = x.w;
+    b[4] = y.x; b[5] = y.y; b[6] = y.z; b[7] = y.w;
+  }
+}
+__device__ __forceinline__ float gate_apply(float graw, float a, float bias, float lb) {
+  return lb * sigmoid(a * (graw + bias));
+}
+
 // Workgroup barrier that orders LDS only.  __syncthreads() is a full
 // release/acquire fence and so also waits for every global load still in
 // flight; this one waits for LDS traffic alone, so prefetches issued before it

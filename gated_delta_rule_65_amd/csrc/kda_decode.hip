@@ -12,7 +12,9 @@
 // "vllm.models.kimi_k3.nvidia.recoverssm.cutedsl.verify") at window 1.  A
 // negative slot produces a zero output row and no state traffic (the null
 // slot of KdaTcVerify); a slot at or past the pool size is treated the same
-// way so that a bad index can never address outside the cache.
+// way so that a bad index can never address outside the cache.  With gate
+// parameters, g is a raw gate: log-decay = lower_bound sigmoid(exp(A_log[h])
+// (g + dt_bias[h][c])), KdaTcVerify's activation.
 //
 // Mapping (HBM-bound: 64 KiB read + 64 KiB written per unit): one 256-thread
 // workgroup per unit; 16 lanes (one DPP row) own one state row, each lane
@@ -32,7 +34,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ g, const T* __restrict__ beta, float* __restrict__ cache,
     const int32_t* __restrict__ idx, T* __restrict__ out, int hqk, int hv, float scale,
-    int use_l2, int num_slots) {
+    int use_l2, int num_slots, const GateArgs ga) {
   const int unit = blockIdx.x;
   const int req = unit / hv, h = unit - req * hv;
   const int hq = h / (hv / hqk);
@@ -62,12 +64,15 @@ __global__ __launch_bounds__(256) void decode_kernel(
   const T* gp = g + ((size_t)req * hv + h) * D;
   const T* vp = v + ((size_t)req * hv + h) * D;
   float qv[8], kv[8], al[8];
+  const float ga_a = ga.a_log ? exp2_fast(ga.a_log[h] * LOG2E) : 0.f;  // exp(A_log[h])
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int c = (e < 4) ? (4 * j + e) : (64 + 4 * j + e - 4);
     qv[e] = to_f32(qp[c]);
     kv[e] = to_f32(kp[c]);
-    al[e] = exp2_fast(to_f32(gp[c]) * LOG2E);
+    float gl = to_f32(gp[c]);
+    if (ga.a_log) gl = gate_apply(gl, ga_a, gate_bias(ga, h, c), ga.lower_bound);
+    al[e] = exp2_fast(gl * LOG2E);
   }
   float vr[8];
 #pragma unroll
@@ -125,7 +130,7 @@ static hipError_t launch_decode_t(const DecodeLaunch& L) {
   hipLaunchKernelGGL(decode_kernel<T>, grid, block, 0, (hipStream_t)L.stream,
                      (const T*)L.q, (const T*)L.k, (const T*)L.v, (const T*)L.g,
                      (const T*)L.beta, L.cache, L.idx, (T*)L.out, L.hqk, L.hv, L.scale,
-                     L.use_l2, L.num_slots);
+                     L.use_l2, L.num_slots, L.gate);
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
 // Host-side launch descriptors between the C-ABI layer and the kernel files.
 #pragma once
+#include "kda_common.hpp"
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -14,6 +15,7 @@ struct DecodeLaunch {
   int dtype, n, hqk, hv, use_l2, num_slots;
   float scale;
   void* stream;
+  GateArgs gate;  // optional gate parameters (a_log == NULL: none)
 };
 hipError_t launch_decode(const DecodeLaunch& L);
 
@@ -41,6 +43,7 @@ struct ChunkLaunch {
   int groups;                 // chunk groups per sequence (1 = plain walk)
   int walk_waves;             // waves per walk workgroup: 2, 4 or 8 (16 columns each)
   int fuse_prep;              // 1: the WY kernel also writes qg, kg_t and decay
+  GateArgs gate;  // optional gate parameters (a_log == NULL: none)
   void** events;              // optional stage events (KDA_EV_*), may be NULL
   int num_events;
   void* stream;

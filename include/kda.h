@@ -131,6 +131,17 @@ typedef struct kda_chunk_args {
                                   (profiling); NULL = none.  The caller owns them. */
   int32_t num_stage_events;
   void *stream;                /* hipStream_t or NULL */
+  /* Gate parameters (optional; both or neither).  With them, g holds a raw
+     gate and the log-decay of a step is
+       lower_bound * sigmoid(exp(A_log[h]) * (g + dt_bias[h][c]))
+     (the activation of KdaTcVerify, page
+     "vllm.models.kimi_k3.nvidia.recoverssm.cutedsl.verify"; chunk_kda of page
+     "mate.kda" takes A_log, dt_bias and lower_bound = -5 by default).
+     lower_bound must lie in [-10, 0]. */
+  const float *A_log;          /* (device) [Hv] fp32, or NULL */
+  const void *dt_bias;         /* (device) [Hv, 128] of dt_bias_dtype, or NULL */
+  int32_t dt_bias_dtype;       /* KDA_F32 or KDA_BF16 */
+  float lower_bound;
 } kda_chunk_args;
 
 /* Stage boundaries of kda_chunk_fwd (indices into stage_events).  Event i is
@@ -209,7 +220,8 @@ typedef struct kda_decode_args {
   const void *q;               /* (device) [n, Hqk, 128] dtype */
   const void *k;               /* (device) [n, Hqk, 128] dtype */
   const void *v;               /* (device) [n, Hv, 128] dtype */
-  const void *g;               /* (device) [n, Hv, 128] dtype, log-decay */
+  const void *g;               /* (device) [n, Hv, 128] dtype, log-decay (or
+                                  the raw gate with A_log / dt_bias) */
   const void *beta;            /* (device) [n, Hv] dtype, logits */
   int32_t dtype;               /* kda_dtype */
   int32_t n;                   /* requests >= 0 */
@@ -223,6 +235,17 @@ typedef struct kda_decode_args {
   int32_t num_slots;
   void *out;                   /* (device) [n, Hv, 128] dtype */
   void *stream;                /* hipStream_t or NULL */
+  /* Gate parameters (optional; both or neither).  With them, g holds a raw
+     gate and the log-decay of a step is
+       lower_bound * sigmoid(exp(A_log[h]) * (g + dt_bias[h][c]))
+     (the activation of KdaTcVerify, page
+     "vllm.models.kimi_k3.nvidia.recoverssm.cutedsl.verify"; the same form as
+     the chunked forward).
+     lower_bound must lie in [-10, 0]. */
+  const float *A_log;          /* (device) [Hv] fp32, or NULL */
+  const void *dt_bias;         /* (device) [Hv, 128] of dt_bias_dtype, or NULL */
+  int32_t dt_bias_dtype;       /* KDA_F32 or KDA_BF16 */
+  float lower_bound;
 } kda_decode_args;
 
 kda_status kda_decode(const kda_decode_args *a);

@@ -216,3 +216,40 @@ def test_planner_picks_groups_only_for_long_chains(lib):
     assert total(num_seqs=1, total_tokens=131072, hqk=32, hv=32) > 0
     # explicit groups always reserve their planes
     assert total(num_seqs=2, total_tokens=256, groups=4) == 4 * 2 * 4 * 3 * 128 * 128 * 4
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: the checks fail first
+
+
+@pytest.mark.parametrize("make,call", [
+    (chunk_args, lambda lib, a: ws_size(lib, a)[0]),
+    (decode_args, lambda lib, a: lib.kda_decode(ctypes.byref(a))),
+], ids=["chunk", "decode"])
+@pytest.mark.parametrize("fields,status", [
+    (dict(A_log=FAKE), B.KDA_ERR_SHAPE),                       # without dt_bias
+    (dict(dt_bias=FAKE), B.KDA_ERR_SHAPE),                     # without A_log
+    (dict(A_log=FAKE, dt_bias=FAKE, dt_bias_dtype=2, lower_bound=-5.0), B.KDA_ERR_DTYPE),
+    (dict(A_log=FAKE, dt_bias=FAKE, dt_bias_dtype=0, lower_bound=-11.0), B.KDA_ERR_UNSUPPORTED),
+    (dict(A_log=FAKE, dt_bias=FAKE, dt_bias_dtype=0, lower_bound=0.5), B.KDA_ERR_UNSUPPORTED),
+    (dict(A_log=FAKE, dt_bias=FAKE, dt_bias_dtype=1, lower_bound=float("nan")),
+     B.KDA_ERR_UNSUPPORTED),
+], ids=["a_only", "bias_only", "bias_f16", "lb_low", "lb_pos", "lb_nan"])
+def test_gate_parameter_checks(lib, make, call, fields, status):
+    a = make(**fields)
+    assert call(lib, a) == status
+    assert lib.kda_last_error().decode() != ""
+
+
+def test_binding_gate_checks():
+    q = cpu((1, 64, 2, 128))
+    v = cpu((1, 64, 4, 128))
+    beta = cpu((1, 64, 4))
+    a_log = torch.zeros(4)
+    with pytest.raises(ValueError, match="together"):
+        B.chunk_kda(q, q, v, v, beta, A_log=a_log)
+    with pytest.raises(ValueError, match="shape"):
+        B.chunk_kda(q, q, v, v, beta, A_log=a_log, dt_bias=torch.zeros(4, 64))
+    with pytest.raises(TypeError):
+        B.chunk_kda(q, q, v, v, beta, A_log=a_log.double(), dt_bias=torch.zeros(4, 128))
+    with pytest.raises(TypeError):
+        B.chunk_kda(q, q, v, v, beta, A_log=a_log, dt_bias=torch.zeros(4, 128).half())

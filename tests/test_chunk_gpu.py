@@ -447,3 +447,41 @@ def test_staged_and_fused_paths_agree():
     assert rel(res[1][0], res[0][0]) < 2e-3 and rel(res[1][1], res[0][1]) < 2e-3
     o_ref, s_ref = oracle_dense(b)
     assert rel(res[1][0], o_ref) < 1e-2 and rel(res[1][1], s_ref) < 1e-2
+
+
+# ------------------------------------------------------------ gate parameters
+
+GATE_CASES = [
+    # (name, lengths, hqk, hv, dtype, path, groups, dt_bias dtype)
+    ("bf16_fused", [300, 64, 1, 200], 2, 4, torch.bfloat16, B.PATH_FUSED, 0, torch.float32),
+    ("bf16_staged", [300, 64, 1, 200], 2, 4, torch.bfloat16, B.PATH_STAGED, 0, torch.float32),
+    ("bf16_bias_bf16", [257, 100], 1, 2, torch.bfloat16, B.PATH_FUSED, 0, torch.bfloat16),
+    ("fp32", [130, 70], 1, 2, torch.float32, B.PATH_FUSED, 0, torch.float32),
+    ("bf16_scan", [1500], 1, 2, torch.bfloat16, B.PATH_FUSED, 4, torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", GATE_CASES, ids=[c[0] for c in GATE_CASES])
+def test_gate_parameters_match_oracle(case):
+    """g as a raw gate: log-decay lower_bound * sigmoid(exp(A_log) (g + dt_bias)),
+    applied in the kernels, against the oracle with the same stored values."""
+    name, lengths, hqk, hv, dt, path, groups, bdt = case
+    b = inputs.make_chunk(lengths, hqk, hv, dtype=dt, seed=90, init=True)
+    gen = torch.Generator().manual_seed(91)
+    b.g = torch.randn(b.g.shape, generator=gen).to(dt)
+    a_log = (torch.rand(hv, generator=gen) * 2 - 1).float()
+    dt_bias = (torch.randn(hv, 128, generator=gen) * 0.5).to(bdt)
+    say("gate", name)
+    q, k, v, g, beta = gpu(b)
+    out, fin = B.chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=b.initial_state.to(DEV),
+                           output_final_state=True, cu_seqlens=b.cu_seqlens.to(DEV),
+                           path=path, groups=groups, A_log=a_log.to(DEV),
+                           dt_bias=dt_bias.to(DEV), lower_bound=-5.0)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence(b.q, b.k, b.v, b.g, b.beta, cu_seqlens=b.cu_seqlens,
+                                     scale=b.scale, initial_state=b.initial_state,
+                                     A_log=a_log.double(), dt_bias=dt_bias.double(),
+                                     lower_bound=-5.0)
+    t_ = tol(dt)
+    assert rel(out.float().cpu().numpy(), o_ref) < t_
+    assert rel(fin.cpu().numpy(), s_ref) < t_

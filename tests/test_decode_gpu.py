@@ -120,3 +120,33 @@ def test_decode_is_deterministic():
     o1 = B.kda_decode(*args, c1, idx)
     o2 = B.kda_decode(*args, c2, idx)
     assert torch.equal(o1, o2) and torch.equal(c1, c2)
+
+
+@pytest.mark.parametrize("dtype,bias_dtype", [(torch.bfloat16, torch.float32),
+                                              (torch.bfloat16, torch.bfloat16),
+                                              (torch.float32, torch.float32)])
+def test_decode_gate_parameters(dtype, bias_dtype):
+    """g as a raw gate with A_log / dt_bias / lower_bound, against the oracle
+    with the same stored parameters."""
+    b = inputs.make_decode(40, 2, 4, 64, dtype=dtype, seed=11)
+    gen = torch.Generator().manual_seed(12)
+    b.g = torch.randn(b.g.shape, generator=gen).to(dtype)
+    a_log = (torch.rand(4, generator=gen) * 2 - 1).float()
+    dt_bias = (torch.randn(4, 128, generator=gen) * 0.5).to(bias_dtype)
+    idx = b.state_indices.clone()
+    idx[5] = -1
+    cache = b.state_cache.to(DEV)
+    args = [t.to(DEV) for t in (b.q, b.k, b.v, b.g, b.beta)]
+    print("decode gate", dtype, bias_dtype, flush=True)
+    out = B.kda_decode(*args, cache, idx.to(DEV), A_log=a_log.to(DEV),
+                       dt_bias=dt_bias.to(DEV), lower_bound=-4.0)
+    torch.cuda.synchronize()
+    ref_out, ref_cache = oracle.decode(b.q, b.k, b.v, b.g, b.beta, b.state_cache, idx,
+                                       A_log=a_log.double(), dt_bias=dt_bias.double(),
+                                       lower_bound=-4.0)
+    tol = 1e-4 if dtype == torch.float32 else 1e-2
+    assert rel(out.float().cpu().numpy(), ref_out) < tol
+    live = idx >= 0
+    rows = idx[live].long()
+    assert rel(cache.cpu()[rows].numpy(), ref_cache[rows.numpy()]) < 1e-5
+    assert np.all(out[5].float().cpu().numpy() == 0.0)
