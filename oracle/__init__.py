@@ -196,3 +196,35 @@ def decode(q, k, v, g, beta, state_cache, state_indices, scale=None,
     out[live] = o
     new_cache[idx[live]] = sf
     return out, new_cache
+
+
+def checkpoints(q, k, v, g, beta, cu_seqlens, offsets, scale=None, use_qk_l2norm=True,
+                initial_state=None, A_log=None, dt_bias=None, lower_bound=-5.0,
+                alignment=64, threads=None):
+    """Mid-prefill state snapshots: for each sequence n with a usable offset
+    (0 < offsets[n] <= length, a multiple of ``alignment``) the recurrent state
+    after its first offsets[n] tokens, V-first fp64 [Hv, 128, 128]; None for
+    the others.  The snapshot of fused_kda_chunk (kda_chunk page): offsets are
+    relative to each sequence's first token, 0 disables, unaligned ones are
+    skipped.  Computed as the recurrence over each prefix alone.
+    """
+    cu = np.asarray(torch.as_tensor(cu_seqlens).cpu().numpy(), dtype=np.int64)
+    offs = np.asarray(torch.as_tensor(offsets).cpu().numpy(), dtype=np.int64)
+    q = _cpu_contig(q, "q"); k = _cpu_contig(k, "k"); v = _cpu_contig(v, "v")
+    g = _cpu_contig(g, "g"); beta = _cpu_contig(beta, "beta")
+    s0 = None if initial_state is None else torch.as_tensor(initial_state).detach().cpu()
+    res = []
+    for n in range(len(cu) - 1):
+        length = cu[n + 1] - cu[n]
+        o = int(offs[n])
+        if o <= 0 or o > length or o % alignment:
+            res.append(None)
+            continue
+        sl = slice(int(cu[n]), int(cu[n]) + o)
+        _, sf = recurrence(q[sl], k[sl], v[sl], g[sl], beta[sl], scale=scale,
+                           use_qk_l2norm=use_qk_l2norm,
+                           initial_state=None if s0 is None else s0[n:n + 1],
+                           A_log=A_log, dt_bias=dt_bias, lower_bound=lower_bound,
+                           threads=threads)
+        res.append(sf[0])
+    return res

@@ -351,3 +351,33 @@ def test_gate_requires_both_parameters():
     b, al, _ = gate_batch(8)
     with pytest.raises(ValueError):
         run_R(b, A_log=al)
+
+
+# ------------------------------------------------------- state checkpoints
+
+def test_checkpoint_at_full_length_is_the_final_state():
+    b = small_batch([128, 192], 1, 2, 21)
+    _, s_full = run_R(b)
+    cks = oracle.checkpoints(b.q, b.k, b.v, b.g, b.beta, b.cu_seqlens, [128, 192],
+                             scale=b.scale, initial_state=b.initial_state)
+    assert rel(cks[0], s_full[0]) < 1e-14 and rel(cks[1], s_full[1]) < 1e-14
+
+
+def test_checkpoint_then_rest_reproduces_the_full_run():
+    """Continuing the recurrence from the snapshot over the remaining tokens
+    gives the full run's outputs and final state."""
+    b = small_batch([200], 1, 2, 22, g_scale=0.5)
+    o_full, s_full = run_R(b)
+    ck = oracle.checkpoints(b.q, b.k, b.v, b.g, b.beta, b.cu_seqlens, [128],
+                            scale=b.scale, initial_state=b.initial_state)[0]
+    sl = slice(128, 200)
+    o2, s2 = oracle.recurrence(b.q[sl], b.k[sl], b.v[sl], b.g[sl], b.beta[sl],
+                               scale=b.scale, initial_state=ck[None])
+    assert rel(o2, o_full[sl]) < 1e-12 and rel(s2[0], s_full[0]) < 1e-12
+
+
+def test_checkpoint_skips_zero_unaligned_and_past_the_end():
+    b = small_batch([100, 64, 70], 1, 1, 23)
+    cks = oracle.checkpoints(b.q, b.k, b.v, b.g, b.beta, b.cu_seqlens, [0, 32, 128],
+                             scale=b.scale, initial_state=b.initial_state)
+    assert cks == [None, None, None]
