@@ -51,6 +51,8 @@ class ChunkArgs(ctypes.Structure):
         ("stream", ctypes.c_void_p),
         ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
         ("dt_bias_dtype", ctypes.c_int32), ("lower_bound", ctypes.c_float),
+        ("checkpoint_state", ctypes.c_void_p), ("checkpoint_offsets", ctypes.c_void_p),
+        ("checkpoint_state_indices", ctypes.c_void_p), ("checkpoint_rows", ctypes.c_int32),
     ]
 
 
@@ -157,6 +159,32 @@ def _gate(A_log, dt_bias, lower_bound, hv, dev):
         _contig(name, t)
         _need(t.device == dev, f"{name} must be on {dev}")
     return A_log, dt_bias, _DTYPES[dt_bias.dtype], float(lower_bound)
+
+
+def _checkpoints(state, offsets, indices, N, hv, dev):
+    """Checked snapshot arguments: (state, int32 offsets, int32 indices or
+    None), or None."""
+    if state is None and offsets is None and indices is None:
+        return None
+    _need(state is not None and offsets is not None,
+          "checkpoint_state and checkpoint_offsets must be given together")
+    _need(state.dtype == torch.float32, "checkpoint_state must be float32", TypeError)
+    _need(state.dim() == 4 and tuple(state.shape[1:]) == (hv, D, D) and state.shape[0] > 0,
+          f"checkpoint_state must be [rows, {hv}, 128, 128]")
+    _need(tuple(offsets.shape) == (N,), f"checkpoint_offsets must have shape [{N}]")
+    _need(offsets.dtype in (torch.int32, torch.int64), "checkpoint_offsets must be integer")
+    offs = offsets.to(device=dev, dtype=torch.int32).contiguous()
+    idx = None
+    if indices is not None:
+        _need(tuple(indices.shape) == (N,), f"checkpoint_state_indices must have shape [{N}]")
+        _need(indices.dtype in (torch.int32, torch.int64),
+              "checkpoint_state_indices must be integer")
+        idx = indices.to(device=dev, dtype=torch.int32).contiguous()
+    else:
+        _need(state.shape[0] >= N, "checkpoint_state needs a row per sequence")
+    _contig("checkpoint_state", state)
+    _need(state.device == dev, f"checkpoint_state must be on {dev}")
+    return state, offs, idx
 
 
 def _set_gate(a, gate):
@@ -289,13 +317,19 @@ def _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state, c
 
 
 def _run_chunk(p, path=PATH_AUTO, groups=0, workspace=None, keep=None, events=None,
-               walk_waves=0, gate=None):
+               walk_waves=0, gate=None, ckpt=None):
     lib = load_library()
     dev = p["q"].device
     a = _chunk_struct(p["q"], p["k"], p["v"], p["g"], p["beta"], p["out"], p["cu"], p["N"],
                       p["T"], p["hqk"], p["hv"], p["scale"], p["l2"], p["init"], p["fin"],
                       p["cache"], p["idx"], p["has_init"], path, groups, _stream(dev),
                       walk_waves, gate)
+    if ckpt is not None:
+        cs, co, ci = ckpt
+        a.checkpoint_state, a.checkpoint_offsets = _ptr(cs), _ptr(co)
+        a.checkpoint_state_indices, a.checkpoint_rows = _ptr(ci), cs.shape[0]
+        if keep is not None:
+            keep["ckpt"] = ckpt
     nbytes = ctypes.c_size_t(0)
     st = lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(nbytes))
     if st != KDA_OK:
@@ -321,7 +355,8 @@ def chunk_kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_sta
               cu_seqlens=None, use_qk_l2norm_in_kernel=True, output=None, final_state=None,
               state_cache=None, state_indices=None, has_initial_state=None, groups=0,
               workspace=None, stage_events=None, walk_waves=0, path=PATH_AUTO,
-              A_log=None, dt_bias=None, lower_bound=-5.0):
+              A_log=None, dt_bias=None, lower_bound=-5.0, checkpoint_state=None,
+              checkpoint_offsets=None, checkpoint_state_indices=None):
     """Chunked KDA forward (chunk_kda's argument set, plus the paged state of
     fused_kda_chunk).  Returns out, or (out, final_state) when
     output_final_state; in paged mode the final states land in state_cache.
@@ -331,13 +366,19 @@ def chunk_kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_sta
     the result is the same up to rounding order).  path: PATH_AUTO,
     PATH_STAGED (prep as its own kernel) or PATH_FUSED.  A_log [Hv] fp32 and
     dt_bias [Hv, 128] fp32/bf16 (both or neither) make g a raw gate with
-    log-decay lower_bound * sigmoid(exp(A_log) * (g + dt_bias))."""
+    log-decay lower_bound * sigmoid(exp(A_log) * (g + dt_bias)).
+    checkpoint_state [rows, Hv, 128, 128] fp32 with checkpoint_offsets [N]
+    (and optionally checkpoint_state_indices [N]) snapshots each sequence's
+    state after its first checkpoint_offsets[n] tokens (0 or a multiple of 64;
+    fused_kda_chunk's checkpoint arguments)."""
     p = _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state,
                        cu_seqlens, use_qk_l2norm_in_kernel, output, final_state,
                        state_cache, state_indices, has_initial_state)
     gate = _gate(A_log, dt_bias, lower_bound, p["hv"], p["q"].device)
+    ck = _checkpoints(checkpoint_state, checkpoint_offsets, checkpoint_state_indices, p["N"],
+                      p["hv"], p["q"].device)
     _run_chunk(p, path=path, groups=groups, workspace=workspace, events=stage_events,
-               walk_waves=walk_waves, gate=gate)
+               walk_waves=walk_waves, gate=gate, ckpt=ck)
     out = p["out"]
     if output_final_state:
         return out, p["fin"]

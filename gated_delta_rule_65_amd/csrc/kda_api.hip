@@ -105,6 +105,14 @@ kda_status check_chunk(const kda_chunk_args* a, bool need_ptrs) {
     const kda_status gs = check_gate(a->A_log, a->dt_bias, a->dt_bias_dtype, a->lower_bound);
     if (gs != KDA_OK) return gs;
   }
+  if ((a->checkpoint_state == nullptr) != (a->checkpoint_offsets == nullptr))
+    return fail(KDA_ERR_SHAPE, "checkpoint_state and checkpoint_offsets go together");
+  if (a->checkpoint_state) {
+    if (a->checkpoint_rows <= 0) return fail(KDA_ERR_SHAPE, "checkpoint_rows must be > 0");
+    if (!a->checkpoint_state_indices && a->checkpoint_rows < a->num_seqs)
+      return fail(KDA_ERR_SHAPE, "checkpoint_state needs a row per sequence (%d), got %d",
+                  a->num_seqs, a->checkpoint_rows);
+  }
   if (a->stage_events && (a->num_stage_events < 0 || a->num_stage_events > KDA_NUM_EVENTS))
     return fail(KDA_ERR_ARG, "num_stage_events must be in [0, %d]", KDA_NUM_EVENTS);
   if (need_ptrs && a->total_tokens > 0) {
@@ -272,6 +280,10 @@ KDA_API kda_status kda_chunk_fwd(const kda_chunk_args* a) {
   L.num_events = a->stage_events ? a->num_stage_events : 0;
   L.fuse_prep = a->path == KDA_PATH_STAGED ? 0 : 1;
   L.gate = gate_of(a->A_log, a->dt_bias, a->dt_bias_dtype, a->lower_bound);
+  L.ckpt = a->checkpoint_state;
+  L.ckpt_off = a->checkpoint_offsets;
+  L.ckpt_idx = a->checkpoint_state_indices;
+  L.ckpt_rows = a->checkpoint_rows;
   L.groups = W.groups;
   L.walk_waves = W.walk_waves;
   L.scan = L.groups > 1 ? (float*)(ws + W.scan) : nullptr;

@@ -900,6 +900,9 @@ struct WalkArgs {
   int nvb, units, max_chunks, groups;
   float* scan;  // group planes (g, n, h): P [k][j], B [v][k], H_in [v][k]
   const uint4* zero;
+  float* ckpt;  // mid-prefill snapshots [rows, hv, 128, 128] or NULL
+  const int32_t *ckpt_off, *ckpt_idx;
+  int ckpt_rows;
 };
 
 constexpr size_t PLANE = (size_t)D * D;
@@ -997,6 +1000,19 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(const WalkArgs<E> a) {
     src = scan_plane(a.scan, g, n, h, a.N, hv, 2);
     if (g == G - 1)
       dst = a.cache ? row : (a.fin ? a.fin + ((size_t)n * hv + h) * PLANE : nullptr);
+  }
+
+  // mid-prefill snapshot: the step after which it is taken (-1: none).  Pass
+  // one of the group scan walks from zero, so only modes 0 and 2 take it.
+  int ck_step = -1;
+  float* ck_dst = nullptr;
+  if (MODE != 1 && a.ckpt) {
+    const int off = a.ckpt_off[n];
+    const int row = a.ckpt_idx ? a.ckpt_idx[n] : n;
+    if (off > 0 && off % C == 0 && off <= sp.eos - sp.bos && row >= 0 && row < a.ckpt_rows) {
+      ck_step = off / C - 1;
+      ck_dst = a.ckpt + ((size_t)row * hv + h) * PLANE;
+    }
   }
 
   // state slice: S[kb][r] = S[k = 16 kb + 4 gq + r][column vcol]  (V-first row vcol)
@@ -1243,6 +1259,12 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(const WalkArgs<E> a) {
                    a.scale * O[ta][3]);
       }
     }
+    if (jc == ck_step) {
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+        *reinterpret_cast<float4*>(ck_dst + (size_t)vcol * D + 16 * kb + 4 * gq) =
+            make_float4(S[kb][0], S[kb][1], S[kb][2], S[kb][3]);
+    }
     if (STAGES == 1 && jc + 1 < jc1) {
       lds_barrier();  // everyone is done with the single stage
       issue_wq(jc + 1, cur);
@@ -1422,6 +1444,8 @@ static hipError_t launch_staged_t(const ChunkLaunch& L) {
   wa.has_init = L.has_init; wa.num_slots = L.num_slots; wa.out = (E*)L.out;
   wa.units = N * L.hv; wa.max_chunks = (int)L.max_chunks; wa.groups = L.groups;
   wa.scan = L.scan; wa.zero = (const uint4*)L.zero;
+  wa.ckpt = L.ckpt; wa.ckpt_off = L.ckpt_off; wa.ckpt_idx = L.ckpt_idx;
+  wa.ckpt_rows = L.ckpt_rows;
   wa.nvb = D / (16 * L.walk_waves);
   switch (L.walk_waves) {
     case 8: launch_walk<E, 8>(L, wa); break;

@@ -44,6 +44,10 @@ struct ChunkLaunch {
   int walk_waves;             // waves per walk workgroup: 2, 4 or 8 (16 columns each)
   int fuse_prep;              // 1: the WY kernel also writes qg, kg_t and decay
   GateArgs gate;  // optional gate parameters (a_log == NULL: none)
+  float* ckpt;                // state snapshots [rows, Hv, 128, 128] or NULL
+  const int32_t* ckpt_off;    // [N] token offsets
+  const int32_t* ckpt_idx;    // [N] destination rows or NULL (row n)
+  int ckpt_rows;
   void** events;              // optional stage events (KDA_EV_*), may be NULL
   int num_events;
   void* stream;

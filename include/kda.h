@@ -142,6 +142,18 @@ typedef struct kda_chunk_args {
   const void *dt_bias;         /* (device) [Hv, 128] of dt_bias_dtype, or NULL */
   int32_t dt_bias_dtype;       /* KDA_F32 or KDA_BF16 */
   float lower_bound;
+  /* Mid-prefill state snapshots (optional; fused_kda_chunk's checkpoint
+     arguments on page "vllm.models.kimi_k3.amd.ops.kda_chunk").  For a
+     sequence n with 0 < checkpoint_offsets[n] <= its length and a multiple of
+     64, the state after its first checkpoint_offsets[n] tokens is written
+     (V-first) to row checkpoint_state_indices[n] of checkpoint_state (row n
+     when the index array is NULL).  A 0, unaligned or too large offset, a row
+     outside [0, checkpoint_rows), and a sequence with a null state slot in
+     paged mode skip the snapshot (the row is left as it is). */
+  float *checkpoint_state;     /* (device) [checkpoint_rows, Hv, 128, 128] fp32 or NULL */
+  const int32_t *checkpoint_offsets;       /* (device) [N]; with checkpoint_state */
+  const int32_t *checkpoint_state_indices; /* (device) [N] or NULL */
+  int32_t checkpoint_rows;
 } kda_chunk_args;
 
 /* Stage boundaries of kda_chunk_fwd (indices into stage_events).  Event i is

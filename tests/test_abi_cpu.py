@@ -253,3 +253,20 @@ def test_binding_gate_checks():
         B.chunk_kda(q, q, v, v, beta, A_log=a_log.double(), dt_bias=torch.zeros(4, 128))
     with pytest.raises(TypeError):
         B.chunk_kda(q, q, v, v, beta, A_log=a_log, dt_bias=torch.zeros(4, 128).half())
+
+
+@pytest.mark.parametrize("fields,status", [
+    (dict(checkpoint_state=FAKE), B.KDA_ERR_SHAPE),                      # no offsets
+    (dict(checkpoint_offsets=FAKE), B.KDA_ERR_SHAPE),                    # no state
+    (dict(checkpoint_state=FAKE, checkpoint_offsets=FAKE, checkpoint_rows=0), B.KDA_ERR_SHAPE),
+    (dict(checkpoint_state=FAKE, checkpoint_offsets=FAKE, checkpoint_rows=1), B.KDA_ERR_SHAPE),
+], ids=["state_only", "offsets_only", "no_rows", "row_per_seq"])
+def test_checkpoint_argument_checks(lib, fields, status):
+    a = chunk_args(**fields)   # 2 sequences
+    assert ws_size(lib, a)[0] == status
+
+
+def test_checkpoint_rows_with_indices_pass_checks(lib):
+    a = chunk_args(checkpoint_state=FAKE, checkpoint_offsets=FAKE, checkpoint_state_indices=FAKE,
+                   checkpoint_rows=1)
+    assert ws_size(lib, a)[0] == B.KDA_OK

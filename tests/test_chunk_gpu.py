@@ -485,3 +485,57 @@ def test_gate_parameters_match_oracle(case):
     t_ = tol(dt)
     assert rel(out.float().cpu().numpy(), o_ref) < t_
     assert rel(fin.cpu().numpy(), s_ref) < t_
+
+
+# ---------------------------------------------------- mid-prefill checkpoints
+
+SENTINEL = 7.0
+
+
+def run_checkpoints(b, offsets, rows, indices=None, groups=0, dtype=None):
+    q, k, v, g, beta = gpu(b)
+    hv = b.v.shape[1]
+    ck = torch.full((rows, hv, 128, 128), SENTINEL, dtype=torch.float32, device=DEV)
+    offs = torch.tensor(offsets, dtype=torch.int32)
+    idx = None if indices is None else torch.tensor(indices, dtype=torch.int32)
+    out, fin = B.chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=b.initial_state.to(DEV),
+                           output_final_state=True, cu_seqlens=b.cu_seqlens.to(DEV),
+                           groups=groups, checkpoint_state=ck, checkpoint_offsets=offs.to(DEV),
+                           checkpoint_state_indices=None if idx is None else idx.to(DEV))
+    torch.cuda.synchronize()
+    refs = oracle.checkpoints(b.q, b.k, b.v, b.g, b.beta, b.cu_seqlens, offs, scale=b.scale,
+                              initial_state=b.initial_state)
+    return ck.cpu().numpy(), refs, out, fin
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_checkpoints_match_oracle_and_skip_unusable_offsets(dt):
+    lengths = [300, 64, 1, 200, 128]
+    b = inputs.make_chunk(lengths, 1, 2, dtype=dt, g_scale=0.5, seed=95, init=True)
+    offsets = [128, 64, 0, 96, 128]     # aligned, = length, disabled, unaligned, = length
+    say("checkpoints", dt)
+    ck, refs, _, fin = run_checkpoints(b, offsets, rows=5)
+    t_ = tol(dt)
+    for n, r in enumerate(refs):
+        if r is None:
+            assert np.all(ck[n] == SENTINEL), n
+        else:
+            assert rel(ck[n], r) < t_, n
+    # an offset equal to the length is the final state, bit for bit
+    assert np.array_equal(ck[4], fin[4].cpu().numpy())
+    assert np.array_equal(ck[1], fin[1].cpu().numpy())
+
+
+def test_checkpoints_through_row_indices():
+    lengths = [300, 64, 200]
+    b = inputs.make_chunk(lengths, 2, 4, dtype=torch.bfloat16, g_scale=0.5, seed=96, init=True)
+    ck, refs, _, _ = run_checkpoints(b, [256, 64, 192], rows=4, indices=[3, -1, 0])
+    assert rel(ck[3], refs[0]) < 1e-2
+    assert rel(ck[0], refs[2]) < 1e-2
+    assert np.all(ck[1] == SENTINEL) and np.all(ck[2] == SENTINEL)
+
+
+def test_checkpoints_under_the_group_scan():
+    b = inputs.make_chunk([1500], 1, 2, dtype=torch.bfloat16, g_scale=0.05, seed=97, init=True)
+    ck, refs, _, _ = run_checkpoints(b, [640], rows=1, groups=4)
+    assert rel(ck[0], refs[0]) < 1e-2
