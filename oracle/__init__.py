@@ -228,3 +228,43 @@ def checkpoints(q, k, v, g, beta, cu_seqlens, offsets, scale=None, use_qk_l2norm
                            threads=threads)
         res.append(sf[0])
     return res
+
+
+def decode_multi(q, k, v, g, beta, state_cache, state_indices, num_accepted_tokens=None,
+                 scale=None, use_qk_l2norm=True, A_log=None, dt_bias=None, lower_bound=-5.0,
+                 threads=None):
+    """Multi-token (speculative) decode over a paged V-first state cache.
+
+    q, k: [B, T, Hqk, 128]; v, g: [B, T, Hv, 128]; beta: [B, T, Hv];
+    state_indices: [B, C] with C >= T; num_accepted_tokens: [B] or None.
+    Request b starts from cache row state_indices[b, a - 1] with
+    a = num_accepted_tokens[b] (row state_indices[b, 0] without it), runs its
+    T tokens in order, and after token t writes its state to row
+    state_indices[b, t] when that index is >= 0.  A start row < 0 (or an
+    accepted count outside [1, C]) skips the request: zero outputs, no writes.
+    Each state is the recurrence over the request's tokens so far (computed
+    here one prefix at a time).  Returns (out [B, T, Hv, 128] fp64, new cache
+    fp64).
+    """
+    idx = np.asarray(torch.as_tensor(state_indices).cpu().numpy(), dtype=np.int64)
+    cache = torch.as_tensor(state_cache).detach().cpu().double().numpy()
+    B, T = q.shape[0], q.shape[1]
+    cols = idx.shape[1]
+    acc = None if num_accepted_tokens is None else \
+        np.asarray(torch.as_tensor(num_accepted_tokens).cpu().numpy(), dtype=np.int64)
+    out = np.zeros(tuple(v.shape), dtype=np.float64)
+    new_cache = cache.copy()
+    for b in range(B):
+        a = 1 if acc is None else int(acc[b])
+        if a < 1 or a > cols or idx[b, a - 1] < 0:
+            continue
+        s0 = cache[idx[b, a - 1]][None]
+        for t in range(T):
+            o, sf = recurrence(q[b, :t + 1], k[b, :t + 1], v[b, :t + 1], g[b, :t + 1],
+                               beta[b, :t + 1], scale=scale, use_qk_l2norm=use_qk_l2norm,
+                               initial_state=s0, A_log=A_log, dt_bias=dt_bias,
+                               lower_bound=lower_bound, threads=threads)
+            out[b, t] = o[t]
+            if idx[b, t] >= 0:
+                new_cache[idx[b, t]] = sf[0]
+    return out, new_cache

@@ -381,3 +381,64 @@ def test_checkpoint_skips_zero_unaligned_and_past_the_end():
     cks = oracle.checkpoints(b.q, b.k, b.v, b.g, b.beta, b.cu_seqlens, [0, 32, 128],
                              scale=b.scale, initial_state=b.initial_state)
     assert cks == [None, None, None]
+
+
+# ------------------------------------------------- multi-token (spec) decode
+
+def spec_batch(B, T, hv, seed, slots=40):
+    d = inputs.make_decode(B * T, 1, hv, slots, dtype=torch.float32, seed=seed)
+    rs = lambda x: x.reshape(B, T, *x.shape[1:])
+    cache = d.state_cache * 25.0  # non-symmetric, visible start
+    return rs(d.q), rs(d.k), rs(d.v), rs(d.g), rs(d.beta), cache
+
+
+def test_decode_multi_single_token_is_decode():
+    q, k, v, g, beta, cache = spec_batch(6, 1, 2, 31)
+    idx = torch.tensor([[3], [7], [-1], [0], [12], [20]])
+    o1, c1 = oracle.decode_multi(q, k, v, g, beta, cache, idx)
+    o2, c2 = oracle.decode(q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0], cache, idx[:, 0])
+    assert np.array_equal(o1[:, 0], o2) and np.array_equal(c1, c2)
+
+
+def test_decode_multi_matches_brute_force_per_token():
+    """Every per-token output and stored state against the dense-matrix brute
+    force over the request's tokens so far (T <= 8)."""
+    q, k, v, g, beta, cache = spec_batch(3, 6, 1, 32)
+    idx = torch.tensor([[i * 6 + t for t in range(6)] for i in range(3)])
+    o, c = oracle.decode_multi(q, k, v, g, beta, cache, idx)
+    for b in range(3):
+        s0 = cache[idx[b, 0]].double().numpy()[None]
+        for t in range(6):
+            sl = slice(0, t + 1)
+            ob, sb = forms.brute(f64(q[b, sl]), f64(k[b, sl]), f64(v[b, sl]), f64(g[b, sl]),
+                                 f64(beta[b, sl]), 128 ** -0.5, True, s0)
+            assert rel(o[b, t], ob[t]) < 1e-12
+            assert rel(c[idx[b, t]], sb[0]) < 1e-12
+
+
+def test_decode_multi_accepted_count_continues_the_chain():
+    """A verify window that starts from the state after the a-th accepted
+    token of the previous window equals one pass over the accepted tokens and
+    the new window."""
+    q, k, v, g, beta, cache = spec_batch(2, 8, 2, 33)
+    rows = torch.tensor([[30, 31, 32, 33], [34, 35, 36, 37]])
+    win1 = tuple(x[:, :4] for x in (q, k, v, g, beta))
+    win2 = tuple(x[:, 4:] for x in (q, k, v, g, beta))
+    _, c1 = oracle.decode_multi(*win1, cache, rows)
+    acc = torch.tensor([2, 4])
+    o2, _ = oracle.decode_multi(*win2, torch.as_tensor(c1), rows, acc)
+    for b, a in enumerate([2, 4]):
+        tok = torch.cat([torch.arange(a), torch.arange(4, 8)])
+        ob, _ = oracle.recurrence(q[b, tok], k[b, tok], v[b, tok], g[b, tok], beta[b, tok],
+                                  initial_state=cache[rows[b, 0]][None])
+        assert rel(o2[b], ob[a:]) < 1e-12
+
+
+def test_decode_multi_skips_a_null_start():
+    q, k, v, g, beta, cache = spec_batch(2, 3, 1, 34)
+    idx = torch.tensor([[-1, 5, 6], [7, 8, 9]])
+    o, c = oracle.decode_multi(q, k, v, g, beta, cache, idx)
+    assert np.all(o[0] == 0)
+    assert np.array_equal(c[5], cache[5].double().numpy())
+    o, c = oracle.decode_multi(q, k, v, g, beta, cache, idx, torch.tensor([0, 4]))
+    assert np.all(o == 0) and np.array_equal(c, cache.double().numpy())
