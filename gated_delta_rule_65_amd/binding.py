@@ -80,6 +80,8 @@ class DecodeArgs(ctypes.Structure):
         ("stream", ctypes.c_void_p),
         ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
         ("dt_bias_dtype", ctypes.c_int32), ("lower_bound", ctypes.c_float),
+        ("tokens", ctypes.c_int32), ("state_index_cols", ctypes.c_int32),
+        ("num_accepted_tokens", ctypes.c_void_p),
     ]
 
 
@@ -425,28 +427,41 @@ def chunk_stages(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=No
 
 
 def kda_decode(q, k, v, g, beta, state_cache, state_indices=None, scale=None,
-               use_qk_l2norm=True, output=None, A_log=None, dt_bias=None, lower_bound=-5.0):
-    """One token per request over the paged V-first fp32 state cache, updated
-    in place.  q, k: [N, Hqk, 128] or [N, 1, Hqk, 128]; v, g: [N, Hv, 128] or
-    [N, 1, Hv, 128]; beta: [N, Hv] or [N, 1, Hv]; state_cache
-    [slots, Hv, 128, 128] fp32; state_indices [N] int32/int64 (negative = skip).
-    With A_log / dt_bias, g is a raw gate (the form chunk_kda takes).
-    Returns out shaped like v."""
+               use_qk_l2norm=True, output=None, A_log=None, dt_bias=None, lower_bound=-5.0,
+               num_accepted_tokens=None):
+    """Paged decode over the V-first fp32 state cache, updated in place
+    (gated_delta_rule_decode's argument set).
+
+    One token per request: q, k [N, Hqk, 128] or [N, 1, Hqk, 128]; v, g
+    [N, Hv, 128] or [N, 1, Hv, 128]; beta [N, Hv] or [N, 1, Hv]; state_indices
+    [N] (negative = skip) or None (identity).  T tokens per request (T <= 8,
+    speculative / multi-token): q, k [N, T, Hqk, 128], v, g [N, T, Hv, 128],
+    beta [N, T, Hv], state_indices [N, C >= T]: the request starts from row
+    state_indices[n, a - 1] (a = num_accepted_tokens[n], column 0 without it)
+    and writes its state after token t to row state_indices[n, t].  With
+    A_log / dt_bias, g is a raw gate (the form chunk_kda takes).  Returns out
+    shaped like v."""
     shape_v = v.shape
     if q.dim() == 4:
-        _need(q.shape[1] == 1, "kda_decode takes one token per request (T = 1)",
-              NotImplementedError)
-        q, k, v, g = q[:, 0], k[:, 0], v[:, 0], g[:, 0]
-        if beta.dim() == 3:
-            beta = beta[:, 0]
-    _need(q.dim() == 3 and q.shape[-1] == D, "q must be [N, Hqk, 128]")
-    _need(k.shape == q.shape, "k must match q")
-    n, hqk = q.shape[0], q.shape[1]
-    _need(v.dim() == 3 and v.shape[0] == n and v.shape[-1] == D, "v must be [N, Hv, 128]")
-    hv = v.shape[1]
-    _need(g.shape == v.shape, "g must have the same shape as v")
+        T = q.shape[1]
+        _need(1 <= T <= 8, "kda_decode takes 1 to 8 tokens per request", NotImplementedError)
+        _need(q.shape[-1] == D, "q must be [N, T, Hqk, 128]")
+        _need(k.shape == q.shape, "k must match q")
+        _need(v.dim() == 4 and v.shape[:2] == q.shape[:2] and v.shape[-1] == D,
+              "v must be [N, T, Hv, 128]")
+        n, hqk, hv = q.shape[0], q.shape[2], v.shape[2]
+        _need(g.shape == v.shape, "g must have the same shape as v")
+        _need(tuple(beta.shape) == (n, T, hv), "beta must be [N, T, Hv]")
+    else:
+        T = 1
+        _need(q.dim() == 3 and q.shape[-1] == D, "q must be [N, Hqk, 128]")
+        _need(k.shape == q.shape, "k must match q")
+        n, hqk = q.shape[0], q.shape[1]
+        _need(v.dim() == 3 and v.shape[0] == n and v.shape[-1] == D, "v must be [N, Hv, 128]")
+        hv = v.shape[1]
+        _need(g.shape == v.shape, "g must have the same shape as v")
+        _need(tuple(beta.shape) == (n, hv), "beta must be [N, Hv]")
     _need(hv % hqk == 0, f"Expected HV to be divisible by H, got HV={hv}, H={hqk}.")
-    _need(tuple(beta.shape) == (n, hv), "beta must be [N, Hv]")
     _need(q.dtype in _DTYPES, f"unsupported dtype {q.dtype}", TypeError)
     for name, t in (("k", k), ("v", v), ("g", g), ("beta", beta)):
         _need(t.dtype == q.dtype, f"{name} must have q's dtype", TypeError)
@@ -456,17 +471,30 @@ def kda_decode(q, k, v, g, beta, state_cache, state_indices=None, scale=None,
           "state must have shape [pool, HV, V, K]")
     _need(state_cache.shape[0] > 0, "state pool must contain at least one slot.")
     dev = q.device
-    idx = None
+    idx, cols = None, 0
     if state_indices is not None:
-        _need(state_indices.dim() == 1 and state_indices.shape[0] == n,
-              f"state_indices must have shape [{n}]")
+        _need(state_indices.dim() in (1, 2) and state_indices.shape[0] == n,
+              f"state_indices must have shape [{n}] or [{n}, T]")
         _need(state_indices.dtype in (torch.int32, torch.int64),
               "state_indices must have dtype torch.int32 or torch.int64", ValueError)
+        if state_indices.dim() == 2:
+            cols = state_indices.shape[1]
+            _need(cols >= T, f"state_indices needs at least {T} columns, got {cols}")
         idx = state_indices.to(device=dev, dtype=torch.int32).contiguous()
+    _need(cols > 0 or (T == 1 and num_accepted_tokens is None),
+          "1D state_indices only support non-speculative single-token decode; use [B, T] "
+          "state_indices for speculative or multi-token decode.")
+    acc = None
+    if num_accepted_tokens is not None:
+        _need(tuple(num_accepted_tokens.shape) == (n,),
+              f"num_accepted_tokens must have shape [B={n}]")
+        _need(num_accepted_tokens.dtype in (torch.int32, torch.int64),
+              "num_accepted_tokens must be integer")
+        acc = num_accepted_tokens.to(device=dev, dtype=torch.int32).contiguous()
     if output is None:
-        output = torch.empty((n, hv, D), dtype=q.dtype, device=dev)
-    _need(output.numel() == n * hv * D and output.dtype == q.dtype,
-          "output must be [N, Hv, 128] of q's dtype")
+        output = torch.empty(tuple(shape_v), dtype=q.dtype, device=dev)
+    _need(output.numel() == n * T * hv * D and output.dtype == q.dtype,
+          "output must be shaped like v, of q's dtype")
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta),
                     ("state_cache", state_cache), ("output", output)):
         _contig(name, t)
@@ -485,6 +513,7 @@ def kda_decode(q, k, v, g, beta, state_cache, state_indices=None, scale=None,
     a.out = _ptr(output)
     a.stream = _stream(dev)
     _set_gate(a, _gate(A_log, dt_bias, lower_bound, hv, dev))
+    a.tokens, a.state_index_cols, a.num_accepted_tokens = T, cols, _ptr(acc)
     st = lib.kda_decode(ctypes.byref(a))
     if st != KDA_OK:
         _raise(lib, st)

@@ -315,6 +315,20 @@ KDA_API kda_status kda_decode(const kda_decode_args* a) {
     const kda_status gs = check_gate(a->A_log, a->dt_bias, a->dt_bias_dtype, a->lower_bound);
     if (gs != KDA_OK) return gs;
   }
+  if (a->tokens < 0 || a->tokens > 8)
+    return fail(KDA_ERR_UNSUPPORTED, "tokens per request must lie in [0, 8], got %d", a->tokens);
+  const int T = a->tokens > 1 ? a->tokens : 1;
+  if (a->state_index_cols < 0) return fail(KDA_ERR_SHAPE, "state_index_cols must be >= 0");
+  if (a->state_index_cols > 0 && !a->state_indices)
+    return fail(KDA_ERR_SHAPE, "state_index_cols needs state_indices");
+  if (a->state_index_cols > 0 && a->state_index_cols < T)
+    return fail(KDA_ERR_SHAPE, "state_indices needs at least %d columns, got %d", T,
+                a->state_index_cols);
+  if ((T > 1 || a->num_accepted_tokens) && a->state_index_cols == 0)
+    return fail(KDA_ERR_SHAPE,
+                "multi-token or speculative decode needs [n, T] state_indices");
+  if ((size_t)a->n * (size_t)T * (size_t)a->hv > 0x7fffffffu)
+    return fail(KDA_ERR_UNSUPPORTED, "n * tokens * hv above 2^31-1");
   if (a->n == 0) return ok();
   if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->out || !a->state_cache)
     return fail(KDA_ERR_ARG, "q, k, v, g, beta, out and state_cache must be non-NULL");
@@ -325,6 +339,9 @@ KDA_API kda_status kda_decode(const kda_decode_args* a) {
   L.use_l2 = a->use_qk_l2norm ? 1 : 0; L.num_slots = a->num_slots; L.scale = a->scale;
   L.stream = a->stream;
   L.gate = gate_of(a->A_log, a->dt_bias, a->dt_bias_dtype, a->lower_bound);
+  L.tokens = T;
+  L.cols = a->state_index_cols;
+  L.accepted = a->num_accepted_tokens;
   hipError_t e = kda::launch_decode(L);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -124,9 +124,133 @@ __global__ __launch_bounds__(256) void decode_kernel(
   }
 }
 
+// Multi-token (speculative) decode: the same row mapping, with the state kept
+// in registers across the request's tokens.  Request req starts from row
+// idx[req][acc[req] - 1] (idx[req][0] without counts); after token t the state
+// is written to row idx[req][t] when that row is in the pool.  A start row
+// outside the pool (or a count outside [1, cols]) zeroes the request's output
+// rows and touches no state.  This is gated_delta_rule_decode's [B, T]
+// state_indices with num_accepted_tokens (page "mate.kda").
+template <typename T>
+__global__ __launch_bounds__(256) void decode_multi_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ g, const T* __restrict__ beta, float* __restrict__ cache,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ acc, T* __restrict__ out,
+    int ntok, int cols, int hqk, int hv, float scale, int use_l2, int num_slots,
+    const GateArgs ga) {
+  const int unit = blockIdx.x;
+  const int req = unit / hv, h = unit - req * hv;
+  const int hq = h / (hv / hqk);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 15, rsub = lane >> 4;
+  const int32_t* ir = idx + (size_t)req * cols;
+  int row0 = -1;
+  if (acc) {
+    const int a = acc[req];
+    if (a >= 1 && a <= cols) row0 = ir[a - 1];
+  } else {
+    row0 = ir[0];
+  }
+  if (row0 < 0 || row0 >= num_slots) {
+    if (tid < D)
+      for (int t = 0; t < ntok; ++t)
+        out[(((size_t)req * ntok + t) * hv + h) * D + tid] = from_f32<T>(0.0f);
+    return;
+  }
+  const float* st0 = cache + ((size_t)row0 * hv + h) * (size_t)(D * D);
+  float4 hs[8][2];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int r = 16 * s + 4 * wave + rsub;
+    const float4* row = reinterpret_cast<const float4*>(st0 + r * D);
+    hs[s][0] = row[j];
+    hs[s][1] = row[16 + j];
+  }
+  const float ga_a = ga.a_log ? exp2_fast(ga.a_log[h] * LOG2E) : 0.f;  // exp(A_log[h])
+  for (int t = 0; t < ntok; ++t) {
+    const size_t tok = (size_t)req * ntok + t;
+    const T* qp = q + (tok * hqk + hq) * D;
+    const T* kp = k + (tok * hqk + hq) * D;
+    const T* gp = g + (tok * hv + h) * D;
+    const T* vp = v + (tok * hv + h) * D;
+    float qv[8], kv[8], al[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = (e < 4) ? (4 * j + e) : (64 + 4 * j + e - 4);
+      qv[e] = to_f32(qp[c]);
+      kv[e] = to_f32(kp[c]);
+      float gl = to_f32(gp[c]);
+      if (ga.a_log) gl = gate_apply(gl, ga_a, gate_bias(ga, h, c), ga.lower_bound);
+      al[e] = exp2_fast(gl * LOG2E);
+    }
+    float vr[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) vr[s] = to_f32(vp[16 * s + 4 * wave + rsub]);
+    const float b = sigmoid(to_f32(beta[tok * hv + h]));
+    if (use_l2) {
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sq += qv[e] * qv[e];
+        sk += kv[e] * kv[e];
+      }
+      sq = row_sum16(sq);
+      sk = row_sum16(sk);
+      const float rq = rsqrtf(sq + L2_EPS), rk = rsqrtf(sk + L2_EPS);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qv[e] *= rq;
+        kv[e] *= rk;
+      }
+    }
+    float kq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kq += kv[e] * qv[e];
+    kq = row_sum16(kq);
+    const int rt = ir[t];
+    float* dst = (rt >= 0 && rt < num_slots) ? cache + ((size_t)rt * hv + h) * (size_t)(D * D)
+                                             : nullptr;
+    T* o = out + (tok * hv + h) * D;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      float x[8] = {hs[s][0].x, hs[s][0].y, hs[s][0].z, hs[s][0].w,
+                    hs[s][1].x, hs[s][1].y, hs[s][1].z, hs[s][1].w};
+      float pk = 0.f, pq = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] *= al[e];
+        pk += x[e] * kv[e];
+        pq += x[e] * qv[e];
+      }
+      pk = row_sum16(pk);
+      pq = row_sum16(pq);
+      const float u = b * (vr[s] - pk);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] += u * kv[e];
+      hs[s][0] = make_float4(x[0], x[1], x[2], x[3]);
+      hs[s][1] = make_float4(x[4], x[5], x[6], x[7]);
+      const int r = 16 * s + 4 * wave + rsub;
+      if (dst) {
+        float4* row = reinterpret_cast<float4*>(dst + r * D);
+        row[j] = hs[s][0];
+        row[16 + j] = hs[s][1];
+      }
+      if (j == 0) o[r] = from_f32<T>(scale * (pq + u * kq));
+    }
+  }
+}
+
 template <typename T>
 static hipError_t launch_decode_t(const DecodeLaunch& L) {
   const dim3 grid((unsigned)((size_t)L.n * L.hv)), block(256);
+  if (L.tokens > 1 || L.cols > 0) {
+    hipLaunchKernelGGL(decode_multi_kernel<T>, grid, block, 0, (hipStream_t)L.stream,
+                       (const T*)L.q, (const T*)L.k, (const T*)L.v, (const T*)L.g,
+                       (const T*)L.beta, L.cache, L.idx, L.accepted, (T*)L.out, L.tokens,
+                       L.cols, L.hqk, L.hv, L.scale, L.use_l2, L.num_slots, L.gate);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(decode_kernel<T>, grid, block, 0, (hipStream_t)L.stream,
                      (const T*)L.q, (const T*)L.k, (const T*)L.v, (const T*)L.g,
                      (const T*)L.beta, L.cache, L.idx, (T*)L.out, L.hqk, L.hv, L.scale,

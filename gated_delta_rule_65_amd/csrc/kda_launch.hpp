@@ -16,6 +16,9 @@ struct DecodeLaunch {
   float scale;
   void* stream;
   GateArgs gate;  // optional gate parameters (a_log == NULL: none)
+  int tokens;                 // tokens per request (1..8)
+  int cols;                   // columns of a 2-D state_indices, 0 for 1-D
+  const int32_t* accepted;    // [n] accepted-token counts or NULL
 };
 hipError_t launch_decode(const DecodeLaunch& L);
 

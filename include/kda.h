@@ -258,6 +258,21 @@ typedef struct kda_decode_args {
   const void *dt_bias;         /* (device) [Hv, 128] of dt_bias_dtype, or NULL */
   int32_t dt_bias_dtype;       /* KDA_F32 or KDA_BF16 */
   float lower_bound;
+  /* Multi-token (speculative) decode, optional: gated_delta_rule_decode's
+     [B, T] state_indices and num_accepted_tokens (page "mate.kda").  With
+     tokens = T in [2, 8] (0 or 1: one token) q, k, v, g carry T tokens per
+     request ([n, T, H, 128], beta [n, T, Hv], out [n, T, Hv, 128]).  With
+     state_index_cols > 0 (>= T) state_indices is [n, state_index_cols]:
+     request n starts from row state_indices[n][a - 1], a =
+     num_accepted_tokens[n] (column 0 when that array is NULL), runs its
+     tokens in order and after token t writes its state to row
+     state_indices[n][t] when 0 <= that index < num_slots.  A start row
+     outside [0, num_slots) or a count outside [1, state_index_cols] skips the
+     request (zero output rows, no state traffic).  T > 1 and
+     num_accepted_tokens need the 2-D index array. */
+  int32_t tokens;
+  int32_t state_index_cols;            /* 0: state_indices is [n] (or NULL) */
+  const int32_t *num_accepted_tokens;  /* (device) [n] or NULL */
 } kda_decode_args;
 
 kda_status kda_decode(const kda_decode_args *a);

@@ -193,9 +193,20 @@ def test_binding_decode_checks():
     cache = cpu((8, 4, 128, 128), torch.float32)
     with pytest.raises(ValueError, match="divisible"):
         B.kda_decode(q, q, cpu((4, 3, 128)), cpu((4, 3, 128)), cpu((4, 3)), cache)
-    with pytest.raises(NotImplementedError):
+    # two tokens per request need [N, T] state indices; more than 8 are not served
+    with pytest.raises(ValueError, match="state_indices"):
         B.kda_decode(cpu((4, 2, 2, 128)), cpu((4, 2, 2, 128)), cpu((4, 2, 4, 128)),
                      cpu((4, 2, 4, 128)), cpu((4, 2, 4)), cache)
+    with pytest.raises(ValueError, match="columns"):
+        B.kda_decode(cpu((4, 2, 2, 128)), cpu((4, 2, 2, 128)), cpu((4, 2, 4, 128)),
+                     cpu((4, 2, 4, 128)), cpu((4, 2, 4)), cache,
+                     torch.zeros((4, 1), dtype=torch.int32))
+    with pytest.raises(NotImplementedError):
+        B.kda_decode(cpu((4, 9, 2, 128)), cpu((4, 9, 2, 128)), cpu((4, 9, 4, 128)),
+                     cpu((4, 9, 4, 128)), cpu((4, 9, 4)), cache)
+    with pytest.raises(ValueError, match="single-token"):
+        B.kda_decode(q, q, v, v, cpu((4, 4)), cache, torch.zeros(4, dtype=torch.int32),
+                     num_accepted_tokens=torch.ones(4, dtype=torch.int32))
     with pytest.raises(ValueError, match="pool"):
         B.kda_decode(q, q, v, v, cpu((4, 4)), cpu((8, 4, 128, 64), torch.float32))
     with pytest.raises(NotImplementedError):
@@ -270,3 +281,16 @@ def test_checkpoint_rows_with_indices_pass_checks(lib):
     a = chunk_args(checkpoint_state=FAKE, checkpoint_offsets=FAKE, checkpoint_state_indices=FAKE,
                    checkpoint_rows=1)
     assert ws_size(lib, a)[0] == B.KDA_OK
+
+
+
+@pytest.mark.parametrize("fields,status", [
+    (dict(tokens=9, state_index_cols=9, state_indices=FAKE), B.KDA_ERR_UNSUPPORTED),
+    (dict(tokens=2), B.KDA_ERR_SHAPE),                                  # needs 2-D indices
+    (dict(tokens=4, state_index_cols=3, state_indices=FAKE), B.KDA_ERR_SHAPE),
+    (dict(state_index_cols=2), B.KDA_ERR_SHAPE),                        # cols without indices
+    (dict(num_accepted_tokens=FAKE, state_indices=FAKE), B.KDA_ERR_SHAPE),  # 1-D with counts
+], ids=["t9", "t2_1d", "cols_short", "cols_no_idx", "acc_1d"])
+def test_multi_token_decode_checks(lib, fields, status):
+    a = decode_args(**fields)
+    assert lib.kda_decode(ctypes.byref(a)) == status

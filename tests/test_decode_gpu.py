@@ -150,3 +150,73 @@ def test_decode_gate_parameters(dtype, bias_dtype):
     rows = idx[live].long()
     assert rel(cache.cpu()[rows].numpy(), ref_cache[rows.numpy()]) < 1e-5
     assert np.all(out[5].float().cpu().numpy() == 0.0)
+
+
+# ------------------------------------------------- multi-token (spec) decode
+
+def spec_case(B, T, hqk, hv, slots, dtype, seed):
+    d = inputs.make_decode(B * T, hqk, hv, slots, dtype=dtype, seed=seed)
+    rs = lambda x: x.reshape(B, T, *x.shape[1:]).contiguous()
+    return rs(d.q), rs(d.k), rs(d.v), rs(d.g), rs(d.beta), d.state_cache
+
+
+def run_spec(q, k, v, g, beta, cache, idx, acc=None, **gate):
+    cd = cache.to(DEV)
+    out = B.kda_decode(*(t.to(DEV) for t in (q, k, v, g, beta)), cd, idx.to(DEV),
+                       num_accepted_tokens=None if acc is None else acc.to(DEV), **gate)
+    torch.cuda.synchronize()
+    og = {k_: (v_.double() if isinstance(v_, torch.Tensor) else v_) for k_, v_ in gate.items()}
+    for k_ in ("A_log", "dt_bias"):
+        if k_ in og:
+            og[k_] = og[k_].cpu()
+    ro, rc = oracle.decode_multi(q, k, v, g, beta, cache, idx, acc, **og)
+    return out.float().cpu().numpy(), ro, cd.cpu().numpy(), rc
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16])
+@pytest.mark.parametrize("T,hqk,hv", [(4, 1, 2), (8, 2, 4), (3, 4, 4)])
+def test_multi_token_decode_matches_oracle(dtype, T, hqk, hv):
+    Bn = 7
+    q, k, v, g, beta, cache = spec_case(Bn, T, hqk, hv, 70, dtype, seed=20 + T)
+    idx = torch.arange(Bn * T, dtype=torch.int32).reshape(Bn, T)
+    idx[2, 1] = -1                      # no store after that token
+    idx[4, 0] = -1                      # null start: skipped request
+    print("spec decode", dtype, T, hqk, hv, flush=True)
+    o, ro, c, rc = run_spec(q, k, v, g, beta, cache, idx)
+    tol = 1e-4 if dtype == torch.float32 else 1e-2
+    assert rel(o, ro) < tol
+    assert np.all(o[4] == 0)
+    assert rel(c, rc) < 1e-5
+
+
+def test_multi_token_decode_accepted_counts():
+    Bn, T = 6, 4
+    q, k, v, g, beta, cache = spec_case(Bn, T, 1, 2, 40, torch.bfloat16, seed=41)
+    idx = torch.arange(Bn * T, dtype=torch.int32).reshape(Bn, T)
+    acc = torch.tensor([1, 2, 3, 4, 0, 5], dtype=torch.int32)   # 0 and 5: skipped
+    o, ro, c, rc = run_spec(q, k, v, g, beta, cache, idx, acc)
+    assert rel(o, ro) < 1e-2
+    assert np.all(o[4] == 0) and np.all(o[5] == 0)
+    assert rel(c, rc) < 1e-5
+
+
+def test_multi_token_decode_single_column_equals_single_token():
+    q, k, v, g, beta, cache = spec_case(9, 1, 2, 4, 20, torch.bfloat16, seed=42)
+    idx = torch.randperm(20)[:9].to(torch.int32)
+    c1, c2 = cache.to(DEV), cache.to(DEV)
+    o1 = B.kda_decode(*(t[:, 0].to(DEV) for t in (q, k, v, g, beta)), c1, idx.to(DEV))
+    o2 = B.kda_decode(*(t.to(DEV) for t in (q, k, v, g, beta)), c2, idx[:, None].to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(o1.cpu(), o2[:, 0].cpu()) and torch.equal(c1.cpu(), c2.cpu())
+
+
+def test_multi_token_decode_with_gate():
+    Bn, T = 5, 6
+    q, k, v, g, beta, cache = spec_case(Bn, T, 1, 2, 40, torch.bfloat16, seed=43)
+    gen = torch.Generator().manual_seed(44)
+    g = torch.randn(g.shape, generator=gen).to(torch.bfloat16)
+    idx = torch.arange(Bn * T, dtype=torch.int32).reshape(Bn, T)
+    gate = dict(A_log=(torch.rand(2, generator=gen) - 0.5).to(DEV),
+                dt_bias=torch.randn(2, 128, generator=gen).to(DEV), lower_bound=-3.0)
+    o, ro, c, rc = run_spec(q, k, v, g, beta, cache, idx, **gate)
+    assert rel(o, ro) < 1e-2 and rel(c, rc) < 1e-5
