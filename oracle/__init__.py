@@ -230,9 +230,26 @@ def checkpoints(q, k, v, g, beta, cu_seqlens, offsets, scale=None, use_qk_l2norm
     return res
 
 
+def round_bf16(x):
+    """fp64 -> nearest bf16 value (ties to even), returned as fp64.  Done in
+    integer arithmetic on the fp64 bit pattern (no intermediate fp32
+    rounding): bf16 keeps the top 7 of fp64's 52 mantissa bits, with fp32's
+    exponent range (values below bf16's smallest normal are flushed to
+    zero here, far below anything a state holds)."""
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    bits = a.view(np.uint64)
+    drop = np.uint64(52 - 7)
+    half = np.uint64(1) << (drop - np.uint64(1))
+    lsb = (bits >> drop) & np.uint64(1)
+    r = ((bits + half - np.uint64(1) + lsb) >> drop) << drop
+    out = r.view(np.float64).copy()
+    out[np.abs(a) < 2.0 ** -126] = 0.0
+    return out
+
+
 def decode_multi(q, k, v, g, beta, state_cache, state_indices, num_accepted_tokens=None,
                  scale=None, use_qk_l2norm=True, A_log=None, dt_bias=None, lower_bound=-5.0,
-                 threads=None):
+                 threads=None, state_bf16=False):
     """Multi-token (speculative) decode over a paged V-first state cache.
 
     q, k: [B, T, Hqk, 128]; v, g: [B, T, Hv, 128]; beta: [B, T, Hv];
@@ -243,8 +260,12 @@ def decode_multi(q, k, v, g, beta, state_cache, state_indices, num_accepted_toke
     state_indices[b, t] when that index is >= 0.  A start row < 0 (or an
     accepted count outside [1, C]) skips the request: zero outputs, no writes.
     Each state is the recurrence over the request's tokens so far (computed
-    here one prefix at a time).  Returns (out [B, T, Hv, 128] fp64, new cache
-    fp64).
+    here one prefix at a time).  With state_bf16 the state is stored in bf16:
+    it is widened for each token's arithmetic and rounded back (to nearest
+    even) after each token, as repeated single-token decode over a bf16 cache
+    would do (mate.kda, gated_delta_rule_decode's bf16 state); outputs read
+    the unrounded state of their token.  Returns (out [B, T, Hv, 128] fp64,
+    new cache fp64).
     """
     idx = np.asarray(torch.as_tensor(state_indices).cpu().numpy(), dtype=np.int64)
     cache = torch.as_tensor(state_cache).detach().cpu().double().numpy()
@@ -259,6 +280,19 @@ def decode_multi(q, k, v, g, beta, state_cache, state_indices, num_accepted_toke
         if a < 1 or a > cols or idx[b, a - 1] < 0:
             continue
         s0 = cache[idx[b, a - 1]][None]
+        if state_bf16:
+            s = round_bf16(s0)
+            for t in range(T):
+                o, sf = recurrence(q[b, t:t + 1], k[b, t:t + 1], v[b, t:t + 1], g[b, t:t + 1],
+                                   beta[b, t:t + 1], scale=scale,
+                                   use_qk_l2norm=use_qk_l2norm, initial_state=s,
+                                   A_log=A_log, dt_bias=dt_bias, lower_bound=lower_bound,
+                                   threads=threads)
+                out[b, t] = o[0]
+                s = round_bf16(sf)
+                if idx[b, t] >= 0:
+                    new_cache[idx[b, t]] = s[0]
+            continue
         for t in range(T):
             o, sf = recurrence(q[b, :t + 1], k[b, :t + 1], v[b, :t + 1], g[b, :t + 1],
                                beta[b, :t + 1], scale=scale, use_qk_l2norm=use_qk_l2norm,

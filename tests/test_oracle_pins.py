@@ -442,3 +442,47 @@ def test_decode_multi_skips_a_null_start():
     assert np.array_equal(c[5], cache[5].double().numpy())
     o, c = oracle.decode_multi(q, k, v, g, beta, cache, idx, torch.tensor([0, 4]))
     assert np.all(o == 0) and np.array_equal(c, cache.double().numpy())
+
+
+# ---------------------------------------------------------- bf16 state storage
+
+def test_round_bf16_matches_torch_on_fp32_values():
+    """On fp32 inputs the fp64-bit rounding agrees with torch's fp32 -> bf16
+    conversion (round to nearest even), ties included."""
+    gen = torch.Generator().manual_seed(50)
+    x = torch.randn(20000, generator=gen) * 10.0 ** torch.randint(-6, 6, (20000,), generator=gen)
+    ties = torch.tensor([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 0.0])
+    x = torch.cat([x, ties]).float()
+    want = x.to(torch.bfloat16).double().numpy()
+    assert np.array_equal(oracle.round_bf16(x.double().numpy()), want)
+
+
+def test_bf16_state_multi_token_equals_repeated_single_token():
+    """A window over a bf16 cache equals one-token steps, each storing the
+    rounded state in the cache (the page's description of bf16 state)."""
+    q, k, v, g, beta, cache = spec_batch(3, 5, 2, 35)
+    cache = torch.as_tensor(oracle.round_bf16(cache.double().numpy()))
+    idx = torch.arange(15).reshape(3, 5)
+    o, c = oracle.decode_multi(q, k, v, g, beta, cache, idx, state_bf16=True)
+    cur = cache.double().numpy().copy()
+    for t in range(5):
+        rows = idx[:, t - 1] if t else idx[:, 0]
+        start = cur[rows.numpy()]
+        ot, st = oracle.recurrence(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t],
+                                   cu_seqlens=np.arange(4), initial_state=start)
+        assert rel(o[:, t], ot) < 1e-14
+        cur[idx[:, t].numpy()] = oracle.round_bf16(st)
+    assert np.array_equal(c, cur)
+
+
+def test_bf16_state_frozen_when_nothing_writes():
+    """b = 0 and g = 0: the bf16 state passes through every token unchanged."""
+    q, k, v, g, beta, cache = spec_batch(2, 4, 1, 36)
+    cache = torch.as_tensor(oracle.round_bf16(cache.double().numpy()))
+    beta = torch.full_like(beta, -1e4)
+    g = torch.zeros_like(g)
+    idx = torch.arange(8).reshape(2, 4)
+    _, c = oracle.decode_multi(q, k, v, g, beta, cache, idx, state_bf16=True)
+    for b in range(2):
+        for t in range(4):
+            assert np.array_equal(c[idx[b, t]], cache[idx[b, 0]].numpy())
