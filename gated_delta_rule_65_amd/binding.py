@@ -53,6 +53,7 @@ class ChunkArgs(ctypes.Structure):
         ("dt_bias_dtype", ctypes.c_int32), ("lower_bound", ctypes.c_float),
         ("checkpoint_state", ctypes.c_void_p), ("checkpoint_offsets", ctypes.c_void_p),
         ("checkpoint_state_indices", ctypes.c_void_p), ("checkpoint_rows", ctypes.c_int32),
+        ("state_dtype", ctypes.c_int32),
     ]
 
 
@@ -81,7 +82,7 @@ class DecodeArgs(ctypes.Structure):
         ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
         ("dt_bias_dtype", ctypes.c_int32), ("lower_bound", ctypes.c_float),
         ("tokens", ctypes.c_int32), ("state_index_cols", ctypes.c_int32),
-        ("num_accepted_tokens", ctypes.c_void_p),
+        ("num_accepted_tokens", ctypes.c_void_p), ("state_dtype", ctypes.c_int32),
     ]
 
 
@@ -228,6 +229,8 @@ def _chunk_struct(q, k, v, g, beta, out, cu, N, T, hqk, hv, scale, l2, init, fin
     a.scale = scale
     a.use_qk_l2norm = 1 if l2 else 0
     a.initial_state, a.final_state = _ptr(init), _ptr(fin)
+    st = init if init is not None else fin
+    a.state_dtype = _DTYPES[st.dtype] if st is not None else 0
     a.state_cache, a.state_indices, a.has_initial_state = _ptr(cache), _ptr(idx), _ptr(has_init)
     a.num_slots = 0 if cache is None else cache.shape[0]
     a.out = _ptr(out)
@@ -290,20 +293,27 @@ def _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state, c
         _need(idx.numel() == N and hinit.numel() == N,
               "state_indices and has_initial_state need one entry per sequence")
     else:
+        # states are fp32 or of q's dtype (chunk_kda's rule), both alike; a new
+        # final state takes the initial state's dtype, else fp32
+        ok_state = (torch.float32, q.dtype)
         if initial_state is not None:
-            _need(initial_state.dtype == torch.float32, "initial_state must be float32",
-                  NotImplementedError)
+            _need(initial_state.dtype in ok_state,
+                  f"initial_state must have dtype {q.dtype} or torch.float32.", TypeError)
             _need(tuple(initial_state.shape) == (N, hv, D, D),
                   f"initial_state must be [{N}, {hv}, 128, 128]")
             init = _contig("initial_state", initial_state)
         if output_final_state:
             if final_state is None:
-                final_state = torch.empty((N, hv, D, D), device=dev, dtype=torch.float32)
-            _need(final_state.dtype == torch.float32, "final_state must be float32",
-                  NotImplementedError)
+                sdt = initial_state.dtype if initial_state is not None else torch.float32
+                final_state = torch.empty((N, hv, D, D), device=dev, dtype=sdt)
+            _need(final_state.dtype in ok_state,
+                  f"final_state must have dtype {q.dtype} or torch.float32.", TypeError)
             _need(tuple(final_state.shape) == (N, hv, D, D),
                   f"final_state must be [{N}, {hv}, 128, 128]")
             fin = _contig("final_state", final_state)
+        if init is not None and fin is not None:
+            _need(init.dtype == fin.dtype, "initial_state and final_state must have the same dtype.",
+                  TypeError)
     if output is None:
         output = torch.empty_like(v)
     _need(output.shape == v.shape or (varlen and output.shape == v3.shape),
@@ -465,8 +475,8 @@ def kda_decode(q, k, v, g, beta, state_cache, state_indices=None, scale=None,
     _need(q.dtype in _DTYPES, f"unsupported dtype {q.dtype}", TypeError)
     for name, t in (("k", k), ("v", v), ("g", g), ("beta", beta)):
         _need(t.dtype == q.dtype, f"{name} must have q's dtype", TypeError)
-    _need(state_cache.dtype == torch.float32, "state_cache must be float32",
-          NotImplementedError)
+    _need(state_cache.dtype in (torch.float32, torch.bfloat16),
+          "state must have dtype torch.float32 or torch.bfloat16", ValueError)
     _need(state_cache.dim() == 4 and tuple(state_cache.shape[1:]) == (hv, D, D),
           "state must have shape [pool, HV, V, K]")
     _need(state_cache.shape[0] > 0, "state pool must contain at least one slot.")
@@ -514,6 +524,7 @@ def kda_decode(q, k, v, g, beta, state_cache, state_indices=None, scale=None,
     a.stream = _stream(dev)
     _set_gate(a, _gate(A_log, dt_bias, lower_bound, hv, dev))
     a.tokens, a.state_index_cols, a.num_accepted_tokens = T, cols, _ptr(acc)
+    a.state_dtype = _DTYPES[state_cache.dtype]
     st = lib.kda_decode(ctypes.byref(a))
     if st != KDA_OK:
         _raise(lib, st)

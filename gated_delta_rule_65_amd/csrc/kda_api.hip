@@ -85,7 +85,11 @@ kda_status check_chunk(const kda_chunk_args* a, bool need_ptrs) {
     if (a->num_seqs > 0 && a->total_tokens % a->num_seqs != 0)
       return fail(KDA_ERR_SHAPE, "dense batch: total_tokens %% num_seqs != 0");
   }
+  if (a->state_dtype != KDA_F32 && a->state_dtype != a->dtype)
+    return fail(KDA_ERR_DTYPE, "initial/final state must be fp32 or of the input dtype");
   const bool paged = a->state_cache != nullptr;
+  if (paged && a->state_dtype != KDA_F32)
+    return fail(KDA_ERR_UNSUPPORTED, "the paged chunk state is fp32");
   if (paged) {
     if (a->initial_state || a->final_state)
       return fail(KDA_ERR_SHAPE, "state_cache replaces initial_state/final_state");
@@ -268,6 +272,7 @@ KDA_API kda_status kda_chunk_fwd(const kda_chunk_args* a) {
   L.total_tokens = a->total_tokens; L.max_chunks = W.max_chunks;
   L.scale = a->scale;
   L.init = a->initial_state; L.fin = a->final_state;
+  L.state_bf16 = a->state_dtype == KDA_BF16 ? 1 : 0;
   L.cache = a->state_cache; L.slots = a->state_indices; L.has_init = a->has_initial_state;
   L.num_slots = a->num_slots;
   L.out = a->out;
@@ -315,6 +320,8 @@ KDA_API kda_status kda_decode(const kda_decode_args* a) {
     const kda_status gs = check_gate(a->A_log, a->dt_bias, a->dt_bias_dtype, a->lower_bound);
     if (gs != KDA_OK) return gs;
   }
+  if (a->state_dtype != KDA_F32 && a->state_dtype != KDA_BF16)
+    return fail(KDA_ERR_DTYPE, "state_cache must be fp32 or bf16");
   if (a->tokens < 0 || a->tokens > 8)
     return fail(KDA_ERR_UNSUPPORTED, "tokens per request must lie in [0, 8], got %d", a->tokens);
   const int T = a->tokens > 1 ? a->tokens : 1;
@@ -335,6 +342,7 @@ KDA_API kda_status kda_decode(const kda_decode_args* a) {
   kda::DecodeLaunch L;
   L.q = a->q; L.k = a->k; L.v = a->v; L.g = a->g; L.beta = a->beta;
   L.cache = a->state_cache; L.idx = a->state_indices; L.out = a->out;
+  L.state_bf16 = a->state_dtype == KDA_BF16 ? 1 : 0;
   L.dtype = a->dtype; L.n = a->n; L.hqk = a->hqk; L.hv = a->hv;
   L.use_l2 = a->use_qk_l2norm ? 1 : 0; L.num_slots = a->num_slots; L.scale = a->scale;
   L.stream = a->stream;

@@ -890,8 +890,9 @@ struct WalkArgs {
   const int32_t* offs;
   int N, hv;
   float scale;
-  const float* init;
-  float* fin;
+  const void* init;  // dense initial / final states: fp32, or bf16 with state_bf16
+  void* fin;
+  int state_bf16;
   float* cache;
   const int32_t* slots;
   const uint8_t* has_init;
@@ -906,6 +907,37 @@ struct WalkArgs {
 };
 
 constexpr size_t PLANE = (size_t)D * D;
+
+// Four values (elements off .. off + 3) of an fp32 or bf16 state plane; bf16
+// is widened exactly on load and rounded to nearest even on store.
+__device__ __forceinline__ f32x4_t plane_load4(const void* p, size_t off, bool bf) {
+  if (bf) {
+    const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16*>(p) + off);
+    return f32x4_t{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                   __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+  }
+  const float4 x = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + off);
+  return f32x4_t{x.x, x.y, x.z, x.w};
+}
+__device__ __forceinline__ void plane_store4(void* p, size_t off, bool bf, const f32x4_t& v) {
+  if (bf) {
+    *reinterpret_cast<uint2*>(reinterpret_cast<bf16*>(p) + off) =
+        make_uint2((uint32_t)bf16_bits(v[0]) | ((uint32_t)bf16_bits(v[1]) << 16),
+                   (uint32_t)bf16_bits(v[2]) | ((uint32_t)bf16_bits(v[3]) << 16));
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p) + off) =
+        make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+// Plane (n, h) of a dense [N, hv, 128, 128] state array of either storage.
+__device__ __forceinline__ const void* dense_plane(const void* base, size_t plane, bool bf) {
+  return bf ? (const void*)(reinterpret_cast<const bf16*>(base) + plane * PLANE)
+            : (const void*)(reinterpret_cast<const float*>(base) + plane * PLANE);
+}
+__device__ __forceinline__ void* dense_plane(void* base, size_t plane, bool bf) {
+  return bf ? (void*)(reinterpret_cast<bf16*>(base) + plane * PLANE)
+            : (void*)(reinterpret_cast<float*>(base) + plane * PLANE);
+}
 __device__ __forceinline__ float* scan_plane(float* scan, int g, int n, int h, int N, int hv,
                                              int which) {
   return scan + ((((size_t)g * N + n) * hv + h) * 3 + which) * PLANE;
@@ -988,18 +1020,25 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(const WalkArgs<E> a) {
     }
     row = a.cache + ((size_t)slot * hv + h) * PLANE;
   }
-  const float* src = nullptr;
-  float* dst = nullptr;
+  // state in (src) and out (dst); dense initial / final states may be bf16
+  const bool dense_bf = !a.cache && a.state_bf16;
+  const void* src = nullptr;
+  void* dst = nullptr;
+  bool src_bf = false, dst_bf = false;
+  const size_t unit_plane = (size_t)n * hv + h;
   if (MODE == 0) {
-    src = a.cache ? (a.has_init[n] ? row : nullptr)
-                  : (a.init ? a.init + ((size_t)n * hv + h) * PLANE : nullptr);
-    dst = a.cache ? row : (a.fin ? a.fin + ((size_t)n * hv + h) * PLANE : nullptr);
+    src = a.cache ? (a.has_init[n] ? (const void*)row : nullptr)
+                  : (a.init ? dense_plane(a.init, unit_plane, dense_bf) : nullptr);
+    dst = a.cache ? (void*)row : (a.fin ? dense_plane(a.fin, unit_plane, dense_bf) : nullptr);
+    src_bf = dst_bf = dense_bf;
   } else if (MODE == 1) {
     dst = scan_plane(a.scan, g, n, h, a.N, hv, tcols ? 0 : 1);
   } else {
     src = scan_plane(a.scan, g, n, h, a.N, hv, 2);
-    if (g == G - 1)
-      dst = a.cache ? row : (a.fin ? a.fin + ((size_t)n * hv + h) * PLANE : nullptr);
+    if (g == G - 1) {
+      dst = a.cache ? (void*)row : (a.fin ? dense_plane(a.fin, unit_plane, dense_bf) : nullptr);
+      dst_bf = dense_bf;
+    }
   }
 
   // mid-prefill snapshot: the step after which it is taken (-1: none).  Pass
@@ -1024,8 +1063,7 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(const WalkArgs<E> a) {
       S[kb] = f32x4_t{k0 == vcol ? 1.f : 0.f, k0 + 1 == vcol ? 1.f : 0.f,
                       k0 + 2 == vcol ? 1.f : 0.f, k0 + 3 == vcol ? 1.f : 0.f};
     } else if (src) {
-      const float4 x = *reinterpret_cast<const float4*>(src + (size_t)vcol * D + 16 * kb + 4 * gq);
-      S[kb] = f32x4_t{x.x, x.y, x.z, x.w};
+      S[kb] = plane_load4(src, (size_t)vcol * D + 16 * kb + 4 * gq, src_bf);
     } else {
       S[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -1277,16 +1315,16 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(const WalkArgs<E> a) {
   }
   if (dst) {
     if (tcols) {
-      // transfer P[k][j] row-major, j = this lane's column
+      // transfer P[k][j] row-major, j = this lane's column (scan plane, fp32)
+      float* pd = reinterpret_cast<float*>(dst);
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(size_t)(16 * kb + 4 * gq + r) * D + vcol] = S[kb][r];
+        for (int r = 0; r < 4; ++r) pd[(size_t)(16 * kb + 4 * gq + r) * D + vcol] = S[kb][r];
     } else {
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb)
-        *reinterpret_cast<float4*>(dst + (size_t)vcol * D + 16 * kb + 4 * gq) =
-            make_float4(S[kb][0], S[kb][1], S[kb][2], S[kb][3]);
+        plane_store4(dst, (size_t)vcol * D + 16 * kb + 4 * gq, dst_bf, S[kb]);
     }
   }
 }
@@ -1308,20 +1346,21 @@ __global__ __launch_bounds__(64) void compose_kernel(const WalkArgs<E> a) {
   const int lane = threadIdx.x, l16 = lane & 15, gq = lane >> 4;
   const int vcol = 16 * rb + l16;
   const int G = a.groups;
-  const float* src = nullptr;
+  const void* src = nullptr;
+  bool src_bf = false;
   if (a.cache) {
     const int slot = a.slots[n];
     if (slot < 0 || slot >= a.num_slots) return;
     if (a.has_init[n]) src = a.cache + ((size_t)slot * hv + h) * PLANE;
   } else if (a.init) {
-    src = a.init + ((size_t)n * hv + h) * PLANE;
+    src_bf = a.state_bf16 != 0;
+    src = dense_plane(a.init, (size_t)n * hv + h, src_bf);
   }
   f32x4_t S[8];
 #pragma unroll
   for (int kb = 0; kb < 8; ++kb) {
     if (src) {
-      const float4 x = *reinterpret_cast<const float4*>(src + (size_t)vcol * D + 16 * kb + 4 * gq);
-      S[kb] = f32x4_t{x.x, x.y, x.z, x.w};
+      S[kb] = plane_load4(src, (size_t)vcol * D + 16 * kb + 4 * gq, src_bf);
     } else {
       S[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -1440,7 +1479,8 @@ static hipError_t launch_staged_t(const ChunkLaunch& L) {
   wa.u_t = (const E*)L.u; wa.aqk = (const E*)L.aqk; wa.decay = L.decay;
   wa.cu = L.cu; wa.dense_len = dense_len; wa.T = T; wa.offs = L.chunk_offsets;
   wa.N = N; wa.hv = L.hv; wa.scale = L.scale;
-  wa.init = L.init; wa.fin = L.fin; wa.cache = L.cache; wa.slots = L.slots;
+  wa.init = L.init; wa.fin = L.fin; wa.state_bf16 = L.state_bf16;
+  wa.cache = (float*)L.cache; wa.slots = L.slots;
   wa.has_init = L.has_init; wa.num_slots = L.num_slots; wa.out = (E*)L.out;
   wa.units = N * L.hv; wa.max_chunks = (int)L.max_chunks; wa.groups = L.groups;
   wa.scan = L.scan; wa.zero = (const uint4*)L.zero;

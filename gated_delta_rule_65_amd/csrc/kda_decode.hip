@@ -29,10 +29,41 @@
 
 namespace kda {
 
-template <typename T>
+// This lane's 8 values of a V-first state row (key channels 4j..4j+3 and
+// 64+4j..64+4j+3): fp32, or bf16 widened on load and rounded (to nearest
+// even) on store.
+__device__ __forceinline__ void row_load(const float* row, int j, float4 (&h)[2]) {
+  h[0] = reinterpret_cast<const float4*>(row)[j];
+  h[1] = reinterpret_cast<const float4*>(row)[16 + j];
+}
+__device__ __forceinline__ float4 widen4(uint2 u) {
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+__device__ __forceinline__ void row_load(const bf16* row, int j, float4 (&h)[2]) {
+  h[0] = widen4(reinterpret_cast<const uint2*>(row)[j]);
+  h[1] = widen4(reinterpret_cast<const uint2*>(row)[16 + j]);
+}
+__device__ __forceinline__ void row_store(float* row, int j, const float4 (&h)[2]) {
+  reinterpret_cast<float4*>(row)[j] = h[0];
+  reinterpret_cast<float4*>(row)[16 + j] = h[1];
+}
+__device__ __forceinline__ uint2 narrow4(float4 x) {
+  return make_uint2((uint32_t)bf16_bits(x.x) | ((uint32_t)bf16_bits(x.y) << 16),
+                    (uint32_t)bf16_bits(x.z) | ((uint32_t)bf16_bits(x.w) << 16));
+}
+__device__ __forceinline__ void row_store(bf16* row, int j, const float4 (&h)[2]) {
+  reinterpret_cast<uint2*>(row)[j] = narrow4(h[0]);
+  reinterpret_cast<uint2*>(row)[16 + j] = narrow4(h[1]);
+}
+// The stored value of a state element (bf16 state: rounded and widened back).
+__device__ __forceinline__ float4 as_stored(float4 x, float*) { return x; }
+__device__ __forceinline__ float4 as_stored(float4 x, bf16*) { return widen4(narrow4(x)); }
+
+template <typename T, typename S>
 __global__ __launch_bounds__(256) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const T* __restrict__ g, const T* __restrict__ beta, float* __restrict__ cache,
+    const T* __restrict__ g, const T* __restrict__ beta, S* __restrict__ cache,
     const int32_t* __restrict__ idx, T* __restrict__ out, int hqk, int hv, float scale,
     int use_l2, int num_slots, const GateArgs ga) {
   const int unit = blockIdx.x;
@@ -47,17 +78,12 @@ __global__ __launch_bounds__(256) void decode_kernel(
     if (tid < D) o[tid] = from_f32<T>(0.0f);
     return;
   }
-  float* st = cache + ((size_t)slot * hv + h) * (size_t)(D * D);
+  S* st = cache + ((size_t)slot * hv + h) * (size_t)(D * D);
 
   // Issue the state loads first: rows r = 16 s + 4 wave + rsub, s = 0..7.
   float4 hs[8][2];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int r = 16 * s + 4 * wave + rsub;
-    const float4* row = reinterpret_cast<const float4*>(st + r * D);
-    hs[s][0] = row[j];
-    hs[s][1] = row[16 + j];
-  }
+  for (int s = 0; s < 8; ++s) row_load(st + (16 * s + 4 * wave + rsub) * D, j, hs[s]);
 
   const T* qp = q + ((size_t)req * hqk + hq) * D;
   const T* kp = k + ((size_t)req * hqk + hq) * D;
@@ -117,9 +143,8 @@ __global__ __launch_bounds__(256) void decode_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] += u * kv[e];
     const int r = 16 * s + 4 * wave + rsub;
-    float4* row = reinterpret_cast<float4*>(st + r * D);
-    row[j] = make_float4(x[0], x[1], x[2], x[3]);
-    row[16 + j] = make_float4(x[4], x[5], x[6], x[7]);
+    const float4 nh[2] = {make_float4(x[0], x[1], x[2], x[3]), make_float4(x[4], x[5], x[6], x[7])};
+    row_store(st + r * D, j, nh);
     if (j == 0) o[r] = from_f32<T>(scale * (pq + u * kq));
   }
 }
@@ -131,10 +156,10 @@ __global__ __launch_bounds__(256) void decode_kernel(
 // outside the pool (or a count outside [1, cols]) zeroes the request's output
 // rows and touches no state.  This is gated_delta_rule_decode's [B, T]
 // state_indices with num_accepted_tokens (page "mate.kda").
-template <typename T>
+template <typename T, typename S>
 __global__ __launch_bounds__(256) void decode_multi_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const T* __restrict__ g, const T* __restrict__ beta, float* __restrict__ cache,
+    const T* __restrict__ g, const T* __restrict__ beta, S* __restrict__ cache,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ acc, T* __restrict__ out,
     int ntok, int cols, int hqk, int hv, float scale, int use_l2, int num_slots,
     const GateArgs ga) {
@@ -158,15 +183,10 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
         out[(((size_t)req * ntok + t) * hv + h) * D + tid] = from_f32<T>(0.0f);
     return;
   }
-  const float* st0 = cache + ((size_t)row0 * hv + h) * (size_t)(D * D);
+  const S* st0 = cache + ((size_t)row0 * hv + h) * (size_t)(D * D);
   float4 hs[8][2];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int r = 16 * s + 4 * wave + rsub;
-    const float4* row = reinterpret_cast<const float4*>(st0 + r * D);
-    hs[s][0] = row[j];
-    hs[s][1] = row[16 + j];
-  }
+  for (int s = 0; s < 8; ++s) row_load(st0 + (16 * s + 4 * wave + rsub) * D, j, hs[s]);
   const float ga_a = ga.a_log ? exp2_fast(ga.a_log[h] * LOG2E) : 0.f;  // exp(A_log[h])
   for (int t = 0; t < ntok; ++t) {
     const size_t tok = (size_t)req * ntok + t;
@@ -209,8 +229,8 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
     for (int e = 0; e < 8; ++e) kq += kv[e] * qv[e];
     kq = row_sum16(kq);
     const int rt = ir[t];
-    float* dst = (rt >= 0 && rt < num_slots) ? cache + ((size_t)rt * hv + h) * (size_t)(D * D)
-                                             : nullptr;
+    S* dst = (rt >= 0 && rt < num_slots) ? cache + ((size_t)rt * hv + h) * (size_t)(D * D)
+                                         : nullptr;
     T* o = out + (tok * hv + h) * D;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -228,41 +248,43 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
       const float u = b * (vr[s] - pk);
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] += u * kv[e];
-      hs[s][0] = make_float4(x[0], x[1], x[2], x[3]);
-      hs[s][1] = make_float4(x[4], x[5], x[6], x[7]);
+      // the next token starts from the state as stored (rounded when bf16)
+      hs[s][0] = as_stored(make_float4(x[0], x[1], x[2], x[3]), (S*)nullptr);
+      hs[s][1] = as_stored(make_float4(x[4], x[5], x[6], x[7]), (S*)nullptr);
       const int r = 16 * s + 4 * wave + rsub;
-      if (dst) {
-        float4* row = reinterpret_cast<float4*>(dst + r * D);
-        row[j] = hs[s][0];
-        row[16 + j] = hs[s][1];
-      }
+      if (dst) row_store(dst + r * D, j, hs[s]);
       if (j == 0) o[r] = from_f32<T>(scale * (pq + u * kq));
     }
   }
 }
 
-template <typename T>
+template <typename T, typename S>
 static hipError_t launch_decode_t(const DecodeLaunch& L) {
   const dim3 grid((unsigned)((size_t)L.n * L.hv)), block(256);
   if (L.tokens > 1 || L.cols > 0) {
-    hipLaunchKernelGGL(decode_multi_kernel<T>, grid, block, 0, (hipStream_t)L.stream,
+    hipLaunchKernelGGL((decode_multi_kernel<T, S>), grid, block, 0, (hipStream_t)L.stream,
                        (const T*)L.q, (const T*)L.k, (const T*)L.v, (const T*)L.g,
-                       (const T*)L.beta, L.cache, L.idx, L.accepted, (T*)L.out, L.tokens,
+                       (const T*)L.beta, (S*)L.cache, L.idx, L.accepted, (T*)L.out, L.tokens,
                        L.cols, L.hqk, L.hv, L.scale, L.use_l2, L.num_slots, L.gate);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(decode_kernel<T>, grid, block, 0, (hipStream_t)L.stream,
+  hipLaunchKernelGGL((decode_kernel<T, S>), grid, block, 0, (hipStream_t)L.stream,
                      (const T*)L.q, (const T*)L.k, (const T*)L.v, (const T*)L.g,
-                     (const T*)L.beta, L.cache, L.idx, (T*)L.out, L.hqk, L.hv, L.scale,
+                     (const T*)L.beta, (S*)L.cache, L.idx, (T*)L.out, L.hqk, L.hv, L.scale,
                      L.use_l2, L.num_slots, L.gate);
   return hipGetLastError();
 }
 
+template <typename T>
+static hipError_t launch_decode_s(const DecodeLaunch& L) {
+  return L.state_bf16 ? launch_decode_t<T, bf16>(L) : launch_decode_t<T, float>(L);
+}
+
 hipError_t launch_decode(const DecodeLaunch& L) {
   switch (L.dtype) {
-    case 0: return launch_decode_t<float>(L);
-    case 1: return launch_decode_t<bf16>(L);
-    default: return launch_decode_t<_Float16>(L);
+    case 0: return launch_decode_s<float>(L);
+    case 1: return launch_decode_s<bf16>(L);
+    default: return launch_decode_s<_Float16>(L);
   }
 }
 

@@ -9,7 +9,8 @@ namespace kda {
 
 struct DecodeLaunch {
   const void *q, *k, *v, *g, *beta;
-  float* cache;
+  void* cache;                // fp32 or bf16 (state_bf16)
+  int state_bf16;
   const int32_t* idx;
   void* out;
   int dtype, n, hqk, hv, use_l2, num_slots;
@@ -29,9 +30,10 @@ struct ChunkLaunch {
   int dtype, num_seqs, hqk, hv, use_l2;
   int64_t total_tokens, max_chunks;
   float scale;
-  const float* init;          // dense initial state or NULL
-  float* fin;                 // dense final state or NULL
-  float* cache;               // paged state or NULL
+  const void* init;           // dense initial state or NULL (fp32, or bf16 with state_bf16)
+  void* fin;                  // dense final state or NULL (same storage)
+  int state_bf16;
+  void* cache;                // paged state (fp32) or NULL
   const int32_t* slots;
   const uint8_t* has_init;
   int num_slots;

@@ -110,8 +110,9 @@ typedef struct kda_chunk_args {
   float scale;                 /* output scale (128^-0.5 is the usual value) */
   int32_t use_qk_l2norm;       /* 1: L2-normalise q and k in the kernels */
   /* dense state mode (both optional, fp32, V-first) */
-  const float *initial_state;  /* (device) [N, Hv, 128, 128] or NULL (= zero) */
-  float *final_state;          /* (device) [N, Hv, 128, 128] or NULL */
+  const void *initial_state;   /* (device) [N, Hv, 128, 128] of state_dtype, or
+                                  NULL (= zero) */
+  void *final_state;           /* (device) [N, Hv, 128, 128] of state_dtype, or NULL */
   /* paged state mode (replaces initial_state / final_state) */
   float *state_cache;          /* (device) [num_slots, Hv, 128, 128] or NULL */
   const int32_t *state_indices;     /* (device) [N]; row per sequence, distinct;
@@ -154,6 +155,12 @@ typedef struct kda_chunk_args {
   const int32_t *checkpoint_offsets;       /* (device) [N]; with checkpoint_state */
   const int32_t *checkpoint_state_indices; /* (device) [N] or NULL */
   int32_t checkpoint_rows;
+  /* Storage of initial_state / final_state: KDA_F32 (0) or the input dtype
+     (chunk_kda's rule on page "mate.kda": the states are fp32 or of q's
+     dtype, both alike).  A bf16 initial state is widened exactly; the final
+     state is rounded to nearest even.  The paged state_cache and the
+     checkpoint rows are always fp32 (page "vllm.models.kimi_k3.amd.ops.kda_chunk"). */
+  int32_t state_dtype;
 } kda_chunk_args;
 
 /* Stage boundaries of kda_chunk_fwd (indices into stage_events).  Event i is
@@ -240,7 +247,8 @@ typedef struct kda_decode_args {
   int32_t hqk, hv;             /* hv % hqk == 0 */
   float scale;
   int32_t use_qk_l2norm;
-  float *state_cache;          /* (device) [num_slots, Hv, 128, 128] fp32 */
+  void *state_cache;           /* (device) [num_slots, Hv, 128, 128] of
+                                  state_dtype */
   const int32_t *state_indices;  /* (device) [n], distinct where >= 0, each
                                     < num_slots; < 0 = skip (zero output row,
                                     no state I/O); NULL = identity (slot n) */
@@ -273,6 +281,11 @@ typedef struct kda_decode_args {
   int32_t tokens;
   int32_t state_index_cols;            /* 0: state_indices is [n] (or NULL) */
   const int32_t *num_accepted_tokens;  /* (device) [n] or NULL */
+  /* Storage of state_cache: KDA_F32 (0) or KDA_BF16.  A bf16 state is
+     widened for each token's arithmetic and rounded back (to nearest even)
+     after each token, as repeated single-token decode would store it
+     (gated_delta_rule_decode's bf16 state, page "mate.kda"). */
+  int32_t state_dtype;
 } kda_decode_args;
 
 kda_status kda_decode(const kda_decode_args *a);

@@ -209,8 +209,8 @@ def test_binding_decode_checks():
                      num_accepted_tokens=torch.ones(4, dtype=torch.int32))
     with pytest.raises(ValueError, match="pool"):
         B.kda_decode(q, q, v, v, cpu((4, 4)), cpu((8, 4, 128, 64), torch.float32))
-    with pytest.raises(NotImplementedError):
-        B.kda_decode(q, q, v, v, cpu((4, 4)), cache.bfloat16())
+    with pytest.raises(ValueError, match="dtype"):
+        B.kda_decode(q, q, v, v, cpu((4, 4)), cache.half())
 
 
 def test_planner_picks_groups_only_for_long_chains(lib):
@@ -294,3 +294,26 @@ def test_checkpoint_rows_with_indices_pass_checks(lib):
 def test_multi_token_decode_checks(lib, fields, status):
     a = decode_args(**fields)
     assert lib.kda_decode(ctypes.byref(a)) == status
+
+
+
+def test_state_dtype_checks(lib):
+    # chunk: the states are fp32 or of the input dtype; the paged chunk state is fp32
+    assert ws_size(lib, chunk_args(state_dtype=2))[0] == B.KDA_ERR_DTYPE   # f16 with bf16 input
+    assert ws_size(lib, chunk_args(state_dtype=1))[0] == B.KDA_OK
+    a = chunk_args(state_dtype=1, state_cache=FAKE, state_indices=FAKE, has_initial_state=FAKE,
+                   num_slots=4)
+    assert ws_size(lib, a)[0] == B.KDA_ERR_UNSUPPORTED
+    # decode: fp32 or bf16 cache
+    assert lib.kda_decode(ctypes.byref(decode_args(state_dtype=2))) == B.KDA_ERR_DTYPE
+
+
+def test_binding_state_dtype_rules():
+    q = cpu((1, 64, 2, 128))
+    v = cpu((1, 64, 4, 128))
+    beta = cpu((1, 64, 4))
+    with pytest.raises(TypeError, match="initial_state"):
+        B.chunk_kda(q, q, v, v, beta, initial_state=cpu((1, 4, 128, 128), torch.float16))
+    with pytest.raises(TypeError, match="same dtype"):
+        B.chunk_kda(q, q, v, v, beta, initial_state=cpu((1, 4, 128, 128)),
+                    output_final_state=True, final_state=cpu((1, 4, 128, 128), torch.float32))

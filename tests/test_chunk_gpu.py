@@ -539,3 +539,37 @@ def test_checkpoints_under_the_group_scan():
     b = inputs.make_chunk([1500], 1, 2, dtype=torch.bfloat16, g_scale=0.05, seed=97, init=True)
     ck, refs, _, _ = run_checkpoints(b, [640], rows=1, groups=4)
     assert rel(ck[0], refs[0]) < 1e-2
+
+
+# ------------------------------------------------------- bf16 initial / final
+
+@pytest.mark.parametrize("groups", [1, 4])
+def test_bf16_initial_and_final_state(groups):
+    """States stored in bf16 (chunk_kda allows q's dtype): the initial state is
+    widened exactly, the final state rounded to nearest even."""
+    b = inputs.make_chunk([700, 300], 1, 2, dtype=torch.bfloat16, g_scale=0.5, seed=98,
+                          init=True)
+    init16 = b.initial_state.to(torch.bfloat16)
+    q, k, v, g, beta = gpu(b)
+    out, fin = B.chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=init16.to(DEV),
+                           output_final_state=True, cu_seqlens=b.cu_seqlens.to(DEV),
+                           groups=groups)
+    torch.cuda.synchronize()
+    assert fin.dtype == torch.bfloat16
+    o_ref, s_ref = oracle.recurrence(b.q, b.k, b.v, b.g, b.beta, cu_seqlens=b.cu_seqlens,
+                                     scale=b.scale, initial_state=init16)
+    assert rel(out.float().cpu().numpy(), o_ref) < 1e-2
+    assert rel(fin.float().cpu().numpy(), s_ref) < 1e-2
+
+
+def test_bf16_state_b0_passes_through_bitwise():
+    """b = 0, g = 0: a bf16 initial state comes back bit for bit."""
+    b = inputs.make_chunk([150, 64], 1, 2, dtype=torch.bfloat16, seed=99, init=True)
+    b.beta.fill_(-1e4)
+    b.g.zero_()
+    init16 = b.initial_state.to(torch.bfloat16)
+    q, k, v, g, beta = gpu(b)
+    _, fin = B.chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=init16.to(DEV),
+                         output_final_state=True, cu_seqlens=b.cu_seqlens.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(fin.cpu(), init16)

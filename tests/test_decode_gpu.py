@@ -220,3 +220,43 @@ def test_multi_token_decode_with_gate():
                 dt_bias=torch.randn(2, 128, generator=gen).to(DEV), lower_bound=-3.0)
     o, ro, c, rc = run_spec(q, k, v, g, beta, cache, idx, **gate)
     assert rel(o, ro) < 1e-2 and rel(c, rc) < 1e-5
+
+
+# ------------------------------------------------------------ bf16 state cache
+
+def test_decode_bf16_state_cache():
+    """bf16 cache: widened for the token's arithmetic, stored rounded to
+    nearest even; against the oracle on the same stored values."""
+    b = inputs.make_decode(60, 2, 4, 80, dtype=torch.bfloat16, seed=61)
+    cache = b.state_cache.to(torch.bfloat16)
+    idx = b.state_indices.clone()
+    idx[7] = -1
+    cd = cache.to(DEV)
+    out = B.kda_decode(*(t.to(DEV) for t in (b.q, b.k, b.v, b.g, b.beta)), cd, idx.to(DEV))
+    torch.cuda.synchronize()
+    ro, rc = oracle.decode(b.q, b.k, b.v, b.g, b.beta, cache, idx)
+    assert rel(out.float().cpu().numpy(), ro) < 1e-2
+    live = idx[idx >= 0].long()
+    got = cd.cpu().float().numpy()[live.numpy()]
+    want = oracle.round_bf16(rc[live.numpy()])
+    assert rel(got, want) < 1e-2
+    # most elements round to the same bf16 value as the fp64 state
+    assert np.mean(got == want) > 0.9
+    untouched = torch.ones(80, dtype=torch.bool)
+    untouched[live] = False
+    assert torch.equal(cd.cpu()[untouched], cache[untouched])
+
+
+def test_multi_token_decode_bf16_state_cache():
+    Bn, T = 6, 5
+    q, k, v, g, beta, cache = spec_case(Bn, T, 1, 2, 40, torch.bfloat16, seed=62)
+    cache = cache.to(torch.bfloat16)
+    idx = torch.arange(Bn * T, dtype=torch.int32).reshape(Bn, T)
+    acc = torch.tensor([1, 1, 2, 3, 5, 4], dtype=torch.int32)
+    cd = cache.to(DEV)
+    out = B.kda_decode(*(t.to(DEV) for t in (q, k, v, g, beta)), cd, idx.to(DEV),
+                       num_accepted_tokens=acc.to(DEV))
+    torch.cuda.synchronize()
+    ro, rc = oracle.decode_multi(q, k, v, g, beta, cache, idx, acc, state_bf16=True)
+    assert rel(out.float().cpu().numpy(), ro) < 1e-2
+    assert rel(cd.cpu().float().numpy(), rc) < 1e-2
