@@ -160,21 +160,45 @@ def cpu_model():
     return "unknown"
 
 
+CPU_BASELINE_SECONDS = 10.0  # whole steps are repeated until this much time has passed
+
+
 def cpu_baseline(batch_cpu, lengths, dec_cpu):
-    """The fp64 oracle on the host: the whole prefill batch (all sequences and
-    heads), then the whole decode batch."""
+    """The fp64 oracle on the host, over whole steps: the prefill batch (all
+    sequences and heads) and, when given, the decode batch.  The decode batch
+    carries only the pool rows its requests touch (gathered, indices
+    renumbered), which is the same work.  Steps repeat until
+    CPU_BASELINE_SECONDS have passed."""
+    import torch
     import oracle
     threads = oracle.default_threads()
-    t0 = time.perf_counter()
-    oracle.recurrence(batch_cpu.q, batch_cpu.k, batch_cpu.v, batch_cpu.g, batch_cpu.beta,
-                      cu_seqlens=batch_cpu.cu_seqlens, scale=batch_cpu.scale,
-                      initial_state=batch_cpu.initial_state, threads=threads)
-    t_chunk = time.perf_counter() - t0
-    return dict(value=sum(lengths) / t_chunk, unit="tokens/s", cores=threads,
+    n_dec = 0
+    if dec_cpu is not None:
+        rows = dec_cpu.state_indices.long()
+        dcache = dec_cpu.state_cache[rows]
+        didx = torch.arange(rows.numel(), dtype=torch.int32)
+        n_dec = rows.numel()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.recurrence(batch_cpu.q, batch_cpu.k, batch_cpu.v, batch_cpu.g, batch_cpu.beta,
+                          cu_seqlens=batch_cpu.cu_seqlens, scale=batch_cpu.scale,
+                          initial_state=batch_cpu.initial_state, threads=threads)
+        if dec_cpu is not None:
+            oracle.decode(dec_cpu.q, dec_cpu.k, dec_cpu.v, dec_cpu.g, dec_cpu.beta, dcache, didx,
+                          scale=dec_cpu.scale, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= CPU_BASELINE_SECONDS:
+            break
+    per_step = el / reps
+    dec_txt = (f" + decode batch ({n_dec} requests x {dec_cpu.v.shape[1]} heads)"
+               if dec_cpu is not None else "")
+    return dict(value=(sum(lengths) + n_dec) / per_step, unit="tokens/s", cores=threads,
                 kind="oracle",
-                sample=(f"whole prefill batch ({len(lengths)} x {lengths[0]} tokens, "
-                        f"{batch_cpu.v.shape[1]} heads), fp64 token recurrence, "
-                        f"{t_chunk:.2f} s on {cpu_model()}"))
+                sample=(f"{reps} whole steps: prefill batch ({len(lengths)} x {lengths[0]} "
+                        f"tokens, {batch_cpu.v.shape[1]} heads){dec_txt}, fp64 token "
+                        f"recurrence, {per_step:.2f} s per step, {el:.1f} s in all on "
+                        f"{cpu_model()}"))
 
 
 # ---------------------------------------------------------------------- main
@@ -409,7 +433,12 @@ def main():
     if not args.no_cpu_baseline:
         cpu = inputs.Batch(cb.q.cpu(), cb.k.cpu(), cb.v.cpu(), cb.g.cpu(), cb.beta.cpu(),
                            cb.cu_seqlens.cpu(), cb.scale, initial_state=cb.initial_state.cpu())
-        res["cpu_baseline"] = cpu_baseline(cpu, lengths, None)
+        dcpu = None
+        if not args.no_decode:
+            dcpu = inputs.Batch(db.q.cpu(), db.k.cpu(), db.v.cpu(), db.g.cpu(), db.beta.cpu(),
+                                db.cu_seqlens.cpu(), db.scale, state_cache=db.state_cache.cpu(),
+                                state_indices=db.state_indices.cpu())
+        res["cpu_baseline"] = cpu_baseline(cpu, lengths, dcpu)
     else:
         res["cpu_baseline"] = None
     for es in ev_sets:

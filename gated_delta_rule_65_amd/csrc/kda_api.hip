@@ -8,6 +8,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <initializer_list>
+
 #include "../../include/kda.h"
 #include "kda_launch.hpp"
 
@@ -37,6 +39,13 @@ size_t elem_size(int dtype) { return dtype == KDA_F32 ? 4 : 2; }
 // Gate parameters: both or neither; dt_bias fp32 or bf16; lower_bound in
 // [-10, 0] (per-step log-decays beyond -10 would leave the exponent range
 // the chunk tiles are built for).
+// Tensor base pointers are read with 8- and 16-byte vector loads.
+bool misaligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (reinterpret_cast<uintptr_t>(p) & 15) return true;
+  return false;
+}
+
 kda_status check_gate(const float* a_log, const void* dt_bias, int32_t dt_dtype, float lb) {
   if ((a_log == nullptr) != (dt_bias == nullptr))
     return fail(KDA_ERR_SHAPE, "A_log and dt_bias must be provided together");
@@ -123,6 +132,9 @@ kda_status check_chunk(const kda_chunk_args* a, bool need_ptrs) {
     if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->out)
       return fail(KDA_ERR_ARG, "q, k, v, g, beta and out must be non-NULL");
   }
+  if (misaligned16({a->q, a->k, a->v, a->g, a->out, a->initial_state, a->final_state,
+                    a->state_cache, a->checkpoint_state, a->dt_bias}))
+    return fail(KDA_ERR_ARG, "tensor base pointers must be 16-byte aligned");
   return KDA_OK;
 }
 
@@ -322,6 +334,8 @@ KDA_API kda_status kda_decode(const kda_decode_args* a) {
   }
   if (a->state_dtype != KDA_F32 && a->state_dtype != KDA_BF16)
     return fail(KDA_ERR_DTYPE, "state_cache must be fp32 or bf16");
+  if (misaligned16({a->q, a->k, a->v, a->g, a->out, a->state_cache, a->dt_bias}))
+    return fail(KDA_ERR_ARG, "tensor base pointers must be 16-byte aligned");
   if (a->tokens < 0 || a->tokens > 8)
     return fail(KDA_ERR_UNSUPPORTED, "tokens per request must lie in [0, 8], got %d", a->tokens);
   const int T = a->tokens > 1 ? a->tokens : 1;

@@ -56,6 +56,54 @@ __device__ __forceinline__ void row_store(bf16* row, int j, const float4 (&h)[2]
   reinterpret_cast<uint2*>(row)[j] = narrow4(h[0]);
   reinterpret_cast<uint2*>(row)[16 + j] = narrow4(h[1]);
 }
+// Four consecutive elements widened to fp32 (one 16-byte or 8-byte load).
+__device__ __forceinline__ void load4(const float* p, float* x) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+}
+__device__ __forceinline__ void load4(const bf16* p, float* x) {
+  const float4 a = widen4(*reinterpret_cast<const uint2*>(p));
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+}
+__device__ __forceinline__ void load4(const _Float16* p, float* x) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  x[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u.x & 0xffffu));
+  x[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u.x >> 16));
+  x[2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u.y & 0xffffu));
+  x[3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u.y >> 16));
+}
+// This lane's 8 channels of a 128-vector: 4j..4j+3 and 64+4j..64+4j+3.
+template <typename T>
+__device__ __forceinline__ void lane8(const T* p, int j, float (&x)[8]) {
+  load4(p + 4 * j, x);
+  load4(p + 64 + 4 * j, x + 4);
+}
+// One token's q, k and per-channel decay factor exp(g) on this lane's 8
+// channels.  All loads are issued before the gate arithmetic so that they
+// stay vector loads in one block.
+template <typename T>
+__device__ __forceinline__ void token_qk_decay(const T* qp, const T* kp, const T* gp, int j,
+                                               int h, const GateArgs& ga, float ga_a,
+                                               float (&qv)[8], float (&kv)[8],
+                                               float (&al)[8]) {
+  float gl[8];
+  lane8(qp, j, qv);
+  lane8(kp, j, kv);
+  lane8(gp, j, gl);
+  if (ga.a_log) {
+    float bias[8];
+    if (ga.bias_bf16) {
+      lane8(reinterpret_cast<const bf16*>(ga.bias) + (size_t)h * D, j, bias);
+    } else {
+      lane8(reinterpret_cast<const float*>(ga.bias) + (size_t)h * D, j, bias);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gl[e] = gate_apply(gl[e], ga_a, bias[e], ga.lower_bound);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) al[e] = exp2_fast(gl[e] * LOG2E);
+}
+
 // The stored value of a state element (bf16 state: rounded and widened back).
 __device__ __forceinline__ float4 as_stored(float4 x, float*) { return x; }
 __device__ __forceinline__ float4 as_stored(float4 x, bf16*) { return widen4(narrow4(x)); }
@@ -91,15 +139,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
   const T* vp = v + ((size_t)req * hv + h) * D;
   float qv[8], kv[8], al[8];
   const float ga_a = ga.a_log ? exp2_fast(ga.a_log[h] * LOG2E) : 0.f;  // exp(A_log[h])
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int c = (e < 4) ? (4 * j + e) : (64 + 4 * j + e - 4);
-    qv[e] = to_f32(qp[c]);
-    kv[e] = to_f32(kp[c]);
-    float gl = to_f32(gp[c]);
-    if (ga.a_log) gl = gate_apply(gl, ga_a, gate_bias(ga, h, c), ga.lower_bound);
-    al[e] = exp2_fast(gl * LOG2E);
-  }
+  token_qk_decay(qp, kp, gp, j, h, ga, ga_a, qv, kv, al);
   float vr[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) vr[s] = to_f32(vp[16 * s + 4 * wave + rsub]);
@@ -195,15 +235,7 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
     const T* gp = g + (tok * hv + h) * D;
     const T* vp = v + (tok * hv + h) * D;
     float qv[8], kv[8], al[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = (e < 4) ? (4 * j + e) : (64 + 4 * j + e - 4);
-      qv[e] = to_f32(qp[c]);
-      kv[e] = to_f32(kp[c]);
-      float gl = to_f32(gp[c]);
-      if (ga.a_log) gl = gate_apply(gl, ga_a, gate_bias(ga, h, c), ga.lower_bound);
-      al[e] = exp2_fast(gl * LOG2E);
-    }
+    token_qk_decay(qp, kp, gp, j, h, ga, ga_a, qv, kv, al);
     float vr[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) vr[s] = to_f32(vp[16 * s + 4 * wave + rsub]);

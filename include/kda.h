@@ -33,7 +33,8 @@
  * Conventions shared by every entry point.
  *  - Pointers marked (device) are HIP device pointers on the current device;
  *    (host) pointers are read before the call returns.  All tensors are
- *    dense, row-major and contiguous.
+ *    dense, row-major and contiguous, and every tensor starts on a 16-byte
+ *    boundary (KDA_ERR_ARG otherwise); beta, A_log and index arrays are exempt.
  *  - The library allocates nothing.  Every buffer, the workspace included,
  *    is owned by the caller and must outlive the queued work.
  *  - Arguments are checked on the host before anything is queued.  On an

@@ -317,3 +317,20 @@ def test_binding_state_dtype_rules():
     with pytest.raises(TypeError, match="same dtype"):
         B.chunk_kda(q, q, v, v, beta, initial_state=cpu((1, 4, 128, 128)),
                     output_final_state=True, final_state=cpu((1, 4, 128, 128), torch.float32))
+
+
+def test_misaligned_tensor_pointers_are_rejected(lib):
+    """Base pointers of the tensors read with vector loads must be 16-byte
+    aligned; the check runs before anything touches device memory."""
+    odd = ctypes.c_void_p(0x1008)
+    for field in ("initial_state", "final_state"):
+        assert ws_size(lib, chunk_args(**{field: odd}))[0] == B.KDA_ERR_ARG
+    assert lib.kda_decode(ctypes.byref(decode_args(q=odd, k=FAKE, v=FAKE, g=FAKE, beta=FAKE,
+                                                   out=FAKE, state_cache=FAKE))) == B.KDA_ERR_ARG
+    assert lib.kda_decode(ctypes.byref(decode_args(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE,
+                                                   out=FAKE, state_cache=odd))) == B.KDA_ERR_ARG
+    # beta is exempt (read one element at a time)
+    a = decode_args(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=ctypes.c_void_p(0x1002), out=FAKE,
+                    state_cache=odd)
+    assert lib.kda_decode(ctypes.byref(a)) == B.KDA_ERR_ARG
+    assert b"16-byte" in lib.kda_last_error()
