@@ -54,6 +54,9 @@ class ChunkArgs(ctypes.Structure):
         ("checkpoint_state", ctypes.c_void_p), ("checkpoint_offsets", ctypes.c_void_p),
         ("checkpoint_state_indices", ctypes.c_void_p), ("checkpoint_rows", ctypes.c_int32),
         ("state_dtype", ctypes.c_int32),
+        ("q_stride", ctypes.c_int64), ("k_stride", ctypes.c_int64),
+        ("v_stride", ctypes.c_int64), ("g_stride", ctypes.c_int64),
+        ("beta_stride", ctypes.c_int64), ("state_slot_stride", ctypes.c_int64),
     ]
 
 
@@ -83,6 +86,9 @@ class DecodeArgs(ctypes.Structure):
         ("dt_bias_dtype", ctypes.c_int32), ("lower_bound", ctypes.c_float),
         ("tokens", ctypes.c_int32), ("state_index_cols", ctypes.c_int32),
         ("num_accepted_tokens", ctypes.c_void_p), ("state_dtype", ctypes.c_int32),
+        ("q_stride", ctypes.c_int64), ("k_stride", ctypes.c_int64),
+        ("v_stride", ctypes.c_int64), ("g_stride", ctypes.c_int64),
+        ("beta_stride", ctypes.c_int64), ("state_slot_stride", ctypes.c_int64),
     ]
 
 
@@ -205,6 +211,53 @@ def _contig(name, t):
     return t
 
 
+def _token_stride(name, t, inner):
+    """Elements between consecutive tokens of an input laid out as
+    [token dims..., H, 128] (inner = 2) or [token dims..., H] (inner = 1, beta),
+    0 when the tensor is contiguous.  A view into a wider projection output
+    (each token's block dense, tokens a fixed stride apart) is passed as it
+    is, without a copy."""
+    if t.is_contiguous():
+        return 0
+    msg = (f"{name} must be contiguous, or a view whose tokens lie a fixed stride apart "
+           f"with each token's last {inner} dims dense")
+    dense = 1
+    for d in range(t.dim() - 1, t.dim() - 1 - inner, -1):
+        _need(t.shape[d] == 1 or t.stride(d) == dense, msg)
+        dense *= t.shape[d]
+    lead = [(t.shape[d], t.stride(d)) for d in range(t.dim() - inner) if t.shape[d] != 1]
+    if not lead:
+        return 0
+    stride = run = lead[-1][1]
+    for size, st in reversed(lead):
+        _need(st == run, msg)
+        run *= size
+    _need(stride >= dense, msg)
+    return 0 if stride == dense else stride
+
+
+def _slot_stride(cache):
+    """Elements between the slots of a [slots, Hv, 128, 128] state pool, 0 when
+    dense (a pool whose slots are padded keeps each slot's planes dense)."""
+    if cache is None or cache.is_contiguous():
+        return 0
+    hv = cache.shape[1]
+    msg = "state pool slots must each be dense [Hv, 128, 128] blocks"
+    _need(cache.stride(3) == 1 and cache.stride(2) == D and (hv == 1 or cache.stride(1) == D * D),
+          msg)
+    if cache.shape[0] == 1:
+        return 0
+    _need(cache.stride(0) >= hv * D * D, msg)
+    return 0 if cache.stride(0) == hv * D * D else cache.stride(0)
+
+
+def _set_strides(a, q, k, v, g, beta, cache):
+    a.q_stride, a.k_stride = _token_stride("q", q, 2), _token_stride("k", k, 2)
+    a.v_stride, a.g_stride = _token_stride("v", v, 2), _token_stride("g", g, 2)
+    a.beta_stride = _token_stride("beta", beta, 1)
+    a.state_slot_stride = _slot_stride(cache)
+
+
 def _as_varlen(x, name, cu_seqlens):
     """[B, T, H, 128] dense, or [S, H, 128] / [1, S, H, 128] with cu_seqlens."""
     if cu_seqlens is None:
@@ -237,6 +290,7 @@ def _chunk_struct(q, k, v, g, beta, out, cu, N, T, hqk, hv, scale, l2, init, fin
     a.path, a.groups, a.walk_waves = path, groups, walk_waves
     a.stream = stream
     _set_gate(a, gate if gate is not None else (None, None, 0, -5.0))
+    _set_strides(a, q, k, v, g, beta, cache)
     return a
 
 
@@ -287,7 +341,7 @@ def _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state, c
         _need(state_cache.dtype == torch.float32, "state_cache must be float32", TypeError)
         _need(state_cache.dim() == 4 and tuple(state_cache.shape[1:]) == (hv, D, D),
               f"state_cache must be [slots, {hv}, 128, 128]")
-        _contig("state_cache", state_cache)
+        _slot_stride(state_cache)
         idx = state_indices.to(device=dev, dtype=torch.int32).contiguous()
         hinit = has_initial_state.to(device=dev, dtype=torch.uint8).contiguous()
         _need(idx.numel() == N and hinit.numel() == N,
@@ -319,10 +373,11 @@ def _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state, c
     _need(output.shape == v.shape or (varlen and output.shape == v3.shape),
           "output must have the same shape as v.")
     _need(output.dtype == q.dtype, "output must have the same dtype as q.", TypeError)
-    for name, t in (("q", q3), ("k", k3), ("v", v3), ("g", g3), ("beta", beta2),
-                    ("output", output)):
-        _contig(name, t)
+    for name, t in (("q", q3), ("k", k3), ("v", v3), ("g", g3), ("beta", beta2)):
+        _token_stride(name, t, 1 if name == "beta" else 2)
         _need(t.device == dev, f"{name} must be on {dev}")
+    _contig("output", output)
+    _need(output.device == dev, f"output must be on {dev}")
     return dict(q=q3, k=k3, v=v3, g=g3, beta=beta2, out=output, cu=cu, N=N, T=T, hqk=hqk,
                 hv=hv, scale=float(scale), l2=bool(use_qk_l2norm_in_kernel), init=init,
                 fin=fin, cache=state_cache if paged else None, idx=idx, has_init=hinit)
@@ -505,10 +560,13 @@ def kda_decode(q, k, v, g, beta, state_cache, state_indices=None, scale=None,
         output = torch.empty(tuple(shape_v), dtype=q.dtype, device=dev)
     _need(output.numel() == n * T * hv * D and output.dtype == q.dtype,
           "output must be shaped like v, of q's dtype")
-    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta),
-                    ("state_cache", state_cache), ("output", output)):
-        _contig(name, t)
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        _token_stride(name, t, 1 if name == "beta" else 2)
         _need(t.device == dev, f"{name} must be on {dev}")
+    _slot_stride(state_cache)
+    _contig("output", output)
+    _need(state_cache.device == dev and output.device == dev,
+          f"state_cache and output must be on {dev}")
     lib = load_library()
     a = DecodeArgs()
     a.struct_size = ctypes.sizeof(DecodeArgs)
@@ -525,6 +583,7 @@ def kda_decode(q, k, v, g, beta, state_cache, state_indices=None, scale=None,
     _set_gate(a, _gate(A_log, dt_bias, lower_bound, hv, dev))
     a.tokens, a.state_index_cols, a.num_accepted_tokens = T, cols, _ptr(acc)
     a.state_dtype = _DTYPES[state_cache.dtype]
+    _set_strides(a, q, k, v, g, beta, state_cache)
     st = lib.kda_decode(ctypes.byref(a))
     if st != KDA_OK:
         _raise(lib, st)

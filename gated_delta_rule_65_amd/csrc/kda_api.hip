@@ -46,6 +46,38 @@ bool misaligned16(std::initializer_list<const void*> ps) {
   return false;
 }
 
+// Resolves the optional per-token input strides (0 = dense) and checks them:
+// at least the dense stride, at most 2^24 elements, and 16-byte token rows
+// for the vector-loaded inputs.
+kda_status resolve_strides(int64_t q, int64_t k, int64_t v, int64_t g, int64_t b, int hqk,
+                           int hv, size_t es, kda::InStrides& out) {
+  const int64_t dq = (int64_t)hqk * KDA_HEAD_DIM, dv = (int64_t)hv * KDA_HEAD_DIM;
+  const int64_t in[5] = {q, k, v, g, b}, dense[5] = {dq, dq, dv, dv, hv};
+  const char* names[5] = {"q", "k", "v", "g", "beta"};
+  int64_t r[5];
+  for (int i = 0; i < 5; ++i) {
+    r[i] = in[i] ? in[i] : dense[i];
+    if (r[i] < dense[i] || r[i] > ((int64_t)1 << 24))
+      return fail(KDA_ERR_SHAPE, "%s_stride %lld must be 0 or in [%lld, 2^24]", names[i],
+                  (long long)in[i], (long long)dense[i]);
+    if (i < 4 && ((size_t)r[i] * es) % 16 != 0)
+      return fail(KDA_ERR_ARG, "%s_stride %lld must keep token rows 16-byte aligned", names[i],
+                  (long long)in[i]);
+  }
+  out = kda::InStrides{r[0], r[1], r[2], r[3], r[4]};
+  return KDA_OK;
+}
+
+// Resolves the optional paged-pool slot stride (0 = dense).
+kda_status resolve_slot_stride(int64_t s, int hv, int64_t& out) {
+  const int64_t dense = (int64_t)hv * KDA_HEAD_DIM * KDA_HEAD_DIM;
+  out = s ? s : dense;
+  if (out < dense || out % 8 != 0)
+    return fail(KDA_ERR_SHAPE, "state_slot_stride %lld must be 0, or >= %lld and a multiple of 8",
+                (long long)s, (long long)dense);
+  return KDA_OK;
+}
+
 kda_status check_gate(const float* a_log, const void* dt_bias, int32_t dt_dtype, float lb) {
   if ((a_log == nullptr) != (dt_bias == nullptr))
     return fail(KDA_ERR_SHAPE, "A_log and dt_bias must be provided together");
@@ -135,6 +167,17 @@ kda_status check_chunk(const kda_chunk_args* a, bool need_ptrs) {
   if (misaligned16({a->q, a->k, a->v, a->g, a->out, a->initial_state, a->final_state,
                     a->state_cache, a->checkpoint_state, a->dt_bias}))
     return fail(KDA_ERR_ARG, "tensor base pointers must be 16-byte aligned");
+  {
+    kda::InStrides st;
+    const kda_status ss = resolve_strides(a->q_stride, a->k_stride, a->v_stride, a->g_stride,
+                                          a->beta_stride, a->hqk, a->hv, elem_size(a->dtype), st);
+    if (ss != KDA_OK) return ss;
+    int64_t slot;
+    if (paged && resolve_slot_stride(a->state_slot_stride, a->hv, slot) != KDA_OK)
+      return KDA_ERR_SHAPE;
+    if (!paged && a->state_slot_stride != 0)
+      return fail(KDA_ERR_SHAPE, "state_slot_stride needs a state_cache");
+  }
   return KDA_OK;
 }
 
@@ -301,6 +344,9 @@ KDA_API kda_status kda_chunk_fwd(const kda_chunk_args* a) {
   L.ckpt_off = a->checkpoint_offsets;
   L.ckpt_idx = a->checkpoint_state_indices;
   L.ckpt_rows = a->checkpoint_rows;
+  resolve_strides(a->q_stride, a->k_stride, a->v_stride, a->g_stride, a->beta_stride, a->hqk,
+                  a->hv, elem_size(a->dtype), L.strides);  // checked above
+  resolve_slot_stride(a->state_slot_stride, a->hv, L.slot_stride);
   L.groups = W.groups;
   L.walk_waves = W.walk_waves;
   L.scan = L.groups > 1 ? (float*)(ws + W.scan) : nullptr;
@@ -336,6 +382,16 @@ KDA_API kda_status kda_decode(const kda_decode_args* a) {
     return fail(KDA_ERR_DTYPE, "state_cache must be fp32 or bf16");
   if (misaligned16({a->q, a->k, a->v, a->g, a->out, a->state_cache, a->dt_bias}))
     return fail(KDA_ERR_ARG, "tensor base pointers must be 16-byte aligned");
+  kda::InStrides strides;
+  {
+    const kda_status ss = resolve_strides(a->q_stride, a->k_stride, a->v_stride, a->g_stride,
+                                          a->beta_stride, a->hqk, a->hv, elem_size(a->dtype),
+                                          strides);
+    if (ss != KDA_OK) return ss;
+  }
+  int64_t slot_stride;
+  if (resolve_slot_stride(a->state_slot_stride, a->hv, slot_stride) != KDA_OK)
+    return KDA_ERR_SHAPE;
   if (a->tokens < 0 || a->tokens > 8)
     return fail(KDA_ERR_UNSUPPORTED, "tokens per request must lie in [0, 8], got %d", a->tokens);
   const int T = a->tokens > 1 ? a->tokens : 1;
@@ -364,6 +420,8 @@ KDA_API kda_status kda_decode(const kda_decode_args* a) {
   L.tokens = T;
   L.cols = a->state_index_cols;
   L.accepted = a->num_accepted_tokens;
+  L.strides = strides;
+  L.slot_stride = slot_stride;
   hipError_t e = kda::launch_decode(L);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const E* __restrict__ q,
                                                    int hqk, int hv, int use_l2,
                                                    E* __restrict__ qg, E* __restrict__ kg_t,
                                                    float* __restrict__ decay,
-                                                   const GateArgs ga) {
+                                                   const GateArgs ga, const InStrides is) {
   constexpr int SK = D + 4;
   __shared__ float sG[C][SK];
   E* sKg = reinterpret_cast<E*>(&sG[0][0]);   // kg tile [64][SKG] after G is consumed
@@ -235,9 +235,9 @@ __global__ __launch_bounds__(256) void prep_kernel(const E* __restrict__ q,
   const int L = p.L;
 
   float qn[4][8], kn[4][8], gx[4][8];
-  load_rows4(q + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, qn);
-  load_rows4(k + ((size_t)p.t0 * hqk + hq) * D, hqk * D, L, kn);
-  load_rows4(g + ((size_t)p.t0 * hv + hq * grp) * D, hv * D, L, gx);
+  load_rows4(q + (size_t)p.t0 * is.q + hq * D, (int)is.q, L, qn);
+  load_rows4(k + (size_t)p.t0 * is.k + hq * D, (int)is.k, L, kn);
+  load_rows4(g + (size_t)p.t0 * is.g + hq * grp * D, (int)is.g, L, gx);
   if (use_l2) {
     l2norm_rows4(qn);
     l2norm_rows4(kn);
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const E* __restrict__ q,
     const int h = hq * grp + gi;
     if (gi > 0) {
       lds_barrier();
-      load_rows4(g + ((size_t)p.t0 * hv + h) * D, hv * D, L, gx);
+      load_rows4(g + (size_t)p.t0 * is.g + h * D, (int)is.g, L, gx);
     }
     if (ga.a_log) {
       // raw gate -> log-decay; rows past L stay 0
@@ -495,7 +495,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     const E* __restrict__ g, const E* __restrict__ beta, const int4* __restrict__ table,
     int hqk, int hv, int use_l2, E* __restrict__ w_out, E* __restrict__ u_t,
     E* __restrict__ aqk, E* __restrict__ qg, E* __restrict__ kg_t, float* __restrict__ decay,
-    int items, int* __restrict__ counter, const GateArgs ga) {
+    int items, int* __restrict__ counter, const GateArgs ga, const InStrides is) {
   constexpr bool SPLIT = std::is_same<E, float>::value;
   using TE = typename TileT<E>::T;
   constexpr int ST = D + (SPLIT ? 4 : 8);        // row stride of the [64 t][128] tiles
@@ -543,10 +543,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   float gA = 0.f, gB[8];  // gate parameters of the item's head (with A_log)
   auto prefetch = [&](int it_, const ChunkPos& pp, int tid) {
     const int h_ = it_ % hv, hq_ = h_ / grp;
-    raw_load(q + ((size_t)pp.t0 * hqk + hq_) * D, hqk * D, pp.L, rq, tid);
-    raw_load(k + ((size_t)pp.t0 * hqk + hq_) * D, hqk * D, pp.L, rk, tid);
-    raw_load(g + ((size_t)pp.t0 * hv + h_) * D, hv * D, pp.L, rgt, tid);
-    rb = beta[(size_t)(pp.t0 + min(tid, pp.L - 1)) * hv + h_];
+    raw_load(q + (size_t)pp.t0 * is.q + hq_ * D, (int)is.q, pp.L, rq, tid);
+    raw_load(k + (size_t)pp.t0 * is.k + hq_ * D, (int)is.k, pp.L, rk, tid);
+    raw_load(g + (size_t)pp.t0 * is.g + h_ * D, (int)is.g, pp.L, rgt, tid);
+    rb = beta[(size_t)(pp.t0 + min(tid, pp.L - 1)) * is.beta + h_];
     if (ga.a_log) {
       gA = ga.a_log[h_];
       gate_bias8(ga, h_, 8 * (tid & 15), gB);
@@ -759,7 +759,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   // products above
   // (rows past L are not zeroed: they meet b = 0 columns of T')
   RawRows<E> rv;
-  raw_load(v + ((size_t)p.t0 * hv + h) * D, hv * D, L, rv, tid);
+  raw_load(v + (size_t)p.t0 * is.v + h * D, (int)is.v, L, rv, tid);
   if (nok) prefetch(nitem, np, tid);  // after v, so waiting for v leaves these in flight
   lds_barrier();
   // (kn 2^G)^T into R0 and v^T into R1 (rows: channels 8 j + e), each
@@ -894,6 +894,7 @@ struct WalkArgs {
   void* fin;
   int state_bf16;
   float* cache;
+  int64_t slot_stride;  // elements between paged state slots
   const int32_t* slots;
   const uint8_t* has_init;
   int num_slots;
@@ -1018,7 +1019,7 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(const WalkArgs<E> a) {
       }
       return;
     }
-    row = a.cache + ((size_t)slot * hv + h) * PLANE;
+    row = a.cache + (size_t)slot * a.slot_stride + (size_t)h * PLANE;
   }
   // state in (src) and out (dst); dense initial / final states may be bf16
   const bool dense_bf = !a.cache && a.state_bf16;
@@ -1351,7 +1352,7 @@ __global__ __launch_bounds__(64) void compose_kernel(const WalkArgs<E> a) {
   if (a.cache) {
     const int slot = a.slots[n];
     if (slot < 0 || slot >= a.num_slots) return;
-    if (a.has_init[n]) src = a.cache + ((size_t)slot * hv + h) * PLANE;
+    if (a.has_init[n]) src = a.cache + (size_t)slot * a.slot_stride + (size_t)h * PLANE;
   } else if (a.init) {
     src_bf = a.state_bf16 != 0;
     src = dense_plane(a.init, (size_t)n * hv + h, src_bf);
@@ -1450,7 +1451,8 @@ static hipError_t launch_staged_t(const ChunkLaunch& L) {
     if (!L.fuse_prep)
       hipLaunchKernelGGL(prep_kernel<E>, dim3((unsigned)L.max_chunks, L.hqk), dim3(256), 0, st,
                          (const E*)L.q, (const E*)L.k, (const E*)L.g, (const int4*)L.table,
-                         L.hqk, L.hv, L.use_l2, (E*)L.qg, (E*)L.kg_t, L.decay, L.gate);
+                         L.hqk, L.hv, L.use_l2, (E*)L.qg, (E*)L.kg_t, L.decay, L.gate,
+                         L.strides);
     mark(L, 2);
     // persistent WY grid: the resident workgroups (LDS allows two per CU for
     // bf16 tiles, one for fp32)
@@ -1463,13 +1465,13 @@ static hipError_t launch_staged_t(const ChunkLaunch& L) {
                          (const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta,
                          (const int4*)L.table, L.hqk, L.hv, L.use_l2, (E*)L.w, (E*)L.u,
                          (E*)L.aqk, (E*)L.qg, (E*)L.kg_t, L.decay, items, wy_counter,
-                         L.gate);
+                         L.gate, L.strides);
     else
       hipLaunchKernelGGL((wy_kernel<E, false>), grid, dim3(256), 0, st, (const E*)L.q,
                          (const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta,
                          (const int4*)L.table, L.hqk, L.hv, L.use_l2, (E*)L.w, (E*)L.u,
                          (E*)L.aqk, (E*)nullptr, (E*)nullptr, (float*)nullptr, items,
-                         wy_counter, L.gate);
+                         wy_counter, L.gate, L.strides);
   } else {
     mark(L, 2);
   }
@@ -1480,7 +1482,7 @@ static hipError_t launch_staged_t(const ChunkLaunch& L) {
   wa.cu = L.cu; wa.dense_len = dense_len; wa.T = T; wa.offs = L.chunk_offsets;
   wa.N = N; wa.hv = L.hv; wa.scale = L.scale;
   wa.init = L.init; wa.fin = L.fin; wa.state_bf16 = L.state_bf16;
-  wa.cache = (float*)L.cache; wa.slots = L.slots;
+  wa.cache = (float*)L.cache; wa.slot_stride = L.slot_stride; wa.slots = L.slots;
   wa.has_init = L.has_init; wa.num_slots = L.num_slots; wa.out = (E*)L.out;
   wa.units = N * L.hv; wa.max_chunks = (int)L.max_chunks; wa.groups = L.groups;
   wa.scan = L.scan; wa.zero = (const uint4*)L.zero;

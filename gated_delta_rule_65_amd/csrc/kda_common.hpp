@@ -50,6 +50,12 @@ struct GateArgs {
   int bias_bf16;
   float lower_bound;
 };
+// Elements between consecutive tokens of each input (heads stay 128 apart
+// inside a token, 1 apart for beta).
+struct InStrides {
+  int64_t q, k, v, g, beta;
+};
+
 __device__ __forceinline__ float gate_bias(const GateArgs& ga, int h, int c) {
   const size_t i = (size_t)h * D + c;
   return ga.bias_bf16 ? to_f32(reinterpret_cast<const bf16*>(ga.bias)[i])

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ g, const T* __restrict__ beta, S* __restrict__ cache,
     const int32_t* __restrict__ idx, T* __restrict__ out, int hqk, int hv, float scale,
-    int use_l2, int num_slots, const GateArgs ga) {
+    int use_l2, int num_slots, const GateArgs ga, const InStrides is, int64_t slot_stride) {
   const int unit = blockIdx.x;
   const int req = unit / hv, h = unit - req * hv;
   const int hq = h / (hv / hqk);
@@ -126,24 +126,24 @@ __global__ __launch_bounds__(256) void decode_kernel(
     if (tid < D) o[tid] = from_f32<T>(0.0f);
     return;
   }
-  S* st = cache + ((size_t)slot * hv + h) * (size_t)(D * D);
+  S* st = cache + (size_t)slot * slot_stride + (size_t)h * (D * D);
 
   // Issue the state loads first: rows r = 16 s + 4 wave + rsub, s = 0..7.
   float4 hs[8][2];
 #pragma unroll
   for (int s = 0; s < 8; ++s) row_load(st + (16 * s + 4 * wave + rsub) * D, j, hs[s]);
 
-  const T* qp = q + ((size_t)req * hqk + hq) * D;
-  const T* kp = k + ((size_t)req * hqk + hq) * D;
-  const T* gp = g + ((size_t)req * hv + h) * D;
-  const T* vp = v + ((size_t)req * hv + h) * D;
+  const T* qp = q + (size_t)req * is.q + hq * D;
+  const T* kp = k + (size_t)req * is.k + hq * D;
+  const T* gp = g + (size_t)req * is.g + h * D;
+  const T* vp = v + (size_t)req * is.v + h * D;
   float qv[8], kv[8], al[8];
   const float ga_a = ga.a_log ? exp2_fast(ga.a_log[h] * LOG2E) : 0.f;  // exp(A_log[h])
   token_qk_decay(qp, kp, gp, j, h, ga, ga_a, qv, kv, al);
   float vr[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) vr[s] = to_f32(vp[16 * s + 4 * wave + rsub]);
-  const float b = sigmoid(to_f32(beta[(size_t)req * hv + h]));
+  const float b = sigmoid(to_f32(beta[(size_t)req * is.beta + h]));
 
   if (use_l2) {
     float sq = 0.f, sk = 0.f;
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
     const T* __restrict__ g, const T* __restrict__ beta, S* __restrict__ cache,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ acc, T* __restrict__ out,
     int ntok, int cols, int hqk, int hv, float scale, int use_l2, int num_slots,
-    const GateArgs ga) {
+    const GateArgs ga, const InStrides is, int64_t slot_stride) {
   const int unit = blockIdx.x;
   const int req = unit / hv, h = unit - req * hv;
   const int hq = h / (hv / hqk);
@@ -223,23 +223,23 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
         out[(((size_t)req * ntok + t) * hv + h) * D + tid] = from_f32<T>(0.0f);
     return;
   }
-  const S* st0 = cache + ((size_t)row0 * hv + h) * (size_t)(D * D);
+  const S* st0 = cache + (size_t)row0 * slot_stride + (size_t)h * (D * D);
   float4 hs[8][2];
 #pragma unroll
   for (int s = 0; s < 8; ++s) row_load(st0 + (16 * s + 4 * wave + rsub) * D, j, hs[s]);
   const float ga_a = ga.a_log ? exp2_fast(ga.a_log[h] * LOG2E) : 0.f;  // exp(A_log[h])
   for (int t = 0; t < ntok; ++t) {
     const size_t tok = (size_t)req * ntok + t;
-    const T* qp = q + (tok * hqk + hq) * D;
-    const T* kp = k + (tok * hqk + hq) * D;
-    const T* gp = g + (tok * hv + h) * D;
-    const T* vp = v + (tok * hv + h) * D;
+    const T* qp = q + tok * is.q + hq * D;
+    const T* kp = k + tok * is.k + hq * D;
+    const T* gp = g + tok * is.g + h * D;
+    const T* vp = v + tok * is.v + h * D;
     float qv[8], kv[8], al[8];
     token_qk_decay(qp, kp, gp, j, h, ga, ga_a, qv, kv, al);
     float vr[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) vr[s] = to_f32(vp[16 * s + 4 * wave + rsub]);
-    const float b = sigmoid(to_f32(beta[tok * hv + h]));
+    const float b = sigmoid(to_f32(beta[tok * is.beta + h]));
     if (use_l2) {
       float sq = 0.f, sk = 0.f;
 #pragma unroll
@@ -261,8 +261,9 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
     for (int e = 0; e < 8; ++e) kq += kv[e] * qv[e];
     kq = row_sum16(kq);
     const int rt = ir[t];
-    S* dst = (rt >= 0 && rt < num_slots) ? cache + ((size_t)rt * hv + h) * (size_t)(D * D)
-                                         : nullptr;
+    S* dst = (rt >= 0 && rt < num_slots)
+                 ? cache + (size_t)rt * slot_stride + (size_t)h * (D * D)
+                 : nullptr;
     T* o = out + (tok * hv + h) * D;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -297,13 +298,14 @@ static hipError_t launch_decode_t(const DecodeLaunch& L) {
     hipLaunchKernelGGL((decode_multi_kernel<T, S>), grid, block, 0, (hipStream_t)L.stream,
                        (const T*)L.q, (const T*)L.k, (const T*)L.v, (const T*)L.g,
                        (const T*)L.beta, (S*)L.cache, L.idx, L.accepted, (T*)L.out, L.tokens,
-                       L.cols, L.hqk, L.hv, L.scale, L.use_l2, L.num_slots, L.gate);
+                       L.cols, L.hqk, L.hv, L.scale, L.use_l2, L.num_slots, L.gate, L.strides,
+                       L.slot_stride);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((decode_kernel<T, S>), grid, block, 0, (hipStream_t)L.stream,
                      (const T*)L.q, (const T*)L.k, (const T*)L.v, (const T*)L.g,
                      (const T*)L.beta, (S*)L.cache, L.idx, (T*)L.out, L.hqk, L.hv, L.scale,
-                     L.use_l2, L.num_slots, L.gate);
+                     L.use_l2, L.num_slots, L.gate, L.strides, L.slot_stride);
   return hipGetLastError();
 }
 

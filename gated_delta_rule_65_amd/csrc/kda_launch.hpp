@@ -20,6 +20,8 @@ struct DecodeLaunch {
   int tokens;                 // tokens per request (1..8)
   int cols;                   // columns of a 2-D state_indices, 0 for 1-D
   const int32_t* accepted;    // [n] accepted-token counts or NULL
+  InStrides strides;          // per-token input strides (resolved, never 0)
+  int64_t slot_stride;        // elements between cache slots (resolved)
 };
 hipError_t launch_decode(const DecodeLaunch& L);
 
@@ -53,6 +55,8 @@ struct ChunkLaunch {
   const int32_t* ckpt_off;    // [N] token offsets
   const int32_t* ckpt_idx;    // [N] destination rows or NULL (row n)
   int ckpt_rows;
+  InStrides strides;          // per-token input strides (resolved, never 0)
+  int64_t slot_stride;        // elements between paged state slots (resolved)
   void** events;              // optional stage events (KDA_EV_*), may be NULL
   int num_events;
   void* stream;

@@ -162,6 +162,22 @@ typedef struct kda_chunk_args {
      state is rounded to nearest even.  The paged state_cache and the
      checkpoint rows are always fp32 (page "vllm.models.kimi_k3.amd.ops.kda_chunk"). */
   int32_t state_dtype;
+  /* Input strides (optional), in elements between consecutive tokens of
+     q, k, v, g and beta; 0 means dense (hqk*128 for q and k, hv*128 for v
+     and g, hv for beta).  Heads stay 128 elements apart inside a token (1
+     for beta).  This serves views into a wider fused projection output,
+     whose beta and g slices keep the projection's row stride and whose q
+     may be a band view (fused_kda_prologue, page
+     "vllm.models.kimi_k3.amd.ops.kda_chunk").  A nonzero stride is at least
+     the dense one and at most 2^24; for q, k, v and g it also keeps every
+     token row 16-byte aligned (a multiple of 16 bytes). */
+  int64_t q_stride, k_stride, v_stride, g_stride, beta_stride;
+  /* Elements between consecutive slots of the paged state pool (0: dense,
+     hv*128*128).  Pools whose slots are padded to a cache page pass the
+     padded stride (KdaTcVerify's state layout, page
+     "vllm.models.kimi_k3.nvidia.recoverssm.cutedsl.verify"): at least
+     hv*128*128 and a multiple of 8 elements. */
+  int64_t state_slot_stride;
 } kda_chunk_args;
 
 /* Stage boundaries of kda_chunk_fwd (indices into stage_events).  Event i is
@@ -287,6 +303,23 @@ typedef struct kda_decode_args {
      after each token, as repeated single-token decode would store it
      (gated_delta_rule_decode's bf16 state, page "mate.kda"). */
   int32_t state_dtype;
+  /* Input strides (optional), in elements between consecutive tokens of
+     q, k, v, g and beta (token n*T + t with T tokens per request); 0 means
+     dense (hqk*128 for q and k, hv*128 for v
+     and g, hv for beta).  Heads stay 128 elements apart inside a token (1
+     for beta).  This serves views into a wider fused projection output,
+     whose beta and g slices keep the projection's row stride and whose q
+     may be a band view (fused_kda_prologue, page
+     "vllm.models.kimi_k3.amd.ops.kda_chunk").  A nonzero stride is at least
+     the dense one and at most 2^24; for q, k, v and g it also keeps every
+     token row 16-byte aligned (a multiple of 16 bytes). */
+  int64_t q_stride, k_stride, v_stride, g_stride, beta_stride;
+  /* Elements between consecutive slots of state_cache (0: dense,
+     hv*128*128).  Pools whose slots are padded to a cache page pass the
+     padded stride (KdaTcVerify's state layout, page
+     "vllm.models.kimi_k3.nvidia.recoverssm.cutedsl.verify"): at least
+     hv*128*128 and a multiple of 8 elements. */
+  int64_t state_slot_stride;
 } kda_decode_args;
 
 kda_status kda_decode(const kda_decode_args *a);

@@ -334,3 +334,55 @@ def test_misaligned_tensor_pointers_are_rejected(lib):
                     state_cache=odd)
     assert lib.kda_decode(ctypes.byref(a)) == B.KDA_ERR_ARG
     assert b"16-byte" in lib.kda_last_error()
+
+
+def test_token_stride_of_projection_views():
+    """Views into a wider projection output pass their per-token stride; a
+    contiguous tensor passes 0; layouts the kernels cannot read are refused."""
+    T, W = 10, 3 * 256 + 2 * 512 + 4
+    proj = torch.zeros(T, W)
+    q = proj[:, :256].view(T, 2, 128)
+    g = proj[:, 768:1280].view(T, 4, 128)
+    beta = proj[:, W - 4:]
+    assert B._token_stride("q", q, 2) == W
+    assert B._token_stride("g", g, 2) == W
+    assert B._token_stride("beta", beta, 1) == W
+    assert B._token_stride("q", q.contiguous(), 2) == 0
+    # [B, T, H, 128] with a batch stride of T tokens flattens to one stride
+    q4 = proj.view(2, 5, W)[..., :256].view(2, 5, 2, 128)
+    assert B._token_stride("q", q4, 2) == W
+    with pytest.raises(ValueError, match="fixed stride"):   # channels not contiguous
+        B._token_stride("q", torch.zeros(T, 128, 2).transpose(1, 2), 2)
+    with pytest.raises(ValueError, match="fixed stride"):   # heads not 128 apart
+        B._token_stride("q", torch.zeros(T, 2, 256)[..., :128], 2)
+    with pytest.raises(ValueError, match="fixed stride"):   # tokens not one stride apart
+        B._token_stride("q", torch.zeros(4, 8, 2, 128)[:, :5], 2)
+    pool = torch.zeros(3, 2 * 128 * 128 + 64)
+    cache = pool[:, :2 * 128 * 128].view(3, 2, 128, 128)
+    assert B._slot_stride(cache) == 2 * 128 * 128 + 64
+    assert B._slot_stride(cache.contiguous()) == 0
+    with pytest.raises(ValueError, match="dense"):
+        B._slot_stride(torch.zeros(3, 2, 128, 128).transpose(2, 3))
+
+
+def test_stride_checks(lib):
+    # chunk_args: hqk = 2, hv = 4, bf16
+    assert ws_size(lib, chunk_args(q_stride=256))[0] == B.KDA_OK          # = dense
+    assert ws_size(lib, chunk_args(q_stride=1024 + 8))[0] == B.KDA_OK     # 16-byte rows
+    assert ws_size(lib, chunk_args(q_stride=255))[0] == B.KDA_ERR_SHAPE   # below dense
+    assert ws_size(lib, chunk_args(g_stride=512 + 4))[0] == B.KDA_ERR_ARG  # 8-byte rows
+    assert ws_size(lib, chunk_args(beta_stride=3))[0] == B.KDA_ERR_SHAPE
+    assert ws_size(lib, chunk_args(beta_stride=4 + 3))[0] == B.KDA_OK     # beta: any stride
+    assert ws_size(lib, chunk_args(v_stride=(1 << 24) + 8))[0] == B.KDA_ERR_SHAPE
+    assert ws_size(lib, chunk_args(state_slot_stride=4 * 128 * 128))[0] == B.KDA_ERR_SHAPE
+    paged = dict(state_cache=FAKE, state_indices=FAKE, has_initial_state=FAKE, num_slots=4)
+    assert ws_size(lib, chunk_args(state_slot_stride=4 * 128 * 128 + 8, **paged))[0] == B.KDA_OK
+    assert ws_size(lib, chunk_args(state_slot_stride=4 * 128 * 128 - 8,
+                                   **paged))[0] == B.KDA_ERR_SHAPE
+    assert ws_size(lib, chunk_args(state_slot_stride=4 * 128 * 128 + 4,
+                                   **paged))[0] == B.KDA_ERR_SHAPE
+    ptrs = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, out=FAKE, state_cache=FAKE)
+    assert lib.kda_decode(ctypes.byref(decode_args(q_stride=100, **ptrs))) == B.KDA_ERR_SHAPE
+    assert lib.kda_decode(ctypes.byref(decode_args(k_stride=260, **ptrs))) == B.KDA_ERR_ARG
+    assert lib.kda_decode(ctypes.byref(decode_args(state_slot_stride=100,
+                                                   **ptrs))) == B.KDA_ERR_SHAPE

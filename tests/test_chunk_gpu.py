@@ -573,3 +573,79 @@ def test_bf16_state_b0_passes_through_bitwise():
                          output_final_state=True, cu_seqlens=b.cu_seqlens.to(DEV))
     torch.cuda.synchronize()
     assert torch.equal(fin.cpu(), init16)
+
+
+# ------------------------------------------------- strided (projection) inputs
+
+def projection_views(tensors, dev, pad=8):
+    """q, k, v, g ([T, H, 128]) and beta ([T, Hv]) copied into bands of one
+    [T, W] buffer, as the slices of a fused projection output; returns views.
+    W keeps every token row 16-byte aligned."""
+    T = tensors[0].shape[0]
+    flat = [t.reshape(T, -1) for t in tensors]
+    W = sum(f.shape[1] for f in flat) + pad
+    W += (-W) % 8
+    proj = torch.full((T, W), float("nan"), dtype=tensors[0].dtype, device=dev)
+    views, off = [], 0
+    for t, f in zip(tensors, flat):
+        proj[:, off:off + f.shape[1]] = f.to(dev)
+        views.append(proj[:, off:off + f.shape[1]].view(t.shape))
+        off += f.shape[1]
+    return views, proj
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("path,groups", [(B.PATH_FUSED, 1), (B.PATH_STAGED, 1),
+                                         (B.PATH_FUSED, 3)])
+def test_strided_projection_inputs(dtype, path, groups):
+    """Inputs read through a per-token stride (bands of one projection buffer,
+    NaN padding between them) equal the contiguous run bit for bit, and the
+    oracle at the usual bar."""
+    b = inputs.make_chunk([300, 190, 64], 2, 4, dtype=dtype, g_scale=0.5, seed=97, init=True)
+    say("strided", dtype, path, groups)
+    (qv, kv, vv, gv, bv), proj = projection_views([b.q, b.k, b.v, b.g, b.beta], DEV)
+    assert not qv.is_contiguous() and qv.stride(0) == proj.shape[1]
+    init = b.initial_state.to(DEV)
+    cu = b.cu_seqlens.to(DEV)
+    kw = dict(scale=b.scale, initial_state=init, output_final_state=True, cu_seqlens=cu,
+              path=path, groups=groups)
+    out_s, fin_s = B.chunk_kda(qv, kv, vv, gv, bv, **kw)
+    out_c, fin_c = B.chunk_kda(*gpu(b), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out_s, out_c) and torch.equal(fin_s, fin_c)
+    o_ref, s_ref = oracle_dense(b)
+    assert rel(out_s.float().cpu().numpy(), o_ref) < tol(dtype)
+    assert rel(fin_s.cpu().numpy(), s_ref) < tol(dtype)
+
+
+def test_strided_inputs_with_gate_and_padded_paged_pool():
+    """Projection views with the gate parameters, into a paged pool whose slots
+    are padded (slot stride above Hv*128*128)."""
+    b = inputs.make_chunk([200, 130], 1, 2, dtype=torch.bfloat16, seed=96,
+                          paged_slots=5)
+    hv = 2
+    al = torch.tensor([0.3, -0.2])
+    dtb = torch.randn(hv, 128, generator=torch.Generator().manual_seed(3)) * 0.5
+    (qv, kv, vv, gv, bv), _ = projection_views([b.q, b.k, b.v, b.g, b.beta], DEV)
+    plane = hv * 128 * 128
+    pool = torch.full((5, plane + 192), float("nan"), device=DEV)
+    cache = pool[:, :plane].view(5, hv, 128, 128)
+    cache.copy_(b.state_cache.to(DEV))
+    ref_cache = b.state_cache.to(DEV).clone()
+    kw = dict(scale=b.scale, cu_seqlens=b.cu_seqlens.to(DEV),
+              state_indices=b.state_indices.to(DEV), has_initial_state=b.has_initial_state.to(DEV),
+              A_log=al.to(DEV), dt_bias=dtb.to(DEV))
+    out_s = B.chunk_kda(qv, kv, vv, gv, bv, state_cache=cache, **kw)
+    out_c = B.chunk_kda(*gpu(b), state_cache=ref_cache, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out_s, out_c)
+    assert torch.equal(cache, ref_cache)
+    assert torch.isnan(pool[:, plane:]).all()   # the padding is never written
+    o_ref, s_ref = oracle.recurrence(b.q, b.k, b.v, b.g, b.beta, cu_seqlens=b.cu_seqlens,
+                                     scale=b.scale, initial_state=b.state_cache[
+                                         b.state_indices.long()] * b.has_initial_state.view(
+                                         -1, 1, 1, 1).float(),
+                                     A_log=al.double(), dt_bias=dtb.double())
+    assert rel(out_s.float().cpu().numpy(), o_ref) < 1e-2
+    live = b.state_indices.long().numpy()
+    assert rel(cache.cpu().numpy()[live], s_ref) < 1e-2

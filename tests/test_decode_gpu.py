@@ -260,3 +260,68 @@ def test_multi_token_decode_bf16_state_cache():
     ro, rc = oracle.decode_multi(q, k, v, g, beta, cache, idx, acc, state_bf16=True)
     assert rel(out.float().cpu().numpy(), ro) < 1e-2
     assert rel(cd.cpu().float().numpy(), rc) < 1e-2
+
+
+# ------------------------------------------------- strided (projection) inputs
+
+def projection_views(tensors, pad=8):
+    """Tensors copied into bands of one [tokens, W] buffer (NaN between
+    bands), returned as views with a per-token stride of W elements."""
+    n = tensors[0].shape[0] * (tensors[0].shape[1] if tensors[0].dim() == 4 else 1)
+    flat = [t.reshape(n, -1) for t in tensors]
+    W = sum(f.shape[1] for f in flat) + pad
+    W += (-W) % 8
+    proj = torch.full((n, W), float("nan"), dtype=tensors[0].dtype, device=DEV)
+    views, off = [], 0
+    for t, f in zip(tensors, flat):
+        proj[:, off:off + f.shape[1]] = f.to(DEV)
+        views.append(proj[:, off:off + f.shape[1]].view(t.shape))
+        off += f.shape[1]
+    return views
+
+
+def padded_pool(cache, pad=64):
+    """The cache as a pool whose slots are padded by `pad` elements (NaN)."""
+    slots, plane = cache.shape[0], cache[0].numel()
+    pool = torch.full((slots, plane + pad), float("nan"), dtype=cache.dtype, device=DEV)
+    view = pool[:, :plane].view(cache.shape)
+    view.copy_(cache.to(DEV))
+    return pool, view
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16])
+def test_decode_strided_inputs_and_padded_pool(dtype):
+    b = inputs.make_decode(40, 2, 4, 64, dtype=dtype, seed=63)
+    idx = b.state_indices.clone()
+    idx[3] = -1
+    views = projection_views([b.q, b.k, b.v, b.g, b.beta])
+    assert not views[0].is_contiguous()
+    pool, cache_s = padded_pool(b.state_cache)
+    cache_c = b.state_cache.to(DEV)
+    out_s = B.kda_decode(*views, cache_s, idx.to(DEV))
+    out_c = B.kda_decode(*(t.to(DEV) for t in (b.q, b.k, b.v, b.g, b.beta)), cache_c,
+                         idx.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(out_s, out_c) and torch.equal(cache_s, cache_c)
+    assert torch.isnan(pool[:, 4 * 128 * 128:]).all()
+    ro, rc = oracle.decode(b.q, b.k, b.v, b.g, b.beta, b.state_cache, idx)
+    assert rel(out_s.float().cpu().numpy(), ro) < (1e-4 if dtype == torch.float32 else 1e-2)
+
+
+def test_multi_token_decode_strided_inputs_bf16_padded_pool():
+    Bn, T = 5, 4
+    q, k, v, g, beta, cache = spec_case(Bn, T, 1, 2, 30, torch.bfloat16, seed=64)
+    cache = cache.to(torch.bfloat16)
+    idx = torch.arange(Bn * T, dtype=torch.int32).reshape(Bn, T)
+    acc = torch.tensor([1, 2, 4, 3, 1], dtype=torch.int32)
+    views = projection_views([q, k, v, g, beta])
+    pool, cache_s = padded_pool(cache)
+    cache_c = cache.to(DEV)
+    out_s = B.kda_decode(*views, cache_s, idx.to(DEV), num_accepted_tokens=acc.to(DEV))
+    out_c = B.kda_decode(*(t.to(DEV) for t in (q, k, v, g, beta)), cache_c, idx.to(DEV),
+                         num_accepted_tokens=acc.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(out_s, out_c) and torch.equal(cache_s, cache_c)
+    assert torch.isnan(pool[:, 2 * 128 * 128:].float()).all()
+    ro, rc = oracle.decode_multi(q, k, v, g, beta, cache, idx, acc, state_bf16=True)
+    assert rel(out_s.float().cpu().numpy(), ro) < 1e-2
