@@ -960,8 +960,16 @@ __device__ __forceinline__ float* scan_plane(float* scan, int g, int n, int h, i
 //         transfer P_g = prod_c (diag(d_c) - kg_c^T w_c)).  No outputs.
 // MODE 2: group pass two.  Group g is walked from its composed start state
 //         H_in(g); outputs for its tokens, the final state from the last group.
-template <typename E, int NW, int MODE>
-__global__ __launch_bounds__(64 * NW) void walk_kernel(const WalkArgs<E> a) {
+//
+// With LW > 0 the workgroup carries LW loader waves besides the NW compute
+// waves (on SIMDs the compute waves leave idle).  The loaders issue every
+// DMA of the ring, so the compute waves issue no loads at all, and they
+// also warm the L2 with the K-side lines of the chunk after next: a chunk
+// step is bound by how fast a CU can pull its ~60 KB of tiles, which is
+// far faster from L2 than from HBM.  Both roles pass the same single
+// barrier per chunk.
+template <typename E, int NW, int MODE, int LW = 0>
+__global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> a) {
   constexpr bool SPLIT = std::is_same<E, float>::value;
   constexpr int STAGES = SPLIT ? 1 : 2;
   constexpr bool OUT = MODE != 1;
@@ -976,6 +984,7 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(const WalkArgs<E> a) {
   // the stage being filled from the stage being read
   __shared__ uint4 smemA[STAGE];
   __shared__ uint4 smemB[STAGES == 2 ? STAGE : 1];
+  __shared__ uint32_t lsink[LW > 0 ? 64 : 1];  // target of the loaders' L2 warm-up (never read)
 
   // The column blocks of one (sequence, head, group) get ids with equal
   // id % 8, so they land on one XCD and share its L2 for the K-side tiles.
@@ -992,6 +1001,10 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(const WalkArgs<E> a) {
   const int vb = tcols ? cb - a.nvb : cb;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  static_assert(LW == 0 || STAGES == 2, "loader waves serve the two-stage ring");
+  const bool loader = LW > 0 && wave >= NW;  // wave-uniform role
+  constexpr int DW = LW > 0 ? LW : NW;         // waves that issue the DMA
+  const int dwave = LW > 0 ? wave - NW : wave;
   const int l16 = lane & 15, gq = lane >> 4;
   const int v0 = vb * BV;                  // first column of the block
   const int vl = 16 * wave + l16;          // this lane's C-tile column inside the block
@@ -1010,7 +1023,7 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(const WalkArgs<E> a) {
     const int slot = a.slots[n];
     if (slot < 0 || slot >= a.num_slots) {
       // null slot: zero output rows, no state traffic
-      if (OUT) {
+      if (OUT && !loader) {
         const int tb = sp.bos + C * jc0, te = min(sp.eos, sp.bos + C * jc1);
         for (int idx = tid; idx < (te - tb) * BV; idx += NT) {
           const int t = idx / BV, vv = idx - t * BV;
@@ -1042,11 +1055,16 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(const WalkArgs<E> a) {
     }
   }
 
+  if (loader) {  // loader waves hold no state columns
+    src = nullptr;
+    dst = nullptr;
+  }
+
   // mid-prefill snapshot: the step after which it is taken (-1: none).  Pass
   // one of the group scan walks from zero, so only modes 0 and 2 take it.
   int ck_step = -1;
   float* ck_dst = nullptr;
-  if (MODE != 1 && a.ckpt) {
+  if (MODE != 1 && a.ckpt && !loader) {
     const int off = a.ckpt_off[n];
     const int row = a.ckpt_idx ? a.ckpt_idx[n] : n;
     if (off > 0 && off % C == 0 && off <= sp.eos - sp.bos && row >= 0 && row < a.ckpt_rows) {
@@ -1077,32 +1095,111 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(const WalkArgs<E> a) {
     const int t0 = sp.bos + C * jc;
     const int L = min(C, sp.eos - t0);
     const size_t rowb = (size_t)hv * D * sizeof(E);
-    dma_tile<C, P128, NW, true>(base + OFF_W, a.w + ((size_t)t0 * hv + h) * D, rowb, L, zero,
-                                wave, lane);
+    dma_tile<C, P128, DW, true>(base + OFF_W, a.w + ((size_t)t0 * hv + h) * D, rowb, L, zero,
+                                dwave, lane);
     if (OUT)
-      dma_tile<C, P128, NW, true>(base + OFF_Q, a.qg + ((size_t)t0 * hv + h) * D, rowb, L, zero,
-                                  wave, lane);
+      dma_tile<C, P128, DW, true>(base + OFF_Q, a.qg + ((size_t)t0 * hv + h) * D, rowb, L, zero,
+                                  dwave, lane);
   };
   auto issue_rest = [&](int jc, uint4* base) {
     const int c = c_first + jc;
     const int t0 = sp.bos + C * jc;
     const int L = min(C, sp.eos - t0);
     if (OUT)
-      dma_tile<C, P64, NW, true>(base + OFF_A, a.aqk + ((size_t)t0 * hv + h) * C,
-                                 (size_t)hv * C * sizeof(E), L, zero, wave, lane);
-    dma_tile<D, P64, NW, false>(base + OFF_K, a.kg_t + ((size_t)c * hv + h) * D * C,
-                                C * sizeof(E), D, zero, wave, lane);
+      dma_tile<C, P64, DW, true>(base + OFF_A, a.aqk + ((size_t)t0 * hv + h) * C,
+                                 (size_t)hv * C * sizeof(E), L, zero, dwave, lane);
+    dma_tile<D, P64, DW, false>(base + OFF_K, a.kg_t + ((size_t)c * hv + h) * D * C,
+                                C * sizeof(E), D, zero, dwave, lane);
     if (!tcols)
-      dma_tile<BV, P64, NW, false>(base + OFF_U, a.u_t + (((size_t)c * hv + h) * D + v0) * C,
-                                   C * sizeof(E), BV, zero, wave, lane);
-    if (wave == NW - 1) {
+      dma_tile<BV, P64, DW, false>(base + OFF_U, a.u_t + (((size_t)c * hv + h) * D + v0) * C,
+                                   C * sizeof(E), BV, zero, dwave, lane);
+    if (dwave == DW - 1) {
       // decay: 32 pieces, lanes 32..63 fill the pad from the zero page
       const char* gp = lane < 32 ? (const char*)(a.decay + ((size_t)c * hv + h) * D) + 16 * lane
                                  : (const char*)zero;
       __builtin_amdgcn_global_load_lds(gp, (lds_vptr)(base + OFF_D), 16, 0, 0);
     }
   };
-  if (jc0 < jc1) {
+  if constexpr (LW > 0) {
+    if (loader) {
+      const size_t rowb = (size_t)hv * D * sizeof(E), rowa = (size_t)hv * C * sizeof(E);
+      // L2 warm-up.  The column-block workgroups of a (sequence, head) share
+      // one XCD's L2 and read the same K-side tiles; each touches its share
+      // of their 128-byte lines (and its own u_t lines) two chunks ahead, so
+      // the stage DMA of the next step finds them in L2 (measured on the
+      // dense 4 x 4096 x 16-head prefill: two ahead beats three, four, six
+      // and eight).  One word per line goes by LDS DMA into a sink that
+      // nobody reads.
+      static_assert(NW == 2 && LW == 2 && sizeof(E) == 2, "warm-up line map: bf16, 32 columns");
+      constexpr int LW_ = 128, LQ = 128, LA = 64, LK = 128, LD = 4;  // lines per tile
+      constexpr int NSH = LW_ + LQ + LA + LK + LD;                    // shared lines
+      constexpr int LU = BV * C * 2 / 128;                            // own u_t lines
+      const int per = (NSH + a.nvb - 1) / a.nvb;
+      auto warm = [&](int jw) __attribute__((always_inline)) {
+        const int c = c_first + jw;
+        const int t0 = sp.bos + C * jw;
+        const int L = min(C, sp.eos - t0);
+        const char* wb = (const char*)(a.w + ((size_t)t0 * hv + h) * D);
+        const char* qb = (const char*)(a.qg + ((size_t)t0 * hv + h) * D);
+        const char* ab = (const char*)(a.aqk + ((size_t)t0 * hv + h) * C);
+        const char* kb = (const char*)(a.kg_t + ((size_t)c * hv + h) * D * C);
+        const char* db = (const char*)(a.decay + ((size_t)c * hv + h) * D);
+        const char* ub = (const char*)(a.u_t + (((size_t)c * hv + h) * D + v0) * C);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int f = 128 * k + 64 * dwave + lane;
+          const char* p = nullptr;
+          if (f < per) {
+            const int i = vb * per + f;
+            if (i < LW_) {
+              if ((i >> 1) < L) p = wb + (size_t)(i >> 1) * rowb + 128 * (i & 1);
+            } else if (i < LW_ + LQ) {
+              const int j = i - LW_;
+              if (OUT && (j >> 1) < L) p = qb + (size_t)(j >> 1) * rowb + 128 * (j & 1);
+            } else if (i < LW_ + LQ + LA) {
+              const int r = i - LW_ - LQ;
+              if (OUT && r < L) p = ab + (size_t)r * rowa;
+            } else if (i < LW_ + LQ + LA + LK) {
+              p = kb + 128 * (i - LW_ - LQ - LA);
+            } else if (i < NSH) {
+              p = db + 128 * (i - LW_ - LQ - LA - LK);
+            }
+          } else if (f < per + LU) {
+            p = ub + 128 * (f - per);
+          }
+          // idle lanes read the zero page: every lane loads, on every path
+          __builtin_amdgcn_global_load_lds(p ? p : (const char*)zero, (lds_vptr)lsink, 4, 0, 0);
+        }
+      };
+      // The loader loop: one barrier per chunk, as in the compute loop.  A
+      // loader first waits until its DMA of chunk jc has landed, leaving only
+      // the two warm-up loads issued after it in flight (vmcnt(2)); after the
+      // barrier the stage of chunk jc - 1 is free and takes chunk jc + 1.
+      // No release fence here: with the warm-up DMA in flight it would wait
+      // for every outstanding load; the asm clobbers keep the compiler from
+      // moving memory accesses across the barrier.
+      if (jc0 >= jc1) return;
+      auto cl = [&](int j) { return min(j, jc1 - 1); };
+      issue_wq(jc0, smemA);
+      issue_rest(jc0, smemA);
+      warm(cl(jc0 + 1));
+      for (int jc = jc0; jc < jc1; ++jc) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0x0f72);  // vmcnt(2): chunk jc's DMA has landed
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (jc + 1 < jc1) {
+          uint4* nxt = ((jc + 1 - jc0) & 1) ? smemB : smemA;
+          issue_wq(jc + 1, nxt);
+          issue_rest(jc + 1, nxt);
+        }
+        warm(cl(jc + 2));
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // no DMA in flight when the wave ends
+      return;
+    }
+  }
+  if (LW == 0 && jc0 < jc1) {
     issue_wq(jc0, smemA);
     issue_rest(jc0, smemA);
   }
@@ -1110,9 +1207,9 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(const WalkArgs<E> a) {
   auto body = [&](int jc, uint4* cur, uint4* nxt) {
     const int t0 = sp.bos + C * jc;
     const int L = min(C, sp.eos - t0);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA of chunk jc has landed
-    lds_barrier();                  // ... and every other wave's
-    const bool more = STAGES == 2 && jc + 1 < jc1;
+    if (LW == 0) __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA of chunk jc has landed
+    lds_barrier();  // ... and every other wave's (loaders: their LDS writes)
+    const bool more = LW == 0 && STAGES == 2 && jc + 1 < jc1;
     const uint4* tW = cur + OFF_W;
     const uint4* tQ = cur + OFF_Q;
     const uint4* tA = cur + OFF_A;
@@ -1414,26 +1511,35 @@ static void mark(const ChunkLaunch& L, int i) {
   if (i < L.num_events && L.events[i]) (void)hipEventRecord((hipEvent_t)L.events[i], (hipStream_t)L.stream);
 }
 
+// Loader waves of the walk: the two-wave bf16 walk leaves two SIMDs of the
+// CU idle, and two loader waves there take over its DMA.
+template <typename E, int NW>
+constexpr int walk_loaders() {
+  return (!std::is_same<E, float>::value && NW == 2) ? 2 : 0;
+}
+
 template <typename E, int NW>
 static void launch_walk(const ChunkLaunch& L, const WalkArgs<E>& wa) {
   hipStream_t st = (hipStream_t)L.stream;
   const int nvb = wa.nvb, units = wa.units, G = wa.groups;
+  constexpr int LW = walk_loaders<E, NW>();
+  const dim3 block(64 * (NW + LW));
   if (G <= 1) {
     const unsigned grid = (unsigned)(((units + 7) / 8) * 8 * nvb);
-    hipLaunchKernelGGL((walk_kernel<E, NW, 0>), dim3(grid), dim3(64 * NW), 0, st, wa);
+    hipLaunchKernelGGL((walk_kernel<E, NW, 0, LW>), dim3(grid), block, 0, st, wa);
     mark(L, 4);
     mark(L, 5);
     mark(L, 6);
     return;
   }
   const int ug = units * G;
-  hipLaunchKernelGGL((walk_kernel<E, NW, 1>), dim3((unsigned)(((ug + 7) / 8) * 8 * 2 * nvb)),
-                     dim3(64 * NW), 0, st, wa);
+  hipLaunchKernelGGL((walk_kernel<E, NW, 1, LW>), dim3((unsigned)(((ug + 7) / 8) * 8 * 2 * nvb)),
+                     block, 0, st, wa);
   mark(L, 4);
   hipLaunchKernelGGL((compose_kernel<E>), dim3((unsigned)(units * 8)), dim3(64), 0, st, wa);
   mark(L, 5);
-  hipLaunchKernelGGL((walk_kernel<E, NW, 2>), dim3((unsigned)(((ug + 7) / 8) * 8 * nvb)),
-                     dim3(64 * NW), 0, st, wa);
+  hipLaunchKernelGGL((walk_kernel<E, NW, 2, LW>), dim3((unsigned)(((ug + 7) / 8) * 8 * nvb)),
+                     block, 0, st, wa);
   mark(L, 6);
 }
 
