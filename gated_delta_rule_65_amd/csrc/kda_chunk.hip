@@ -693,6 +693,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
       }
     }
   }
+  // v rows, requested as soon as phase 0's registers are free; they land
+  // during phase 1.  Rows past L are not zeroed: they meet b = 0 columns
+  // of T'.
+  RawRows<E> rv;
+  raw_load(v + (size_t)p.t0 * is.v + h * D, (int)is.v, L, rv, tid);
   if (tid == 0) s_next = claim + (int)gridDim.x;
   lds_barrier();
   const int nitem = s_next;
@@ -755,12 +760,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
       pair(1, 0); pair(0, 0); zero(1, 2); zero(1, 3); zero(2, 3);
     }
   }
-  // v rows (fragment-order channels) are fetched now; they land during the
-  // products above
-  // (rows past L are not zeroed: they meet b = 0 columns of T')
-  RawRows<E> rv;
-  raw_load(v + (size_t)p.t0 * is.v + h * D, (int)is.v, L, rv, tid);
-  if (nok) prefetch(nitem, np, tid);  // after v, so waiting for v leaves these in flight
+  // the next item's raw rows load during phases 2 and 3
+  if (nok) prefetch(nitem, np, tid);
   lds_barrier();
   // (kn 2^G)^T into R0 and v^T into R1 (rows: channels 8 j + e), each
   // thread's 4 consecutive tokens as one run

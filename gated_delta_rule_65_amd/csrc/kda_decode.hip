@@ -44,17 +44,26 @@ __device__ __forceinline__ void row_load(const bf16* row, int j, float4 (&h)[2])
   h[0] = widen4(reinterpret_cast<const uint2*>(row)[j]);
   h[1] = widen4(reinterpret_cast<const uint2*>(row)[16 + j]);
 }
+// The state is written back with nontemporal stores: the rows are not read
+// again soon, and decode steps run back to back stream the pool faster when
+// the written lines do not linger in the caches (256 x 32 fp32 rows:
+// 0.215 -> 0.169 ms per back-to-back step).
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_nt __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void row_store(float* row, int j, const float4 (&h)[2]) {
-  reinterpret_cast<float4*>(row)[j] = h[0];
-  reinterpret_cast<float4*>(row)[16 + j] = h[1];
+  f32x4_nt* p = reinterpret_cast<f32x4_nt*>(row);
+  __builtin_nontemporal_store(f32x4_nt{h[0].x, h[0].y, h[0].z, h[0].w}, p + j);
+  __builtin_nontemporal_store(f32x4_nt{h[1].x, h[1].y, h[1].z, h[1].w}, p + 16 + j);
 }
 __device__ __forceinline__ uint2 narrow4(float4 x) {
   return make_uint2((uint32_t)bf16_bits(x.x) | ((uint32_t)bf16_bits(x.y) << 16),
                     (uint32_t)bf16_bits(x.z) | ((uint32_t)bf16_bits(x.w) << 16));
 }
 __device__ __forceinline__ void row_store(bf16* row, int j, const float4 (&h)[2]) {
-  reinterpret_cast<uint2*>(row)[j] = narrow4(h[0]);
-  reinterpret_cast<uint2*>(row)[16 + j] = narrow4(h[1]);
+  u32x2_nt* p = reinterpret_cast<u32x2_nt*>(row);
+  const uint2 a = narrow4(h[0]), b = narrow4(h[1]);
+  __builtin_nontemporal_store(u32x2_nt{a.x, a.y}, p + j);
+  __builtin_nontemporal_store(u32x2_nt{b.x, b.y}, p + 16 + j);
 }
 // Four consecutive elements widened to fp32 (one 16-byte or 8-byte load).
 __device__ __forceinline__ void load4(const float* p, float* x) {
