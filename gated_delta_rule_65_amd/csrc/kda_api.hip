@@ -191,7 +191,10 @@ int64_t max_chunks_of(const kda_chunk_args* a) {
 // its time; one walk workgroup is resident per CU (its LDS ring fills most of
 // the CU).  Cost in chunk-steps: waves of resident workgroups times chain
 // length, with the group scan paying pass one (2x the columns, no outputs),
-// G compose steps and pass two over chains G times shorter.
+// G compose steps and pass two over chains G times shorter.  Without groups
+// the longest sequence's chain is a floor as well: exact for a dense batch,
+// estimated at 6x the mean chain for varlen (the lengths live on the device;
+// 6x is the longest of a log-uniform 64..8192 mix).
 struct WalkPlan {
   int groups, waves;
 };
@@ -201,10 +204,14 @@ WalkPlan plan_walk(const kda_chunk_args* a) {
   const int N = a->num_seqs > 0 ? a->num_seqs : 1;
   const int64_t units = (int64_t)N * a->hv;
   const double nc = (double)max_chunks_of(a) / N;  // chunks per sequence (mean bound)
+  const double chain =
+      a->cu_seqlens ? std::min((double)max_chunks_of(a), 6.0 * nc) : nc;  // longest chain
   const int waves_opts[3] = {2, 4, 8};
-  // time of one chunk step of a workgroup, by waves (measured on MI355X: the
-  // step is latency-bound, so wider workgroups take longer per step)
-  const double step_cost[3] = {1.0, 1.12, 1.55};
+  // time of one chunk step of a workgroup, by waves (measured on MI355X on
+  // the dense 4 x 4096 x 16-head prefill: wider workgroups take longer per
+  // step; the two-wave bf16 walk has loader waves and warms L2)
+  const double cost_bf16[3] = {1.0, 1.45, 2.0}, cost_f32[3] = {1.0, 1.12, 1.55};
+  const double* step_cost = a->dtype == KDA_BF16 ? cost_bf16 : cost_f32;
   WalkPlan best = {1, 2};
   double best_cost = 1e300;
   for (int wi = 0; wi < 3; ++wi) {
@@ -214,7 +221,7 @@ WalkPlan plan_walk(const kda_chunk_args* a) {
       if (a->groups > 0 && G != a->groups) continue;
       double cost;
       if (G == 1) {
-        cost = std::ceil((double)(units * nvb) / cap) * nc * step_cost[wi];
+        cost = std::max(std::ceil((double)(units * nvb) / cap) * nc, chain) * step_cost[wi];
       } else {
         const double cpg = std::ceil(nc / G);
         const double r1 = std::ceil((double)(units * G * 2 * nvb) / cap);
