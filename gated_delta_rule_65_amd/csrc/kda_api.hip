@@ -226,7 +226,8 @@ WalkPlan plan_walk(const kda_chunk_args* a) {
         const double cpg = std::ceil(nc / G);
         const double r1 = std::ceil((double)(units * G * 2 * nvb) / cap);
         const double r2 = std::ceil((double)(units * G * nvb) / cap);
-        cost = (0.8 * r1 + r2) * cpg * step_cost[wi] + G;
+        // the group chains (pass one and pass two) have a floor as well
+        cost = std::max((0.8 * r1 + r2) * cpg, 1.8 * std::ceil(chain / G)) * step_cost[wi] + G;
       }
       if (cost < best_cost * 0.999) {
         best_cost = cost;

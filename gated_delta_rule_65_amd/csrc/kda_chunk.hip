@@ -960,7 +960,8 @@ __device__ __forceinline__ float* scan_plane(float* scan, int g, int n, int h, i
 //         transfer columns started at the identity with u = 0 (the group
 //         transfer P_g = prod_c (diag(d_c) - kg_c^T w_c)).  No outputs.
 // MODE 2: group pass two.  Group g is walked from its composed start state
-//         H_in(g); outputs for its tokens, the final state from the last group.
+//         H_in(g); outputs for its tokens, the final state from the group
+//         that holds the sequence's last chunk.
 //
 // With LW > 0 the workgroup carries LW loader waves besides the NW compute
 // waves (on SIMDs the compute waves leave idle).  The loaders issue every
@@ -985,7 +986,6 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
   // the stage being filled from the stage being read
   __shared__ uint4 smemA[STAGE];
   __shared__ uint4 smemB[STAGES == 2 ? STAGE : 1];
-  __shared__ uint32_t lsink[LW > 0 ? 64 : 1];  // target of the loaders' L2 warm-up (never read)
 
   // The column blocks of one (sequence, head, group) get ids with equal
   // id % 8, so they land on one XCD and share its L2 for the K-side tiles.
@@ -1050,7 +1050,11 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
     dst = scan_plane(a.scan, g, n, h, a.N, hv, tcols ? 0 : 1);
   } else {
     src = scan_plane(a.scan, g, n, h, a.N, hv, 2);
-    if (g == G - 1) {
+    // the group holding the sequence's last chunk writes the final state
+    // (group 0 for an empty sequence: its start state is an exact copy), so
+    // the final state is the walk's own, as is a checkpoint at the end
+    const int g_last = nch_all > 0 ? (nch_all - 1) / cpg : 0;
+    if (g == g_last) {
       dst = a.cache ? (void*)row : (a.fin ? dense_plane(a.fin, unit_plane, dense_bf) : nullptr);
       dst_bf = dense_bf;
     }
@@ -1124,19 +1128,62 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
   if constexpr (LW > 0) {
     if (loader) {
       const size_t rowb = (size_t)hv * D * sizeof(E), rowa = (size_t)hv * C * sizeof(E);
+      // Register sets of the ring fetch: this wave's pieces of one chunk's tiles.
+      constexpr int PW = C * P128 / 64 / LW, PA = C * P64 / 64 / LW;
+      constexpr int PK = D * P64 / 64 / LW, PU = BV * P64 / 64 / LW;
+      struct Regs {
+        u32x4_t w[PW], q[PW], a[PA], k[PK], u[PU], d;
+      };
+      const uint32_t offW = tile_off0<P128, LW>(rowb, dwave, lane);
+      const uint32_t offA = tile_off0<P64, LW>(rowa, dwave, lane);
+      const uint32_t offK = tile_off0<P64, LW>(C * sizeof(E), dwave, lane);
+      // Every load is issued on every path (u_t and decay by both waves,
+      // rows of a short chunk from the zero page), so each wave's load count
+      // per chunk is fixed and the compiler's waits stay exact.
+      auto fetch = [&](int jc, Regs& R) __attribute__((always_inline)) {
+        const int c = c_first + jc;
+        const int t0 = sp.bos + C * jc;
+        const int L = min(C, sp.eos - t0);
+        const E* wsrc = a.w + ((size_t)t0 * hv + h) * D;
+        const E* qsrc = a.qg + ((size_t)t0 * hv + h) * D;
+        const E* asrc = a.aqk + ((size_t)t0 * hv + h) * C;
+        if (L == C) {
+          tile_fetch_full<C, P128, LW>(R.w, wsrc, rowb, offW);
+          tile_fetch_full<C, P128, LW>(R.q, qsrc, rowb, offW);
+          tile_fetch_full<C, P64, LW>(R.a, asrc, rowa, offA);
+        } else {  // the last chunk of a sequence: rows past L come from the zero page
+          tile_fetch<C, P128, LW, true>(R.w, wsrc, rowb, L, zero, dwave, lane);
+          tile_fetch<C, P128, LW, true>(R.q, qsrc, rowb, L, zero, dwave, lane);
+          tile_fetch<C, P64, LW, true>(R.a, asrc, rowa, L, zero, dwave, lane);
+        }
+        tile_fetch_full<D, P64, LW>(R.k, a.kg_t + ((size_t)c * hv + h) * D * C, C * sizeof(E),
+                                    offK);
+        tile_fetch_full<BV, P64, LW>(R.u, a.u_t + (((size_t)c * hv + h) * D + v0) * C,
+                                     C * sizeof(E), offK);
+        // decay: 32 pieces, lanes 32..63 fill the pad from the zero page
+        const char* gp = lane < 32
+                             ? (const char*)(a.decay + ((size_t)c * hv + h) * D) + 16 * lane
+                             : (const char*)zero;
+        R.d = *reinterpret_cast<const u32x4_t*>(gp);
+      };
+      auto put = [&](uint4* base, const Regs& R) __attribute__((always_inline)) {
+        tile_put<C, P128, LW>(base + OFF_W, R.w, dwave, lane);
+        tile_put<C, P128, LW>(base + OFF_Q, R.q, dwave, lane);
+        tile_put<C, P64, LW>(base + OFF_A, R.a, dwave, lane);
+        tile_put<D, P64, LW>(base + OFF_K, R.k, dwave, lane);
+        if (!tcols) tile_put<BV, P64, LW>(base + OFF_U, R.u, dwave, lane);
+        if (dwave == LW - 1) *reinterpret_cast<u32x4_t*>(base + OFF_D + lane) = R.d;
+      };
       // L2 warm-up.  The column-block workgroups of a (sequence, head) share
       // one XCD's L2 and read the same K-side tiles; each touches its share
-      // of their 128-byte lines (and its own u_t lines) two chunks ahead, so
-      // the stage DMA of the next step finds them in L2 (measured on the
-      // dense 4 x 4096 x 16-head prefill: two ahead beats three, four, six
-      // and eight).  One word per line goes by LDS DMA into a sink that
-      // nobody reads.
+      // of their 128-byte lines (and its own u_t lines) of the chunk after
+      // next, so the next step's fetch finds them in L2.  One word per line.
       static_assert(NW == 2 && LW == 2 && sizeof(E) == 2, "warm-up line map: bf16, 32 columns");
       constexpr int LW_ = 128, LQ = 128, LA = 64, LK = 128, LD = 4;  // lines per tile
       constexpr int NSH = LW_ + LQ + LA + LK + LD;                    // shared lines
       constexpr int LU = BV * C * 2 / 128;                            // own u_t lines
       const int per = (NSH + a.nvb - 1) / a.nvb;
-      auto warm = [&](int jw) __attribute__((always_inline)) {
+      auto warm = [&](int jw, uint32_t (&W)[2]) __attribute__((always_inline)) {
         const int c = c_first + jw;
         const int t0 = sp.bos + C * jw;
         const int L = min(C, sp.eos - t0);
@@ -1169,33 +1216,42 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
             p = ub + 128 * (f - per);
           }
           // idle lanes read the zero page: every lane loads, on every path
-          __builtin_amdgcn_global_load_lds(p ? p : (const char*)zero, (lds_vptr)lsink, 4, 0, 0);
+          W[k] = *reinterpret_cast<const uint32_t*>(p ? p : (const char*)zero);
         }
       };
-      // The loader loop: one barrier per chunk, as in the compute loop.  A
-      // loader first waits until its DMA of chunk jc has landed, leaving only
-      // the two warm-up loads issued after it in flight (vmcnt(2)); after the
-      // barrier the stage of chunk jc - 1 is free and takes chunk jc + 1.
-      // No release fence here: with the warm-up DMA in flight it would wait
-      // for every outstanding load; the asm clobbers keep the compiler from
-      // moving memory accesses across the barrier.
+      // The warm-up words are consumed (by an empty asm) a step later, after
+      // that step's fetch is issued, so the wait for them leaves it in flight.
+      auto sink = [&](const uint32_t (&W)[2]) __attribute__((always_inline)) {
+        asm volatile("" ::"v"(W[0] + W[1]));
+      };
+      // The loader loop: one barrier per chunk, as in the compute loop.  After
+      // the barrier of chunk jc the stage of chunk jc - 1 is free: the loaders
+      // request chunk jc + 1 into registers, warm chunk jc + 2, and write the
+      // registers into the free stage once they land (from L2, thanks to the
+      // warm-up a step earlier).  The barrier follows the loaders' LDS writes
+      // (lgkmcnt(0)); no release fence, which would also wait for the
+      // warm-up loads, and asm clobbers keep the compiler from moving memory
+      // accesses across it.
       if (jc0 >= jc1) return;
       auto cl = [&](int j) { return min(j, jc1 - 1); };
-      issue_wq(jc0, smemA);
-      issue_rest(jc0, smemA);
-      warm(cl(jc0 + 1));
+      Regs R;
+      uint32_t W[2];
+      fetch(jc0, R);
+      warm(cl(jc0 + 1), W);
+      put(smemA, R);
       for (int jc = jc0; jc < jc1; ++jc) {
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(0x0f72);  // vmcnt(2): chunk jc's DMA has landed
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's stage writes are done
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (jc + 1 < jc1) {
-          uint4* nxt = ((jc + 1 - jc0) & 1) ? smemB : smemA;
-          issue_wq(jc + 1, nxt);
-          issue_rest(jc + 1, nxt);
+          fetch(jc + 1, R);
+          sink(W);
+          warm(cl(jc + 2), W);
+          put(((jc + 1 - jc0) & 1) ? smemB : smemA, R);
         }
-        warm(cl(jc + 2));
       }
+      sink(W);
       __builtin_amdgcn_s_waitcnt(0);  // no DMA in flight when the wave ends
       return;
     }
@@ -1445,6 +1501,9 @@ __global__ __launch_bounds__(64) void compose_kernel(const WalkArgs<E> a) {
   const int lane = threadIdx.x, l16 = lane & 15, gq = lane >> 4;
   const int vcol = 16 * rb + l16;
   const int G = a.groups;
+  // the walk's split of the sequence's chunks into groups
+  const int nch_all = max(0, min(a.offs[n + 1], a.max_chunks) - a.offs[n]);
+  const int cpg = (nch_all + G - 1) / G;
   const void* src = nullptr;
   bool src_bf = false;
   if (a.cache) {
@@ -1471,6 +1530,9 @@ __global__ __launch_bounds__(64) void compose_kernel(const WalkArgs<E> a) {
       *reinterpret_cast<float4*>(hin + (size_t)vcol * D + 16 * kb + 4 * gq) =
           make_float4(S[kb][0], S[kb][1], S[kb][2], S[kb][3]);
     if (g == G - 1) break;
+    // an empty group's transfer is exactly the identity and its B zero: the
+    // state passes on bit for bit (a zero-length sequence keeps its state)
+    if (min(nch_all, g * cpg) >= min(nch_all, g * cpg + cpg)) continue;
     const float* P = scan_plane(a.scan, g, n, h, a.N, hv, 0);
     const float* Bp = scan_plane(a.scan, g, n, h, a.N, hv, 1);
     FragS Hf[4];

@@ -72,6 +72,53 @@ __device__ __forceinline__ void dma_one(int m, uint4* tile, const void* src, siz
   __builtin_amdgcn_global_load_lds(gp, (lds_vptr)(tile + 64 * q), 16, 0, 0);
 }
 
+// The pieces of dma_tile through registers: tile_fetch loads this wave's
+// pieces (no wait), tile_put writes them to their LDS slots.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <int R, int P, int NW, bool CHECK>
+__device__ __forceinline__ void tile_fetch(u32x4_t* regs, const void* src, size_t stride,
+                                           int valid, const void* zero, int wave, int lane) {
+  static_assert((R * P) % (64 * NW) == 0, "tile must split evenly over the waves");
+  constexpr int PER = R * P / 64 / NW;
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int q = wave + NW * m;
+    const int l = 64 * q + lane;
+    const int r = l / P, ps = l - r * P;
+    const int p = ps ^ (r & 7);
+    const char* gp = (const char*)src + (size_t)r * stride + 16 * p;
+    if (CHECK) gp = (r < valid) ? gp : (const char*)zero;
+    regs[m] = *reinterpret_cast<const u32x4_t*>(gp);
+  }
+}
+// Full tiles without row checks: when 64 / P rows per wave instruction times
+// NW is a multiple of 8, a lane's swizzle is the same for every instruction,
+// so one per-lane byte offset (tile_off0) and a uniform per-instruction base
+// address the whole tile.
+template <int P, int NW>
+__device__ __forceinline__ uint32_t tile_off0(size_t stride, int wave, int lane) {
+  const int l = 64 * wave + lane;
+  const int r = l / P, ps = l - r * P;
+  return (uint32_t)((size_t)r * stride + 16 * (ps ^ (r & 7)));
+}
+template <int R, int P, int NW>
+__device__ __forceinline__ void tile_fetch_full(u32x4_t* regs, const void* src, size_t stride,
+                                                uint32_t off0) {
+  constexpr int PER = R * P / 64 / NW, RQ = 64 / P;
+  static_assert((RQ * NW) % 8 == 0, "the swizzle must not change between instructions");
+#pragma unroll
+  for (int m = 0; m < PER; ++m)
+    regs[m] = *reinterpret_cast<const u32x4_t*>(
+        (const char*)src + (size_t)(RQ * NW * m) * stride + off0);
+}
+template <int R, int P, int NW>
+__device__ __forceinline__ void tile_put(uint4* tile, const u32x4_t* regs, int wave, int lane) {
+  constexpr int PER = R * P / 64 / NW;
+#pragma unroll
+  for (int m = 0; m < PER; ++m)
+    *reinterpret_cast<u32x4_t*>(tile + 64 * (wave + NW * m) + lane) = regs[m];
+}
+
 // Fragment of a swizzled bf16 tile: logical piece `unit` of row r.
 template <int P>
 __device__ __forceinline__ FragB frag_bf16(const uint4* tile, int r, int unit) {
