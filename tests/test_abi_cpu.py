@@ -386,3 +386,31 @@ def test_stride_checks(lib):
     assert lib.kda_decode(ctypes.byref(decode_args(k_stride=260, **ptrs))) == B.KDA_ERR_ARG
     assert lib.kda_decode(ctypes.byref(decode_args(state_slot_stride=100,
                                                    **ptrs))) == B.KDA_ERR_SHAPE
+
+
+def test_planner_picks_measured_best_on_the_standard_workloads():
+    """Host-only planning (no device work): the dense prefill walks without
+    groups on 2-wave workgroups, the varlen GVA batch on 4-wave workgroups,
+    and the single long sequence takes the 8-group scan on 8-wave ones."""
+    from gated_delta_rule_65_amd import inputs
+
+    def plan(wl):
+        r = inputs.WORKLOADS[wl]
+        hqk, hv, dt = r["hqk"], r["hv"], r["dtype"]
+        if r["kind"] == "chunk_paged":
+            gen = torch.Generator()
+            gen.manual_seed(1)
+            lengths = inputs.varlen_lengths(gen, r["S"], r["N"], r["lo"], r["hi"])
+            T = sum(lengths)
+            q = torch.zeros(T, hqk, 128, dtype=dt)
+            v = torch.zeros(T, hv, 128, dtype=dt)
+            cu = torch.tensor([0] + torch.tensor(lengths).cumsum(0).tolist(), dtype=torch.int32)
+            return B.chunk_plan(q, q, v, v, torch.zeros(T, hv, dtype=dt), cu_seqlens=cu)
+        shp = (r["B"], r["T"])
+        q = torch.zeros(*shp, hqk, 128, dtype=dt)
+        v = torch.zeros(*shp, hv, 128, dtype=dt)
+        return B.chunk_plan(q, q, v, v, torch.zeros(*shp, hv, dtype=dt))
+
+    assert plan("dense_prefill") == (1, 2)
+    assert plan("varlen_gva_paged") == (1, 4)
+    assert plan("long_single") == (8, 8)

@@ -649,3 +649,25 @@ def test_strided_inputs_with_gate_and_padded_paged_pool():
     assert rel(out_s.float().cpu().numpy(), o_ref) < 1e-2
     live = b.state_indices.long().numpy()
     assert rel(cache.cpu().numpy()[live], s_ref) < 1e-2
+
+
+# -------------------------------------------- exactness under the group scan
+
+@pytest.mark.parametrize("groups", [2, 4])
+def test_group_scan_keeps_empty_sequences_and_end_checkpoints_exact(groups):
+    """With the group scan, a zero-length sequence keeps its state bit for
+    bit (empty groups compose exactly) and a checkpoint at a sequence's end
+    equals its final state bit for bit (the group holding the last chunk
+    writes the final state), also when later groups are empty."""
+    lengths = [300, 0, 64, 130]
+    b = inputs.make_chunk(lengths, 1, 2, dtype=torch.bfloat16, g_scale=0.5, seed=88, init=True)
+    say("scan exactness", groups)
+    offsets = [0, 0, 64, 128]
+    ck, refs, out, fin = run_checkpoints(b, offsets, rows=4, groups=groups)
+    fin = fin.cpu()
+    assert torch.equal(fin[1], b.initial_state[1])
+    assert np.array_equal(ck[2], fin[2].numpy())
+    o_ref, s_ref = oracle_dense(b)
+    assert rel(out.float().cpu().numpy(), o_ref) < 1e-2
+    assert rel(fin.numpy(), s_ref) < 1e-2
+    assert rel(ck[3], refs[3]) < 1e-2
