@@ -836,6 +836,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
       for (int jj = 0; jj < 8; ++jj) x[jj] *= bb[jj];
       Tf[ta][s] = make_frag<SPLIT>(x);
     }
+  // Paired 16-byte stores: a lane's w values of column blocks 2 wv and
+  // 2 wv + 1 (same token) are adjacent in the packed key order, and its u_t
+  // values of token blocks 2 m and 2 m + 1 (same channel) in the packed
+  // token order.
+  float wk[4][4];  // w of column block 2 wv, kept for the paired store
 #pragma unroll
   for (int cbi = 0; cbi < 2; ++cbi) {
     const int cb = 2 * wv + cbi;
@@ -854,6 +859,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
         Yv[s] = FragB{__builtin_bit_cast(bf16x8_t, Vt[tslot<TE>(row, 4 * s + gq)])};
       }
     }
+    float uk[4];  // u of the even token block, kept for the paired store
 #pragma unroll
     for (int ta = 0; ta < 4; ++ta) {
       f32x4_t aw = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
@@ -864,12 +870,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
         mma(au, Tf[ta][1], Yv[1]);
       }
       const int t = 16 * ta + l16;
-      if (t < L)
-        store4(w_out + ((size_t)(p.t0 + t) * hv + h) * D + packed_index(16 * cb + 4 * gq), aw[0],
-               aw[1], aw[2], aw[3]);
+      if (cbi == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wk[ta][r] = aw[r];
+      } else if (t < L) {
+        const float x[8] = {wk[ta][0], wk[ta][1], wk[ta][2], wk[ta][3],
+                            aw[0], aw[1], aw[2], aw[3]};
+        store8(w_out + ((size_t)(p.t0 + t) * hv + h) * D + packed_index(32 * wv + 4 * gq), x);
+      }
       // u_t[c][h][v][packed t]: rows t = 16 ta + 4 gq + r of column `row` (zero past L)
-      E* du = u_t + (((size_t)c * hv + h) * D + row) * C + packed_index(16 * ta + 4 * gq);
-      store4(du, au[0], au[1], au[2], au[3]);
+      if (ta & 1) {
+        const float x[8] = {uk[0], uk[1], uk[2], uk[3], au[0], au[1], au[2], au[3]};
+        store8(u_t + (((size_t)c * hv + h) * D + row) * C + packed_index(16 * (ta - 1) + 4 * gq),
+               x);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) uk[r] = au[r];
+      }
     }
   }
   lds_barrier();  // the next item rewrites every region
