@@ -49,16 +49,23 @@ __device__ __forceinline__ SeqSpan seq_span(const int32_t* cu, int n, int dense_
   return {b, e};
 }
 
-// offs[n] = first chunk of sequence n; offs[N] = number of chunks; and the
-// chunk records table[c] = (sequence, first token, length, 0) for every c below
-// max_chunks (length 0 past the last chunk), so a kernel finds its chunk with
-// one 16-byte load.
+// Chunk table: per-sequence chunk offsets (offs[n] = first chunk of sequence
+// n, offs[N] = number of chunks) and one record (sequence, first token,
+// length, 0) per chunk below max_chunks, length 0 past the last chunk, so a
+// kernel finds its chunk with one 16-byte load.
+// The chunk counts are scanned with wave shuffles and one LDS pass over the
+// 16 wave totals; the records are then filled in parallel, each thread
+// finding its chunk's sequence by binary search over the offsets (held in LDS
+// up to OFFS_LDS sequences; beyond that each thread writes its own sequences'
+// records in turn).
+constexpr int OFFS_LDS = 8192;
 __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* cu, int N,
                                                              int dense_len, int T,
                                                              int32_t* offs, int4* table,
                                                              int max_chunks, uint4* zero) {
-  __shared__ int32_t part[1024];
-  const int tid = threadIdx.x;
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t soffs[OFFS_LDS + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid < 65) zero[tid] = make_uint4(0, 0, 0, 0);  // the zero page the walk DMAs from,
                                                      // then the WY work counter
   const int per = (N + 1023) / 1024;
@@ -68,23 +75,60 @@ __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* cu, 
     const SeqSpan s = seq_span(cu, n, dense_len, T);
     sum += (s.eos - s.bos + C - 1) / C;
   }
-  part[tid] = sum;
+  // inclusive scan inside the wave, then across the 16 wave totals
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  if (tid < 16) {
+    int x = wsum[tid];
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int v = __shfl_up(x, off, 16);
+      if (tid >= off) x += v;
+    }
+    wsum[tid] = x;  // inclusive over waves
   }
-  int run = part[tid] - sum;
-  for (int n = s0; n < s1; ++n) {
-    offs[n] = run;
-    const SeqSpan s = seq_span(cu, n, dense_len, T);
-    for (int t0 = s.bos; t0 < s.eos; t0 += C, ++run)
-      if (run < max_chunks) table[run] = make_int4(n, t0, min(C, s.eos - t0), 0);
+  __syncthreads();
+  const int run0 = (wave > 0 ? wsum[wave - 1] : 0) + incl - sum;  // exclusive
+  const int total = wsum[15];
+  const bool in_lds = N <= OFFS_LDS;
+  {
+    int run = run0;
+    for (int n = s0; n < s1; ++n) {
+      offs[n] = run;
+      if (in_lds) soffs[n] = run;
+      const SeqSpan s = seq_span(cu, n, dense_len, T);
+      const int nc = (s.eos - s.bos + C - 1) / C;
+      if (!in_lds)
+        for (int j = 0; j < nc; ++j)
+          if (run + j < max_chunks)
+            table[run + j] = make_int4(n, s.bos + C * j, min(C, s.eos - s.bos - C * j), 0);
+      run += nc;
+    }
   }
-  const int total = part[1023];
   if (tid == 1023) offs[N] = total;
+  if (in_lds) {
+    if (tid == 0) soffs[N] = total;
+    __syncthreads();
+    for (int c = tid; c < min(total, max_chunks); c += 1024) {
+      // the sequence n with soffs[n] <= c < soffs[n + 1] (empty sequences share
+      // their offset with the next one; the search lands on the last of them,
+      // which is the non-empty one)
+      int lo = 0, hi = N - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (soffs[mid] <= c) lo = mid; else hi = mid - 1;
+      }
+      const SeqSpan s = seq_span(cu, lo, dense_len, T);
+      const int t0 = s.bos + C * (c - soffs[lo]);
+      table[c] = make_int4(lo, t0, min(C, s.eos - t0), 0);
+    }
+  }
   for (int c = total + tid; c < max_chunks; c += 1024) table[c] = make_int4(0, 0, 0, 0);
 }
 

@@ -671,3 +671,28 @@ def test_group_scan_keeps_empty_sequences_and_end_checkpoints_exact(groups):
     assert rel(out.float().cpu().numpy(), o_ref) < 1e-2
     assert rel(fin.numpy(), s_ref) < 1e-2
     assert rel(ck[3], refs[3]) < 1e-2
+
+
+# ------------------------------------------------------------- chunk table
+
+@pytest.mark.parametrize("n_seqs,max_len,init", [(2000, 200, True), (9000, 3, False)])
+def test_chunk_table_for_many_sequences(n_seqs, max_len, init):
+    """Thousands of sequences (some empty): the chunk offsets are the prefix
+    sums of ceil(length / 64), and the outputs and final states match the
+    oracle.  9000 sequences exceed the chunk-table kernel's LDS offset cache
+    (8192) and take its per-thread path."""
+    gen = torch.Generator().manual_seed(n_seqs)
+    lengths = torch.randint(0, max_len + 1, (n_seqs,), generator=gen).tolist()
+    b = inputs.make_chunk(lengths, 1, 1, dtype=torch.bfloat16, g_scale=0.5, seed=n_seqs,
+                          init=init)
+    say("chunk table", n_seqs)
+    st = B.chunk_stages(*gpu(b), cu_seqlens=b.cu_seqlens.to(DEV), scale=b.scale,
+                        initial_state=None if b.initial_state is None else
+                        b.initial_state.to(DEV), path=B.PATH_FUSED)
+    torch.cuda.synchronize()
+    counts = torch.tensor([(L + 63) // 64 for L in lengths])
+    want = torch.cat([torch.zeros(1, dtype=torch.long), counts.cumsum(0)])
+    assert torch.equal(st["chunk_offsets"].cpu().long(), want)
+    o_ref, s_ref = oracle_dense(b)
+    assert rel(st["out"].float().cpu().numpy(), o_ref) < 1e-2
+    assert rel(st["final_state"].cpu().numpy(), s_ref) < 1e-2
