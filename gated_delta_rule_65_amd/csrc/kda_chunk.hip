@@ -1208,14 +1208,19 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
         const E* wsrc = a.w + ((size_t)t0 * hv + h) * D;
         const E* qsrc = a.qg + ((size_t)t0 * hv + h) * D;
         const E* asrc = a.aqk + ((size_t)t0 * hv + h) * C;
+        // (qg and aqk only feed the outputs: pass one of the scan skips them)
         if (L == C) {
           tile_fetch_full<C, P128, LW>(R.w, wsrc, rowb, offW);
-          tile_fetch_full<C, P128, LW>(R.q, qsrc, rowb, offW);
-          tile_fetch_full<C, P64, LW>(R.a, asrc, rowa, offA);
+          if (OUT) {
+            tile_fetch_full<C, P128, LW>(R.q, qsrc, rowb, offW);
+            tile_fetch_full<C, P64, LW>(R.a, asrc, rowa, offA);
+          }
         } else {  // the last chunk of a sequence: rows past L come from the zero page
           tile_fetch<C, P128, LW, true>(R.w, wsrc, rowb, L, zero, dwave, lane);
-          tile_fetch<C, P128, LW, true>(R.q, qsrc, rowb, L, zero, dwave, lane);
-          tile_fetch<C, P64, LW, true>(R.a, asrc, rowa, L, zero, dwave, lane);
+          if (OUT) {
+            tile_fetch<C, P128, LW, true>(R.q, qsrc, rowb, L, zero, dwave, lane);
+            tile_fetch<C, P64, LW, true>(R.a, asrc, rowa, L, zero, dwave, lane);
+          }
         }
         tile_fetch_full<D, P64, LW>(R.k, a.kg_t + ((size_t)c * hv + h) * D * C, C * sizeof(E),
                                     offK);
@@ -1229,8 +1234,10 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
       };
       auto put = [&](uint4* base, const Regs& R) __attribute__((always_inline)) {
         tile_put<C, P128, LW>(base + OFF_W, R.w, dwave, lane);
-        tile_put<C, P128, LW>(base + OFF_Q, R.q, dwave, lane);
-        tile_put<C, P64, LW>(base + OFF_A, R.a, dwave, lane);
+        if (OUT) {
+          tile_put<C, P128, LW>(base + OFF_Q, R.q, dwave, lane);
+          tile_put<C, P64, LW>(base + OFF_A, R.a, dwave, lane);
+        }
         tile_put<D, P64, LW>(base + OFF_K, R.k, dwave, lane);
         if (!tcols) tile_put<BV, P64, LW>(base + OFF_U, R.u, dwave, lane);
         if (dwave == LW - 1) *reinterpret_cast<u32x4_t*>(base + OFF_D + lane) = R.d;
