@@ -57,6 +57,7 @@ class ChunkArgs(ctypes.Structure):
         ("q_stride", ctypes.c_int64), ("k_stride", ctypes.c_int64),
         ("v_stride", ctypes.c_int64), ("g_stride", ctypes.c_int64),
         ("beta_stride", ctypes.c_int64), ("state_slot_stride", ctypes.c_int64),
+        ("max_seqlen", ctypes.c_int64),
     ]
 
 
@@ -271,7 +272,7 @@ def _as_varlen(x, name, cu_seqlens):
 
 
 def _chunk_struct(q, k, v, g, beta, out, cu, N, T, hqk, hv, scale, l2, init, fin, cache,
-                  idx, has_init, path, groups, stream, walk_waves=0, gate=None):
+                  idx, has_init, path, groups, stream, walk_waves=0, gate=None, max_seqlen=0):
     a = ChunkArgs()
     a.struct_size = ctypes.sizeof(ChunkArgs)
     a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
@@ -291,6 +292,7 @@ def _chunk_struct(q, k, v, g, beta, out, cu, N, T, hqk, hv, scale, l2, init, fin
     a.stream = stream
     _set_gate(a, gate if gate is not None else (None, None, 0, -5.0))
     _set_strides(a, q, k, v, g, beta, cache)
+    a.max_seqlen = max_seqlen
     return a
 
 
@@ -326,9 +328,13 @@ def _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state, c
               "cu_seqlens must have dtype torch.int32 or torch.int64.", TypeError)
         cu = cu_seqlens.to(device=dev, dtype=torch.int32).contiguous()
         N = cu.numel() - 1
+        # planning hint: known without a device sync only for host offsets
+        max_seqlen = (int((cu_seqlens[1:] - cu_seqlens[:-1]).max())
+                      if cu_seqlens.device.type == "cpu" and N > 0 else 0)
     else:
         cu = None
         N = B
+        max_seqlen = 0
     if scale is None:
         scale = D ** -0.5
     paged = state_cache is not None
@@ -380,7 +386,8 @@ def _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state, c
     _need(output.device == dev, f"output must be on {dev}")
     return dict(q=q3, k=k3, v=v3, g=g3, beta=beta2, out=output, cu=cu, N=N, T=T, hqk=hqk,
                 hv=hv, scale=float(scale), l2=bool(use_qk_l2norm_in_kernel), init=init,
-                fin=fin, cache=state_cache if paged else None, idx=idx, has_init=hinit)
+                fin=fin, cache=state_cache if paged else None, idx=idx, has_init=hinit,
+                max_seqlen=max(0, max_seqlen))
 
 
 def _run_chunk(p, path=PATH_AUTO, groups=0, workspace=None, keep=None, events=None,
@@ -390,7 +397,7 @@ def _run_chunk(p, path=PATH_AUTO, groups=0, workspace=None, keep=None, events=No
     a = _chunk_struct(p["q"], p["k"], p["v"], p["g"], p["beta"], p["out"], p["cu"], p["N"],
                       p["T"], p["hqk"], p["hv"], p["scale"], p["l2"], p["init"], p["fin"],
                       p["cache"], p["idx"], p["has_init"], path, groups, _stream(dev),
-                      walk_waves, gate)
+                      walk_waves, gate, p["max_seqlen"])
     if ckpt is not None:
         cs, co, ci = ckpt
         a.checkpoint_state, a.checkpoint_offsets = _ptr(cs), _ptr(co)
@@ -423,7 +430,7 @@ def chunk_kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_sta
               state_cache=None, state_indices=None, has_initial_state=None, groups=0,
               workspace=None, stage_events=None, walk_waves=0, path=PATH_AUTO,
               A_log=None, dt_bias=None, lower_bound=-5.0, checkpoint_state=None,
-              checkpoint_offsets=None, checkpoint_state_indices=None):
+              checkpoint_offsets=None, checkpoint_state_indices=None, max_seqlen=None):
     """Chunked KDA forward (chunk_kda's argument set, plus the paged state of
     fused_kda_chunk).  Returns out, or (out, final_state) when
     output_final_state; in paged mode the final states land in state_cache.
@@ -437,10 +444,14 @@ def chunk_kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_sta
     checkpoint_state [rows, Hv, 128, 128] fp32 with checkpoint_offsets [N]
     (and optionally checkpoint_state_indices [N]) snapshots each sequence's
     state after its first checkpoint_offsets[n] tokens (0 or a multiple of 64;
-    fused_kda_chunk's checkpoint arguments)."""
+    fused_kda_chunk's checkpoint arguments).  max_seqlen: the longest sequence's
+    length, a planning hint for varlen batches (taken from cu_seqlens when it
+    is a host tensor; results never depend on it)."""
     p = _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state,
                        cu_seqlens, use_qk_l2norm_in_kernel, output, final_state,
                        state_cache, state_indices, has_initial_state)
+    if max_seqlen is not None:
+        p["max_seqlen"] = int(max_seqlen)
     gate = _gate(A_log, dt_bias, lower_bound, p["hv"], p["q"].device)
     ck = _checkpoints(checkpoint_state, checkpoint_offsets, checkpoint_state_indices, p["N"],
                       p["hv"], p["q"].device)
@@ -591,14 +602,16 @@ def kda_decode(q, k, v, g, beta, state_cache, state_indices=None, scale=None,
 
 
 def chunk_plan(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_state=False,
-               groups=0, walk_waves=0):
+               groups=0, walk_waves=0, max_seqlen=None):
     """The walk's launch plan (groups, walk_waves) that chunk_kda takes for
     these arguments.  Host-side only: nothing runs on the device."""
     p = _prepare_chunk(q, k, v, g, beta, None, initial_state, output_final_state, cu_seqlens,
                        True, None, None, None, None, None)
+    if max_seqlen is not None:
+        p["max_seqlen"] = int(max_seqlen)
     a = _chunk_struct(p["q"], p["k"], p["v"], p["g"], p["beta"], p["out"], p["cu"], p["N"],
                       p["T"], p["hqk"], p["hv"], p["scale"], True, p["init"], p["fin"], None,
-                      None, None, PATH_AUTO, groups, None, walk_waves)
+                      None, None, PATH_AUTO, groups, None, walk_waves, None, p["max_seqlen"])
     lay = WsLayout()
     lib = load_library()
     st = lib.kda_chunk_ws_layout(ctypes.byref(a), ctypes.byref(lay))

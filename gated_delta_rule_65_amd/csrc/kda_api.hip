@@ -143,6 +143,7 @@ kda_status check_chunk(const kda_chunk_args* a, bool need_ptrs) {
   if (a->path != KDA_PATH_AUTO && a->path != KDA_PATH_STAGED && a->path != KDA_PATH_FUSED)
     return fail(KDA_ERR_UNSUPPORTED, "unknown path %d", a->path);
   if (a->groups < 0) return fail(KDA_ERR_SHAPE, "groups must be >= 0");
+  if (a->max_seqlen < 0) return fail(KDA_ERR_SHAPE, "max_seqlen must be >= 0");
   if (a->groups > 64) return fail(KDA_ERR_UNSUPPORTED, "groups above 64");
   if (a->walk_waves != 0 && a->walk_waves != 2 && a->walk_waves != 4 && a->walk_waves != 8)
     return fail(KDA_ERR_ARG, "walk_waves must be 0, 2, 4 or 8");
@@ -191,10 +192,9 @@ int64_t max_chunks_of(const kda_chunk_args* a) {
 // its time; one walk workgroup is resident per CU (its LDS ring fills most of
 // the CU).  Cost in chunk-steps: waves of resident workgroups times chain
 // length, with the group scan paying pass one (2x the columns, no outputs),
-// G compose steps and pass two over chains G times shorter.  Without groups
-// the longest sequence's chain is a floor as well: exact for a dense batch,
-// estimated at 6x the mean chain for varlen (the lengths live on the device;
-// 6x is the longest of a log-uniform 64..8192 mix).
+// G compose steps and pass two over chains G times shorter.  The longest
+// sequence's chain is a floor as well: exact for a dense batch, from the
+// max_seqlen hint for varlen, else taken as the mean.
 struct WalkPlan {
   int groups, waves;
 };
@@ -204,8 +204,10 @@ WalkPlan plan_walk(const kda_chunk_args* a) {
   const int N = a->num_seqs > 0 ? a->num_seqs : 1;
   const int64_t units = (int64_t)N * a->hv;
   const double nc = (double)max_chunks_of(a) / N;  // chunks per sequence (mean bound)
-  const double chain =
-      a->cu_seqlens ? std::min((double)max_chunks_of(a), 6.0 * nc) : nc;  // longest chain
+  const double chain =  // chunks of the longest sequence
+      (a->cu_seqlens && a->max_seqlen > 0)
+          ? std::min((double)max_chunks_of(a), std::ceil((double)a->max_seqlen / KDA_CHUNK))
+          : nc;
   const int waves_opts[3] = {2, 4, 8};
   // time of one chunk step of a workgroup, by waves (measured on MI355X on
   // the dense 4 x 4096 x 16-head prefill: wider workgroups take longer per

@@ -1246,12 +1246,16 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
       // one XCD's L2 and read the same K-side tiles; each touches its share
       // of their 128-byte lines (and its own u_t lines) of the chunk after
       // next, so the next step's fetch finds them in L2.  One word per line.
-      static_assert(NW == 2 && LW == 2 && sizeof(E) == 2, "warm-up line map: bf16, 32 columns");
+      static_assert((NW == 2 || NW == 4) && LW == 2 && sizeof(E) == 2,
+                    "warm-up line map: bf16, 32 or 64 columns");
       constexpr int LW_ = 128, LQ = 128, LA = 64, LK = 128, LD = 4;  // lines per tile
       constexpr int NSH = LW_ + LQ + LA + LK + LD;                    // shared lines
       constexpr int LU = BV * C * 2 / 128;                            // own u_t lines
-      const int per = (NSH + a.nvb - 1) / a.nvb;
-      auto warm = [&](int jw, uint32_t (&W)[2]) __attribute__((always_inline)) {
+      constexpr int NVB = 8 / NW;                                     // workgroups sharing
+      constexpr int PER = (NSH + NVB - 1) / NVB;                      // shared lines each
+      constexpr int KW = (PER + LU + 64 * LW - 1) / (64 * LW);        // loads per wave
+      const int per = PER;
+      auto warm = [&](int jw, uint32_t (&W)[KW]) __attribute__((always_inline)) {
         const int c = c_first + jw;
         const int t0 = sp.bos + C * jw;
         const int L = min(C, sp.eos - t0);
@@ -1262,8 +1266,8 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
         const char* db = (const char*)(a.decay + ((size_t)c * hv + h) * D);
         const char* ub = (const char*)(a.u_t + (((size_t)c * hv + h) * D + v0) * C);
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int f = 128 * k + 64 * dwave + lane;
+        for (int k = 0; k < KW; ++k) {
+          const int f = 64 * LW * k + 64 * dwave + lane;
           const char* p = nullptr;
           if (f < per) {
             const int i = vb * per + f;
@@ -1289,8 +1293,11 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
       };
       // The warm-up words are consumed (by an empty asm) a step later, after
       // that step's fetch is issued, so the wait for them leaves it in flight.
-      auto sink = [&](const uint32_t (&W)[2]) __attribute__((always_inline)) {
-        asm volatile("" ::"v"(W[0] + W[1]));
+      auto sink = [&](const uint32_t (&W)[KW]) __attribute__((always_inline)) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int k = 0; k < KW; ++k) x += W[k];
+        asm volatile("" ::"v"(x));
       };
       // The loader loop: one barrier per chunk, as in the compute loop.  After
       // the barrier of chunk jc the stage of chunk jc - 1 is free: the loaders
@@ -1303,7 +1310,7 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
       if (jc0 >= jc1) return;
       auto cl = [&](int j) { return min(j, jc1 - 1); };
       Regs R;
-      uint32_t W[2];
+      uint32_t W[KW];
       fetch(jc0, R);
       warm(cl(jc0 + 1), W);
       put(smemA, R);
@@ -1646,7 +1653,9 @@ static void mark(const ChunkLaunch& L, int i) {
 // CU idle, and two loader waves there take over its DMA.
 template <typename E, int NW>
 constexpr int walk_loaders() {
-  return (!std::is_same<E, float>::value && NW == 2) ? 2 : 0;
+  // two- and four-wave bf16 walks; an eight-wave workgroup already fills the
+  // SIMDs, and its waves' registers leave no room for two more
+  return (!std::is_same<E, float>::value && (NW == 2 || NW == 4)) ? 2 : 0;
 }
 
 template <typename E, int NW>

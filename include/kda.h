@@ -178,6 +178,11 @@ typedef struct kda_chunk_args {
      "vllm.models.kimi_k3.nvidia.recoverssm.cutedsl.verify"): at least
      hv*128*128 and a multiple of 8 elements. */
   int64_t state_slot_stride;
+  /* Planning hint (optional): the longest sequence's token count, or 0 when
+     unknown (cu_seqlens lives on the device).  It only steers the choice of
+     chunk groups and walk width; results do not depend on it.  Without it a
+     varlen batch is planned as if its sequences were equally long. */
+  int64_t max_seqlen;
 } kda_chunk_args;
 
 /* Stage boundaries of kda_chunk_fwd (indices into stage_events).  Event i is

@@ -414,3 +414,25 @@ def test_planner_picks_measured_best_on_the_standard_workloads():
     assert plan("dense_prefill") == (1, 2)
     assert plan("varlen_gva_paged") == (1, 4)
     assert plan("long_single") == (8, 8)
+
+
+def test_planner_max_seqlen_hint(lib):
+    """The longest sequence bounds a varlen walk.  With host offsets the
+    binding passes it as a planning hint; without it the batch is planned as
+    if its sequences were equally long, so an equal-length batch given in
+    varlen form plans like the dense one."""
+    def varlen(lengths, hqk, hv):
+        T = sum(lengths)
+        q = torch.zeros(T, hqk, 128, dtype=torch.bfloat16)
+        v = torch.zeros(T, hv, 128, dtype=torch.bfloat16)
+        cu = torch.tensor([0] + torch.tensor(lengths).cumsum(0).tolist(), dtype=torch.int32)
+        return q, v, torch.zeros(T, hv, dtype=torch.bfloat16), cu
+    q, v, beta, cu = varlen([4096] * 4, 16, 16)
+    assert B.chunk_plan(q, q, v, v, beta, cu_seqlens=cu) == (1, 2)
+    assert B.chunk_plan(q, q, v, v, beta, cu_seqlens=cu, max_seqlen=0) == (1, 2)
+    # one long sequence among short ones: the hint moves the plan
+    q, v, beta, cu = varlen([8192] + [128] * 60, 4, 16)
+    with_hint = B.chunk_plan(q, q, v, v, beta, cu_seqlens=cu)
+    without = B.chunk_plan(q, q, v, v, beta, cu_seqlens=cu, max_seqlen=0)
+    assert with_hint != without
+    assert ws_size(lib, chunk_args(max_seqlen=-1))[0] == B.KDA_ERR_SHAPE
