@@ -696,3 +696,62 @@ def test_chunk_table_for_many_sequences(n_seqs, max_len, init):
     o_ref, s_ref = oracle_dense(b)
     assert rel(st["out"].float().cpu().numpy(), o_ref) < 1e-2
     assert rel(st["final_state"].cpu().numpy(), s_ref) < 1e-2
+
+
+# ------------------------------------------------ seeded mixed configurations
+
+def _mixed_case(i):
+    """Configuration i of a fixed seeded draw: sequence lengths (some empty,
+    ragged tails), GVA ratio, dtype, gate parameters, dense or paged state,
+    projection-view inputs, and an explicit or planned walk shape."""
+    gen = torch.Generator().manual_seed(1000 + i)
+    r = lambda n: int(torch.randint(0, n, (1,), generator=gen))
+    n_seqs = 1 + r(5)
+    lengths = [r(4) * 64 + r(65) if r(5) else 0 for _ in range(n_seqs)]
+    if sum(lengths) == 0:
+        lengths[0] = 70
+    hqk = [1, 2][r(2)]
+    hv = hqk * [1, 2, 4][r(3)]
+    dtype = [torch.bfloat16, torch.bfloat16, torch.float32][r(3)]
+    return dict(lengths=lengths, hqk=hqk, hv=hv, dtype=dtype, gate=bool(r(2)), paged=bool(r(2)),
+                strided=bool(r(2)) and dtype == torch.bfloat16, groups=[0, 1, 2, 3][r(4)],
+                waves=[0, 2, 4, 8][r(4)], seed=2000 + i)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_mixed_configurations_match_oracle(i):
+    cfg = _mixed_case(i)
+    say("mixed", i, cfg)
+    b = inputs.make_chunk(cfg["lengths"], cfg["hqk"], cfg["hv"], dtype=cfg["dtype"], g_scale=0.5,
+                          seed=cfg["seed"], init=not cfg["paged"],
+                          paged_slots=len(cfg["lengths"]) + 3 if cfg["paged"] else 0)
+    hv = cfg["hv"]
+    gk = {}
+    if cfg["gate"]:
+        gg = torch.Generator().manual_seed(cfg["seed"])
+        gk = dict(A_log=torch.randn(hv, generator=gg) * 0.3,
+                  dt_bias=torch.randn(hv, 128, generator=gg) * 0.5)
+    if cfg["strided"]:
+        (q, k, v, g, beta), _ = projection_views([b.q, b.k, b.v, b.g, b.beta], DEV)
+    else:
+        q, k, v, g, beta = gpu(b)
+    kw = dict(scale=b.scale, cu_seqlens=b.cu_seqlens.to(DEV), groups=cfg["groups"],
+              walk_waves=cfg["waves"], **{k_: v_.to(DEV) for k_, v_ in gk.items()})
+    if cfg["paged"]:
+        cache = b.state_cache.to(DEV)
+        out = B.chunk_kda(q, k, v, g, beta, state_cache=cache,
+                          state_indices=b.state_indices.to(DEV),
+                          has_initial_state=b.has_initial_state.to(DEV), **kw)
+        s0 = b.state_cache[b.state_indices.long()] * b.has_initial_state.view(-1, 1, 1, 1).float()
+    else:
+        out, fin = B.chunk_kda(q, k, v, g, beta, initial_state=b.initial_state.to(DEV),
+                               output_final_state=True, **kw)
+        s0 = b.initial_state
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence(b.q, b.k, b.v, b.g, b.beta, cu_seqlens=b.cu_seqlens,
+                                     scale=b.scale, initial_state=s0,
+                                     **{k_: v_.double() for k_, v_ in gk.items()})
+    t_ = tol(cfg["dtype"])
+    assert rel(out.float().cpu().numpy(), o_ref) < t_
+    got = cache.cpu()[b.state_indices.long()] if cfg["paged"] else fin.cpu()
+    assert rel(got.numpy(), s_ref) < t_
