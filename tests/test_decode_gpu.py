@@ -325,3 +325,41 @@ def test_multi_token_decode_strided_inputs_bf16_padded_pool():
     assert torch.isnan(pool[:, 2 * 128 * 128:].float()).all()
     ro, rc = oracle.decode_multi(q, k, v, g, beta, cache, idx, acc, state_bf16=True)
     assert rel(out_s.float().cpu().numpy(), ro) < 1e-2
+
+
+# ------------------------------------------------ seeded mixed configurations
+
+@pytest.mark.parametrize("i", range(10))
+def test_mixed_decode_configurations_match_oracle(i):
+    """Configuration i of a fixed seeded draw: request count, tokens per
+    request (1..8), GVA ratio, input dtype, fp32 or bf16 pool, gate
+    parameters, projection-view inputs, accepted-token counts."""
+    gen = torch.Generator().manual_seed(3000 + i)
+    r = lambda n: int(torch.randint(0, n, (1,), generator=gen))
+    Bn, T = 1 + r(9), 1 + r(8)
+    hqk = [1, 2][r(2)]
+    hv = hqk * [1, 2, 4][r(3)]
+    dtype = [torch.bfloat16, torch.float16, torch.float32][r(3)]
+    state_bf16 = bool(r(2))
+    print("mixed decode", i, Bn, T, hqk, hv, dtype, state_bf16, flush=True)
+    q, k, v, g, beta, cache = spec_case(Bn, T, hqk, hv, Bn * T + 4, dtype, seed=4000 + i)
+    if state_bf16:
+        cache = cache.to(torch.bfloat16)
+    idx = torch.randperm(Bn * T + 4, generator=gen)[:Bn * T].to(torch.int32).reshape(Bn, T)
+    idx[0, T - 1] = -1                                   # one skipped store
+    acc = torch.randint(1, T + 1, (Bn,), generator=gen).to(torch.int32)
+    gk = {}
+    if r(2):
+        gk = dict(A_log=torch.randn(hv, generator=gen) * 0.3,
+                  dt_bias=torch.randn(hv, 128, generator=gen) * 0.5)
+    views = projection_views([q, k, v, g, beta]) if r(2) and dtype != torch.float32 else \
+        [t.to(DEV) for t in (q, k, v, g, beta)]
+    cd = cache.to(DEV)
+    out = B.kda_decode(*views, cd, idx.to(DEV), num_accepted_tokens=acc.to(DEV),
+                       **{k_: v_.to(DEV) for k_, v_ in gk.items()})
+    torch.cuda.synchronize()
+    ro, rc = oracle.decode_multi(q, k, v, g, beta, cache, idx, acc, state_bf16=state_bf16,
+                                 **{k_: v_.double() for k_, v_ in gk.items()})
+    t_ = 1e-4 if dtype == torch.float32 and not state_bf16 else 1e-2
+    assert rel(out.float().cpu().numpy(), ro) < t_
+    assert rel(cd.cpu().float().numpy(), rc) < t_
