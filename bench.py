@@ -5,10 +5,11 @@ One step = one chunked forward over the dense-prefill workload (B=4, T=4096,
 Hqk=Hv=16, D=128, bf16, fp32 initial and final state) followed by one paged
 decode over the decode workload (256 requests x 32 heads, fp32 cache
 [1024, 32, 128, 128]), inputs resident in HBM.  W untimed warm-up steps, then K
-timed steps bracketed by device synchronisation, with two HIP events per step
-on the library's stream (chunk start, decode start) for the launch durations
-of the two calls.  The per-kernel breakdown of the chunk forward comes from a
-separate pass with the library's stage events.
+timed steps bracketed by device synchronisation, with nothing else queued
+between them.  After the timed region: K more steps with two HIP events per
+step on the library's stream (chunk start, decode start) for the launch
+durations of the two calls, K chunk forwards with the library's stage events
+for the per-kernel breakdown, and K decode launches back to back.
 
 Printed: one JSON line.  ``value`` is whole-step throughput: the tokens of a
 step (16384 prefill + 256 decode) over the mean wall time of a timed step.
@@ -304,11 +305,19 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # The timed region: exactly `steps` whole steps.  Two events per step on
-    # the library's stream (chunk start, decode start; the next step's chunk
-    # start closes the decode) give the launch durations of the two calls.
-    tev = [ev.create() for _ in range(2 * args.steps + 1)]
+    # The timed region: exactly `steps` whole steps and nothing else (an event
+    # recorded between the calls of a step adds a few microseconds of queue
+    # idle time at each boundary, so the per-call figures come from the pass
+    # below).
     t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # An instrumented pass of `steps` more steps: two events per step on the
+    # library's stream (chunk start, decode start; the next step's chunk start
+    # closes the decode) give the launch durations of the two calls.
+    tev = [ev.create() for _ in range(2 * args.steps + 1)]
     for i in range(args.steps):
         ev.record(tev[2 * i], stream)
         chunk()
@@ -317,7 +326,6 @@ def main():
             decode()
     ev.record(tev[2 * args.steps], stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     if args.no_decode:
         chunk_ms = [ev.ms(tev[2 * i], tev[2 * i + 2]) for i in range(args.steps)]
         dec_ms = []

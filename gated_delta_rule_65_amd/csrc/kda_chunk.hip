@@ -450,11 +450,14 @@ __device__ __forceinline__ void raw_decode(const RawRows<E>& x, int L, float (&o
                                            int tid) {
   const int rg = tid >> 4;
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    raw_vals(x, it, out[it]);
-    const bool live = 4 * rg + it < L;  // ... and are zeroed here
+  for (int it = 0; it < 4; ++it) raw_vals(x, it, out[it]);
+  if (L < C) {  // a ragged chunk (uniform in the workgroup): rows past L are zeroed here
 #pragma unroll
-    for (int e = 0; e < 8; ++e) out[it][e] = live ? out[it][e] : 0.f;
+    for (int it = 0; it < 4; ++it) {
+      const bool live = 4 * rg + it < L;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[it][e] = live ? out[it][e] : 0.f;
+    }
   }
 }
 // Channel e (0..7) of the 4 rows of a raw tile as 4 consecutive values.
