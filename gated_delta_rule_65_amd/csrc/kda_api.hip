@@ -118,6 +118,9 @@ kda_status check_chunk(const kda_chunk_args* a, bool need_ptrs) {
   if (a->hqk <= 0 || a->hv <= 0) return fail(KDA_ERR_SHAPE, "head counts must be > 0");
   if (a->hv % a->hqk != 0)
     return fail(KDA_ERR_SHAPE, "GVA needs hv (%d) divisible by hqk (%d)", a->hv, a->hqk);
+  // work items (chunk, value head) are counted in 32 bits
+  if ((a->total_tokens / KDA_CHUNK + a->num_seqs) * (int64_t)a->hv > (int64_t)INT32_MAX)
+    return fail(KDA_ERR_UNSUPPORTED, "(chunks + sequences) x hv above 2^31-1");
   if (!isfinite(a->scale)) return fail(KDA_ERR_SHAPE, "scale must be finite");
   if (a->cu_seqlens == nullptr) {
     if (a->num_seqs == 0 && a->total_tokens != 0)

@@ -104,7 +104,8 @@ typedef struct kda_chunk_args {
   const void *beta;            /* (device) [T_tot, Hv] dtype, logits */
   int32_t dtype;               /* kda_dtype: KDA_F32 or KDA_BF16 */
   int32_t num_seqs;            /* N >= 0 */
-  int64_t total_tokens;        /* T_tot >= 0 */
+  int64_t total_tokens;        /* T_tot >= 0; KDA_ERR_UNSUPPORTED above 2^31 - 1, or when
+                                  (T_tot / 64 + num_seqs) * hv is */
   const int32_t *cu_seqlens;   /* (device) [N+1] non-decreasing, cu[0] = 0,
                                   cu[N] = T_tot; or NULL (dense) */
   int32_t hqk, hv;             /* heads; hv % hqk == 0 */

@@ -97,6 +97,14 @@ def test_chunk_checks(lib, field, value, status):
     assert lib.kda_last_error().decode() != ""
 
 
+def test_chunk_counts_beyond_32_bits_are_rejected(lib):
+    # tokens, and (chunks + sequences) x value heads, are counted in 32 bits
+    for a in (chunk_args(total_tokens=2 ** 31), chunk_args(total_tokens=2 ** 30, hv=256)):
+        assert ws_size(lib, a)[0] == B.KDA_ERR_UNSUPPORTED
+        assert lib.kda_chunk_fwd(ctypes.byref(a)) == B.KDA_ERR_UNSUPPORTED
+    assert ws_size(lib, chunk_args(total_tokens=2 ** 30, hv=64))[0] == B.KDA_OK
+
+
 def test_chunk_state_modes_are_exclusive(lib):
     fake = ctypes.c_void_p(0x1000)   # never dereferenced: the checks fail first
     a = chunk_args(state_cache=fake, initial_state=fake, num_slots=4)
