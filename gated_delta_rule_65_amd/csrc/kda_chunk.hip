@@ -536,7 +536,7 @@ __device__ __forceinline__ void unit_vals_t(const uint4* tile, int r, int piece,
 //
 // With PREP the kernel also writes the prep outputs (qg, kg_t, decay), so the
 // inputs are read from HBM once for the whole intra-chunk stage.
-template <typename E, bool PREP>
+template <typename E, bool PREP, bool GATE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void wy_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ g, const E* __restrict__ beta, const int4* __restrict__ table,
@@ -587,16 +587,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   bool ok = item < items && locate_chunk(item / hv, table, p);
   RawRows<E> rq, rk, rgt;
   E rb;
-  float gA = 0.f, gB[8];  // gate parameters of the item's head (with A_log)
+  float gA = 0.f;  // gate parameters of the item's head (GATE): A_log, dt_bias bits
+  uint4 gB0 = make_uint4(0, 0, 0, 0), gB1 = gB0;
   auto prefetch = [&](int it_, const ChunkPos& pp, int tid) {
     const int h_ = it_ % hv, hq_ = h_ / grp;
     raw_load(q + (size_t)pp.t0 * is.q + hq_ * D, (int)is.q, pp.L, rq, tid);
     raw_load(k + (size_t)pp.t0 * is.k + hq_ * D, (int)is.k, pp.L, rk, tid);
     raw_load(g + (size_t)pp.t0 * is.g + h_ * D, (int)is.g, pp.L, rgt, tid);
     rb = beta[(size_t)(pp.t0 + min(tid, pp.L - 1)) * is.beta + h_];
-    if (ga.a_log) {
+    if constexpr (GATE) {
       gA = ga.a_log[h_];
-      gate_bias8(ga, h_, 8 * (tid & 15), gB);
+      gate_bias8_bits(ga, h_, 8 * (tid & 15), gB0, gB1);
     }
   };
   if (ok) prefetch(item, p, (int)threadIdx.x);
@@ -614,7 +615,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   const int c = item / hv, h = item - c * hv;
   const int L = p.L;
   int claim = 0;
-  if (tid == 0) claim = atomicAdd(counter, 1);  // the next item; published below
+  // the next item; published below.  atomicInc (with no wrap below 2^32) is
+  // an add of 1 that the compiler's atomic combining leaves as it is: the
+  // combined form reads its result back at once, so every item would start by
+  // waiting for the atomic and for all of the previous item's stores.
+  if (tid == 0) claim = (int)atomicInc(reinterpret_cast<unsigned*>(counter), 0xffffffffu);
 
   // kn 2^G for phase 3, kept (per channel, 4 tokens) across phase 1
   typename Col4<E>::T kgp[8];
@@ -625,8 +630,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     raw_decode(rq, L, qx, tid);
     raw_decode(rk, L, kx, tid);
     raw_decode(rgt, L, G, tid);
-    if (ga.a_log) {
+    if constexpr (GATE) {
       // raw gate -> log-decay; rows past L stay 0
+      float gB[8];
+      gate_bias8_decode(ga, gB0, gB1, gB);
       const float a = exp2_fast(gA * LOG2E);
 #pragma unroll
       for (int it = 0; it < 4; ++it)
@@ -807,8 +814,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
       pair(1, 0); pair(0, 0); zero(1, 2); zero(1, 3); zero(2, 3);
     }
   }
-  // the next item's raw rows load during phases 2 and 3
-  if (nok) prefetch(nitem, np, tid);
+  // the next item's raw rows load during phases 2 and 3.  Without a next
+  // item the current rows are fetched again (in bounds, unused): a
+  // branch-free fetch keeps the wait for this item's v rows below from also
+  // waiting for these loads.
+  prefetch(nok ? nitem : item, nok ? np : p, tid);
   lds_barrier();
   // (kn 2^G)^T into R0 and v^T into R1 (rows: channels 8 j + e), each
   // thread's 4 consecutive tokens as one run
@@ -1686,6 +1696,17 @@ static void launch_walk(const ChunkLaunch& L, const WalkArgs<E>& wa) {
   mark(L, 6);
 }
 
+// The WY kernel; without PREP the prep outputs come from prep_kernel.
+template <typename E, bool PREP, bool GATE>
+static void launch_wy(const ChunkLaunch& L, dim3 grid, int items, int* counter) {
+  hipLaunchKernelGGL((wy_kernel<E, PREP, GATE>), grid, dim3(256), 0, (hipStream_t)L.stream,
+                     (const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.g,
+                     (const E*)L.beta, (const int4*)L.table, L.hqk, L.hv, L.use_l2, (E*)L.w,
+                     (E*)L.u, (E*)L.aqk, PREP ? (E*)L.qg : (E*)nullptr,
+                     PREP ? (E*)L.kg_t : (E*)nullptr, PREP ? L.decay : (float*)nullptr, items,
+                     counter, L.gate, L.strides);
+}
+
 template <typename E>
 static hipError_t launch_staged_t(const ChunkLaunch& L) {
   hipStream_t st = (hipStream_t)L.stream;
@@ -1709,18 +1730,17 @@ static hipError_t launch_staged_t(const ChunkLaunch& L) {
     const int resident = cu_count() * (std::is_same<E, float>::value ? 1 : 2);
     const dim3 grid((unsigned)std::max(1, std::min(items, resident)));
     int* wy_counter = reinterpret_cast<int*>((char*)L.zero + 1024);
-    if (L.fuse_prep)
-      hipLaunchKernelGGL((wy_kernel<E, true>), grid, dim3(256), 0, st, (const E*)L.q,
-                         (const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta,
-                         (const int4*)L.table, L.hqk, L.hv, L.use_l2, (E*)L.w, (E*)L.u,
-                         (E*)L.aqk, (E*)L.qg, (E*)L.kg_t, L.decay, items, wy_counter,
-                         L.gate, L.strides);
-    else
-      hipLaunchKernelGGL((wy_kernel<E, false>), grid, dim3(256), 0, st, (const E*)L.q,
-                         (const E*)L.k, (const E*)L.v, (const E*)L.g, (const E*)L.beta,
-                         (const int4*)L.table, L.hqk, L.hv, L.use_l2, (E*)L.w, (E*)L.u,
-                         (E*)L.aqk, (E*)nullptr, (E*)nullptr, (float*)nullptr, items,
-                         wy_counter, L.gate, L.strides);
+    if (L.gate.a_log) {
+      if (L.fuse_prep)
+        launch_wy<E, true, true>(L, grid, items, wy_counter);
+      else
+        launch_wy<E, false, true>(L, grid, items, wy_counter);
+    } else {
+      if (L.fuse_prep)
+        launch_wy<E, true, false>(L, grid, items, wy_counter);
+      else
+        launch_wy<E, false, false>(L, grid, items, wy_counter);
+    }
   } else {
     mark(L, 2);
   }

@@ -79,6 +79,30 @@ __device__ __forceinline__ void gate_bias8(const GateArgs& ga, int h, int c0, fl
     b[4] = y.x; b[5] = y.y; b[6] = y.z; b[7] = y.w;
   }
 }
+// The same 8 biases fetched as raw bits with no branch (two 16-byte loads,
+// both inside the bias array: a bf16 row reads its one piece twice), so that a
+// caller can issue them among other prefetches and decode them later.
+__device__ __forceinline__ void gate_bias8_bits(const GateArgs& ga, int h, int c0, uint4& b0,
+                                                uint4& b1) {
+  const size_t i = (size_t)h * D + c0;
+  const char* p = reinterpret_cast<const char*>(ga.bias) + i * (ga.bias_bf16 ? 2 : 4);
+  b0 = *reinterpret_cast<const uint4*>(p);
+  b1 = *reinterpret_cast<const uint4*>(p + (ga.bias_bf16 ? 0 : 16));
+}
+__device__ __forceinline__ void gate_bias8_decode(const GateArgs& ga, const uint4& b0,
+                                                  const uint4& b1, float (&b)[8]) {
+  const uint32_t w[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+  if (ga.bias_bf16) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      b[2 * d] = __uint_as_float(w[d] << 16);
+      b[2 * d + 1] = __uint_as_float(w[d] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) b[d] = __uint_as_float(w[d]);
+  }
+}
 __device__ __forceinline__ float gate_apply(float graw, float a, float bias, float lb) {
   return lb * sigmoid(a * (graw + bias));
 }
