@@ -207,7 +207,7 @@ __device__ __forceinline__ void l2norm_rows4(float (&x)[4][8]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) s += x[it][e] * x[it][e];
     s = row_sum16(s);
-    const float r = rsqrtf(s + L2_EPS);
+    const float r = rsq(s + L2_EPS);
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[it][e] *= r;
   }
@@ -710,8 +710,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
       float xq[8], xl[8], xr[8], xg[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float up = exp2_fast(G[it][e] - Gm[e]);
-        const float dn = exp2_fast(Gm[e] - G[it][e]);
+        const float dg = G[it][e] - Gm[e];
+        const float up = exp2_fast(dg);
+        const float dn = exp2_fast(-dg);  // the negation is a source modifier
         xq[e] = qx[it][e] * up;
         xl[e] = kx[it][e] * up;
         xr[e] = kx[it][e] * dn;
@@ -865,10 +866,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
 #pragma unroll
     for (int r = 0; r < 16; ++r) sTt[(16 * a + r) * SA + 16 * a + lane] = x[r];
   }
-  for (int idx = tid; idx < C * C; idx += 256) {
-    const int t = idx >> 6, i = idx & 63;
-    if ((i >> 4) > (t >> 4)) sTt[t * SA + i] = 0.f;
-  }
   lds_barrier();
   // levels a - b = 1, 2, 3 of the off-diagonal blocks, one block per wave
   if (wv < 3) wy_offdiag<SA>(wv + 1, wv, sA, sTt, lane);
@@ -886,11 +883,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     for (int s = 0; s < 2; ++s) {
       if (s == 1 && ta < 2) continue;  // T' is lower triangular
       const int i0 = 32 * s + 8 * gq;
+      // Upper blocks of T are never written; the two that these fragments
+      // span, (0, 1) and (2, 3), are taken as zero here.
+      const bool upper = ((ta == 0 && s == 0) || (ta == 2 && s == 1)) && gq >= 2;
       float x[8], bb[8];
       row8(sTt + (16 * ta + l16) * SA + i0, x);
       row8(sB + i0, bb);
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) x[jj] *= bb[jj];
+      for (int jj = 0; jj < 8; ++jj) x[jj] = upper ? 0.f : x[jj] * bb[jj];
       Tf[ta][s] = make_frag<SPLIT>(x);
     }
   // Paired 16-byte stores: a lane's w values of column blocks 2 wv and

@@ -38,6 +38,9 @@ template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float f) {
 // 2^x on the hardware exp unit.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 1/sqrt(x) on the hardware unit, for arguments kept normal by an epsilon.
+__device__ __forceinline__ float rsq(float x) { return __builtin_amdgcn_rsqf(x); }
+
 __device__ __forceinline__ float sigmoid(float x) {
   return 1.0f / (1.0f + exp2_fast(-x * LOG2E));
 }

@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
     }
     sq = row_sum16(sq);
     sk = row_sum16(sk);
-    const float rq = rsqrtf(sq + L2_EPS), rk = rsqrtf(sk + L2_EPS);
+    const float rq = rsq(sq + L2_EPS), rk = rsq(sk + L2_EPS);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       qv[e] *= rq;
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
       }
       sq = row_sum16(sq);
       sk = row_sum16(sk);
-      const float rq = rsqrtf(sq + L2_EPS), rk = rsqrtf(sk + L2_EPS);
+      const float rq = rsq(sq + L2_EPS), rk = rsq(sk + L2_EPS);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         qv[e] *= rq;
