@@ -816,10 +816,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     }
   }
   // the next item's raw rows load during phases 2 and 3.  Without a next
-  // item the current rows are fetched again (in bounds, unused): a
-  // branch-free fetch keeps the wait for this item's v rows below from also
-  // waiting for these loads.
-  prefetch(nok ? nitem : item, nok ? np : p, tid);
+  // item the first row of the current chunk is fetched by every lane (in
+  // bounds, unused, a few hundred bytes): a branch-free fetch keeps the wait
+  // for this item's v rows below from also waiting for these loads.
+  const ChunkPos pf = nok ? np : ChunkPos{p.n, p.t0, 1};
+  prefetch(nok ? nitem : item, pf, tid);
   lds_barrier();
   // (kn 2^G)^T into R0 and v^T into R1 (rows: channels 8 j + e), each
   // thread's 4 consecutive tokens as one run
@@ -867,12 +868,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     for (int r = 0; r < 16; ++r) sTt[(16 * a + r) * SA + 16 * a + lane] = x[r];
   }
   lds_barrier();
-  // levels a - b = 1, 2, 3 of the off-diagonal blocks, one block per wave
-  if (wv < 3) wy_offdiag<SA>(wv + 1, wv, sA, sTt, lane);
-  lds_barrier();
-  if (wv < 2) wy_offdiag<SA>(wv + 2, wv, sA, sTt, lane);
-  lds_barrier();
-  if (wv == 0) wy_offdiag<SA>(3, 0, sA, sTt, lane);
+  // Off-diagonal blocks by columns: T_ab needs only T_aa and the blocks T_cb
+  // (b <= c < a) of its own column, so wave b walks column b downwards, reading
+  // back what it wrote itself (a wave's LDS accesses complete in order), and
+  // one barrier closes the phase.
+  if (wv < 3)
+    for (int a = wv + 1; a < 4; ++a) wy_offdiag<SA>(a, wv, sA, sTt, lane);
   lds_barrier();
 
   // ---- phase 3: T' = T diag(b); w^T = (kn 2^G)^T T'^T and u = T' v
