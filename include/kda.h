@@ -131,7 +131,8 @@ typedef struct kda_chunk_args {
                                   or 8 (a tuning knob; results do not change) */
   void **stage_events;         /* optional hipEvent_t[num_stage_events], recorded
                                   on `stream` at the stage boundaries below
-                                  (profiling); NULL = none.  The caller owns them. */
+                                  (profiling); NULL = none, and a NULL entry skips
+                                  its boundary.  The caller owns them. */
   int32_t num_stage_events;
   void *stream;                /* hipStream_t or NULL */
   /* Gate parameters (optional; both or neither).  With them, g holds a raw

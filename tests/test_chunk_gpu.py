@@ -299,6 +299,40 @@ def test_deterministic():
     assert np.array_equal(r1[0], r2[0]) and np.array_equal(r1[1], r2[1])
 
 
+def test_stage_events_sparse():
+    """Stage events with NULL entries: only the given boundaries are recorded,
+    the events complete, and the results equal a call without events bit for bit
+    (also under the group scan, whose boundaries differ)."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    hip.hipEventQuery.argtypes = [ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    b = inputs.make_chunk([300, 77, 0, 129], 2, 4, seed=33, init=True)
+    q, k, v, g, beta = gpu(b)
+    init = b.initial_state.to(DEV)
+    cu = b.cu_seqlens.to(DEV)
+    for groups in (1, 2):
+        ref_o, ref_s = B.chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=init,
+                                   output_final_state=True, cu_seqlens=cu, groups=groups)
+        evs = []
+        for _ in range(2):
+            e = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(e)) == 0
+            evs.append(e.value)
+        # boundaries: after the table and after WY; every other entry NULL
+        o, s = B.chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=init,
+                           output_final_state=True, cu_seqlens=cu, groups=groups,
+                           stage_events=[None, evs[0], None, evs[1], None, None, None])
+        torch.cuda.synchronize()
+        for e in evs:
+            assert hip.hipEventSynchronize(ctypes.c_void_p(e)) == 0
+            assert hip.hipEventQuery(ctypes.c_void_p(e)) == 0  # recorded and complete
+            hip.hipEventDestroy(ctypes.c_void_p(e))
+        assert torch.equal(o, ref_o) and torch.equal(s, ref_s)
+
+
 # --------------------------------------------------------------- full workloads
 
 def test_dense_prefill_workload():
