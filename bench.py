@@ -220,6 +220,130 @@ def copy_calibration(dev):
                 launches=3)
 
 
+def next_rows(dev):
+    """The rows beyond the hot path, each timed against its plain counterpart:
+    gate parameters, mid-prefill checkpoints and inputs read through a
+    per-token stride on the dense-prefill chunked forward; multi-token
+    (speculative) decode and a bf16 state pool on the decode workload.  Inputs
+    are resident in HBM.  The clocks drift with the recent load by several
+    percent, so a row and its plain counterpart are timed alternately (three
+    rounds of 20 calls after 3 warm-up calls, CUDA events) and the medians are
+    compared."""
+    import torch
+    from gated_delta_rule_65_amd import binding as B
+    from gated_delta_rule_65_amd import inputs
+
+    def timed(fn, reps=20, warm=3):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def against(plain_fn, fn, rounds=3):
+        tp, tv = [], []
+        for _ in range(rounds):
+            tp.append(timed(plain_fn))
+            tv.append(timed(fn))
+        return sorted(tp)[rounds // 2], sorted(tv)[rounds // 2]
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    res = {}
+    # ---- chunked forward: dense prefill in varlen form with the max_seqlen hint
+    wl = inputs.WORKLOADS["dense_prefill"]
+    cb = inputs.make_workload("dense_prefill", device=dev)
+    T, N, hv = cb.q.shape[0], wl["B"], wl["hv"]
+    base = dict(scale=cb.scale, initial_state=cb.initial_state, output_final_state=True,
+                cu_seqlens=cb.cu_seqlens, max_seqlen=wl["T"])
+
+    def plain():
+        B.chunk_kda(cb.q, cb.k, cb.v, cb.g, cb.beta, **base)
+
+    def chunk_row(fn, **extra):
+        p_ms, ms = against(plain, fn)
+        return dict(ms=round(ms, 4), plain_ms=round(p_ms, 4),
+                    tokens_per_s=round(T / ms * 1e3, 1), vs_plain=round(p_ms / ms, 3), **extra)
+
+    # f1: g as a raw gate, lower_bound * sigmoid(exp(A_log) (g + dt_bias)); with
+    # A_log = 0, dt_bias = 0 and g ~ N(0, 1) this is the workload's own g draw
+    g_raw = torch.randn(cb.g.shape, generator=gen, device=dev).to(cb.g.dtype)
+    a_log = torch.zeros(hv, device=dev)
+    dt_bias = torch.zeros(hv, 128, device=dev)
+    res["f1_gate_parameters"] = chunk_row(
+        lambda: B.chunk_kda(cb.q, cb.k, cb.v, g_raw, cb.beta, A_log=a_log, dt_bias=dt_bias,
+                            **base))
+    # f2: one mid-prefill snapshot per sequence, at half its length
+    ck_state = torch.empty(N, hv, 128, 128, device=dev)
+    ck_off = torch.full((N,), wl["T"] // 2, dtype=torch.int32, device=dev)
+    res["f2_checkpoints"] = chunk_row(
+        lambda: B.chunk_kda(cb.q, cb.k, cb.v, cb.g, cb.beta, checkpoint_state=ck_state,
+                            checkpoint_offsets=ck_off, **base),
+        snapshot=f"1 per sequence at token {wl['T'] // 2}")
+    # f4: q, k, v, g, beta as bands of one [T, W] projection output (per-token stride)
+    flat = [x.reshape(T, -1) for x in (cb.q, cb.k, cb.v, cb.g, cb.beta)]
+    W = sum(f.shape[1] for f in flat) + 8
+    W += (-W) % 8
+    proj = torch.empty((T, W), dtype=cb.q.dtype, device=dev)
+    views, off = [], 0
+    for x, f in zip((cb.q, cb.k, cb.v, cb.g, cb.beta), flat):
+        proj[:, off:off + f.shape[1]] = f
+        views.append(proj[:, off:off + f.shape[1]].view(x.shape))
+        off += f.shape[1]
+    res["f4_strided_inputs"] = chunk_row(lambda: B.chunk_kda(*views, **base),
+                                         layout=f"bands of one [{T}, {W}] bf16 buffer")
+    del cb, proj, views, g_raw
+    torch.cuda.empty_cache()
+    # ---- decode: 256 requests x 32 heads over a [1024, 32, 128, 128] pool
+    dwl = inputs.WORKLOADS["decode_paged"]
+    db = inputs.make_workload("decode_paged", device=dev)
+    n, hqk, dhv = dwl["N"], dwl["hqk"], dwl["hv"]
+    state1 = n * dhv * 128 * 128 * 4 * 2
+    io1 = decode_work(n, hqk, dhv, 2)["bytes"] - state1
+
+    def dplain():
+        B.kda_decode(db.q, db.k, db.v, db.g, db.beta, db.state_cache, db.state_indices,
+                     scale=db.scale)
+
+    def decode_row(fn, byt, **extra):
+        p_ms, ms = against(dplain, fn)
+        return dict(ms=round(ms, 4), plain_ms=round(p_ms, 4), gb_s=round(byt / ms / 1e6, 1),
+                    hbm_frac=round(byt / ms / 1e6 / PEAK_HBM_GBS, 4),
+                    plain_gb_s=round((state1 + io1) / p_ms / 1e6, 1), **extra)
+
+    # f4: the same decode over a bf16 pool (rounded after each token)
+    cache16 = db.state_cache.to(torch.bfloat16)
+    res["f4_bf16_state_decode"] = decode_row(
+        lambda: B.kda_decode(db.q, db.k, db.v, db.g, db.beta, cache16, db.state_indices,
+                             scale=db.scale),
+        n * dhv * 128 * 128 * 2 * 2 + io1)
+    del cache16
+    torch.cuda.empty_cache()
+    # f3: 4 tokens per request, each token's state stored to its own pool row
+    tt = 4
+    slots = db.state_cache.shape[0]
+
+    def draw(shape, s=1.0):
+        return (s * torch.randn(shape, generator=gen, device=dev)).to(torch.bfloat16)
+    qm, km = draw((n, tt, hqk, 128)), draw((n, tt, hqk, 128))
+    vm, bm = draw((n, tt, dhv, 128)), draw((n, tt, dhv))
+    gm = (-5.0 * torch.sigmoid(torch.randn((n, tt, dhv, 128), generator=gen,
+                                           device=dev))).to(torch.bfloat16)
+    idx = torch.randperm(slots, generator=gen, device=dev)[:n * tt].to(torch.int32).view(n, tt)
+    row = decode_row(
+        lambda: B.kda_decode(qm, km, vm, gm, bm, db.state_cache, idx, scale=db.scale),
+        n * dhv * 128 * 128 * 4 * (1 + tt) + tt * io1, tokens_per_request=tt)
+    row["tokens_per_s"] = round(n * tt / row["ms"] * 1e3, 1)
+    res["f3_multi_token_decode"] = row
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,6 +363,10 @@ def main():
                     help="after the timed region, run a plain elementwise copy of "
                          f"{CAL_BYTES >> 20} MiB (reads and writes that many bytes) three "
                          "times: the reference kernel for scaling HBM byte counters")
+    ap.add_argument("--next-rows", action="store_true",
+                    help="instead of the step: time the rows beyond the hot path (gate "
+                         "parameters, checkpoints, strided inputs, multi-token decode, bf16 "
+                         "state) against their plain counterparts; one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -253,6 +381,10 @@ def main():
     B.load_library()   # raises if the HIP library is not built
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.next_rows:
+        print(json.dumps(dict(kind="next_rows", data="synthetic", dtype="bf16",
+                              rows=next_rows(dev))))
+        return
     ev = HipEvents()
     stream = torch.cuda.current_stream(dev).cuda_stream
 
