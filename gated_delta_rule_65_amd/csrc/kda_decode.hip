@@ -205,7 +205,168 @@ __global__ __launch_bounds__(256) void decode_kernel(
 // outside the pool (or a count outside [1, cols]) zeroes the request's output
 // rows and touches no state.  This is gated_delta_rule_decode's [B, T]
 // state_indices with num_accepted_tokens (page "mate.kda").
+// The raw bits of one token's inputs on this lane (q, k, g: 8 channels each;
+// the lane's 8 v rows; beta), so that the next token can be fetched before this
+// token's state stores: the memory counter completes operations in issue
+// order, and a fetch issued after the stores would wait for them.
+template <typename T> struct Raw4 { using U = uint2; };
+template <> struct Raw4<float> { using U = float4; };
+template <typename T>
+__device__ __forceinline__ typename Raw4<T>::U raw4(const T* p) {
+  return *reinterpret_cast<const typename Raw4<T>::U*>(p);
+}
+__device__ __forceinline__ void unraw4(const float4& a, const float*, float* x) {
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+}
+__device__ __forceinline__ void unraw4(const uint2& u, const bf16*, float* x) {
+  const float4 a = widen4(u);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+}
+__device__ __forceinline__ void unraw4(const uint2& u, const _Float16*, float* x) {
+  x[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u.x & 0xffffu));
+  x[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u.x >> 16));
+  x[2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u.y & 0xffffu));
+  x[3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u.y >> 16));
+}
+template <typename T> struct TokRaw {
+  typename Raw4<T>::U q0, q1, k0, k1, g0, g1;
+  T v[8];
+  T b;
+};
+
+// The multi-token decode's per-request context.
+template <typename T, typename S> struct MultiCtx {
+  const T *q, *k, *v, *g, *beta;
+  S* cache;
+  const int32_t* ir;  // this request's row of state_indices
+  T* out;
+  int ntok, hv, hq, h, req, num_slots;
+  float scale, ga_a;
+  int use_l2;
+  InStrides is;
+  int64_t slot_stride;
+  GateArgs ga;
+};
+
 template <typename T, typename S>
+__device__ __forceinline__ void tok_fetch(const MultiCtx<T, S>& c, int t, int j, int wave,
+                                          int rsub, TokRaw<T>& r) {
+  const size_t tok = (size_t)c.req * c.ntok + t;
+  const T* qp = c.q + tok * c.is.q + c.hq * D;
+  const T* kp = c.k + tok * c.is.k + c.hq * D;
+  const T* gp = c.g + tok * c.is.g + c.h * D;
+  const T* vp = c.v + tok * c.is.v + c.h * D;
+  r.q0 = raw4(qp + 4 * j);
+  r.q1 = raw4(qp + 64 + 4 * j);
+  r.k0 = raw4(kp + 4 * j);
+  r.k1 = raw4(kp + 64 + 4 * j);
+  r.g0 = raw4(gp + 4 * j);
+  r.g1 = raw4(gp + 64 + 4 * j);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) r.v[s] = vp[16 * s + 4 * wave + rsub];
+  r.b = c.beta[tok * c.is.beta + c.h];
+}
+
+// Token t: decay, delta write and read-out on the state rows in hs; its
+// inputs are in cur, and the next token's are fetched into nxt first (the
+// last token fetches its own again: in bounds, unused).  ALL: every stored
+// row is valid, so the stores need no branch.
+template <typename T, typename S, bool GATE, bool ALL>
+__device__ __forceinline__ void multi_token_step(const MultiCtx<T, S>& c, int t, int j, int wave,
+                                                 int rsub, const float (&bias)[8],
+                                                 float4 (&hs)[8][2], TokRaw<T>& nxt) {
+  const TokRaw<T> cur = nxt;
+  tok_fetch(c, min(t + 1, c.ntok - 1), j, wave, rsub, nxt);
+  float qv[8], kv[8], gl[8], vr[8], al[8];
+  unraw4(cur.q0, (const T*)nullptr, qv);
+  unraw4(cur.q1, (const T*)nullptr, qv + 4);
+  unraw4(cur.k0, (const T*)nullptr, kv);
+  unraw4(cur.k1, (const T*)nullptr, kv + 4);
+  unraw4(cur.g0, (const T*)nullptr, gl);
+  unraw4(cur.g1, (const T*)nullptr, gl + 4);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) vr[s] = to_f32(cur.v[s]);
+  if constexpr (GATE) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gl[e] = gate_apply(gl[e], c.ga_a, bias[e], c.ga.lower_bound);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) al[e] = exp2_fast(gl[e] * LOG2E);
+  const float b = sigmoid(to_f32(cur.b));
+  if (c.use_l2) {
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sq += qv[e] * qv[e];
+      sk += kv[e] * kv[e];
+    }
+    sq = row_sum16(sq);
+    sk = row_sum16(sk);
+    const float rq = rsq(sq + L2_EPS), rk = rsq(sk + L2_EPS);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qv[e] *= rq;
+      kv[e] *= rk;
+    }
+  }
+  float kq = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) kq += kv[e] * qv[e];
+  kq = row_sum16(kq);
+  const int rt = c.ir[t];
+  S* dst = (ALL || (rt >= 0 && rt < c.num_slots))
+               ? c.cache + (size_t)rt * c.slot_stride + (size_t)c.h * (D * D)
+               : nullptr;
+  float ov[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    float x[8] = {hs[s][0].x, hs[s][0].y, hs[s][0].z, hs[s][0].w,
+                  hs[s][1].x, hs[s][1].y, hs[s][1].z, hs[s][1].w};
+    float pk = 0.f, pq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] *= al[e];
+      pk += x[e] * kv[e];
+      pq += x[e] * qv[e];
+    }
+    pk = row_sum16(pk);
+    pq = row_sum16(pq);
+    const float u = b * (vr[s] - pk);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] += u * kv[e];
+    // the next token starts from the state as stored (rounded when bf16)
+    hs[s][0] = as_stored(make_float4(x[0], x[1], x[2], x[3]), (S*)nullptr);
+    hs[s][1] = as_stored(make_float4(x[4], x[5], x[6], x[7]), (S*)nullptr);
+    const int r = 16 * s + 4 * wave + rsub;
+    if (ALL)
+      row_store(dst + r * D, j, hs[s]);
+    else if (dst)
+      row_store(dst + r * D, j, hs[s]);
+    ov[s] = c.scale * (pq + u * kq);
+  }
+  // Outputs: every lane of a 16-lane row group holds the values of the group's
+  // 8 rows; lanes j and j + 8 both write row s = j & 7 (the same value), so
+  // the store needs no branch either.
+  const int so = j & 7;
+  float val = ov[0];
+#pragma unroll
+  for (int s = 1; s < 8; ++s) val = so == s ? ov[s] : val;
+  T* o = c.out + (((size_t)c.req * c.ntok + t) * c.hv + c.h) * D;
+  o[16 * so + 4 * wave + rsub] = from_f32<T>(val);
+}
+
+template <typename T, typename S, bool GATE, bool ALL>
+__device__ __forceinline__ void multi_tokens(const MultiCtx<T, S>& c, int j, int wave, int rsub,
+                                             const float (&bias)[8], float4 (&hs)[8][2],
+                                             TokRaw<T>& nxt) {
+  // token 0 peeled: inside the loop every iteration then starts with the same
+  // operations in flight (the next token's fetch, then the previous token's
+  // stores), and the compiler's wait for the fetch leaves the stores alone
+  multi_token_step<T, S, GATE, ALL>(c, 0, j, wave, rsub, bias, hs, nxt);
+  for (int t = 1; t < c.ntok; ++t) multi_token_step<T, S, GATE, ALL>(c, t, j, wave, rsub, bias, hs, nxt);
+}
+
+template <typename T, typename S, bool GATE>
 __global__ __launch_bounds__(256) void decode_multi_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ g, const T* __restrict__ beta, S* __restrict__ cache,
@@ -232,79 +393,39 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
         out[(((size_t)req * ntok + t) * hv + h) * D + tid] = from_f32<T>(0.0f);
     return;
   }
+  MultiCtx<T, S> c{q, k, v, g, beta, cache, ir, out, ntok, hv, hq, h, req, num_slots,
+                   scale, 0.f, use_l2, is, slot_stride, ga};
+  float bias[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if constexpr (GATE) {
+    c.ga_a = exp2_fast(ga.a_log[h] * LOG2E);  // exp(A_log[h])
+    if (ga.bias_bf16)
+      lane8(reinterpret_cast<const bf16*>(ga.bias) + (size_t)h * D, j, bias);
+    else
+      lane8(reinterpret_cast<const float*>(ga.bias) + (size_t)h * D, j, bias);
+  }
+  bool all = true;  // every state the request stores lands in the pool
+  for (int t = 0; t < ntok; ++t) {
+    const int rt = ir[t];
+    all = all && rt >= 0 && rt < num_slots;
+  }
   const S* st0 = cache + (size_t)row0 * slot_stride + (size_t)h * (D * D);
   float4 hs[8][2];
 #pragma unroll
   for (int s = 0; s < 8; ++s) row_load(st0 + (16 * s + 4 * wave + rsub) * D, j, hs[s]);
-  const float ga_a = ga.a_log ? exp2_fast(ga.a_log[h] * LOG2E) : 0.f;  // exp(A_log[h])
-  for (int t = 0; t < ntok; ++t) {
-    const size_t tok = (size_t)req * ntok + t;
-    const T* qp = q + tok * is.q + hq * D;
-    const T* kp = k + tok * is.k + hq * D;
-    const T* gp = g + tok * is.g + h * D;
-    const T* vp = v + tok * is.v + h * D;
-    float qv[8], kv[8], al[8];
-    token_qk_decay(qp, kp, gp, j, h, ga, ga_a, qv, kv, al);
-    float vr[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) vr[s] = to_f32(vp[16 * s + 4 * wave + rsub]);
-    const float b = sigmoid(to_f32(beta[tok * is.beta + h]));
-    if (use_l2) {
-      float sq = 0.f, sk = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sq += qv[e] * qv[e];
-        sk += kv[e] * kv[e];
-      }
-      sq = row_sum16(sq);
-      sk = row_sum16(sk);
-      const float rq = rsq(sq + L2_EPS), rk = rsq(sk + L2_EPS);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qv[e] *= rq;
-        kv[e] *= rk;
-      }
-    }
-    float kq = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) kq += kv[e] * qv[e];
-    kq = row_sum16(kq);
-    const int rt = ir[t];
-    S* dst = (rt >= 0 && rt < num_slots)
-                 ? cache + (size_t)rt * slot_stride + (size_t)h * (D * D)
-                 : nullptr;
-    T* o = out + (tok * hv + h) * D;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      float x[8] = {hs[s][0].x, hs[s][0].y, hs[s][0].z, hs[s][0].w,
-                    hs[s][1].x, hs[s][1].y, hs[s][1].z, hs[s][1].w};
-      float pk = 0.f, pq = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[e] *= al[e];
-        pk += x[e] * kv[e];
-        pq += x[e] * qv[e];
-      }
-      pk = row_sum16(pk);
-      pq = row_sum16(pq);
-      const float u = b * (vr[s] - pk);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] += u * kv[e];
-      // the next token starts from the state as stored (rounded when bf16)
-      hs[s][0] = as_stored(make_float4(x[0], x[1], x[2], x[3]), (S*)nullptr);
-      hs[s][1] = as_stored(make_float4(x[4], x[5], x[6], x[7]), (S*)nullptr);
-      const int r = 16 * s + 4 * wave + rsub;
-      if (dst) row_store(dst + r * D, j, hs[s]);
-      if (j == 0) o[r] = from_f32<T>(scale * (pq + u * kq));
-    }
-  }
+  TokRaw<T> nxt;
+  tok_fetch(c, 0, j, wave, rsub, nxt);
+  if (all)
+    multi_tokens<T, S, GATE, true>(c, j, wave, rsub, bias, hs, nxt);
+  else
+    multi_tokens<T, S, GATE, false>(c, j, wave, rsub, bias, hs, nxt);
 }
 
 template <typename T, typename S>
 static hipError_t launch_decode_t(const DecodeLaunch& L) {
   const dim3 grid((unsigned)((size_t)L.n * L.hv)), block(256);
   if (L.tokens > 1 || L.cols > 0) {
-    hipLaunchKernelGGL((decode_multi_kernel<T, S>), grid, block, 0, (hipStream_t)L.stream,
+    auto mk = L.gate.a_log ? decode_multi_kernel<T, S, true> : decode_multi_kernel<T, S, false>;
+    hipLaunchKernelGGL(mk, grid, block, 0, (hipStream_t)L.stream,
                        (const T*)L.q, (const T*)L.k, (const T*)L.v, (const T*)L.g,
                        (const T*)L.beta, (S*)L.cache, L.idx, L.accepted, (T*)L.out, L.tokens,
                        L.cols, L.hqk, L.hv, L.scale, L.use_l2, L.num_slots, L.gate, L.strides,
