@@ -41,8 +41,11 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // 1/sqrt(x) on the hardware unit, for arguments kept normal by an epsilon.
 __device__ __forceinline__ float rsq(float x) { return __builtin_amdgcn_rsqf(x); }
 
+// 1 / (1 + e^-x) with the hardware reciprocal (1 ulp): the denominator is
+// >= 1 or +inf, so there is no denormal or overflow case, and saturated inputs
+// give exactly 1 and 0.
 __device__ __forceinline__ float sigmoid(float x) {
-  return 1.0f / (1.0f + exp2_fast(-x * LOG2E));
+  return __builtin_amdgcn_rcpf(1.0f + exp2_fast(-x * LOG2E));
 }
 
 // Optional gate parameters (the raw gate g becomes the log-decay
