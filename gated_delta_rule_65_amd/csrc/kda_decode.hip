@@ -18,20 +18,32 @@
 //
 // Mapping (HBM-bound: 64 KiB read + 64 KiB written per unit): one 256-thread
 // workgroup per unit; 16 lanes (one DPP row) own one state row, each lane
-// holding 8 key channels {4j..4j+3} and {64+4j..64+4j+3} (j = lane % 16) so
-// that each float4 access of a 16-lane group is 256 contiguous bytes.  The
+// holding 8 key channels (j = lane % 16): {4j..4j+3} and {64+4j..64+4j+3} for
+// an fp32 state, so that each float4 access of a 16-lane group is 256
+// contiguous bytes, and {8j..8j+7} for a bf16 state, so that a lane's share
+// of a row is one 16-byte access.  q, k, g and the gate bias follow the same
+// channel split.  The
 // 8 row-steps of a thread are all loaded before any arithmetic, which keeps
 // 16 KiB per wave in flight.  The two dot products per row are 16-lane DPP
 // reductions; (row . qn) after the write is formed as
 // (decayed row . qn) + u_v (kn . qn) so that one reduction pass suffices.
+#include <type_traits>
+
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
 
-// This lane's 8 values of a V-first state row (key channels 4j..4j+3 and
-// 64+4j..64+4j+3): fp32, or bf16 widened on load and rounded (to nearest
-// even) on store.
+// The two 4-channel pieces of lane j's 8 key channels for a state of type S.
+template <typename S> __device__ __forceinline__ int piece0(int j) {
+  return std::is_same<S, bf16>::value ? 8 * j : 4 * j;
+}
+template <typename S> __device__ __forceinline__ int piece1(int j) {
+  return std::is_same<S, bf16>::value ? 8 * j + 4 : 64 + 4 * j;
+}
+
+// This lane's 8 values of a V-first state row (key channels piece0.., piece1..):
+// fp32, or bf16 widened on load and rounded (to nearest even) on store.
 __device__ __forceinline__ void row_load(const float* row, int j, float4 (&h)[2]) {
   h[0] = reinterpret_cast<const float4*>(row)[j];
   h[1] = reinterpret_cast<const float4*>(row)[16 + j];
@@ -41,15 +53,16 @@ __device__ __forceinline__ float4 widen4(uint2 u) {
                      __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
 __device__ __forceinline__ void row_load(const bf16* row, int j, float4 (&h)[2]) {
-  h[0] = widen4(reinterpret_cast<const uint2*>(row)[j]);
-  h[1] = widen4(reinterpret_cast<const uint2*>(row)[16 + j]);
+  const uint4 u = reinterpret_cast<const uint4*>(row)[j];  // channels 8j .. 8j + 7
+  h[0] = widen4(make_uint2(u.x, u.y));
+  h[1] = widen4(make_uint2(u.z, u.w));
 }
 // The state is written back with nontemporal stores: the rows are not read
 // again soon, and decode steps run back to back stream the pool faster when
 // the written lines do not linger in the caches (256 x 32 fp32 rows:
 // 0.215 -> 0.169 ms per back-to-back step).
 typedef float f32x4_nt __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_nt __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void row_store(float* row, int j, const float4 (&h)[2]) {
   f32x4_nt* p = reinterpret_cast<f32x4_nt*>(row);
   __builtin_nontemporal_store(f32x4_nt{h[0].x, h[0].y, h[0].z, h[0].w}, p + j);
@@ -60,10 +73,9 @@ __device__ __forceinline__ uint2 narrow4(float4 x) {
                     (uint32_t)bf16_bits(x.z) | ((uint32_t)bf16_bits(x.w) << 16));
 }
 __device__ __forceinline__ void row_store(bf16* row, int j, const float4 (&h)[2]) {
-  u32x2_nt* p = reinterpret_cast<u32x2_nt*>(row);
   const uint2 a = narrow4(h[0]), b = narrow4(h[1]);
-  __builtin_nontemporal_store(u32x2_nt{a.x, a.y}, p + j);
-  __builtin_nontemporal_store(u32x2_nt{b.x, b.y}, p + 16 + j);
+  __builtin_nontemporal_store(u32x4_nt{a.x, a.y, b.x, b.y},
+                              reinterpret_cast<u32x4_nt*>(row) + j);
 }
 // Four consecutive elements widened to fp32 (one 16-byte or 8-byte load).
 __device__ __forceinline__ void load4(const float* p, float* x) {
@@ -81,30 +93,30 @@ __device__ __forceinline__ void load4(const _Float16* p, float* x) {
   x[2] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u.y & 0xffffu));
   x[3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u.y >> 16));
 }
-// This lane's 8 channels of a 128-vector: 4j..4j+3 and 64+4j..64+4j+3.
-template <typename T>
+// This lane's 8 channels of a 128-vector, split as the state S's rows are.
+template <typename S, typename T>
 __device__ __forceinline__ void lane8(const T* p, int j, float (&x)[8]) {
-  load4(p + 4 * j, x);
-  load4(p + 64 + 4 * j, x + 4);
+  load4(p + piece0<S>(j), x);
+  load4(p + piece1<S>(j), x + 4);
 }
 // One token's q, k and per-channel decay factor exp(g) on this lane's 8
 // channels.  All loads are issued before the gate arithmetic so that they
 // stay vector loads in one block.
-template <typename T>
+template <typename S, typename T>
 __device__ __forceinline__ void token_qk_decay(const T* qp, const T* kp, const T* gp, int j,
                                                int h, const GateArgs& ga, float ga_a,
                                                float (&qv)[8], float (&kv)[8],
                                                float (&al)[8]) {
   float gl[8];
-  lane8(qp, j, qv);
-  lane8(kp, j, kv);
-  lane8(gp, j, gl);
+  lane8<S>(qp, j, qv);
+  lane8<S>(kp, j, kv);
+  lane8<S>(gp, j, gl);
   if (ga.a_log) {
     float bias[8];
     if (ga.bias_bf16) {
-      lane8(reinterpret_cast<const bf16*>(ga.bias) + (size_t)h * D, j, bias);
+      lane8<S>(reinterpret_cast<const bf16*>(ga.bias) + (size_t)h * D, j, bias);
     } else {
-      lane8(reinterpret_cast<const float*>(ga.bias) + (size_t)h * D, j, bias);
+      lane8<S>(reinterpret_cast<const float*>(ga.bias) + (size_t)h * D, j, bias);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) gl[e] = gate_apply(gl[e], ga_a, bias[e], ga.lower_bound);
@@ -148,7 +160,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
   const T* vp = v + (size_t)req * is.v + h * D;
   float qv[8], kv[8], al[8];
   const float ga_a = ga.a_log ? exp2_fast(ga.a_log[h] * LOG2E) : 0.f;  // exp(A_log[h])
-  token_qk_decay(qp, kp, gp, j, h, ga, ga_a, qv, kv, al);
+  token_qk_decay<S>(qp, kp, gp, j, h, ga, ga_a, qv, kv, al);
   float vr[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) vr[s] = to_f32(vp[16 * s + 4 * wave + rsub]);
@@ -256,12 +268,12 @@ __device__ __forceinline__ void tok_fetch(const MultiCtx<T, S>& c, int t, int j,
   const T* kp = c.k + tok * c.is.k + c.hq * D;
   const T* gp = c.g + tok * c.is.g + c.h * D;
   const T* vp = c.v + tok * c.is.v + c.h * D;
-  r.q0 = raw4(qp + 4 * j);
-  r.q1 = raw4(qp + 64 + 4 * j);
-  r.k0 = raw4(kp + 4 * j);
-  r.k1 = raw4(kp + 64 + 4 * j);
-  r.g0 = raw4(gp + 4 * j);
-  r.g1 = raw4(gp + 64 + 4 * j);
+  r.q0 = raw4(qp + piece0<S>(j));
+  r.q1 = raw4(qp + piece1<S>(j));
+  r.k0 = raw4(kp + piece0<S>(j));
+  r.k1 = raw4(kp + piece1<S>(j));
+  r.g0 = raw4(gp + piece0<S>(j));
+  r.g1 = raw4(gp + piece1<S>(j));
 #pragma unroll
   for (int s = 0; s < 8; ++s) r.v[s] = vp[16 * s + 4 * wave + rsub];
   r.b = c.beta[tok * c.is.beta + c.h];
@@ -399,9 +411,9 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
   if constexpr (GATE) {
     c.ga_a = exp2_fast(ga.a_log[h] * LOG2E);  // exp(A_log[h])
     if (ga.bias_bf16)
-      lane8(reinterpret_cast<const bf16*>(ga.bias) + (size_t)h * D, j, bias);
+      lane8<S>(reinterpret_cast<const bf16*>(ga.bias) + (size_t)h * D, j, bias);
     else
-      lane8(reinterpret_cast<const float*>(ga.bias) + (size_t)h * D, j, bias);
+      lane8<S>(reinterpret_cast<const float*>(ga.bias) + (size_t)h * D, j, bias);
   }
   bool all = true;  // every state the request stores lands in the pool
   for (int t = 0; t < ntok; ++t) {
