@@ -1,24 +1,27 @@
 #!/usr/bin/env python3
 """Throughput of the KDA hot path on one MI355X.
 
-One step = one chunked forward over the dense-prefill workload (B=4, T=4096,
-Hqk=Hv=16, D=128, bf16, fp32 initial and final state) followed by one paged
-decode over the decode workload (256 requests x 32 heads, fp32 cache
-[1024, 32, 128, 128]), inputs resident in HBM.  W untimed warm-up steps, then K
-timed steps bracketed by device synchronisation, with nothing else queued
-between them.  After the timed region: K more steps with two HIP events per
-step on the library's stream (chunk start, decode start) for the launch
-durations of the two calls, K chunk forwards with the library's stage events
-for the per-kernel breakdown, and K decode launches back to back.
+One step = one chunked forward over the long single-sequence prefill
+(B=1, T=131072, Hqk=Hv=32, D=128, bf16, slow decay g = -0.5 sigmoid(N(0,1)),
+fp32 initial and final state), the largest of the workloads, inputs resident
+in HBM.  W untimed warm-up steps, then K timed steps bracketed by device
+synchronisation, with nothing else queued between them.  ``value`` is its
+tokens/s: 131072 tokens over the mean wall time of a step.
 
-Printed: one JSON line.  ``value`` is whole-step throughput: the tokens of a
-step (16384 prefill + 256 decode) over the mean wall time of a timed step.
-``chunk_tokens_per_s`` is the chunk forward alone.  ``roofline`` describes the
-kernel that takes the most time in a step (HBM traffic from rocprofv3 byte
-counters scaled by a plain copy kernel, when recorded for the current kernel
-sources); ``kernels`` lists all of them.  ``cpu_baseline`` times the fp64 CPU
-oracle on the host.  ``--copy-calibration`` adds the reference copy kernel
-after the timed region.
+After the timed region, each with HIP events on the library's stream:
+  * K more calls with the library's stage events: the per-kernel breakdown
+    of the headline workload and ``roofline`` (its dominant kernel);
+  * the chunk path as a whole (all kernels of a call) against the bf16 MFMA
+    peak: ``roofline_chunk_path``;
+  * the other prefill workloads, each timed alone (``legs``): the dense
+    prefill (B=4, T=4096, H=16) and the varlen GVA batch (24 sequences,
+    32768 tokens, Hqk=8, Hv=32, paged fp32 state);
+  * the paged decode (256 requests x 32 heads, fp32 pool [1024, 32, 128,
+    128], updated in place) after a dense-prefill chunk forward and back to
+    back: ``decode`` and ``roofline_decode`` (state bytes against HBM).
+``cpu_baseline`` times the fp64 CPU oracle over the headline workload on the
+host.  ``--copy-calibration`` adds the reference copy kernel for scaling HBM
+byte counters.
 """
 from __future__ import annotations
 
@@ -161,45 +164,36 @@ def cpu_model():
     return "unknown"
 
 
-CPU_BASELINE_SECONDS = 10.0  # whole steps are repeated until this much time has passed
+CPU_BASELINE_SECONDS = 10.0  # whole calls are repeated until this much time has passed
 
 
-def cpu_baseline(batch_cpu, lengths, dec_cpu):
-    """The fp64 oracle on the host, over whole steps: the prefill batch (all
-    sequences and heads) and, when given, the decode batch.  The decode batch
-    carries only the pool rows its requests touch (gathered, indices
-    renumbered), which is the same work.  Steps repeat until
-    CPU_BASELINE_SECONDS have passed."""
-    import torch
+def cpu_baseline(batch_cpu, name):
+    """The fp64 oracle on the host over whole calls of the headline workload
+    (every sequence, head and token), repeated until CPU_BASELINE_SECONDS have
+    passed.  Threads: the oracle's default (the host's cores, capped at the
+    16-thread CPU share of one GPU); the host's core count is reported
+    beside it."""
     import oracle
     threads = oracle.default_threads()
-    n_dec = 0
-    if dec_cpu is not None:
-        rows = dec_cpu.state_indices.long()
-        dcache = dec_cpu.state_cache[rows]
-        didx = torch.arange(rows.numel(), dtype=torch.int32)
-        n_dec = rows.numel()
+    T = batch_cpu.q.shape[0]
+    hv = batch_cpu.v.shape[1]
     reps, t0 = 0, time.perf_counter()
     while True:
         oracle.recurrence(batch_cpu.q, batch_cpu.k, batch_cpu.v, batch_cpu.g, batch_cpu.beta,
                           cu_seqlens=batch_cpu.cu_seqlens, scale=batch_cpu.scale,
                           initial_state=batch_cpu.initial_state, threads=threads)
-        if dec_cpu is not None:
-            oracle.decode(dec_cpu.q, dec_cpu.k, dec_cpu.v, dec_cpu.g, dec_cpu.beta, dcache, didx,
-                          scale=dec_cpu.scale, threads=threads)
         reps += 1
         el = time.perf_counter() - t0
         if el >= CPU_BASELINE_SECONDS:
             break
-    per_step = el / reps
-    dec_txt = (f" + decode batch ({n_dec} requests x {dec_cpu.v.shape[1]} heads)"
-               if dec_cpu is not None else "")
-    return dict(value=(sum(lengths) + n_dec) / per_step, unit="tokens/s", cores=threads,
-                kind="oracle",
-                sample=(f"{reps} whole steps: prefill batch ({len(lengths)} x {lengths[0]} "
-                        f"tokens, {batch_cpu.v.shape[1]} heads){dec_txt}, fp64 token "
-                        f"recurrence, {per_step:.2f} s per step, {el:.1f} s in all on "
-                        f"{cpu_model()}"))
+    per = el / reps
+    units = batch_cpu.num_seqs * hv
+    return dict(value=round(T / per, 1), unit="tokens/s", cores=threads,
+                host_cores=os.cpu_count(), kind="oracle",
+                sample=(f"{reps} whole call(s) of {name} ({T} tokens x {hv} heads, "
+                        f"{units} independent (sequence, head) chains), fp64 token "
+                        f"recurrence on {threads} threads, {per:.2f} s per call, "
+                        f"{el:.1f} s in all on {cpu_model()}"))
 
 
 # ---------------------------------------------------------------------- main
@@ -344,21 +338,175 @@ def next_rows(dev):
     return res
 
 
+STAGES = ["table", "prep", "wy", "walk", "compose", "pass2"]
+# kernel names per stage, by plan (the chunk-table kernel is its own stage)
+KERNEL_OF = {"table": "chunk_offsets_kernel", "prep": "prep_kernel", "wy": "wy_kernel",
+             "walk": "walk_kernel", "compose": "compose_kernel", "pass2": "walk_kernel"}
+
+
+class ChunkCase:
+    """One prefill workload resident in HBM with preallocated outputs and
+    workspace; call() queues one kda_chunk_fwd on the current stream."""
+
+    def __init__(self, name, dev, args):
+        import torch
+        from gated_delta_rule_65_amd import binding as B
+        from gated_delta_rule_65_amd import inputs
+        self.B, self.name, self.args = B, name, args
+        wl = inputs.WORKLOADS[name]
+        self.b = b = inputs.make_workload(name, device=dev)
+        self.lengths = b.meta["lengths"]
+        self.hqk, self.hv = b.q.shape[1], b.v.shape[1]
+        self.T = b.q.shape[0]
+        self.paged = b.state_cache is not None
+        self.out = torch.empty_like(b.v)
+        self.fin = None if self.paged else torch.empty(
+            (b.num_seqs, self.hv, 128, 128), device=dev, dtype=torch.float32)
+        self.max_seqlen = max(self.lengths)
+        self.path = {"auto": B.PATH_AUTO, "staged": B.PATH_STAGED,
+                     "fused": B.PATH_FUSED}[args.path]
+        self.kw = dict(scale=b.scale, cu_seqlens=b.cu_seqlens, max_seqlen=self.max_seqlen,
+                       groups=args.groups, walk_waves=args.walk_waves, path=self.path,
+                       output=self.out)
+        if self.paged:
+            self.kw.update(state_cache=b.state_cache, state_indices=b.state_indices,
+                           has_initial_state=b.has_initial_state)
+        else:
+            self.kw.update(initial_state=b.initial_state, output_final_state=True,
+                           final_state=self.fin)
+        self.plan = B.chunk_plan(b.q, b.k, b.v, b.g, b.beta, cu_seqlens=b.cu_seqlens,
+                                 initial_state=None if self.paged else b.initial_state,
+                                 output_final_state=not self.paged, groups=args.groups,
+                                 walk_waves=args.walk_waves, max_seqlen=self.max_seqlen)
+        nbytes = B.chunk_workspace_bytes(b.q, b.k, b.v, b.g, b.beta, **self._ws_kw())
+        self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        es = 2 if b.q.dtype == torch.bfloat16 else 4
+        self.work = chunk_work(self.lengths, self.hqk, self.hv, es, True, True)
+        self.flops = self.work["wy"]["flops"] + self.work["walk"]["flops"]
+
+    def _ws_kw(self):
+        kw = dict(self.kw)
+        kw.pop("output", None)
+        kw.pop("final_state", None)
+        return kw
+
+    def call(self, events=None):
+        b = self.b
+        self.B.chunk_kda(b.q, b.k, b.v, b.g, b.beta, workspace=self.ws, stage_events=events,
+                         **self.kw)
+
+    def cpu_batch(self):
+        from gated_delta_rule_65_amd import inputs
+        b = self.b
+        return inputs.Batch(b.q.cpu(), b.k.cpu(), b.v.cpu(), b.g.cpu(), b.beta.cpu(),
+                            b.cu_seqlens.cpu(), b.scale,
+                            initial_state=None if b.initial_state is None
+                            else b.initial_state.cpu())
+
+
+def timed_calls(ev, stream, fn, n, warm=3):
+    """Mean ms of n back-to-back calls of fn, by two HIP events on stream."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a_, b_ = ev.create(), ev.create()
+    ev.record(a_, stream)
+    for _ in range(n):
+        fn()
+    ev.record(b_, stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(a_, b_) / n
+    ev.destroy(a_)
+    ev.destroy(b_)
+    return ms
+
+
+def stage_breakdown(ev, case, n):
+    """Mean ms per stage over n calls with the library's stage events."""
+    import torch
+    sets = [[ev.create() for _ in range(len(STAGES) + 1)] for _ in range(n)]
+    for i in range(n):
+        case.call(sets[i])
+    torch.cuda.synchronize()
+    per = {st: 0.0 for st in STAGES}
+    for i in range(n):
+        for j, st in enumerate(STAGES):
+            per[st] += ev.ms(sets[i][j], sets[i][j + 1]) / n
+    for es in sets:
+        for e in es:
+            ev.destroy(e)
+    return per
+
+
+def kernel_rows(case, per):
+    """Per-kernel figures of one chunked forward from its stage times."""
+    w = case.work
+    fused_prep = case.path != case.B.PATH_STAGED
+    groups = case.plan[0]
+    rows = {}
+    if per["table"] > 0:
+        rows["table"] = dict(kernel=KERNEL_OF["table"], ms=round(per["table"], 4))
+    if not fused_prep and per["prep"] > 0:
+        s = per["prep"] / 1e3
+        rows["prep"] = dict(kernel="prep_kernel", ms=round(per["prep"], 4), bound="hbm",
+                            gb_s=round(w["prep"]["bytes"] / s / 1e9, 1),
+                            frac=round(w["prep"]["bytes"] / s / 1e9 / PEAK_HBM_GBS, 4),
+                            algorithmic_bytes=w["prep"]["bytes"])
+    if per["wy"] > 0:
+        wk = "intra" if fused_prep else "wy"
+        s = per["wy"] / 1e3
+        rows["wy"] = dict(kernel="wy_kernel", ms=round(per["wy"], 4), bound="mfma",
+                          tflops=round(w[wk]["flops"] / s / 1e12, 2),
+                          frac=round(w[wk]["flops"] / s / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          gb_s=round(w[wk]["bytes"] / s / 1e9, 1),
+                          algorithmic_flops=w[wk]["flops"], algorithmic_bytes=w[wk]["bytes"])
+        if fused_prep:
+            rows["wy"]["note"] = "prep folded in (reads q, k, v, g, beta; writes all intermediates)"
+    walk_ms = per["walk"] + per["compose"] + per["pass2"]
+    if walk_ms > 0:
+        s = walk_ms / 1e3
+        rows["walk"] = dict(kernel="walk_kernel", ms=round(walk_ms, 4), bound="mfma",
+                            tflops=round(w["walk"]["flops"] / s / 1e12, 2),
+                            frac=round(w["walk"]["flops"] / s / 1e12 / PEAK_BF16_TFLOPS, 4),
+                            algorithmic_flops=w["walk"]["flops"],
+                            algorithmic_bytes=w["walk"]["bytes"])
+        if groups > 1:
+            rows["walk"]["note"] = (f"group scan, G = {groups}: pass one "
+                                    f"{per['walk']:.4f} ms, compose {per['compose']:.4f} ms, "
+                                    f"pass two {per['pass2']:.4f} ms; algorithmic flops "
+                                    "are the plain walk's (pass one is scan overhead)")
+    return rows
+
+
+def chunk_leg(ev, stream, case, n):
+    """A prefill workload timed alone: whole call and its kernels."""
+    ms = timed_calls(ev, stream, case.call, n)
+    per = stage_breakdown(ev, case, max(3, n // 2))
+    s = ms / 1e3
+    return dict(workload=case.name, tokens=case.T, ms=round(ms, 4),
+                tokens_per_s=round(case.T / s, 1), tflops=round(case.flops / s / 1e12, 2),
+                mfma_frac=round(case.flops / s / 1e12 / PEAK_BF16_TFLOPS, 4),
+                groups=case.plan[0], walk_waves=case.plan[1],
+                kernels=kernel_rows(case, per))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_single",
+                    choices=["long_single", "dense_prefill", "varlen_gva_paged"],
+                    help="the headline prefill workload (default: the largest)")
     ap.add_argument("--groups", type=int, default=0, help="chunk groups (0 = auto)")
     ap.add_argument("--walk-waves", type=int, default=0,
                     help="waves per walk workgroup: 0 = auto, 2, 4 or 8")
     ap.add_argument("--path", choices=["auto", "staged", "fused"], default="auto",
                     help="chunk path: prep as its own kernel (staged) or folded into WY")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-decode-back-to-back", action="store_true",
-                    help="skip timing decode launched back to back (after the timed region), "
-                         "as a serving loop runs it")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the other prefill workloads and the decode")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run a plain elementwise copy of "
                          f"{CAL_BYTES >> 20} MiB (reads and writes that many bytes) three "
@@ -388,203 +536,131 @@ def main():
     ev = HipEvents()
     stream = torch.cuda.current_stream(dev).cuda_stream
 
-    # inputs resident in HBM
-    wl = inputs.WORKLOADS["dense_prefill"]
-    lengths = [wl["T"]] * wl["B"]
-    cb = inputs.make_workload("dense_prefill", device=dev)
-    hqk, hv = wl["hqk"], wl["hv"]
-    T = sum(lengths)
-    q4 = cb.q.view(wl["B"], wl["T"], hqk, 128)
-    k4 = cb.k.view(wl["B"], wl["T"], hqk, 128)
-    v4 = cb.v.view(wl["B"], wl["T"], hv, 128)
-    g4 = cb.g.view(wl["B"], wl["T"], hv, 128)
-    b4 = cb.beta.view(wl["B"], wl["T"], hv)
-    out = torch.empty_like(v4)
-    fin = torch.empty((wl["B"], hv, 128, 128), device=dev, dtype=torch.float32)
-    dwl = inputs.WORKLOADS["decode_paged"]
-    db = inputs.make_workload("decode_paged", device=dev)
-    dout = torch.empty_like(db.v)
-    # one workspace, sized once
-    p = B._prepare_chunk(q4, k4, v4, g4, b4, cb.scale, cb.initial_state, True, None, True,
-                         out, fin, None, None, None)
-    nbytes = ctypes.c_size_t(0)
-    a = B._chunk_struct(p["q"], p["k"], p["v"], p["g"], p["beta"], p["out"], None, p["N"],
-                        p["T"], hqk, hv, p["scale"], True, p["init"], p["fin"], None, None,
-                        None, 0, args.groups, ctypes.c_void_p(stream), args.walk_waves)
-    B.load_library().kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(nbytes))
-    ws = torch.empty(nbytes.value, dtype=torch.uint8, device=dev)
-
-    nev = B.NUM_STAGE_EVENTS
-    ev_sets = [[ev.create() for _ in range(nev)] for _ in range(args.steps)]
-
-    path = {"auto": B.PATH_AUTO, "staged": B.PATH_STAGED, "fused": B.PATH_FUSED}[args.path]
-
-    def chunk(evs=None):
-        B.chunk_kda(q4, k4, v4, g4, b4, scale=cb.scale, initial_state=cb.initial_state,
-                    output_final_state=True, output=out, final_state=fin,
-                    groups=args.groups, walk_waves=args.walk_waves, workspace=ws,
-                    stage_events=evs, path=path)
-
-    def decode():
-        B.kda_decode(db.q, db.k, db.v, db.g, db.beta, db.state_cache, db.state_indices,
-                     scale=db.scale, output=dout)
-
-    def step():
-        chunk()
-        if not args.no_decode:
-            decode()
-
+    # ---- the headline step: one chunked forward over the headline workload
+    print(f"bench: {args.workload}: inputs", file=sys.stderr, flush=True)
+    case = ChunkCase(args.workload, dev, args)
     for _ in range(args.warmup):
-        step()
+        case.call()
     torch.cuda.synchronize()
-    # The timed region: exactly `steps` whole steps and nothing else (an event
-    # recorded between the calls of a step adds a few microseconds of queue
-    # idle time at each boundary, so the per-call figures come from the pass
-    # below).
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        case.call()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # An instrumented pass of `steps` more steps: two events per step on the
-    # library's stream (chunk start, decode start; the next step's chunk start
-    # closes the decode) give the launch durations of the two calls.
-    tev = [ev.create() for _ in range(2 * args.steps + 1)]
-    for i in range(args.steps):
-        ev.record(tev[2 * i], stream)
-        chunk()
-        if not args.no_decode:
-            ev.record(tev[2 * i + 1], stream)
-            decode()
-    ev.record(tev[2 * args.steps], stream)
-    torch.cuda.synchronize()
-    if args.no_decode:
-        chunk_ms = [ev.ms(tev[2 * i], tev[2 * i + 2]) for i in range(args.steps)]
-        dec_ms = []
-    else:
-        chunk_ms = [ev.ms(tev[2 * i], tev[2 * i + 1]) for i in range(args.steps)]
-        dec_ms = [ev.ms(tev[2 * i + 1], tev[2 * i + 2]) for i in range(args.steps)]
-    for e in tev:
-        ev.destroy(e)
-
-    # After the timed region: the per-kernel breakdown from the library's
-    # stage events, and decode launched back to back (each launch then also
-    # waits out the write-back of the previous one's state rows).
-    for i in range(args.steps):
-        chunk(ev_sets[i])
-    torch.cuda.synchronize()
-    dec_b2b_ms = None
-    if not args.no_decode_back_to_back and not args.no_decode:
-        a_, b_ = ev.create(), ev.create()
-        ev.record(a_, stream)
-        for _ in range(args.steps):
-            decode()
-        ev.record(b_, stream)
-        torch.cuda.synchronize()
-        dec_b2b_ms = ev.ms(a_, b_) / args.steps
-        ev.destroy(a_)
-        ev.destroy(b_)
-
-    names = ["table", "prep", "wy", "walk", "compose", "pass2"]
-    per = {n: [] for n in names}
-    for i in range(args.steps):
-        e = ev_sets[i]
-        for j, n in enumerate(names):
-            per[n].append(ev.ms(e[j], e[j + 1]))
-    mean = lambda xs: sum(xs) / max(len(xs), 1)
-    t_chunk = mean(chunk_ms) / 1e3
-    work = chunk_work(lengths, hqk, hv, 2, True, True)
-    flops = work["wy"]["flops"] + work["walk"]["flops"]
-
-    # the fused path records an empty prep stage: its WY kernel carries prep
-    fused = args.path != "staged"
-    kernels = {}
-    stages = (("wy", "intra", "mfma"),) if fused else (("prep", "prep", "hbm"),
-                                                      ("wy", "wy", "mfma"))
-    for n, wk, bound in stages + (("walk", "walk", "mfma"),):
-        ms = mean(per[n])
-        if ms <= 0:
-            continue
-        s = ms / 1e3
-        gbs = work[wk]["bytes"] / s / 1e9
-        tfl = work[wk]["flops"] / s / 1e12
-        kernels[n] = dict(ms=round(ms, 4), bound=bound, gb_s=round(gbs, 1),
-                          tflops=round(tfl, 2), hbm_frac=round(gbs / PEAK_HBM_GBS, 4),
-                          frac=round((gbs / PEAK_HBM_GBS) if bound == "hbm"
-                                     else (tfl / PEAK_BF16_TFLOPS), 4))
-        if n == "wy" and fused:
-            kernels[n]["note"] = "prep folded in (reads q, k, v, g, beta; writes all intermediates)"
-    for n in ("compose", "pass2"):
-        ms = mean(per[n])
-        if ms > 0.003:
-            kernels[n] = dict(ms=round(ms, 4))
-    dec = None
-    if not args.no_decode:
-        dw = decode_work(dwl["N"], dwl["hqk"], dwl["hv"], 2)
-        s = mean(dec_ms) / 1e3
-        gbs = dw["bytes"] / s / 1e9
-        kernels["decode"] = dict(ms=round(s * 1e3, 4), bound="hbm", gb_s=round(gbs, 1),
-                                 frac=round(gbs / PEAK_HBM_GBS, 4))
-        dec = dict(ms=round(s * 1e3, 4), gb_s=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4),
-                   state_gb_s=round(dw["state_bytes"] / s / 1e9, 1),
-                   back_to_back_ms=None if dec_b2b_ms is None else round(dec_b2b_ms, 4),
-                   back_to_back_gb_s=None if dec_b2b_ms is None else
-                   round(dw["bytes"] / (dec_b2b_ms / 1e3) / 1e9, 1),
-                   workload=f"{dwl['N']} requests x {dwl['hv']} heads, cache "
-                            f"[{dwl['slots']}, {dwl['hv']}, 128, 128] fp32")
-
-    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    step_s = wall / args.steps
+    print(f"bench: {args.workload}: {step_s * 1e3:.3f} ms per step", file=sys.stderr,
+          flush=True)
+    call_ms = timed_calls(ev, stream, case.call, args.steps, warm=0)
+    per = stage_breakdown(ev, case, args.steps)
+    kernels = kernel_rows(case, per)
+    # the dominant kernel of the step (its algorithmic work per launch over its
+    # event-timed launch duration)
+    dom = max((k for k in kernels if k != "table"), key=lambda k: kernels[k]["ms"])
     kd = kernels[dom]
-    kname = {"prep": "prep_kernel", "wy": "wy_kernel", "walk": "walk_kernel",
-             "decode": "decode_kernel"}[dom]
-    wkey = "intra" if (dom == "wy" and fused) else dom
     if kd["bound"] == "hbm":
-        wb = work[wkey]["bytes"] if dom != "decode" else decode_work(
-            dwl["N"], dwl["hqk"], dwl["hv"], 2)["bytes"]
         roof = dict(bound="hbm", achieved=kd["gb_s"], peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=kd["frac"], kernel=kname, algorithmic_bytes=wb)
+                    frac=kd["frac"], kernel=kd["kernel"],
+                    algorithmic_bytes=kd["algorithmic_bytes"])
     else:
         roof = dict(bound="mfma", achieved=kd["tflops"], peak=PEAK_BF16_TFLOPS,
-                    unit="TFLOP/s", frac=kd["frac"], kernel=kname,
-                    algorithmic_flops=work[wkey]["flops"])
-    roof["traffic"] = load_traffic(kname)
+                    unit="TFLOP/s", frac=kd["frac"], kernel=kd["kernel"],
+                    algorithmic_flops=kd["algorithmic_flops"])
+    roof["traffic"] = load_traffic(kd["kernel"]) if case.plan[0] <= 1 or dom != "walk" else None
     roof["launch_ms"] = kd["ms"]
-
-    n_dec = 0 if args.no_decode else dwl["N"]
-    step_s = wall / args.steps
+    if "note" in kd:
+        roof["note"] = kd["note"]
+    cs = call_ms / 1e3
+    roof_path = dict(bound="mfma", achieved=round(case.flops / cs / 1e12, 2),
+                     peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                     frac=round(case.flops / cs / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     kernel="whole chunked forward (every kernel of one call)",
+                     algorithmic_flops=case.flops, launch_ms=round(call_ms, 4))
+    wl = inputs.WORKLOADS[args.workload]
+    config = dict(workload=args.workload, B=len(case.lengths), T=max(case.lengths),
+                  tokens=case.T, hqk=case.hqk, hv=case.hv, head_dim=128, chunk=64,
+                  dtype="bf16", g="-%g*sigmoid(N(0,1))" % wl["g_scale"],
+                  state="paged fp32" if case.paged else "fp32 initial+final",
+                  groups=case.plan[0], walk_waves=case.plan[1], path=args.path)
     res = dict(
-        metric=METRIC, value=round((T + n_dec) / step_s, 1), unit="tokens/s", n_gpus=1,
-        steps=args.steps, warmup=args.warmup,
-        ms_per_step=round(wall / args.steps * 1e3, 4), higher_is_better=True,
-        scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
-        config=dict(workload="dense_prefill", B=wl["B"], T=wl["T"], hqk=hqk, hv=hv,
-                    head_dim=128, chunk=64, state="fp32 initial+final",
-                    groups=args.groups, walk_waves=args.walk_waves,
-                    path="fused" if fused else "staged",
-                    decode=None if dec is None else dec["workload"],
-                    value_counts=f"{T} prefill + {n_dec} decode tokens per step"),
-        chunk_ms=round(t_chunk * 1e3, 4),
-        chunk_tokens_per_s=round(T / t_chunk, 1),
-        tflops=round(flops / t_chunk / 1e12, 2),
-        mfma_frac=round(flops / t_chunk / 1e12 / PEAK_BF16_TFLOPS, 4),
-        decode=dec, kernels=kernels, roofline=roof,
+        metric=METRIC, value=round(case.T / step_s, 1), unit="tokens/s", n_gpus=1,
+        steps=args.steps, warmup=args.warmup, ms_per_step=round(step_s * 1e3, 4),
+        higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16",
+        data="synthetic", config=config,
+        chunk_ms=round(call_ms, 4), tflops=roof_path["achieved"], mfma_frac=roof_path["frac"],
+        kernels=kernels, roofline=roof, roofline_chunk_path=roof_path,
     )
+    cpu_in = None
+    if not args.no_cpu_baseline:
+        cpu_in = case.cpu_batch()
+    del case
+    torch.cuda.empty_cache()
+
+    # ---- the other prefill workloads and the decode, each timed alone
+    if not args.no_legs:
+        legs = {}
+        for name in ("dense_prefill", "varlen_gva_paged", "long_single"):
+            if name == args.workload:
+                continue
+            print(f"bench: leg {name}", file=sys.stderr, flush=True)
+            c = ChunkCase(name, dev, args)
+            legs[name] = chunk_leg(ev, stream, c, 10)
+            if name == "dense_prefill":
+                dense = c
+            else:
+                del c
+            torch.cuda.empty_cache()
+        res["legs"] = legs
+        print("bench: decode", file=sys.stderr, flush=True)
+        if args.workload == "dense_prefill" or "dense" not in locals():
+            dense = ChunkCase("dense_prefill", dev, args)
+        dwl = inputs.WORKLOADS["decode_paged"]
+        db = inputs.make_workload("decode_paged", device=dev)
+        dout = torch.empty_like(db.v)
+
+        def decode():
+            B.kda_decode(db.q, db.k, db.v, db.g, db.beta, db.state_cache, db.state_indices,
+                         scale=db.scale, output=dout)
+        # in a step after a chunk forward (its writes still draining), and back to back
+        for _ in range(3):
+            dense.call()
+            decode()
+        torch.cuda.synchronize()
+        tev = [ev.create() for _ in range(2 * args.steps)]
+        for i in range(args.steps):
+            dense.call()
+            ev.record(tev[2 * i], stream)
+            decode()
+            ev.record(tev[2 * i + 1], stream)
+        torch.cuda.synchronize()
+        dec_ms = sum(ev.ms(tev[2 * i], tev[2 * i + 1]) for i in range(args.steps)) / args.steps
+        for e in tev:
+            ev.destroy(e)
+        b2b_ms = timed_calls(ev, stream, decode, args.steps)
+        dw = decode_work(dwl["N"], dwl["hqk"], dwl["hv"], 2)
+        gbs = dw["bytes"] / (dec_ms / 1e3) / 1e9
+        gbs_b2b = dw["bytes"] / (b2b_ms / 1e3) / 1e9
+        res["decode"] = dict(
+            workload=f"{dwl['N']} requests x {dwl['hv']} heads, cache [{dwl['slots']}, "
+                     f"{dwl['hv']}, 128, 128] fp32, in place",
+            ms=round(dec_ms, 4), gb_s=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4),
+            back_to_back_ms=round(b2b_ms, 4), back_to_back_gb_s=round(gbs_b2b, 1),
+            back_to_back_hbm_frac=round(gbs_b2b / PEAK_HBM_GBS, 4),
+            tokens_per_s=round(dwl["N"] / (dec_ms / 1e3), 1))
+        res["roofline_decode"] = dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS,
+                                      unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4),
+                                      kernel="decode_kernel", algorithmic_bytes=dw["bytes"],
+                                      traffic=load_traffic("decode_kernel"),
+                                      launch_ms=round(dec_ms, 4),
+                                      note="launched after a dense-prefill chunked forward")
+        del dense, db
+        torch.cuda.empty_cache()
     if args.copy_calibration:
         res["copy_calibration"] = copy_calibration(dev)
-    if not args.no_cpu_baseline:
-        cpu = inputs.Batch(cb.q.cpu(), cb.k.cpu(), cb.v.cpu(), cb.g.cpu(), cb.beta.cpu(),
-                           cb.cu_seqlens.cpu(), cb.scale, initial_state=cb.initial_state.cpu())
-        dcpu = None
-        if not args.no_decode:
-            dcpu = inputs.Batch(db.q.cpu(), db.k.cpu(), db.v.cpu(), db.g.cpu(), db.beta.cpu(),
-                                db.cu_seqlens.cpu(), db.scale, state_cache=db.state_cache.cpu(),
-                                state_indices=db.state_indices.cpu())
-        res["cpu_baseline"] = cpu_baseline(cpu, lengths, dcpu)
+    if cpu_in is not None:
+        print("bench: cpu baseline", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(cpu_in, args.workload)
     else:
         res["cpu_baseline"] = None
-    for es in ev_sets:
-        for e in es:
-            ev.destroy(e)
     print(json.dumps(res))
 
 

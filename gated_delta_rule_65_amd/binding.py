@@ -463,6 +463,30 @@ def chunk_kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_sta
     return out
 
 
+def chunk_workspace_bytes(q, k, v, g, beta, scale=None, initial_state=None,
+                          output_final_state=False, cu_seqlens=None,
+                          use_qk_l2norm_in_kernel=True, state_cache=None, state_indices=None,
+                          has_initial_state=None, groups=0, walk_waves=0, path=PATH_AUTO,
+                          max_seqlen=None):
+    """Workspace bytes chunk_kda needs for these arguments (host-side only),
+    so that a caller can allocate it once and pass it to every call."""
+    p = _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state,
+                       cu_seqlens, use_qk_l2norm_in_kernel, None, None,
+                       state_cache, state_indices, has_initial_state)
+    if max_seqlen is not None:
+        p["max_seqlen"] = int(max_seqlen)
+    a = _chunk_struct(p["q"], p["k"], p["v"], p["g"], p["beta"], p["out"], p["cu"], p["N"],
+                      p["T"], p["hqk"], p["hv"], p["scale"], p["l2"], p["init"], p["fin"],
+                      p["cache"], p["idx"], p["has_init"], path, groups, None, walk_waves,
+                      None, p["max_seqlen"])
+    lib = load_library()
+    nbytes = ctypes.c_size_t(0)
+    st = lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(nbytes))
+    if st != KDA_OK:
+        _raise(lib, st)
+    return int(nbytes.value)
+
+
 def chunk_stages(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=None,
                  use_qk_l2norm_in_kernel=True, groups=1, path=PATH_STAGED):
     """Run the chunk path (PATH_STAGED: prep as its own kernel; PATH_FUSED:

@@ -37,8 +37,10 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 size_t elem_size(int dtype) { return dtype == KDA_F32 ? 4 : 2; }
 
 // Gate parameters: both or neither; dt_bias fp32 or bf16; lower_bound in
-// [-10, 0] (per-step log-decays beyond -10 would leave the exponent range
-// the chunk tiles are built for).
+// [-5, 0], so the step log-decay lower_bound * sigmoid(..) stays in the
+// [-5, 0] range that the chunk kernels' block-referenced exponents are built
+// for (beyond it the factor between two 16-token block references can
+// underflow fp32 while the true coupling is O(1)).
 // Tensor base pointers are read with 8- and 16-byte vector loads.
 bool misaligned16(std::initializer_list<const void*> ps) {
   for (const void* p : ps)
@@ -84,8 +86,8 @@ kda_status check_gate(const float* a_log, const void* dt_bias, int32_t dt_dtype,
   if (!a_log) return KDA_OK;
   if (dt_dtype != KDA_F32 && dt_dtype != KDA_BF16)
     return fail(KDA_ERR_DTYPE, "dt_bias must be fp32 or bf16");
-  if (!(lb >= -10.0f && lb <= 0.0f))
-    return fail(KDA_ERR_UNSUPPORTED, "lower_bound must lie in [-10, 0]");
+  if (!(lb >= -5.0f && lb <= 0.0f))
+    return fail(KDA_ERR_UNSUPPORTED, "lower_bound must lie in [-5, 0]");
   return KDA_OK;
 }
 

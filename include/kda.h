@@ -141,7 +141,8 @@ typedef struct kda_chunk_args {
      (the activation of KdaTcVerify, page
      "vllm.models.kimi_k3.nvidia.recoverssm.cutedsl.verify"; chunk_kda of page
      "mate.kda" takes A_log, dt_bias and lower_bound = -5 by default).
-     lower_bound must lie in [-10, 0]. */
+     lower_bound must lie in [-5, 0] (KDA_ERR_UNSUPPORTED otherwise), which
+     keeps every step log-decay in the [-5, 0] range stated above. */
   const float *A_log;          /* (device) [Hv] fp32, or NULL */
   const void *dt_bias;         /* (device) [Hv, 128] of dt_bias_dtype, or NULL */
   int32_t dt_bias_dtype;       /* KDA_F32 or KDA_BF16 */
@@ -285,7 +286,8 @@ typedef struct kda_decode_args {
      (the activation of KdaTcVerify, page
      "vllm.models.kimi_k3.nvidia.recoverssm.cutedsl.verify"; the same form as
      the chunked forward).
-     lower_bound must lie in [-10, 0]. */
+     lower_bound must lie in [-5, 0] (KDA_ERR_UNSUPPORTED otherwise), which
+     keeps every step log-decay in the [-5, 0] range stated above. */
   const float *A_log;          /* (device) [Hv] fp32, or NULL */
   const void *dt_bias;         /* (device) [Hv, 128] of dt_bias_dtype, or NULL */
   int32_t dt_bias_dtype;       /* KDA_F32 or KDA_BF16 */

@@ -249,10 +249,11 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: the checks fail first
     (dict(dt_bias=FAKE), B.KDA_ERR_SHAPE),                     # without A_log
     (dict(A_log=FAKE, dt_bias=FAKE, dt_bias_dtype=2, lower_bound=-5.0), B.KDA_ERR_DTYPE),
     (dict(A_log=FAKE, dt_bias=FAKE, dt_bias_dtype=0, lower_bound=-11.0), B.KDA_ERR_UNSUPPORTED),
+    (dict(A_log=FAKE, dt_bias=FAKE, dt_bias_dtype=0, lower_bound=-5.01), B.KDA_ERR_UNSUPPORTED),
     (dict(A_log=FAKE, dt_bias=FAKE, dt_bias_dtype=0, lower_bound=0.5), B.KDA_ERR_UNSUPPORTED),
     (dict(A_log=FAKE, dt_bias=FAKE, dt_bias_dtype=1, lower_bound=float("nan")),
      B.KDA_ERR_UNSUPPORTED),
-], ids=["a_only", "bias_only", "bias_f16", "lb_low", "lb_pos", "lb_nan"])
+], ids=["a_only", "bias_only", "bias_f16", "lb_low", "lb_below_5", "lb_pos", "lb_nan"])
 def test_gate_parameter_checks(lib, make, call, fields, status):
     a = make(**fields)
     assert call(lib, a) == status

@@ -2,13 +2,16 @@
 
 Tolerance: relative L2 <= 1e-2 for bf16/fp16 inputs (bf16 output rounding alone
 is ~2e-3) and <= 1e-4 for fp32 inputs; the state is fp32 throughout, so the
-updated cache rows are held to 1e-5 (the only error is fp32 arithmetic).
+updated cache rows are held to 1e-5 (the only error is fp32 arithmetic).  Each
+bar holds over the whole tensor and for the worst unit: every (request, token,
+head) output row, every state plane (tests/parity.py).
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
+import parity
 from gated_delta_rule_65_amd import binding as B
 from gated_delta_rule_65_amd import inputs
 
@@ -17,9 +20,17 @@ DEV = "cuda:0"
 
 
 def rel(a, b):
+    """max(whole-tensor rel-L2, worst unit): units are the state planes of a
+    cache, and each (request, token, head) row of an output."""
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
-    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+    if a.ndim >= 3 and a.shape[-2:] == (128, 128):
+        return parity.rel(a, b)
+    if a.ndim >= 3:
+        a = a.reshape(-1, a.shape[-2], a.shape[-1])
+        b = b.reshape(-1, b.shape[-2], b.shape[-1])
+        return parity.rel(a, b, np.arange(a.shape[0] + 1))
+    return parity.rel(a, b)
 
 
 def run_case(batch, l2=True, scale=None, null=()):
