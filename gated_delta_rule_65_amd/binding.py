@@ -96,7 +96,8 @@ class DecodeArgs(ctypes.Structure):
 _lib = None
 _lock = threading.Lock()
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_ws_layout",
-           "kda_decode", "kda_status_str", "kda_last_error", "kda_version")
+           "kda_decode", "kda_status_str", "kda_last_error", "kda_version",
+           "kda_chunk_fwd_noalloc")
 
 
 def library_path() -> str:
@@ -116,6 +117,8 @@ def load_library():
             P = ctypes.POINTER
             lib.kda_chunk_fwd.argtypes = [P(ChunkArgs)]
             lib.kda_chunk_fwd.restype = ctypes.c_int
+            lib.kda_chunk_fwd_noalloc.argtypes = [P(ChunkArgs)]
+            lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
             lib.kda_chunk_fwd_workspace_size.argtypes = [P(ChunkArgs), P(ctypes.c_size_t)]
             lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_int
             lib.kda_chunk_ws_layout.argtypes = [P(ChunkArgs), P(WsLayout)]
@@ -391,7 +394,7 @@ def _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state, c
 
 
 def _run_chunk(p, path=PATH_AUTO, groups=0, workspace=None, keep=None, events=None,
-               walk_waves=0, gate=None, ckpt=None):
+               walk_waves=0, gate=None, ckpt=None, no_alloc=False):
     lib = load_library()
     dev = p["q"].device
     a = _chunk_struct(p["q"], p["k"], p["v"], p["g"], p["beta"], p["out"], p["cu"], p["N"],
@@ -404,6 +407,18 @@ def _run_chunk(p, path=PATH_AUTO, groups=0, workspace=None, keep=None, events=No
         a.checkpoint_state_indices, a.checkpoint_rows = _ptr(ci), cs.shape[0]
         if keep is not None:
             keep["ckpt"] = ckpt
+    if events is not None:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        a.stage_events = ctypes.cast(arr, ctypes.c_void_p)
+        a.num_stage_events = len(events)
+    if no_alloc:
+        # the library's static scratch replaces the workspace
+        st = lib.kda_chunk_fwd_noalloc(ctypes.byref(a))
+        if st != KDA_OK:
+            _raise(lib, st)
+        if keep is not None:
+            keep["args"] = a
+        return a
     nbytes = ctypes.c_size_t(0)
     st = lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(nbytes))
     if st != KDA_OK:
@@ -412,10 +427,6 @@ def _run_chunk(p, path=PATH_AUTO, groups=0, workspace=None, keep=None, events=No
         workspace = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=dev)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = workspace.numel() * workspace.element_size()
-    if events is not None:
-        arr = (ctypes.c_void_p * len(events))(*events)
-        a.stage_events = ctypes.cast(arr, ctypes.c_void_p)
-        a.num_stage_events = len(events)
     st = lib.kda_chunk_fwd(ctypes.byref(a))
     if st != KDA_OK:
         _raise(lib, st)
@@ -430,7 +441,8 @@ def chunk_kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_sta
               state_cache=None, state_indices=None, has_initial_state=None, groups=0,
               workspace=None, stage_events=None, walk_waves=0, path=PATH_AUTO,
               A_log=None, dt_bias=None, lower_bound=-5.0, checkpoint_state=None,
-              checkpoint_offsets=None, checkpoint_state_indices=None, max_seqlen=None):
+              checkpoint_offsets=None, checkpoint_state_indices=None, max_seqlen=None,
+              no_alloc=False):
     """Chunked KDA forward (chunk_kda's argument set, plus the paged state of
     fused_kda_chunk).  Returns out, or (out, final_state) when
     output_final_state; in paged mode the final states land in state_cache.
@@ -446,7 +458,11 @@ def chunk_kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_sta
     state after its first checkpoint_offsets[n] tokens (0 or a multiple of 64;
     fused_kda_chunk's checkpoint arguments).  max_seqlen: the longest sequence's
     length, a planning hint for varlen batches (taken from cu_seqlens when it
-    is a host tensor; results never depend on it)."""
+    is a host tensor; results never depend on it).  no_alloc: run through
+    kda_chunk_fwd_noalloc, whose workspace is the library's static 64 MiB
+    per-device scratch (no workspace argument; calls on one device must not
+    overlap)."""
+    _need(not (no_alloc and workspace is not None), "no_alloc takes no workspace")
     p = _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state,
                        cu_seqlens, use_qk_l2norm_in_kernel, output, final_state,
                        state_cache, state_indices, has_initial_state)
@@ -456,7 +472,7 @@ def chunk_kda(q, k, v, g, beta, scale=None, initial_state=None, output_final_sta
     ck = _checkpoints(checkpoint_state, checkpoint_offsets, checkpoint_state_indices, p["N"],
                       p["hv"], p["q"].device)
     _run_chunk(p, path=path, groups=groups, workspace=workspace, events=stage_events,
-               walk_waves=walk_waves, gate=gate, ckpt=ck)
+               walk_waves=walk_waves, gate=gate, ckpt=ck, no_alloc=no_alloc)
     out = p["out"]
     if output_final_state:
         return out, p["fin"]

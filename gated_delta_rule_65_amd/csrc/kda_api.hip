@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "../../include/kda.h"
 #include "kda_launch.hpp"
@@ -323,16 +324,12 @@ KDA_API kda_status kda_chunk_ws_layout(const kda_chunk_args* a, kda_ws_layout* l
   return ok();
 }
 
-KDA_API kda_status kda_chunk_fwd(const kda_chunk_args* a) {
-  kda_status s = check_chunk(a, true);
-  if (s != KDA_OK) return s;
-  kda_ws_layout W;
-  layout_of(a, &W);
-  if (a->workspace_bytes < W.total || (W.total > 0 && a->workspace == nullptr))
-    return fail(KDA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", W.total,
-                a->workspace_bytes);
+namespace {
+
+// The chunked forward over an already checked argument set and a workspace
+// of at least W.total bytes.
+kda_status run_chunk(const kda_chunk_args* a, const kda_ws_layout& W, char* ws) {
   if (a->num_seqs == 0) return ok();
-  char* ws = (char*)a->workspace;
   kda::ChunkLaunch L;
   memset(&L, 0, sizeof(L));
   L.q = a->q; L.k = a->k; L.v = a->v; L.g = a->g; L.beta = a->beta;
@@ -370,6 +367,74 @@ KDA_API kda_status kda_chunk_fwd(const kda_chunk_args* a) {
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
+
+}  // namespace
+
+// Static scratch of the no-allocation entry point: one copy per device,
+// allocated when the code object loads on that device and held until the
+// process ends.  Host code never passes `scratch` itself to a kernel (its
+// host-side name is not a device address): it resolves the device address
+// once per device with hipGetSymbolAddress and uses that.
+namespace kda_noalloc {
+constexpr size_t SCRATCH_BYTES = (size_t)64 << 20;
+__device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+}  // namespace kda_noalloc
+
+namespace {
+using kda_noalloc::SCRATCH_BYTES;
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];
+
+// The current device's scratch address, resolved on the first call per
+// device (with that device current).
+kda_status scratch_of_current_device(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= MAX_DEVICES)
+    return fail(KDA_ERR_UNSUPPORTED, "device %d beyond the %d devices served", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(kda_noalloc::scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(KDA_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = (char*)g_scratch_ptr[dev];
+  return KDA_OK;
+}
+
+}  // namespace
+
+KDA_API kda_status kda_chunk_fwd(const kda_chunk_args* a) {
+  kda_status s = check_chunk(a, true);
+  if (s != KDA_OK) return s;
+  kda_ws_layout W;
+  layout_of(a, &W);
+  if (a->workspace_bytes < W.total || (W.total > 0 && a->workspace == nullptr))
+    return fail(KDA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", W.total,
+                a->workspace_bytes);
+  return run_chunk(a, W, (char*)a->workspace);
+}
+
+KDA_API kda_status kda_chunk_fwd_noalloc(const kda_chunk_args* a) {
+  kda_status s = check_chunk(a, true);
+  if (s != KDA_OK) return s;
+  kda_ws_layout W;
+  layout_of(a, &W);
+  if (W.total > SCRATCH_BYTES)
+    return fail(KDA_ERR_WORKSPACE,
+                "this call needs %zu bytes of workspace, beyond the %zu-byte static scratch",
+                W.total, SCRATCH_BYTES);
+  if (a->num_seqs == 0) return ok();
+  char* ws = nullptr;
+  s = scratch_of_current_device(&ws);
+  if (s != KDA_OK) return s;
+  return run_chunk(a, W, ws);
+}
+
 
 KDA_API kda_status kda_decode(const kda_decode_args* a) {
   if (!a) return fail(KDA_ERR_ARG, "args is NULL");

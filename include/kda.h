@@ -221,6 +221,22 @@ kda_status kda_chunk_fwd_workspace_size(const kda_chunk_args *a, size_t *bytes);
 kda_status kda_chunk_fwd(const kda_chunk_args *a);
 
 /*
+ * kda_chunk_fwd_noalloc -- kda_chunk_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same computation, arguments and results, but
+ * a->workspace and a->workspace_bytes are ignored.  The workspace is a static
+ * device array of the library, 64 MiB per device (allocated when the library's
+ * code object loads on a device and held until the process ends); a call
+ * whose kda_chunk_fwd_workspace_size() exceeds it returns KDA_ERR_WORKSPACE
+ * and queues nothing.  Every call on one device shares that array: calls
+ * whose queued work overlaps on one device (two streams, or two threads)
+ * race and corrupt each other's results; serialise them.  The library makes
+ * no hipMalloc / hipFree or allocating library call on this path; the array
+ * needs no clearing between calls (each call initialises what it reads).
+ */
+kda_status kda_chunk_fwd_noalloc(const kda_chunk_args *a);
+
+/*
  * Layout of the staged path's intermediates inside the workspace, for tests
  * and tools.  Offsets are in bytes from the workspace base; "chunks" is the
  * bound n_chunks_max = total_tokens / 64 + num_seqs used for sizing.  G is the
