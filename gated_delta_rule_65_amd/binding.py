@@ -21,7 +21,7 @@ _LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 KDA_OK, KDA_ERR_SHAPE, KDA_ERR_DTYPE, KDA_ERR_UNSUPPORTED = 0, 1, 2, 3
 KDA_ERR_WORKSPACE, KDA_ERR_HIP, KDA_ERR_ARG = 4, 5, 6
-PATH_AUTO, PATH_STAGED, PATH_FUSED = 0, 1, 2
+PATH_AUTO, PATH_STAGED, PATH_FUSED, PATH_ONCHIP = 0, 1, 2, 3
 
 _DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 
@@ -642,7 +642,7 @@ def kda_decode(q, k, v, g, beta, state_cache, state_indices=None, scale=None,
 
 
 def chunk_plan(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_state=False,
-               groups=0, walk_waves=0, max_seqlen=None):
+               groups=0, walk_waves=0, max_seqlen=None, path=PATH_AUTO):
     """The walk's launch plan (groups, walk_waves) that chunk_kda takes for
     these arguments.  Host-side only: nothing runs on the device."""
     p = _prepare_chunk(q, k, v, g, beta, None, initial_state, output_final_state, cu_seqlens,
@@ -651,7 +651,7 @@ def chunk_plan(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_fin
         p["max_seqlen"] = int(max_seqlen)
     a = _chunk_struct(p["q"], p["k"], p["v"], p["g"], p["beta"], p["out"], p["cu"], p["N"],
                       p["T"], p["hqk"], p["hv"], p["scale"], True, p["init"], p["fin"], None,
-                      None, None, PATH_AUTO, groups, None, walk_waves, None, p["max_seqlen"])
+                      None, None, path, groups, None, walk_waves, None, p["max_seqlen"])
     lay = WsLayout()
     lib = load_library()
     st = lib.kda_chunk_ws_layout(ctypes.byref(a), ctypes.byref(lay))

@@ -146,8 +146,11 @@ kda_status check_chunk(const kda_chunk_args* a, bool need_ptrs) {
   } else if (a->state_indices || a->has_initial_state) {
     return fail(KDA_ERR_SHAPE, "state_indices/has_initial_state need a state_cache");
   }
-  if (a->path != KDA_PATH_AUTO && a->path != KDA_PATH_STAGED && a->path != KDA_PATH_FUSED)
+  if (a->path != KDA_PATH_AUTO && a->path != KDA_PATH_STAGED && a->path != KDA_PATH_FUSED &&
+      a->path != KDA_PATH_ONCHIP)
     return fail(KDA_ERR_UNSUPPORTED, "unknown path %d", a->path);
+  if (a->path == KDA_PATH_ONCHIP && a->dtype != KDA_BF16)
+    return fail(KDA_ERR_UNSUPPORTED, "the on-chip path takes bf16 inputs");
   if (a->groups < 0) return fail(KDA_ERR_SHAPE, "groups must be >= 0");
   if (a->max_seqlen < 0) return fail(KDA_ERR_SHAPE, "max_seqlen must be >= 0");
   if (a->groups > 64) return fail(KDA_ERR_UNSUPPORTED, "groups above 64");
@@ -206,7 +209,7 @@ struct WalkPlan {
 };
 
 WalkPlan plan_walk(const kda_chunk_args* a) {
-  const int cap = 256;  // resident walk workgroups
+  const int cap = kda::cu_count_host();  // resident walk workgroups
   const int N = a->num_seqs > 0 ? a->num_seqs : 1;
   const int64_t units = (int64_t)N * a->hv;
   const double nc = (double)max_chunks_of(a) / N;  // chunks per sequence (mean bound)
@@ -248,12 +251,66 @@ WalkPlan plan_walk(const kda_chunk_args* a) {
   return best;
 }
 
+// The path a call takes: AUTO is the prep-folded staged path, the faster
+// of the paths on every workload measured so far (the on-chip path trades
+// the intermediates' HBM traffic for a longer serial step per chunk).
+int32_t path_of(const kda_chunk_args* a) {
+  if (a->path != KDA_PATH_AUTO) return a->path;
+  return KDA_PATH_FUSED;
+}
+
+// Launch plan of the on-chip path: the chunk groups G.  One chain (a
+// (sequence, head) pair, or one group of it) is one 4-wave workgroup.  Two
+// walk / pass-two workgroups share a CU (a step of each then costs ~1.3 of a
+// lone one's); a pass-one workgroup (twice the state columns) fills a CU and
+// its step costs ~1.1.  Cost in chunk steps: waves of resident chains times
+// chunks per chain, plus a compose per group; the longest sequence's chain is
+// a floor (exact for a dense batch, from the max_seqlen hint for varlen,
+// else the mean).
+WalkPlan plan_onchip(const kda_chunk_args* a) {
+  const int cus = kda::cu_count_host();
+  const int N = a->num_seqs > 0 ? a->num_seqs : 1;
+  const int64_t units = (int64_t)N * a->hv;
+  const double nc = (double)max_chunks_of(a) / N;
+  const double chain =
+      (a->cu_seqlens && a->max_seqlen > 0)
+          ? std::min((double)max_chunks_of(a), std::ceil((double)a->max_seqlen / KDA_CHUNK))
+          : nc;
+  // time of `chains` chains of `steps` chunk steps on resident workgroups
+  auto walk = [&](double chains, double steps, int per_cu, double shared) {
+    const double waves = std::ceil(chains / (per_cu * (double)cus));
+    const double share = (per_cu > 1 && chains > cus) ? shared : 1.0;
+    return waves * steps * share;
+  };
+  WalkPlan best = {1, 4};
+  double best_cost = 1e300;
+  for (int G = 1; G <= 64; G *= 2) {
+    if (a->groups > 0 && G != a->groups) continue;
+    double cost;
+    if (G == 1) {
+      cost = std::max(walk((double)units, nc, 2, 1.3), chain);
+    } else {
+      const double cpg = std::ceil(nc / G);
+      cost = walk((double)units * G, cpg, 1, 1.0) * 1.1 + walk((double)units * G, cpg, 2, 1.3) +
+             0.25 * G;
+      cost = std::max(cost, 2.1 * std::ceil(chain / G));
+    }
+    if (cost < best_cost * 0.999) {
+      best_cost = cost;
+      best = {G, 4};
+    }
+  }
+  if (a->groups > 0 && best.groups != a->groups) best = {a->groups, 4};  // G not a power of 2
+  return best;
+}
+
 kda_status layout_of(const kda_chunk_args* a, kda_ws_layout* L) {
   memset(L, 0, sizeof(*L));
   const size_t es = elem_size(a->dtype);
   const size_t T = (size_t)a->total_tokens, H = (size_t)a->hv;
   const int64_t mc = max_chunks_of(a);
-  const WalkPlan plan = plan_walk(a);
+  const bool onchip = path_of(a) == KDA_PATH_ONCHIP;
+  const WalkPlan plan = onchip ? plan_onchip(a) : plan_walk(a);
   const int groups = plan.groups;
   size_t off = 0;
   L->max_chunks = mc;
@@ -265,6 +322,17 @@ kda_status layout_of(const kda_chunk_args* a, kda_ws_layout* L) {
   off = align_up(off + 1024 + 256, 256);  // zero page, then the WY work counter
   L->table = off;
   off = align_up(off + 16 * (size_t)mc, 256);
+  if (onchip) {
+    // no intermediates: the stage regions are empty
+    L->qg = L->kg_t = L->decay = L->w = L->u = L->aqk = off;
+    L->scan = off;
+    if (groups > 1) {
+      const size_t planes = (size_t)groups * (size_t)a->num_seqs * H;
+      off = align_up(off + planes * 3 * KDA_HEAD_DIM * KDA_HEAD_DIM * sizeof(float), 256);
+    }
+    L->total = off;
+    return KDA_OK;
+  }
   L->qg = off;
   off = align_up(off + T * H * KDA_HEAD_DIM * es, 256);
   L->kg_t = off;
@@ -350,7 +418,7 @@ kda_status run_chunk(const kda_chunk_args* a, const kda_ws_layout& W, char* ws) 
   L.w = ws + W.w; L.u = ws + W.u; L.aqk = ws + W.aqk;
   L.events = a->stage_events;
   L.num_events = a->stage_events ? a->num_stage_events : 0;
-  L.fuse_prep = a->path == KDA_PATH_STAGED ? 0 : 1;
+  L.fuse_prep = path_of(a) == KDA_PATH_STAGED ? 0 : 1;
   L.gate = gate_of(a->A_log, a->dt_bias, a->dt_bias_dtype, a->lower_bound);
   L.ckpt = a->checkpoint_state;
   L.ckpt_off = a->checkpoint_offsets;
@@ -363,7 +431,8 @@ kda_status run_chunk(const kda_chunk_args* a, const kda_ws_layout& W, char* ws) 
   L.walk_waves = W.walk_waves;
   L.scan = L.groups > 1 ? (float*)(ws + W.scan) : nullptr;
   L.stream = a->stream;
-  hipError_t e = kda::launch_chunk_staged(L);
+  hipError_t e = path_of(a) == KDA_PATH_ONCHIP ? kda::launch_chunk_onchip(L)
+                                               : kda::launch_chunk_staged(L);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }

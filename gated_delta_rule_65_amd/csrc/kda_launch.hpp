@@ -62,5 +62,12 @@ struct ChunkLaunch {
   void* stream;
 };
 hipError_t launch_chunk_staged(const ChunkLaunch& L);
+// The on-chip path (bf16): the intra-chunk stage inside the walk; the
+// workspace holds only the chunk table and the group-scan planes.
+hipError_t launch_chunk_onchip(const ChunkLaunch& L);
+// The chunk-table kernel alone (offsets, records, zero page).
+void launch_chunk_table(const ChunkLaunch& L);
+// Compute units of the current device (256 when the query fails).
+int cu_count_host();
 
 }  // namespace kda

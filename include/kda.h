@@ -82,10 +82,14 @@ typedef enum kda_status {
 
 /* Execution plan of the chunked forward. */
 typedef enum kda_path {
-  KDA_PATH_AUTO = 0,    /* the library picks (KDA_PATH_FUSED) */
+  KDA_PATH_AUTO = 0,    /* the library picks (today KDA_PATH_FUSED) */
   KDA_PATH_STAGED = 1,  /* prep -> wy -> walk, intermediates in the workspace */
-  KDA_PATH_FUSED = 2    /* prep folded into the WY kernel (one pass over q, k,
+  KDA_PATH_FUSED = 2,   /* prep folded into the WY kernel (one pass over q, k,
                            g) -> walk; same intermediates, same results */
+  KDA_PATH_ONCHIP = 3   /* bf16 only: the intra-chunk stage is recomputed
+                           inside the walk per chunk, in LDS; HBM carries only
+                           inputs, outputs and states, and the workspace holds
+                           only the chunk table and the group-scan planes */
 } kda_path;
 
 /*

@@ -58,7 +58,7 @@ def test_struct_size_agrees_and_workspace_is_sized(lib):
 
 
 def test_workspace_layout_is_ordered_and_covers_intermediates(lib):
-    a = chunk_args()
+    a = chunk_args(path=B.PATH_FUSED)
     lay = B.WsLayout()
     assert lib.kda_chunk_ws_layout(ctypes.byref(a), ctypes.byref(lay)) == B.KDA_OK
     assert lay.max_chunks == 256 // 64 + 2
@@ -71,10 +71,31 @@ def test_workspace_layout_is_ordered_and_covers_intermediates(lib):
     assert lay.total >= lay.aqk + 256 * 4 * 64 * 2
     assert all(o % 256 == 0 for o in offs)
     # groups add the scan planes: 3 planes of 128x128 fp32 per (group, seq, head)
-    g = chunk_args(groups=4)
+    g = chunk_args(groups=4, path=B.PATH_FUSED)
     lay4 = B.WsLayout()
     assert lib.kda_chunk_ws_layout(ctypes.byref(g), ctypes.byref(lay4)) == B.KDA_OK
     assert lay4.total - lay4.scan >= 4 * 2 * 4 * 3 * 128 * 128 * 4
+
+
+def test_onchip_workspace_holds_only_the_table_and_scan_planes(lib):
+    """The on-chip path keeps no intermediate regions: only the chunk table
+    and (under the group scan) the scan planes."""
+    for path in (B.PATH_ONCHIP,):
+        a = chunk_args(path=path, groups=1)
+        lay = B.WsLayout()
+        assert lib.kda_chunk_ws_layout(ctypes.byref(a), ctypes.byref(lay)) == B.KDA_OK
+        assert lay.qg == lay.kg_t == lay.decay == lay.w == lay.u == lay.aqk == lay.scan
+        assert lay.total == lay.scan
+        assert lay.scan - lay.table >= 16 * lay.max_chunks
+        g = chunk_args(path=path, groups=4)
+        assert lib.kda_chunk_ws_layout(ctypes.byref(g), ctypes.byref(lay)) == B.KDA_OK
+        assert lay.total - lay.scan == 4 * 2 * 4 * 3 * 128 * 128 * 4
+    # the on-chip path is bf16 only; AUTO keeps the staged layout
+    assert ws_size(lib, chunk_args(dtype=0, path=B.PATH_ONCHIP))[0] == B.KDA_ERR_UNSUPPORTED
+    for dtype in (0, 1):
+        a = chunk_args(dtype=dtype)
+        assert lib.kda_chunk_ws_layout(ctypes.byref(a), ctypes.byref(lay)) == B.KDA_OK
+        assert lay.kg_t > lay.qg
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -222,9 +243,10 @@ def test_binding_decode_checks():
 
 
 def test_planner_picks_groups_only_for_long_chains(lib):
-    """Workspace grows by the scan planes exactly when the planner groups."""
+    """Workspace grows by the scan planes exactly when the planner groups
+    (staged walk planner)."""
     def total(**kw):
-        a = chunk_args(**kw)
+        a = chunk_args(path=B.PATH_FUSED, **kw)
         lay = B.WsLayout()
         assert lib.kda_chunk_ws_layout(ctypes.byref(a), ctypes.byref(lay)) == B.KDA_OK
         return lay.total - lay.scan
@@ -414,11 +436,12 @@ def test_planner_picks_measured_best_on_the_standard_workloads():
             q = torch.zeros(T, hqk, 128, dtype=dt)
             v = torch.zeros(T, hv, 128, dtype=dt)
             cu = torch.tensor([0] + torch.tensor(lengths).cumsum(0).tolist(), dtype=torch.int32)
-            return B.chunk_plan(q, q, v, v, torch.zeros(T, hv, dtype=dt), cu_seqlens=cu)
+            return B.chunk_plan(q, q, v, v, torch.zeros(T, hv, dtype=dt), cu_seqlens=cu,
+                                path=B.PATH_FUSED)
         shp = (r["B"], r["T"])
         q = torch.zeros(*shp, hqk, 128, dtype=dt)
         v = torch.zeros(*shp, hv, 128, dtype=dt)
-        return B.chunk_plan(q, q, v, v, torch.zeros(*shp, hv, dtype=dt))
+        return B.chunk_plan(q, q, v, v, torch.zeros(*shp, hv, dtype=dt), path=B.PATH_FUSED)
 
     assert plan("dense_prefill") == (1, 2)
     assert plan("varlen_gva_paged") == (1, 4)
@@ -436,12 +459,13 @@ def test_planner_max_seqlen_hint(lib):
         v = torch.zeros(T, hv, 128, dtype=torch.bfloat16)
         cu = torch.tensor([0] + torch.tensor(lengths).cumsum(0).tolist(), dtype=torch.int32)
         return q, v, torch.zeros(T, hv, dtype=torch.bfloat16), cu
+    F = B.PATH_FUSED
     q, v, beta, cu = varlen([4096] * 4, 16, 16)
-    assert B.chunk_plan(q, q, v, v, beta, cu_seqlens=cu) == (1, 2)
-    assert B.chunk_plan(q, q, v, v, beta, cu_seqlens=cu, max_seqlen=0) == (1, 2)
+    assert B.chunk_plan(q, q, v, v, beta, cu_seqlens=cu, path=F) == (1, 2)
+    assert B.chunk_plan(q, q, v, v, beta, cu_seqlens=cu, max_seqlen=0, path=F) == (1, 2)
     # one long sequence among short ones: the hint moves the plan
     q, v, beta, cu = varlen([8192] + [128] * 60, 4, 16)
-    with_hint = B.chunk_plan(q, q, v, v, beta, cu_seqlens=cu)
-    without = B.chunk_plan(q, q, v, v, beta, cu_seqlens=cu, max_seqlen=0)
+    with_hint = B.chunk_plan(q, q, v, v, beta, cu_seqlens=cu, path=F)
+    without = B.chunk_plan(q, q, v, v, beta, cu_seqlens=cu, max_seqlen=0, path=F)
     assert with_hint != without
     assert ws_size(lib, chunk_args(max_seqlen=-1))[0] == B.KDA_ERR_SHAPE

@@ -25,6 +25,26 @@ DEV = "cuda:0"
 from parity import rel, report, first_rows, first_cu  # noqa: E402
 
 
+_PATH = {"path": B.PATH_AUTO}
+
+
+@pytest.fixture(autouse=True, params=["auto", "onchip"])
+def chunk_path(request):
+    """Every case runs twice: on the library's default plan, and with bf16
+    calls sent down the on-chip path (the intra-chunk stage recomputed inside
+    the walk).  fp32 calls keep the default plan, the on-chip path being
+    bf16-only; calls that name a path keep it."""
+    _PATH["path"] = B.PATH_ONCHIP if request.param == "onchip" else B.PATH_AUTO
+    yield request.param
+    _PATH["path"] = B.PATH_AUTO
+
+
+def chunk_kda(q, *a, **kw):
+    if kw.get("path", B.PATH_AUTO) == B.PATH_AUTO and q.dtype == torch.bfloat16:
+        kw["path"] = _PATH["path"]
+    return B.chunk_kda(q, *a, **kw)
+
+
 def tol(dtype):
     return 1e-4 if dtype == torch.float32 else 1e-2
 
@@ -41,7 +61,7 @@ def run_dense_state(batch, groups=0, l2=True, walk_waves=0):
     """Varlen call with dense initial/final states."""
     q, k, v, g, beta = gpu(batch)
     init = None if batch.initial_state is None else batch.initial_state.to(DEV)
-    out, fin = B.chunk_kda(q, k, v, g, beta, scale=batch.scale, initial_state=init,
+    out, fin = chunk_kda(q, k, v, g, beta, scale=batch.scale, initial_state=init,
                            output_final_state=True, cu_seqlens=batch.cu_seqlens.to(DEV),
                            use_qk_l2norm_in_kernel=l2, groups=groups,
                            walk_waves=walk_waves)
@@ -109,11 +129,11 @@ def test_no_l2norm_custom_scale():
 def test_dense_4d_input_matches_varlen():
     b = inputs.make_chunk([96, 96], 2, 2, seed=8, init=True)
     q, k, v, g, beta = gpu(b)
-    out4, fin4 = B.chunk_kda(q.view(2, 96, 2, 128), k.view(2, 96, 2, 128),
+    out4, fin4 = chunk_kda(q.view(2, 96, 2, 128), k.view(2, 96, 2, 128),
                              v.view(2, 96, 2, 128), g.view(2, 96, 2, 128),
                              beta.view(2, 96, 2), scale=b.scale,
                              initial_state=b.initial_state.to(DEV), output_final_state=True)
-    out, fin = B.chunk_kda(q, k, v, g, beta, scale=b.scale,
+    out, fin = chunk_kda(q, k, v, g, beta, scale=b.scale,
                            initial_state=b.initial_state.to(DEV), output_final_state=True,
                            cu_seqlens=b.cu_seqlens.to(DEV))
     assert torch.equal(out4.view_as(out), out) and torch.equal(fin4, fin)
@@ -223,7 +243,7 @@ def test_exact_overwrite_with_orthonormal_keys(dt):
     beta = torch.full((T, hv), 40.0, dtype=dt)
     cu = torch.tensor([0, T], dtype=torch.int32, device=DEV)
     say("overwrite", dt)
-    out, fin = B.chunk_kda(k.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), beta.to(DEV), scale=1.0,
+    out, fin = chunk_kda(k.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), beta.to(DEV), scale=1.0,
                            output_final_state=True, cu_seqlens=cu,
                            use_qk_l2norm_in_kernel=False)
     assert torch.equal(out.cpu(), v)
@@ -241,7 +261,7 @@ def test_paged_state_equals_dense_and_leaves_other_rows():
     say("paged")
     q, k, v, g, beta = gpu(b)
     cache = b.state_cache.to(DEV)
-    out = B.chunk_kda(q, k, v, g, beta, scale=b.scale, cu_seqlens=b.cu_seqlens.to(DEV),
+    out = chunk_kda(q, k, v, g, beta, scale=b.scale, cu_seqlens=b.cu_seqlens.to(DEV),
                       state_cache=cache, state_indices=b.state_indices.to(DEV),
                       has_initial_state=b.has_initial_state.to(DEV))
     torch.cuda.synchronize()
@@ -267,7 +287,7 @@ def test_paged_null_slot_gives_zero_rows_and_no_state_io():
     say("null slot")
     q, k, v, g, beta = gpu(b)
     cache = b.state_cache.to(DEV)
-    out = B.chunk_kda(q, k, v, g, beta, scale=b.scale, cu_seqlens=b.cu_seqlens.to(DEV),
+    out = chunk_kda(q, k, v, g, beta, scale=b.scale, cu_seqlens=b.cu_seqlens.to(DEV),
                       state_cache=cache, state_indices=b.state_indices.to(DEV),
                       has_initial_state=b.has_initial_state.to(DEV))
     torch.cuda.synchronize()
@@ -286,7 +306,7 @@ def test_empty_batch_and_all_empty_sequences():
     b = inputs.make_chunk([0, 0], 1, 1, seed=1, init=True)
     q, k, v, g, beta = gpu(b)
     init = b.initial_state.to(DEV)
-    out, fin = B.chunk_kda(q, k, v, g, beta, initial_state=init, output_final_state=True,
+    out, fin = chunk_kda(q, k, v, g, beta, initial_state=init, output_final_state=True,
                            cu_seqlens=b.cu_seqlens.to(DEV))
     torch.cuda.synchronize()
     assert out.numel() == 0 and torch.equal(fin, init)
@@ -314,7 +334,7 @@ def test_stage_events_sparse():
     init = b.initial_state.to(DEV)
     cu = b.cu_seqlens.to(DEV)
     for groups in (1, 2):
-        ref_o, ref_s = B.chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=init,
+        ref_o, ref_s = chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=init,
                                    output_final_state=True, cu_seqlens=cu, groups=groups)
         evs = []
         for _ in range(2):
@@ -322,7 +342,7 @@ def test_stage_events_sparse():
             assert hip.hipEventCreate(ctypes.byref(e)) == 0
             evs.append(e.value)
         # boundaries: after the table and after WY; every other entry NULL
-        o, s = B.chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=init,
+        o, s = chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=init,
                            output_final_state=True, cu_seqlens=cu, groups=groups,
                            stage_events=[None, evs[0], None, evs[1], None, None, None])
         torch.cuda.synchronize()
@@ -361,7 +381,7 @@ def test_varlen_gva_paged_workload():
     say("varlen_gva_paged", b.meta["lengths"])
     q, k, v, g, beta = gpu(b)
     cache = b.state_cache.to(DEV)
-    out = B.chunk_kda(q, k, v, g, beta, scale=b.scale, cu_seqlens=b.cu_seqlens.to(DEV),
+    out = chunk_kda(q, k, v, g, beta, scale=b.scale, cu_seqlens=b.cu_seqlens.to(DEV),
                       state_cache=cache, state_indices=b.state_indices.to(DEV),
                       has_initial_state=b.has_initial_state.to(DEV))
     torch.cuda.synchronize()
@@ -415,7 +435,7 @@ def test_gate_at_its_lower_bound(groups):
     dt_bias = (60.0 * sign).expand(2, 128).contiguous()
     say("gate at lower bound", groups)
     q, k, v, g, beta = gpu(b)
-    out, fin = B.chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=b.initial_state.to(DEV),
+    out, fin = chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=b.initial_state.to(DEV),
                            output_final_state=True, cu_seqlens=b.cu_seqlens.to(DEV),
                            groups=groups, A_log=a_log.to(DEV), dt_bias=dt_bias.to(DEV),
                            lower_bound=-5.0)
@@ -476,7 +496,7 @@ def test_group_scan_paged_with_null_slot():
     b.has_initial_state = torch.tensor([1, 1, 0], dtype=torch.uint8)
     q, k, v, g, beta = gpu(b)
     cache = b.state_cache.to(DEV)
-    out = B.chunk_kda(q, k, v, g, beta, scale=b.scale, cu_seqlens=b.cu_seqlens.to(DEV),
+    out = chunk_kda(q, k, v, g, beta, scale=b.scale, cu_seqlens=b.cu_seqlens.to(DEV),
                       state_cache=cache, state_indices=b.state_indices.to(DEV),
                       has_initial_state=b.has_initial_state.to(DEV), groups=4)
     torch.cuda.synchronize()
@@ -501,10 +521,10 @@ def test_auto_plan_uses_groups_for_long_single_sequence():
     G, W = B.chunk_plan(q, k, v, g, beta, cu_seqlens=b.cu_seqlens.to(DEV),
                         initial_state=b.initial_state.to(DEV), output_final_state=True)
     assert G > 1 and W in (2, 4, 8)
-    out_auto, fin_auto = B.chunk_kda(q, k, v, g, beta, scale=b.scale,
+    out_auto, fin_auto = chunk_kda(q, k, v, g, beta, scale=b.scale,
                                      initial_state=b.initial_state.to(DEV),
                                      output_final_state=True, cu_seqlens=b.cu_seqlens.to(DEV))
-    out1, fin1 = B.chunk_kda(q, k, v, g, beta, scale=b.scale,
+    out1, fin1 = chunk_kda(q, k, v, g, beta, scale=b.scale,
                              initial_state=b.initial_state.to(DEV), output_final_state=True,
                              cu_seqlens=b.cu_seqlens.to(DEV), groups=1)
     torch.cuda.synchronize()
@@ -519,7 +539,7 @@ def test_staged_and_fused_paths_agree():
     q, k, v, g, beta = gpu(b)
     res = []
     for path in (B.PATH_STAGED, B.PATH_FUSED):
-        o, s = B.chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=b.initial_state.to(DEV),
+        o, s = chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=b.initial_state.to(DEV),
                            output_final_state=True, cu_seqlens=b.cu_seqlens.to(DEV), path=path)
         torch.cuda.synchronize()
         res.append((o.float().cpu().numpy(), s.cpu().numpy()))
@@ -553,7 +573,7 @@ def test_gate_parameters_match_oracle(case):
     dt_bias = (torch.randn(hv, 128, generator=gen) * 0.5).to(bdt)
     say("gate", name)
     q, k, v, g, beta = gpu(b)
-    out, fin = B.chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=b.initial_state.to(DEV),
+    out, fin = chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=b.initial_state.to(DEV),
                            output_final_state=True, cu_seqlens=b.cu_seqlens.to(DEV),
                            path=path, groups=groups, A_log=a_log.to(DEV),
                            dt_bias=dt_bias.to(DEV), lower_bound=-5.0)
@@ -578,7 +598,7 @@ def run_checkpoints(b, offsets, rows, indices=None, groups=0, dtype=None):
     ck = torch.full((rows, hv, 128, 128), SENTINEL, dtype=torch.float32, device=DEV)
     offs = torch.tensor(offsets, dtype=torch.int32)
     idx = None if indices is None else torch.tensor(indices, dtype=torch.int32)
-    out, fin = B.chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=b.initial_state.to(DEV),
+    out, fin = chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=b.initial_state.to(DEV),
                            output_final_state=True, cu_seqlens=b.cu_seqlens.to(DEV),
                            groups=groups, checkpoint_state=ck, checkpoint_offsets=offs.to(DEV),
                            checkpoint_state_indices=None if idx is None else idx.to(DEV))
@@ -631,7 +651,7 @@ def test_bf16_initial_and_final_state(groups):
                           init=True)
     init16 = b.initial_state.to(torch.bfloat16)
     q, k, v, g, beta = gpu(b)
-    out, fin = B.chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=init16.to(DEV),
+    out, fin = chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=init16.to(DEV),
                            output_final_state=True, cu_seqlens=b.cu_seqlens.to(DEV),
                            groups=groups)
     torch.cuda.synchronize()
@@ -649,7 +669,7 @@ def test_bf16_state_b0_passes_through_bitwise():
     b.g.zero_()
     init16 = b.initial_state.to(torch.bfloat16)
     q, k, v, g, beta = gpu(b)
-    _, fin = B.chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=init16.to(DEV),
+    _, fin = chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=init16.to(DEV),
                          output_final_state=True, cu_seqlens=b.cu_seqlens.to(DEV))
     torch.cuda.synchronize()
     assert torch.equal(fin.cpu(), init16)
@@ -689,8 +709,8 @@ def test_strided_projection_inputs(dtype, path, groups):
     cu = b.cu_seqlens.to(DEV)
     kw = dict(scale=b.scale, initial_state=init, output_final_state=True, cu_seqlens=cu,
               path=path, groups=groups)
-    out_s, fin_s = B.chunk_kda(qv, kv, vv, gv, bv, **kw)
-    out_c, fin_c = B.chunk_kda(*gpu(b), **kw)
+    out_s, fin_s = chunk_kda(qv, kv, vv, gv, bv, **kw)
+    out_c, fin_c = chunk_kda(*gpu(b), **kw)
     torch.cuda.synchronize()
     assert torch.equal(out_s, out_c) and torch.equal(fin_s, fin_c)
     o_ref, s_ref = oracle_dense(b)
@@ -715,8 +735,8 @@ def test_strided_inputs_with_gate_and_padded_paged_pool():
     kw = dict(scale=b.scale, cu_seqlens=b.cu_seqlens.to(DEV),
               state_indices=b.state_indices.to(DEV), has_initial_state=b.has_initial_state.to(DEV),
               A_log=al.to(DEV), dt_bias=dtb.to(DEV))
-    out_s = B.chunk_kda(qv, kv, vv, gv, bv, state_cache=cache, **kw)
-    out_c = B.chunk_kda(*gpu(b), state_cache=ref_cache, **kw)
+    out_s = chunk_kda(qv, kv, vv, gv, bv, state_cache=cache, **kw)
+    out_c = chunk_kda(*gpu(b), state_cache=ref_cache, **kw)
     torch.cuda.synchronize()
     assert torch.equal(out_s, out_c)
     assert torch.equal(cache, ref_cache)
@@ -819,12 +839,12 @@ def test_mixed_configurations_match_oracle(i):
               walk_waves=cfg["waves"], **{k_: v_.to(DEV) for k_, v_ in gk.items()})
     if cfg["paged"]:
         cache = b.state_cache.to(DEV)
-        out = B.chunk_kda(q, k, v, g, beta, state_cache=cache,
+        out = chunk_kda(q, k, v, g, beta, state_cache=cache,
                           state_indices=b.state_indices.to(DEV),
                           has_initial_state=b.has_initial_state.to(DEV), **kw)
         s0 = b.state_cache[b.state_indices.long()] * b.has_initial_state.view(-1, 1, 1, 1).float()
     else:
-        out, fin = B.chunk_kda(q, k, v, g, beta, initial_state=b.initial_state.to(DEV),
+        out, fin = chunk_kda(q, k, v, g, beta, initial_state=b.initial_state.to(DEV),
                                output_final_state=True, **kw)
         s0 = b.initial_state
     torch.cuda.synchronize()
