@@ -180,3 +180,31 @@ def make_workload(name, device="cpu", seed=0):
                    init=r["init"])
     b.meta["workload"] = name
     return b
+
+
+def make_verify(lengths, window, hqk, hv, slots, dtype=torch.bfloat16, g_scale=5.0, seed=0,
+                null=(), device="cpu"):
+    """A speculative verify batch: request b holds lengths[b] <= window draft
+    tokens (rows query_start[b] .. query_start[b+1]) over a paged cache with
+    distinct random slots; the requests listed in ``null`` get slot -1.  The
+    accepted counts are uniform in [1, lengths[b]] (0 for an empty window).
+    Draw order: q, k, v, g, beta, cache, slots, accepted counts."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    B, T = len(lengths), int(sum(lengths))
+    q = _normal(gen, (T, hqk, D), device, dtype)
+    k = _normal(gen, (T, hqk, D), device, dtype)
+    v = _normal(gen, (T, hv, D), device, dtype)
+    g = _gate(gen, (T, hv, D), device, dtype, g_scale)
+    beta = _normal(gen, (T, hv), device, dtype)
+    cache = _normal(gen, (slots, hv, D, D), device, torch.float32, 0.02)
+    idx = torch.randperm(slots, generator=gen, device=device)[:B].to(torch.int32)
+    for b in null:
+        idx[b] = -1
+    u = torch.rand(B, generator=gen, device=device, dtype=torch.float64).cpu()
+    acc = torch.tensor([0 if n == 0 else 1 + min(n - 1, int(float(x) * n))
+                        for n, x in zip(lengths, u)], dtype=torch.int32)
+    qs = torch.tensor([0] + list(lengths), dtype=torch.int64).cumsum(0).to(torch.int32)
+    return Batch(q, k, v, g, beta, qs.to(device), state_cache=cache, state_indices=idx,
+                 meta=dict(hqk=hqk, hv=hv, g_scale=g_scale, slots=slots, window=window,
+                           accepted=acc.to(device)))

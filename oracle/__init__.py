@@ -9,6 +9,13 @@ Contents
 --------
 ``recurrence``      the definition, token by token (C, fp64, threaded): see
                     ``kda_oracle.c`` for the formula and its sources.
+``decode``, ``decode_multi``, ``checkpoints``
+                    one-token and multi-token decode over a paged cache, and
+                    mid-prefill state snapshots, as the recurrence.
+``verify``, ``commit``
+                    the record-based speculative window (outputs and records
+                    by the window form, no state) and the state rebuilt from
+                    the records once the accepted count is known.
 ``forms``           independent fp64 forms used to pin the recurrence: the naive
                     chunked (WY) form, the short-window closed form, brute force
                     with dense 128x128 transition matrices, and special cases.
@@ -24,6 +31,8 @@ import threading
 
 import numpy as np
 import torch
+
+from . import forms
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_oracle.c")
@@ -302,3 +311,142 @@ def decode_multi(q, k, v, g, beta, state_cache, state_indices, num_accepted_toke
             if idx[b, t] >= 0:
                 new_cache[idx[b, t]] = sf[0]
     return out, new_cache
+
+
+# ------------------------------------------------ verify window and commit
+#
+# The record-based speculative step of page
+# "vllm.models.kimi_k3.nvidia.recoverssm.cutedsl.verify" (class KdaTcVerify):
+# a request's window of at most Q <= 8 draft tokens is run from the slot's
+# state S0 by the window closed form, writing the outputs and two records per
+# (request, head, token) -- corr = the delta correction u_t, and kg = the raw
+# key followed by the raw gate -- and no state.  Once the accepted count a is
+# known, the commit rebuilds the state after the first a tokens from S0 and
+# the records alone.  The pages show the verify step and name the records;
+# the commit is our reading of what they are for (the recurrence with its
+# corrections given, see ``commit``).
+
+
+def _f64(x):
+    return torch.as_tensor(x).detach().cpu().double().numpy()
+
+
+def gate_log_decay(g_raw, h, A_log=None, dt_bias=None, lower_bound=-5.0):
+    """Step log-decay of value head h from a raw gate [..., 128]: with gate
+    parameters lower_bound * sigmoid(exp(A_log[h]) * (g_raw + dt_bias[h])),
+    KdaTcVerify's activation (page
+    "vllm.models.kimi_k3.nvidia.recoverssm.cutedsl.verify", step 2); without
+    them g_raw already is the log-decay."""
+    g_raw = np.asarray(g_raw, dtype=np.float64)
+    if A_log is None:
+        return g_raw
+    a = np.exp(float(_f64(A_log)[h]))
+    return lower_bound / (1.0 + np.exp(-a * (g_raw + _f64(dt_bias)[h])))
+
+
+def verify(q, k, v, g, beta, query_start, state_cache, state_indices, window,
+           scale=None, use_qk_l2norm=True, A_log=None, dt_bias=None, lower_bound=-5.0):
+    """The verify step: outputs and records of each request's window.
+
+    q, k: [T, Hqk, 128]; v, g: [T, Hv, 128]; beta: [T, Hv] logits; request b
+    owns rows [query_start[b], query_start[b+1]) and its first
+    min(length, window) tokens are run; state_cache [slots, Hv, 128(V),
+    128(K)] (read only); state_indices [B] (a slot outside [0, slots) skips
+    the request: zero output rows, no records).
+
+    Per (request, head), with cum_t the inclusive cumulative log-decay over the
+    window and qn, kn the (optionally L2-normalised) query and key, the page's
+    window form (step 4 of KdaTcVerify): probes p_t = e^cum_t kn_t and
+    r_t = scale e^cum_t qn_t, weights w_i = e^-cum_i kn_i, couplings
+    c_ti = w_i . p_t (i < t) and d_ti = w_i . r_t (i <= t), then in token order
+      u_t = b_t (v_t - S0^T p_t - sum_{i<t} c_ti u_i),
+      o_t = S0^T r_t + sum_{i<=t} d_ti u_i,
+    with S0 the K x V state (S0[k][v] = cache[slot, h, v, k]).
+
+    Returns (out [T, Hv, 128], corr [B, Hv, window, 128] = u_t,
+    kg [B, Hv, window, 256] = raw k of the head's query-key head, then raw g),
+    fp64; record rows a request does not write are NaN.
+    """
+    qs = np.asarray(_f64(query_start), dtype=np.int64)
+    idx = np.asarray(_f64(state_indices), dtype=np.int64)
+    cache = _f64(state_cache)
+    qd, kd, vd, gd, bd = (_f64(x) for x in (q, k, v, g, beta))
+    Ttot, hqk, K = qd.shape
+    hv = vd.shape[1]
+    grp = hv // hqk
+    B = len(qs) - 1
+    Q = int(window)
+    if scale is None:
+        scale = K ** -0.5
+    out = np.zeros((Ttot, hv, 128))
+    corr = np.full((B, hv, Q, 128), np.nan)
+    kg = np.full((B, hv, Q, 2 * K), np.nan)
+    for b in range(B):
+        bos = int(qs[b])
+        n = max(0, min(int(qs[b + 1]) - bos, Q))
+        slot = int(idx[b])
+        if n == 0 or slot < 0 or slot >= cache.shape[0]:
+            continue
+        rows = slice(bos, bos + n)
+        for h in range(hv):
+            hq = h // grp
+            qn, kn = qd[rows, hq], kd[rows, hq]
+            if use_qk_l2norm:
+                qn, kn = forms.l2n(qn), forms.l2n(kn)
+            bt = forms.sigmoid(bd[rows, h])
+            cum = np.cumsum(gate_log_decay(gd[rows, h], h, A_log, dt_bias, lower_bound), axis=0)
+            S0 = cache[slot, h].T
+            p = np.exp(cum) * kn
+            r = scale * np.exp(cum) * qn
+            w = np.exp(-cum) * kn
+            u = np.zeros((n, 128))
+            for t in range(n):
+                acc = vd[bos + t, h] - S0.T @ p[t]
+                for i in range(t):
+                    acc = acc - np.dot(w[i], p[t]) * u[i]
+                u[t] = bt[t] * acc
+                o = S0.T @ r[t]
+                for i in range(t + 1):
+                    o = o + np.dot(w[i], r[t]) * u[i]
+                out[bos + t, h] = o
+            corr[b, h, :n] = u
+            kg[b, h, :n, :K] = kd[rows, hq]
+            kg[b, h, :n, K:] = gd[rows, h]
+    return out, corr, kg
+
+
+def commit(state_cache, state_indices, num_accepted_tokens, corr, kg, use_qk_l2norm=True,
+           A_log=None, dt_bias=None, lower_bound=-5.0, state_bf16=False):
+    """The state after each request's first a = num_accepted_tokens[b] window
+    tokens, rebuilt from the slot's state and the verify records alone.
+
+    The recurrence's step is S_t = diag(e^g_t) S_{t-1} + kn_t u_t^T, where
+    u_t = b_t (v_t - (diag(e^g_t) S_{t-1})^T kn_t) is exactly the correction
+    the verify step records; so with the records given the state after token
+    a - 1 is that step applied for t = 0 .. a-1, with kn_t and g_t recomputed
+    from the raw key and raw gate in kg.  A request with a slot outside the
+    pool, or a count outside [0, window], is skipped; a = 0 leaves the state.
+    With state_bf16 the new state is rounded (to nearest even) once, as it
+    is stored once.  Returns the new cache, fp64 (a copy).
+    """
+    idx = np.asarray(_f64(state_indices), dtype=np.int64)
+    acc = np.asarray(_f64(num_accepted_tokens), dtype=np.int64)
+    cache = _f64(state_cache)
+    u_all, kg_all = _f64(corr), _f64(kg)
+    B, hv, Q = u_all.shape[:3]
+    K = kg_all.shape[-1] // 2
+    new = cache.copy()
+    for b in range(B):
+        slot, a = int(idx[b]), int(acc[b])
+        if slot < 0 or slot >= cache.shape[0] or a < 0 or a > Q or a == 0:
+            continue
+        for h in range(hv):
+            kn = kg_all[b, h, :a, :K]
+            if use_qk_l2norm:
+                kn = forms.l2n(kn)
+            gl = gate_log_decay(kg_all[b, h, :a, K:], h, A_log, dt_bias, lower_bound)
+            S = cache[slot, h].T.copy()
+            for t in range(a):
+                S = np.exp(gl[t])[:, None] * S + np.outer(kn[t], u_all[b, h, t])
+            new[slot, h] = round_bf16(S.T) if state_bf16 else S.T
+    return new

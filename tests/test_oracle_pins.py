@@ -486,3 +486,147 @@ def test_bf16_state_frozen_when_nothing_writes():
     for b in range(2):
         for t in range(4):
             assert np.array_equal(c[idx[b, t]], cache[idx[b, 0]].numpy())
+
+
+# ------------------------------------------- verify window with records, commit
+#
+# oracle.verify runs the window form of KdaTcVerify and writes records instead
+# of states; oracle.commit rebuilds a state from them.  Pinned against the C
+# recurrence (another code path: token by token, states carried), the dense
+# brute force, and multi-token decode; the commit at every accepted count pins
+# each recorded correction u_t and both halves of the kg record.
+
+def verify_batch(lengths, hqk, hv, seed, dtype=torch.float32, null=(), gate=False):
+    b = inputs.make_verify(lengths, 8, hqk, hv, 24, dtype=dtype, seed=seed, null=null)
+    b.state_cache = b.state_cache * 25.0  # non-symmetric, visible start
+    al = db = None
+    if gate:
+        gen = torch.Generator().manual_seed(seed + 200)
+        b.g = torch.randn(b.g.shape, generator=gen).to(dtype)  # raw gate ~ N(0, 1)
+        al = torch.rand(hv, generator=gen, dtype=torch.float64) * 2 - 1
+        db = torch.randn(hv, 128, generator=gen, dtype=torch.float64)
+    return b, al, db
+
+
+def run_verify(b, al=None, db=None, scale=None):
+    return oracle.verify(b.q, b.k, b.v, b.g, b.beta, b.cu_seqlens, b.state_cache,
+                         b.state_indices, 8, scale=scale, A_log=al, dt_bias=db)
+
+
+def window_R(b, req, ntok=None, al=None, db=None, scale=None):
+    """The C recurrence over request req's first ntok window tokens from its slot."""
+    s, e = int(b.cu_seqlens[req]), int(b.cu_seqlens[req + 1])
+    e = e if ntok is None else s + ntok
+    sl = slice(s, e)
+    return oracle.recurrence(b.q[sl], b.k[sl], b.v[sl], b.g[sl], b.beta[sl], scale=scale,
+                             initial_state=b.state_cache[int(b.state_indices[req])][None],
+                             A_log=al, dt_bias=db)
+
+
+@pytest.mark.parametrize("gate", [False, True])
+@pytest.mark.parametrize("hqk,hv", [(2, 2), (1, 3)])
+def test_verify_outputs_match_the_recurrence(gate, hqk, hv):
+    lengths = [3, 8, 1, 0, 5, 8, 2]
+    b, al, db = verify_batch(lengths, hqk, hv, 60, null=(5,), gate=gate)
+    out, corr, kg = run_verify(b, al, db, scale=0.3)
+    for req, n in enumerate(lengths):
+        s = int(b.cu_seqlens[req])
+        if req == 5 or n == 0:
+            assert np.all(out[s:s + n] == 0)
+            assert np.all(np.isnan(corr[req])) and np.all(np.isnan(kg[req]))
+            continue
+        o, _ = window_R(b, req, al=al, db=db, scale=0.3)
+        assert rel(out[s:s + n], o) < 1e-12
+        assert np.all(np.isnan(corr[req, :, n:])) and not np.any(np.isnan(corr[req, :, :n]))
+
+
+@pytest.mark.parametrize("gate", [False, True])
+def test_commit_at_every_count_is_the_recurrence_state(gate):
+    lengths = [8, 5, 1, 7]
+    b, al, db = verify_batch(lengths, 2, 4, 61, gate=gate)
+    _, corr, kg = run_verify(b, al, db)
+    cache0 = f64(b.state_cache)
+    for a in range(0, 9):
+        acc = torch.tensor([min(a, n) for n in lengths])
+        new = oracle.commit(b.state_cache, b.state_indices, acc, corr, kg, A_log=al, dt_bias=db)
+        touched = set()
+        for req, n in enumerate(lengths):
+            slot = int(b.state_indices[req])
+            touched.add(slot)
+            m = min(a, n)
+            if m == 0:
+                assert np.array_equal(new[slot], cache0[slot])
+                continue
+            _, sf = window_R(b, req, m, al=al, db=db)
+            assert rel(new[slot], sf[0]) < 1e-12
+        rest = [s for s in range(cache0.shape[0]) if s not in touched]
+        assert np.array_equal(new[rest], cache0[rest])
+
+
+def test_verify_and_commit_match_brute_force():
+    lengths = [6, 4]
+    b, _, _ = verify_batch(lengths, 1, 1, 62)
+    out, corr, kg = run_verify(b)
+    new = oracle.commit(b.state_cache, b.state_indices, torch.tensor(lengths), corr, kg)
+    for req in range(2):
+        s, e = int(b.cu_seqlens[req]), int(b.cu_seqlens[req + 1])
+        slot = int(b.state_indices[req])
+        ob, sb = forms.brute(f64(b.q[s:e]), f64(b.k[s:e]), f64(b.v[s:e]), f64(b.g[s:e]),
+                             f64(b.beta[s:e]), 128 ** -0.5, True,
+                             f64(b.state_cache[slot])[None])
+        assert rel(out[s:e], ob) < 1e-12
+        assert rel(new[slot], sb[0]) < 1e-12
+
+
+def test_verify_and_commit_match_multi_token_decode():
+    """Same draft windows through multi-token decode (a state stored after
+    every token): equal outputs, and the commit at count a equals the state
+    decode stored after token a - 1."""
+    B, T = 3, 6
+    b, _, _ = verify_batch([T] * B, 2, 2, 63)
+    out, corr, kg = run_verify(b)
+    rs = lambda x: x.reshape(B, T, *x.shape[1:])
+    slots = 24
+    rows = torch.tensor([[(b_ * T + t) % slots for t in range(T)] for b_ in range(B)])
+    rows[:, 0] = b.state_indices.long()
+    taken = set(int(x) for x in b.state_indices)
+    free = [s for s in range(slots) if s not in taken]
+    rows[:, 1:] = torch.tensor(free[:B * (T - 1)]).reshape(B, T - 1)
+    od, cd = oracle.decode_multi(rs(b.q), rs(b.k), rs(b.v), rs(b.g), rs(b.beta),
+                                 b.state_cache, rows)
+    assert rel(out.reshape(B, T, 2, 128), od) < 1e-12
+    for a in (1, 4, 6):
+        new = oracle.commit(b.state_cache, b.state_indices, torch.tensor([a] * B), corr, kg)
+        for req in range(B):
+            want = cd[int(rows[req, a - 1])] if a > 1 else cd[int(rows[req, 0])]
+            assert rel(new[int(b.state_indices[req])], want) < 1e-12
+
+
+def test_verify_records_hold_the_raw_key_and_gate():
+    lengths = [2, 5]
+    b, _, _ = verify_batch(lengths, 2, 4, 64, dtype=torch.bfloat16)
+    _, _, kg = run_verify(b)
+    for req, n in enumerate(lengths):
+        s = int(b.cu_seqlens[req])
+        for h in range(4):
+            assert np.array_equal(kg[req, h, :n, :128], f64(b.k[s:s + n, h // 2]))
+            assert np.array_equal(kg[req, h, :n, 128:], f64(b.g[s:s + n, h]))
+
+
+def test_commit_skips_null_slots_and_counts_outside_the_window():
+    b, _, _ = verify_batch([4, 4, 4], 1, 1, 65, null=(1,))
+    _, corr, kg = run_verify(b)
+    cache0 = f64(b.state_cache)
+    new = oracle.commit(b.state_cache, b.state_indices, torch.tensor([9, 2, -1]), corr, kg)
+    assert np.array_equal(new, cache0)
+
+
+def test_commit_bf16_state_rounds_once():
+    b, _, _ = verify_batch([5], 1, 2, 66)
+    b.state_cache = torch.as_tensor(oracle.round_bf16(f64(b.state_cache)))
+    _, corr, kg = run_verify(b)
+    new = oracle.commit(b.state_cache, b.state_indices, torch.tensor([5]), corr, kg,
+                        state_bf16=True)
+    _, sf = window_R(b, 0)
+    slot = int(b.state_indices[0])
+    assert np.array_equal(new[slot], oracle.round_bf16(sf[0]))
