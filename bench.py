@@ -335,6 +335,44 @@ def next_rows(dev):
         n * dhv * 128 * 128 * 4 * (1 + tt) + tt * io1, tokens_per_request=tt)
     row["tokens_per_s"] = round(n * tt / row["ms"] * 1e3, 1)
     res["f3_multi_token_decode"] = row
+    # f3: the record-based verify of the same windows (outputs and records, no
+    # state), then the commit of a random accepted prefix from the records
+    qs = torch.arange(n + 1, dtype=torch.int32, device=dev) * tt
+    flat = [x.reshape(n * tt, *x.shape[2:]) for x in (qm, km, vm, gm, bm)]
+    sidx = idx[:, 0].contiguous()
+    outv = torch.empty((n * tt, dhv, 128), dtype=torch.bfloat16, device=dev)
+    corr = torch.empty((n, dhv, tt, 128), device=dev)
+    kgr = torch.empty((n, dhv, tt, 256), dtype=torch.bfloat16, device=dev)
+    acc = torch.randint(1, tt + 1, (n,), generator=gen, device=dev, dtype=torch.int32)
+
+    def multi():
+        B.kda_decode(qm, km, vm, gm, bm, db.state_cache, idx, scale=db.scale)
+
+    def verify():
+        B.kda_verify(*flat, qs, db.state_cache, sidx, tt, scale=db.scale, output=outv, corr=corr,
+                     kg=kgr)
+
+    def commit():
+        B.kda_commit(db.state_cache, sidx, acc, corr, kgr)
+
+    units = n * dhv
+    io_tok = 2 * hqk * 256 + dhv * (3 * 256 + 2)       # q, k; v, g, out; beta
+    rec_tok = 128 * 4 + 256 * 2                         # corr fp32, kg bf16
+    v_bytes = units * 128 * 128 * 4 + n * tt * io_tok + units * tt * rec_tok
+    c_bytes = units * 128 * 128 * 4 * 2 + dhv * int(acc.sum()) * rec_tok
+    m_ms, v_ms = against(multi, verify)
+    c_ms = timed(commit)
+    res["f3_verify_window"] = dict(
+        tokens_per_request=tt, verify_ms=round(v_ms, 4), commit_ms=round(c_ms, 4),
+        multi_token_decode_ms=round(m_ms, 4),
+        vs_multi_token_decode=round(m_ms / (v_ms + c_ms), 3),
+        verify_gb_s=round(v_bytes / v_ms / 1e6, 1),
+        verify_hbm_frac=round(v_bytes / v_ms / 1e6 / PEAK_HBM_GBS, 4),
+        commit_gb_s=round(c_bytes / c_ms / 1e6, 1),
+        commit_hbm_frac=round(c_bytes / c_ms / 1e6 / PEAK_HBM_GBS, 4),
+        bytes_per_unit=dict(verify=round(v_bytes / units), commit=round(c_bytes / units),
+                            multi_token_decode=128 * 128 * 4 * (1 + tt) + round(tt * io1 / units)),
+        accepted_mean=round(float(acc.float().mean()), 3))
     return res
 
 

@@ -93,11 +93,47 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class VerifyArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32), ("query_start", ctypes.c_void_p), ("n", ctypes.c_int32),
+        ("hqk", ctypes.c_int32), ("hv", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("use_qk_l2norm", ctypes.c_int32),
+        ("state_cache", ctypes.c_void_p), ("state_dtype", ctypes.c_int32),
+        ("state_slot_stride", ctypes.c_int64), ("state_indices", ctypes.c_void_p),
+        ("num_slots", ctypes.c_int32),
+        ("corr", ctypes.c_void_p), ("kg", ctypes.c_void_p), ("out", ctypes.c_void_p),
+        ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+        ("dt_bias_dtype", ctypes.c_int32), ("lower_bound", ctypes.c_float),
+        ("q_stride", ctypes.c_int64), ("k_stride", ctypes.c_int64),
+        ("v_stride", ctypes.c_int64), ("g_stride", ctypes.c_int64),
+        ("beta_stride", ctypes.c_int64),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+class CommitArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_size_t),
+        ("state_cache", ctypes.c_void_p), ("state_dtype", ctypes.c_int32),
+        ("state_slot_stride", ctypes.c_int64), ("num_slots", ctypes.c_int32),
+        ("state_indices", ctypes.c_void_p), ("num_accepted_tokens", ctypes.c_void_p),
+        ("corr", ctypes.c_void_p), ("kg", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+        ("n", ctypes.c_int32), ("hv", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("use_qk_l2norm", ctypes.c_int32),
+        ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+        ("dt_bias_dtype", ctypes.c_int32), ("lower_bound", ctypes.c_float),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 _lock = threading.Lock()
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_ws_layout",
            "kda_decode", "kda_status_str", "kda_last_error", "kda_version",
-           "kda_chunk_fwd_noalloc")
+           "kda_chunk_fwd_noalloc", "kda_verify", "kda_commit")
 
 
 def library_path() -> str:
@@ -639,6 +675,132 @@ def kda_decode(q, k, v, g, beta, state_cache, state_indices=None, scale=None,
     if st != KDA_OK:
         _raise(lib, st)
     return output.view(shape_v) if output.numel() == v.numel() else output
+
+
+def _pool_checks(state_cache, hv, dev):
+    _need(state_cache.dtype in (torch.float32, torch.bfloat16),
+          "state must have dtype torch.float32 or torch.bfloat16", ValueError)
+    _need(state_cache.dim() == 4 and tuple(state_cache.shape[1:]) == (hv, D, D),
+          "state must have shape [pool, HV, V, K]")
+    _need(state_cache.shape[0] > 0, "state pool must contain at least one slot.")
+    _need(state_cache.device == dev, f"state_cache must be on {dev}")
+    _slot_stride(state_cache)
+
+
+def _int32_vec(x, n, name, dev):
+    _need(tuple(x.shape) == (n,), f"{name} must have shape [{n}]")
+    _need(x.dtype in (torch.int32, torch.int64), f"{name} must be integer", ValueError)
+    return x.to(device=dev, dtype=torch.int32).contiguous()
+
+
+def kda_verify(q, k, v, g, beta, query_start, state_cache, state_indices, window,
+               scale=None, use_qk_l2norm=True, A_log=None, dt_bias=None, lower_bound=-5.0,
+               output=None, corr=None, kg=None):
+    """The record-based speculative verify step (KdaTcVerify's window form):
+    request b runs its tokens q[query_start[b]:query_start[b+1]] (at most
+    `window` <= 8 of them) from slot state_indices[b] of the paged state, and
+    the step writes the outputs and, per (request, head, token), the records
+    corr = the delta correction u_t (fp32) and kg = raw key then raw gate (q's
+    dtype), but no state.
+
+    q, k [T, Hqk, 128]; v, g [T, Hv, 128]; beta [T, Hv]; query_start [B + 1];
+    state_cache [pool, Hv, 128, 128] fp32 or bf16 (read only); state_indices
+    [B] (outside the pool: zero outputs, no records).  Returns (out [T, Hv,
+    128], corr [B, Hv, window, 128], kg [B, Hv, window, 256])."""
+    _need(q.dim() == 3 and q.shape[-1] == D, "q must be [T, Hqk, 128]")
+    _need(k.shape == q.shape, "k must match q")
+    T, hqk = q.shape[0], q.shape[1]
+    _need(v.dim() == 3 and v.shape[0] == T and v.shape[-1] == D, "v must be [T, Hv, 128]")
+    hv = v.shape[1]
+    _need(g.shape == v.shape, "g must have the same shape as v")
+    _need(tuple(beta.shape) == (T, hv), "beta must be [T, Hv]")
+    _need(hv % hqk == 0, f"Expected HV to be divisible by H, got HV={hv}, H={hqk}.")
+    _need(q.dtype in _DTYPES, f"unsupported dtype {q.dtype}", TypeError)
+    for name, t in (("k", k), ("v", v), ("g", g), ("beta", beta)):
+        _need(t.dtype == q.dtype, f"{name} must have q's dtype", TypeError)
+    _need(1 <= int(window) <= 8, "window must lie in [1, 8]")
+    dev = q.device
+    n = query_start.numel() - 1
+    _need(query_start.dim() == 1 and n >= 0, "query_start must be [B + 1]")
+    qs = query_start.to(device=dev, dtype=torch.int32).contiguous()
+    idx = _int32_vec(state_indices, n, "state_indices", dev)
+    _pool_checks(state_cache, hv, dev)
+    W = int(window)
+    if output is None:
+        output = torch.zeros((T, hv, D), dtype=q.dtype, device=dev)
+    if corr is None:
+        corr = torch.zeros((n, hv, W, D), dtype=torch.float32, device=dev)
+    if kg is None:
+        kg = torch.zeros((n, hv, W, 2 * D), dtype=q.dtype, device=dev)
+    _need(tuple(output.shape) == (T, hv, D) and output.dtype == q.dtype,
+          "output must be [T, Hv, 128] of q's dtype")
+    _need(tuple(corr.shape) == (n, hv, W, D) and corr.dtype == torch.float32,
+          "corr must be [B, Hv, window, 128] fp32")
+    _need(tuple(kg.shape) == (n, hv, W, 2 * D) and kg.dtype == q.dtype,
+          "kg must be [B, Hv, window, 256] of q's dtype")
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        _token_stride(name, t, 1 if name == "beta" else 2)
+        _need(t.device == dev, f"{name} must be on {dev}")
+    for name, t in (("output", output), ("corr", corr), ("kg", kg)):
+        _contig(name, t)
+        _need(t.device == dev, f"{name} must be on {dev}")
+    lib = load_library()
+    a = VerifyArgs()
+    a.struct_size = ctypes.sizeof(VerifyArgs)
+    a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
+    a.dtype = _DTYPES[q.dtype]
+    a.query_start, a.n, a.hqk, a.hv, a.window = _ptr(qs), n, hqk, hv, W
+    a.scale = float(D ** -0.5 if scale is None else scale)
+    a.use_qk_l2norm = 1 if use_qk_l2norm else 0
+    a.state_cache, a.state_dtype = _ptr(state_cache), _DTYPES[state_cache.dtype]
+    a.state_indices, a.num_slots = _ptr(idx), state_cache.shape[0]
+    a.corr, a.kg, a.out = _ptr(corr), _ptr(kg), _ptr(output)
+    _set_gate(a, _gate(A_log, dt_bias, lower_bound, hv, dev))
+    _set_strides(a, q, k, v, g, beta, state_cache)
+    a.stream = _stream(dev)
+    st = lib.kda_verify(ctypes.byref(a))
+    if st != KDA_OK:
+        _raise(lib, st)
+    return output, corr, kg
+
+
+def kda_commit(state_cache, state_indices, num_accepted_tokens, corr, kg, use_qk_l2norm=True,
+               A_log=None, dt_bias=None, lower_bound=-5.0):
+    """Rebuild each request's state after its first a = num_accepted_tokens[b]
+    window tokens from its slot's state and the kda_verify records, in place
+    (a = 0, a count outside [0, window] or a slot outside the pool: left
+    alone).  corr [B, Hv, window, 128] fp32 and kg [B, Hv, window, 256] as
+    kda_verify returned them; the key normalisation and gate parameters must
+    be the ones the verify step used."""
+    _need(corr.dim() == 4 and corr.shape[-1] == D and corr.dtype == torch.float32,
+          "corr must be [B, Hv, window, 128] fp32")
+    n, hv, W = corr.shape[:3]
+    _need(1 <= W <= 8, "window must lie in [1, 8]")
+    _need(tuple(kg.shape) == (n, hv, W, 2 * D) and kg.dtype in _DTYPES,
+          "kg must be [B, Hv, window, 256]")
+    dev = corr.device
+    idx = _int32_vec(state_indices, n, "state_indices", dev)
+    acc = _int32_vec(num_accepted_tokens, n, "num_accepted_tokens", dev)
+    _pool_checks(state_cache, hv, dev)
+    for name, t in (("corr", corr), ("kg", kg)):
+        _contig(name, t)
+        _need(t.device == dev, f"{name} must be on {dev}")
+    lib = load_library()
+    a = CommitArgs()
+    a.struct_size = ctypes.sizeof(CommitArgs)
+    a.state_cache, a.state_dtype = _ptr(state_cache), _DTYPES[state_cache.dtype]
+    a.state_slot_stride = _slot_stride(state_cache)
+    a.num_slots = state_cache.shape[0]
+    a.state_indices, a.num_accepted_tokens = _ptr(idx), _ptr(acc)
+    a.corr, a.kg, a.dtype = _ptr(corr), _ptr(kg), _DTYPES[kg.dtype]
+    a.n, a.hv, a.window = n, hv, W
+    a.use_qk_l2norm = 1 if use_qk_l2norm else 0
+    _set_gate(a, _gate(A_log, dt_bias, lower_bound, hv, dev))
+    a.stream = _stream(dev)
+    st = lib.kda_commit(ctypes.byref(a))
+    if st != KDA_OK:
+        _raise(lib, st)
+    return state_cache
 
 
 def chunk_plan(q, k, v, g, beta, cu_seqlens=None, initial_state=None, output_final_state=False,

@@ -37,11 +37,6 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 size_t elem_size(int dtype) { return dtype == KDA_F32 ? 4 : 2; }
 
-// Gate parameters: both or neither; dt_bias fp32 or bf16; lower_bound in
-// [-5, 0], so the step log-decay lower_bound * sigmoid(..) stays in the
-// [-5, 0] range that the chunk kernels' block-referenced exponents are built
-// for (beyond it the factor between two 16-token block references can
-// underflow fp32 while the true coupling is O(1)).
 // Tensor base pointers are read with 8- and 16-byte vector loads.
 bool misaligned16(std::initializer_list<const void*> ps) {
   for (const void* p : ps)
@@ -81,6 +76,11 @@ kda_status resolve_slot_stride(int64_t s, int hv, int64_t& out) {
   return KDA_OK;
 }
 
+// Gate parameters: both or neither; dt_bias fp32 or bf16; lower_bound in
+// [-5, 0], so the step log-decay lower_bound * sigmoid(..) stays in the
+// [-5, 0] range that the chunk kernels' block-referenced exponents are built
+// for (beyond it the factor between two 16-token block references can
+// underflow fp32 while the true coupling is O(1)).
 kda_status check_gate(const float* a_log, const void* dt_bias, int32_t dt_dtype, float lb) {
   if ((a_log == nullptr) != (dt_bias == nullptr))
     return fail(KDA_ERR_SHAPE, "A_log and dt_bias must be provided together");
@@ -572,6 +572,103 @@ KDA_API kda_status kda_decode(const kda_decode_args* a) {
   L.strides = strides;
   L.slot_stride = slot_stride;
   hipError_t e = kda::launch_decode(L);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+KDA_API kda_status kda_verify(const kda_verify_args* a) {
+  if (!a) return fail(KDA_ERR_ARG, "args is NULL");
+  if (a->struct_size != sizeof(kda_verify_args))
+    return fail(KDA_ERR_ARG, "struct_size %zu != sizeof(kda_verify_args) %zu", a->struct_size,
+                sizeof(kda_verify_args));
+  if (a->dtype != KDA_F32 && a->dtype != KDA_BF16 && a->dtype != KDA_F16)
+    return fail(KDA_ERR_DTYPE, "unknown dtype %d", a->dtype);
+  if (a->n < 0) return fail(KDA_ERR_SHAPE, "n must be >= 0");
+  if (a->hqk <= 0 || a->hv <= 0) return fail(KDA_ERR_SHAPE, "head counts must be > 0");
+  if (a->hv % a->hqk != 0)
+    return fail(KDA_ERR_SHAPE, "GVA needs hv (%d) divisible by hqk (%d)", a->hv, a->hqk);
+  if (a->window < 1 || a->window > 8)
+    return fail(KDA_ERR_SHAPE, "window must lie in [1, 8], got %d", a->window);
+  if (!isfinite(a->scale)) return fail(KDA_ERR_SHAPE, "scale must be finite");
+  if (a->num_slots <= 0) return fail(KDA_ERR_SHAPE, "state pool must have at least one slot");
+  if (a->state_dtype != KDA_F32 && a->state_dtype != KDA_BF16)
+    return fail(KDA_ERR_DTYPE, "state_cache must be fp32 or bf16");
+  {
+    const kda_status gs = check_gate(a->A_log, a->dt_bias, a->dt_bias_dtype, a->lower_bound);
+    if (gs != KDA_OK) return gs;
+  }
+  if ((size_t)a->n * (size_t)a->hv > 0x7fffffffu)
+    return fail(KDA_ERR_UNSUPPORTED, "n * hv above 2^31-1");
+  if (misaligned16({a->q, a->k, a->v, a->g, a->out, a->state_cache, a->kg, a->corr, a->dt_bias}))
+    return fail(KDA_ERR_ARG, "tensor base pointers must be 16-byte aligned");
+  kda::InStrides strides;
+  {
+    const kda_status ss = resolve_strides(a->q_stride, a->k_stride, a->v_stride, a->g_stride,
+                                          a->beta_stride, a->hqk, a->hv, elem_size(a->dtype),
+                                          strides);
+    if (ss != KDA_OK) return ss;
+  }
+  int64_t slot_stride;
+  if (resolve_slot_stride(a->state_slot_stride, a->hv, slot_stride) != KDA_OK)
+    return KDA_ERR_SHAPE;
+  if (a->n == 0) return ok();
+  if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->query_start || !a->state_cache ||
+      !a->state_indices || !a->corr || !a->kg || !a->out)
+    return fail(KDA_ERR_ARG,
+                "q, k, v, g, beta, query_start, state_cache, state_indices, corr, kg and out "
+                "must be non-NULL");
+  kda::VerifyLaunch L;
+  L.q = a->q; L.k = a->k; L.v = a->v; L.g = a->g; L.beta = a->beta;
+  L.query_start = a->query_start;
+  L.cache = a->state_cache; L.state_bf16 = a->state_dtype == KDA_BF16 ? 1 : 0;
+  L.idx = a->state_indices; L.corr = a->corr; L.kg = a->kg; L.out = a->out;
+  L.dtype = a->dtype; L.n = a->n; L.hqk = a->hqk; L.hv = a->hv; L.window = a->window;
+  L.use_l2 = a->use_qk_l2norm ? 1 : 0; L.num_slots = a->num_slots; L.scale = a->scale;
+  L.gate = gate_of(a->A_log, a->dt_bias, a->dt_bias_dtype, a->lower_bound);
+  L.strides = strides; L.slot_stride = slot_stride; L.stream = a->stream;
+  hipError_t e = kda::launch_verify(L);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+KDA_API kda_status kda_commit(const kda_commit_args* a) {
+  if (!a) return fail(KDA_ERR_ARG, "args is NULL");
+  if (a->struct_size != sizeof(kda_commit_args))
+    return fail(KDA_ERR_ARG, "struct_size %zu != sizeof(kda_commit_args) %zu", a->struct_size,
+                sizeof(kda_commit_args));
+  if (a->dtype != KDA_F32 && a->dtype != KDA_BF16 && a->dtype != KDA_F16)
+    return fail(KDA_ERR_DTYPE, "unknown dtype %d", a->dtype);
+  if (a->n < 0) return fail(KDA_ERR_SHAPE, "n must be >= 0");
+  if (a->hv <= 0) return fail(KDA_ERR_SHAPE, "head count must be > 0");
+  if (a->window < 1 || a->window > 8)
+    return fail(KDA_ERR_SHAPE, "window must lie in [1, 8], got %d", a->window);
+  if (a->num_slots <= 0) return fail(KDA_ERR_SHAPE, "state pool must have at least one slot");
+  if (a->state_dtype != KDA_F32 && a->state_dtype != KDA_BF16)
+    return fail(KDA_ERR_DTYPE, "state_cache must be fp32 or bf16");
+  {
+    const kda_status gs = check_gate(a->A_log, a->dt_bias, a->dt_bias_dtype, a->lower_bound);
+    if (gs != KDA_OK) return gs;
+  }
+  if ((size_t)a->n * (size_t)a->hv > 0x7fffffffu)
+    return fail(KDA_ERR_UNSUPPORTED, "n * hv above 2^31-1");
+  if (misaligned16({a->state_cache, a->kg, a->corr, a->dt_bias}))
+    return fail(KDA_ERR_ARG, "tensor base pointers must be 16-byte aligned");
+  int64_t slot_stride;
+  if (resolve_slot_stride(a->state_slot_stride, a->hv, slot_stride) != KDA_OK)
+    return KDA_ERR_SHAPE;
+  if (a->n == 0) return ok();
+  if (!a->state_cache || !a->state_indices || !a->num_accepted_tokens || !a->corr || !a->kg)
+    return fail(KDA_ERR_ARG,
+                "state_cache, state_indices, num_accepted_tokens, corr and kg must be non-NULL");
+  kda::CommitLaunch L;
+  L.cache = a->state_cache; L.state_bf16 = a->state_dtype == KDA_BF16 ? 1 : 0;
+  L.idx = a->state_indices; L.accepted = a->num_accepted_tokens;
+  L.corr = a->corr; L.kg = a->kg;
+  L.dtype = a->dtype; L.n = a->n; L.hv = a->hv; L.window = a->window;
+  L.use_l2 = a->use_qk_l2norm ? 1 : 0; L.num_slots = a->num_slots;
+  L.gate = gate_of(a->A_log, a->dt_bias, a->dt_bias_dtype, a->lower_bound);
+  L.slot_stride = slot_stride; L.stream = a->stream;
+  hipError_t e = kda::launch_commit(L);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }

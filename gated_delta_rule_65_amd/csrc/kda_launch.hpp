@@ -25,6 +25,40 @@ struct DecodeLaunch {
 };
 hipError_t launch_decode(const DecodeLaunch& L);
 
+// The record-based verify window (outputs and records, no state).
+struct VerifyLaunch {
+  const void *q, *k, *v, *g, *beta;
+  const int32_t* query_start;  // [n + 1]
+  const void* cache;           // fp32 or bf16 (state_bf16), read only
+  int state_bf16;
+  const int32_t* idx;          // [n] slots
+  float* corr;                 // [n, hv, window, 128]
+  void* kg;                    // [n, hv, window, 256], input dtype
+  void* out;                   // [T, hv, 128]
+  int dtype, n, hqk, hv, window, use_l2, num_slots;
+  float scale;
+  GateArgs gate;
+  InStrides strides;
+  int64_t slot_stride;
+  void* stream;
+};
+hipError_t launch_verify(const VerifyLaunch& L);
+
+// The commit of the accepted prefix from the verify records.
+struct CommitLaunch {
+  void* cache;
+  int state_bf16;
+  const int32_t* idx;          // [n] slots
+  const int32_t* accepted;     // [n]
+  const float* corr;
+  const void* kg;
+  int dtype, n, hv, window, use_l2, num_slots;
+  GateArgs gate;
+  int64_t slot_stride;
+  void* stream;
+};
+hipError_t launch_commit(const CommitLaunch& L);
+
 // The staged chunked forward: every buffer already carved from the workspace.
 struct ChunkLaunch {
   const void *q, *k, *v, *g, *beta;

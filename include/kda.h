@@ -353,6 +353,108 @@ typedef struct kda_decode_args {
 
 kda_status kda_decode(const kda_decode_args *a);
 
+/*
+ * kda_verify_args -- the record-based speculative verify step (KdaTcVerify,
+ * page "vllm.models.kimi_k3.nvidia.recoverssm.cutedsl.verify": its argument
+ * list, the window closed form of its step 4 and its corr / kg records).
+ *
+ * Request b owns token rows [query_start[b], query_start[b+1]) of q, k, v,
+ * g, beta and out, at most `window` of them (rows past the window are not
+ * read and their out rows are left as they are).  From the state S0 in slot
+ * state_indices[b] (read only) each (request, value head) runs its tokens
+ * with, over the window, the inclusive cumulative log-decay cum_t, the
+ * (optionally L2-normalised) query qn_t and key kn_t, and b_t = sigmoid(beta):
+ *   probes   p_t = e^cum_t kn_t,  r_t = scale e^cum_t qn_t,  w_i = e^-cum_i kn_i
+ *   u_t = b_t (v_t - S0^T p_t - sum_{i<t} (w_i . p_t) u_i)
+ *   o_t = S0^T r_t + sum_{i<=t} (w_i . r_t) u_i
+ * (S0^T p: the V-first rows of S0 dotted with p), which equals the token
+ * recurrence.  It writes out and the records, and no state:
+ *   corr[b][h][t][:]        = u_t (fp32, 128 value channels)
+ *   kg[b][h][t][0 .. 127]   = the raw key k_t of the head's query-key head
+ *   kg[b][h][t][128 .. 255] = the raw gate g_t,
+ * both in the input dtype, for t below the request's token count; record
+ * rows past it are left as they are.  A slot outside [0, num_slots) gives zero
+ * out rows and writes no records.  The step log-decays must lie in [-5, 0]
+ * (the gate parameters guarantee it), so that e^(+-cum) stays inside fp32 over
+ * 8 tokens.
+ *
+ * Errors: KDA_ERR_ARG (NULL args or pointer, bad struct_size, misaligned
+ * base), KDA_ERR_DTYPE, KDA_ERR_SHAPE (heads, window outside [1, 8], slots,
+ * strides), KDA_ERR_UNSUPPORTED (sizes past 2^31, lower_bound outside
+ * [-5, 0]); nothing is queued on error.  Asynchronous on `stream`.
+ */
+typedef struct kda_verify_args {
+  size_t struct_size;          /* = sizeof(kda_verify_args) */
+  const void *q;               /* (device) [T, Hqk, 128] dtype (token stride q_stride) */
+  const void *k;               /* (device) [T, Hqk, 128] dtype */
+  const void *v;               /* (device) [T, Hv, 128] dtype */
+  const void *g;               /* (device) [T, Hv, 128] dtype: log-decay, or the raw
+                                  gate with A_log / dt_bias */
+  const void *beta;            /* (device) [T, Hv] dtype, logits */
+  int32_t dtype;               /* kda_dtype: KDA_F32, KDA_BF16 or KDA_F16 */
+  const int32_t *query_start;  /* (device) [n + 1], non-decreasing */
+  int32_t n;                   /* requests >= 0 */
+  int32_t hqk, hv;             /* hv % hqk == 0 */
+  int32_t window;              /* tokens per request at most, 1..8 */
+  float scale;
+  int32_t use_qk_l2norm;
+  const void *state_cache;     /* (device) [num_slots, Hv, 128(V), 128(K)] of state_dtype */
+  int32_t state_dtype;         /* KDA_F32 or KDA_BF16 */
+  int64_t state_slot_stride;   /* elements between slots, 0 = hv*128*128 */
+  const int32_t *state_indices;  /* (device) [n] */
+  int32_t num_slots;
+  float *corr;                 /* (device) [n, Hv, window, 128] fp32 */
+  void *kg;                    /* (device) [n, Hv, window, 256] dtype */
+  void *out;                   /* (device) [T, Hv, 128] dtype */
+  const float *A_log;          /* (device) [Hv] fp32, or NULL (gate parameters, */
+  const void *dt_bias;         /*  as kda_decode's) [Hv, 128] or NULL */
+  int32_t dt_bias_dtype;
+  float lower_bound;
+  int64_t q_stride, k_stride, v_stride, g_stride, beta_stride;  /* 0 = dense */
+  void *stream;                /* hipStream_t or NULL */
+} kda_verify_args;
+
+kda_status kda_verify(const kda_verify_args *a);
+
+/*
+ * kda_commit_args -- the state after the accepted prefix of each verify
+ * window, rebuilt from the slot's state and kda_verify's records alone.
+ *
+ * The recurrence's step is S_t = diag(e^g_t) S_{t-1} + kn_t u_t^T, and u_t is
+ * exactly the recorded correction, so for a = num_accepted_tokens[b] the
+ * state after the first a window tokens is that step applied for
+ * t = 0 .. a-1, with kn_t (L2-normalised when use_qk_l2norm) and g_t (through
+ * the gate parameters when given) recomputed from the raw key and gate in kg.
+ * It is written back to slot state_indices[b] in place (a bf16 state is
+ * rounded to nearest even once).  The pages name the records but do not show
+ * this step; it is the reading that makes them sufficient.  a = 0, a count
+ * outside [0, window] or a slot outside [0, num_slots) leaves the request's
+ * state alone.  The caller keeps a at most the request's verified token count
+ * (record rows past it hold whatever was there).  Slots of one call must be
+ * distinct.  Errors as kda_verify's; asynchronous on `stream`.
+ */
+typedef struct kda_commit_args {
+  size_t struct_size;          /* = sizeof(kda_commit_args) */
+  void *state_cache;           /* (device) [num_slots, Hv, 128, 128] of state_dtype, in place */
+  int32_t state_dtype;         /* KDA_F32 or KDA_BF16 */
+  int64_t state_slot_stride;   /* 0 = hv*128*128 */
+  int32_t num_slots;
+  const int32_t *state_indices;        /* (device) [n] */
+  const int32_t *num_accepted_tokens;  /* (device) [n] */
+  const float *corr;           /* (device) [n, Hv, window, 128] fp32 (from kda_verify) */
+  const void *kg;              /* (device) [n, Hv, window, 256] dtype (from kda_verify) */
+  int32_t dtype;               /* kg's kda_dtype */
+  int32_t n, hv, window;
+  int32_t use_qk_l2norm;
+  const float *A_log;          /* as kda_verify's */
+  const void *dt_bias;
+  int32_t dt_bias_dtype;
+  float lower_bound;
+  void *stream;
+} kda_commit_args;
+
+kda_status kda_commit(const kda_commit_args *a);
+
 /* Static text for a status code. */
 const char *kda_status_str(int32_t status);
 /* Detail of the calling thread's last failed call ("" if none). */

@@ -6,6 +6,7 @@ host-side checks before anything is queued.
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 import torch
@@ -469,3 +470,124 @@ def test_planner_max_seqlen_hint(lib):
     without = B.chunk_plan(q, q, v, v, beta, cu_seqlens=cu, max_seqlen=0, path=F)
     assert with_hint != without
     assert ws_size(lib, chunk_args(max_seqlen=-1))[0] == B.KDA_ERR_SHAPE
+
+
+# ------------------------------------------------- verify window and commit
+
+def verify_args(**kw):
+    a = B.VerifyArgs()
+    a.struct_size = ctypes.sizeof(B.VerifyArgs)
+    a.dtype, a.n, a.hqk, a.hv, a.window = 1, 4, 2, 4, 4
+    a.scale, a.use_qk_l2norm, a.num_slots, a.lower_bound = 0.1, 1, 8, -5.0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def commit_args(**kw):
+    a = B.CommitArgs()
+    a.struct_size = ctypes.sizeof(B.CommitArgs)
+    a.dtype, a.n, a.hv, a.window, a.num_slots, a.use_qk_l2norm = 1, 4, 4, 4, 8, 1
+    a.lower_bound = -5.0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """Every field offset of the ctypes mirrors equals the C header's (gcc)."""
+    structs = {"kda_chunk_args": B.ChunkArgs, "kda_decode_args": B.DecodeArgs,
+               "kda_verify_args": B.VerifyArgs, "kda_commit_args": B.CommitArgs}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "kda.h"', 'int main(void) {']
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    want = {}
+    for cname, py in structs.items():
+        want[f"{cname} size"] = ctypes.sizeof(py)
+        for f, _ in py._fields_:
+            want[f"{cname} {f}"] = getattr(py, f).offset
+    for line in filter(None, got):
+        key, val = line.rsplit(" ", 1)
+        assert want[key] == int(val), line
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("hv", 3, B.KDA_ERR_SHAPE),
+    ("dtype", 5, B.KDA_ERR_DTYPE),
+    ("n", -1, B.KDA_ERR_SHAPE),
+    ("window", 0, B.KDA_ERR_SHAPE),
+    ("window", 9, B.KDA_ERR_SHAPE),
+    ("num_slots", 0, B.KDA_ERR_SHAPE),
+    ("state_dtype", 2, B.KDA_ERR_DTYPE),
+    ("struct_size", 8, B.KDA_ERR_ARG),
+    ("state_slot_stride", 100, B.KDA_ERR_SHAPE),
+    ("q_stride", 8, B.KDA_ERR_SHAPE),
+])
+def test_verify_checks(lib, field, value, status):
+    assert lib.kda_verify(ctypes.byref(verify_args(**{field: value}))) == status
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("hv", 0, B.KDA_ERR_SHAPE),
+    ("dtype", 5, B.KDA_ERR_DTYPE),
+    ("n", -1, B.KDA_ERR_SHAPE),
+    ("window", 9, B.KDA_ERR_SHAPE),
+    ("num_slots", 0, B.KDA_ERR_SHAPE),
+    ("state_dtype", 2, B.KDA_ERR_DTYPE),
+    ("struct_size", 8, B.KDA_ERR_ARG),
+])
+def test_commit_checks(lib, field, value, status):
+    assert lib.kda_commit(ctypes.byref(commit_args(**{field: value}))) == status
+
+
+def test_verify_and_commit_null_pointers_gate_and_empty_batch(lib):
+    # n > 0 with NULL tensors: rejected before any launch
+    assert lib.kda_verify(ctypes.byref(verify_args())) == B.KDA_ERR_ARG
+    assert lib.kda_commit(ctypes.byref(commit_args())) == B.KDA_ERR_ARG
+    # gate parameters: both or neither, lower_bound in [-5, 0]
+    one = ctypes.c_float(0.0)
+    assert lib.kda_verify(ctypes.byref(verify_args(A_log=ctypes.addressof(one)))) == \
+        B.KDA_ERR_SHAPE
+    assert lib.kda_commit(ctypes.byref(commit_args(
+        A_log=ctypes.addressof(one), dt_bias=ctypes.addressof(one), lower_bound=-6.0))) == \
+        B.KDA_ERR_UNSUPPORTED
+    # an empty batch is a no-op
+    assert lib.kda_verify(ctypes.byref(verify_args(n=0))) == B.KDA_OK
+    assert lib.kda_commit(ctypes.byref(commit_args(n=0))) == B.KDA_OK
+
+
+def test_binding_verify_and_commit_checks():
+    q = torch.zeros(5, 2, 128, dtype=torch.bfloat16)
+    v = torch.zeros(5, 4, 128, dtype=torch.bfloat16)
+    beta = torch.zeros(5, 4, dtype=torch.bfloat16)
+    cache = torch.zeros(3, 4, 128, 128)
+    qs = torch.tensor([0, 2, 5])
+    idx = torch.tensor([0, 1])
+    with pytest.raises(ValueError):   # window past 8
+        B.kda_verify(q, q, v, v, beta, qs, cache, idx, 9)
+    with pytest.raises(ValueError):   # Hv not a multiple of Hqk
+        B.kda_verify(q[:, :1].expand(5, 3, 128), q[:, :1].expand(5, 3, 128), v, v, beta,
+                     qs, cache, idx, 4)
+    with pytest.raises(TypeError):    # mixed dtypes
+        B.kda_verify(q, q.float(), v, v, beta, qs, cache, idx, 4)
+    with pytest.raises(ValueError):   # state_indices shape
+        B.kda_verify(q, q, v, v, beta, qs, cache, torch.tensor([0]), 4)
+    with pytest.raises(ValueError):   # pool of the wrong head count
+        B.kda_verify(q, q, v, v, beta, qs, cache[:, :2], idx, 4)
+    corr = torch.zeros(2, 4, 4, 128)
+    kg = torch.zeros(2, 4, 4, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):   # corr must be fp32
+        B.kda_commit(cache, idx, torch.tensor([1, 2]), corr.double(), kg)
+    with pytest.raises(ValueError):   # kg shape
+        B.kda_commit(cache, idx, torch.tensor([1, 2]), corr, kg[:, :, :3])
+    with pytest.raises(ValueError):   # accepted counts shape
+        B.kda_commit(cache, idx, torch.tensor([1]), corr, kg)
