@@ -322,7 +322,7 @@ def _chunk_struct(q, k, v, g, beta, out, cu, N, T, hqk, hv, scale, l2, init, fin
     a.scale = scale
     a.use_qk_l2norm = 1 if l2 else 0
     a.initial_state, a.final_state = _ptr(init), _ptr(fin)
-    st = init if init is not None else fin
+    st = init if init is not None else (fin if fin is not None else cache)
     a.state_dtype = _DTYPES[st.dtype] if st is not None else 0
     a.state_cache, a.state_indices, a.has_initial_state = _ptr(cache), _ptr(idx), _ptr(has_init)
     a.num_slots = 0 if cache is None else cache.shape[0]
@@ -357,8 +357,9 @@ def _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state, c
     T = q3.shape[0]
     beta2 = beta.reshape(T, -1) if not varlen else beta
     _need(tuple(beta2.shape) == (T, hv), "beta must have shape [B, T, Hv].")
-    _need(q.dtype in (torch.float32, torch.bfloat16),
-          "chunk_kda supports torch.float32 and torch.bfloat16 inputs.", TypeError)
+    _need(q.dtype in (torch.float32, torch.bfloat16, torch.float16),
+          "chunk_kda supports torch.float32, torch.bfloat16 and torch.float16 inputs.",
+          TypeError)
     for name, t in (("k", k), ("v", v), ("g", g), ("beta", beta)):
         _need(t.dtype == q.dtype, "k, v, g and beta must have the same dtype as q.", TypeError)
     dev = q.device
@@ -383,7 +384,10 @@ def _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state, c
               "state_cache replaces initial_state/output_final_state")
         _need(state_indices is not None and has_initial_state is not None,
               "state_cache needs state_indices and has_initial_state")
-        _need(state_cache.dtype == torch.float32, "state_cache must be float32", TypeError)
+        _need(state_cache.dtype in (torch.float32, q.dtype) and
+              state_cache.dtype != torch.float16,
+              f"state_cache must have dtype torch.float32 or {q.dtype} (not float16).",
+              TypeError)
         _need(state_cache.dim() == 4 and tuple(state_cache.shape[1:]) == (hv, D, D),
               f"state_cache must be [slots, {hv}, 128, 128]")
         _slot_stride(state_cache)
@@ -394,7 +398,7 @@ def _prepare_chunk(q, k, v, g, beta, scale, initial_state, output_final_state, c
     else:
         # states are fp32 or of q's dtype (chunk_kda's rule), both alike; a new
         # final state takes the initial state's dtype, else fp32
-        ok_state = (torch.float32, q.dtype)
+        ok_state = (torch.float32,) if q.dtype == torch.float16 else (torch.float32, q.dtype)
         if initial_state is not None:
             _need(initial_state.dtype in ok_state,
                   f"initial_state must have dtype {q.dtype} or torch.float32.", TypeError)

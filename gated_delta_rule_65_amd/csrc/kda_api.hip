@@ -109,11 +109,8 @@ kda_status check_chunk(const kda_chunk_args* a, bool need_ptrs) {
   if (a->struct_size != sizeof(kda_chunk_args))
     return fail(KDA_ERR_ARG, "struct_size %zu != sizeof(kda_chunk_args) %zu",
                 a->struct_size, sizeof(kda_chunk_args));
-  if (a->dtype != KDA_F32 && a->dtype != KDA_BF16) {
-    if (a->dtype == KDA_F16)
-      return fail(KDA_ERR_DTYPE, "the chunked forward takes fp32 or bf16 inputs");
+  if (a->dtype != KDA_F32 && a->dtype != KDA_BF16 && a->dtype != KDA_F16)
     return fail(KDA_ERR_DTYPE, "unknown dtype %d", a->dtype);
-  }
   if (a->num_seqs < 0) return fail(KDA_ERR_SHAPE, "num_seqs must be >= 0");
   if (a->total_tokens < 0) return fail(KDA_ERR_SHAPE, "total_tokens must be >= 0");
   if (a->total_tokens > (int64_t)INT32_MAX)
@@ -134,9 +131,9 @@ kda_status check_chunk(const kda_chunk_args* a, bool need_ptrs) {
   }
   if (a->state_dtype != KDA_F32 && a->state_dtype != a->dtype)
     return fail(KDA_ERR_DTYPE, "initial/final state must be fp32 or of the input dtype");
+  if (a->state_dtype == KDA_F16)
+    return fail(KDA_ERR_UNSUPPORTED, "states are stored in fp32 or bf16, not fp16");
   const bool paged = a->state_cache != nullptr;
-  if (paged && a->state_dtype != KDA_F32)
-    return fail(KDA_ERR_UNSUPPORTED, "the paged chunk state is fp32");
   if (paged) {
     if (a->initial_state || a->final_state)
       return fail(KDA_ERR_SHAPE, "state_cache replaces initial_state/final_state");
@@ -304,9 +301,13 @@ WalkPlan plan_onchip(const kda_chunk_args* a) {
   return best;
 }
 
+// Element size of the staged intermediates: bf16 for bf16 inputs, fp32 for
+// fp32 and fp16 inputs (fp16 runs on the fp32 kernels).
+size_t inter_size(int dtype) { return dtype == KDA_BF16 ? 2 : 4; }
+
 kda_status layout_of(const kda_chunk_args* a, kda_ws_layout* L) {
   memset(L, 0, sizeof(*L));
-  const size_t es = elem_size(a->dtype);
+  const size_t es = inter_size(a->dtype);
   const size_t T = (size_t)a->total_tokens, H = (size_t)a->hv;
   const int64_t mc = max_chunks_of(a);
   const bool onchip = path_of(a) == KDA_PATH_ONCHIP;

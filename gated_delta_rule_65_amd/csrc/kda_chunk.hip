@@ -138,6 +138,15 @@ __device__ __forceinline__ void load8(const bf16* p, float (&x)[8]) {
     x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
   }
 }
+__device__ __forceinline__ void load8(const _Float16* p, float (&x)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xffffu));
+    x[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+  }
+}
 __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
   const float4 a = *reinterpret_cast<const float4*>(p);
   const float4 b = *reinterpret_cast<const float4*>(p + 4);
@@ -229,10 +238,10 @@ __device__ __forceinline__ float ld_elem(const float* p) { return *p; }
 // GVA group.  Streaming: reads q, k, g once and writes qg (token-major, key
 // channel packed), kg_t (chunk-major, token packed) and decay.  The LDS G tile
 // doubles as the transpose buffer of kg.
-template <typename E>
-__global__ __launch_bounds__(256) void prep_kernel(const E* __restrict__ q,
-                                                   const E* __restrict__ k,
-                                                   const E* __restrict__ g,
+template <typename E, typename I>
+__global__ __launch_bounds__(256) void prep_kernel(const I* __restrict__ q,
+                                                   const I* __restrict__ k,
+                                                   const I* __restrict__ g,
                                                    const int4* __restrict__ table,
                                                    int hqk, int hv, int use_l2,
                                                    E* __restrict__ qg, E* __restrict__ kg_t,
@@ -340,10 +349,10 @@ __global__ __launch_bounds__(256) void prep_kernel(const E* __restrict__ q,
 //
 // With PREP the kernel also writes the prep outputs (qg, kg_t, decay), so the
 // inputs are read from HBM once for the whole intra-chunk stage.
-template <typename E, bool PREP, bool GATE>
+template <typename E, bool PREP, bool GATE, typename I>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void wy_kernel(
-    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
-    const E* __restrict__ g, const E* __restrict__ beta, const int4* __restrict__ table,
+    const I* __restrict__ q, const I* __restrict__ k, const I* __restrict__ v,
+    const I* __restrict__ g, const I* __restrict__ beta, const int4* __restrict__ table,
     int hqk, int hv, int use_l2, E* __restrict__ w_out, E* __restrict__ u_t,
     E* __restrict__ aqk, E* __restrict__ qg, E* __restrict__ kg_t, float* __restrict__ decay,
     int items, int* __restrict__ counter, const GateArgs ga, const InStrides is) {
@@ -389,8 +398,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   int item = blockIdx.x;
   ChunkPos p;
   bool ok = item < items && locate_chunk(item / hv, table, p);
-  RawRows<E> rq, rk, rgt;
-  E rb;
+  RawRows<I> rq, rk, rgt;
+  I rb;
   float gA = 0.f;  // gate parameters of the item's head (GATE): A_log, dt_bias bits
   uint4 gB0 = make_uint4(0, 0, 0, 0), gB1 = gB0;
   auto prefetch = [&](int it_, const ChunkPos& pp, int tid) {
@@ -555,7 +564,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   // v rows, requested as soon as phase 0's registers are free; they land
   // during phase 1.  Rows past L are not zeroed: they meet b = 0 columns
   // of T'.
-  RawRows<E> rv;
+  RawRows<I> rv;
   raw_load(v + (size_t)p.t0 * is.v + h * D, (int)is.v, L, rv, tid);
   if (tid == 0) s_next = claim + (int)gridDim.x;
   lds_barrier();
@@ -834,7 +843,7 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
   const int cpg = (nch_all + G - 1) / G;
   const int jc0 = min(nch_all, g * cpg), jc1 = min(nch_all, jc0 + cpg);
 
-  float* row = nullptr;  // paged cache row of this (sequence, head)
+  void* row = nullptr;  // paged pool plane of this (sequence, head)
   if (a.cache) {
     const int slot = a.slots[n];
     if (slot < 0 || slot >= a.num_slots) {
@@ -843,24 +852,28 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
         const int tb = sp.bos + C * jc0, te = min(sp.eos, sp.bos + C * jc1);
         for (int idx = tid; idx < (te - tb) * BV; idx += NT) {
           const int t = idx / BV, vv = idx - t * BV;
-          a.out[((size_t)(tb + t) * hv + h) * D + v0 + vv] = from_f32<E>(0.f);
+          const size_t o = ((size_t)(tb + t) * hv + h) * D + v0 + vv;
+          if (a.out16)
+            a.out16[o] = (_Float16)0.f;
+          else
+            a.out[o] = from_f32<E>(0.f);
         }
       }
       return;
     }
-    row = a.cache + (size_t)slot * a.slot_stride + (size_t)h * PLANE;
+    row = pool_plane(a.cache, a.slot_stride, slot, h, a.state_bf16 != 0);
   }
-  // state in (src) and out (dst); dense initial / final states may be bf16
-  const bool dense_bf = !a.cache && a.state_bf16;
+  // state in (src) and out (dst): fp32, or bf16 (dense states or the pool)
+  const bool state_bf = a.state_bf16 != 0;
   const void* src = nullptr;
   void* dst = nullptr;
   bool src_bf = false, dst_bf = false;
   const size_t unit_plane = (size_t)n * hv + h;
   if (MODE == 0) {
-    src = a.cache ? (a.has_init[n] ? (const void*)row : nullptr)
-                  : (a.init ? dense_plane(a.init, unit_plane, dense_bf) : nullptr);
-    dst = a.cache ? (void*)row : (a.fin ? dense_plane(a.fin, unit_plane, dense_bf) : nullptr);
-    src_bf = dst_bf = dense_bf;
+    src = a.cache ? (a.has_init[n] ? row : nullptr)
+                  : (a.init ? dense_plane(a.init, unit_plane, state_bf) : nullptr);
+    dst = a.cache ? row : (a.fin ? dense_plane(a.fin, unit_plane, state_bf) : nullptr);
+    src_bf = dst_bf = state_bf;
   } else if (MODE == 1) {
     dst = scan_plane(a.scan, g, n, h, a.N, hv, tcols ? 0 : 1);
   } else {
@@ -870,8 +883,8 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
     // the final state is the walk's own, as is a checkpoint at the end
     const int g_last = nch_all > 0 ? (nch_all - 1) / cpg : 0;
     if (g == g_last) {
-      dst = a.cache ? (void*)row : (a.fin ? dense_plane(a.fin, unit_plane, dense_bf) : nullptr);
-      dst_bf = dense_bf;
+      dst = a.cache ? row : (a.fin ? dense_plane(a.fin, unit_plane, state_bf) : nullptr);
+      dst_bf = state_bf;
     }
   }
 
@@ -1266,19 +1279,29 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
     }
     if (OUT) {
       // rows t = 16 ta + l16 of this lane's 4 output columns
-      E* op = a.out + ((size_t)(t0 + l16) * hv + h) * D + v0 + 16 * wave + 4 * gq;
+      const size_t ob = ((size_t)(t0 + l16) * hv + h) * D + v0 + 16 * wave + 4 * gq;
       const size_t tstep = (size_t)16 * hv * D;
-      if (L == C) {
+      auto put = [&](auto* op) {
+        if (L == C) {
 #pragma unroll
-        for (int ta = 0; ta < 4; ++ta)
-          store4(op + ta * tstep, a.scale * O[ta][0], a.scale * O[ta][1], a.scale * O[ta][2],
-                 a.scale * O[ta][3]);
-      } else {
-#pragma unroll
-        for (int ta = 0; ta < 4; ++ta)
-          if (16 * ta + l16 < L)
+          for (int ta = 0; ta < 4; ++ta)
             store4(op + ta * tstep, a.scale * O[ta][0], a.scale * O[ta][1], a.scale * O[ta][2],
                    a.scale * O[ta][3]);
+        } else {
+#pragma unroll
+          for (int ta = 0; ta < 4; ++ta)
+            if (16 * ta + l16 < L)
+              store4(op + ta * tstep, a.scale * O[ta][0], a.scale * O[ta][1],
+                     a.scale * O[ta][2], a.scale * O[ta][3]);
+        }
+      };
+      if constexpr (std::is_same<E, float>::value) {
+        if (a.out16)
+          put(a.out16 + ob);
+        else
+          put(a.out + ob);
+      } else {
+        put(a.out + ob);
       }
     }
     if (jc == ck_step) {
@@ -1352,17 +1375,20 @@ static void launch_walk(const ChunkLaunch& L, const WalkArgs<E>& wa) {
 }
 
 // The WY kernel; without PREP the prep outputs come from prep_kernel.
-template <typename E, bool PREP, bool GATE>
+template <typename E, bool PREP, bool GATE, typename I>
 static void launch_wy(const ChunkLaunch& L, dim3 grid, int items, int* counter) {
-  hipLaunchKernelGGL((wy_kernel<E, PREP, GATE>), grid, dim3(256), 0, (hipStream_t)L.stream,
-                     (const E*)L.q, (const E*)L.k, (const E*)L.v, (const E*)L.g,
-                     (const E*)L.beta, (const int4*)L.table, L.hqk, L.hv, L.use_l2, (E*)L.w,
+  hipLaunchKernelGGL((wy_kernel<E, PREP, GATE, I>), grid, dim3(256), 0, (hipStream_t)L.stream,
+                     (const I*)L.q, (const I*)L.k, (const I*)L.v, (const I*)L.g,
+                     (const I*)L.beta, (const int4*)L.table, L.hqk, L.hv, L.use_l2, (E*)L.w,
                      (E*)L.u, (E*)L.aqk, PREP ? (E*)L.qg : (E*)nullptr,
                      PREP ? (E*)L.kg_t : (E*)nullptr, PREP ? L.decay : (float*)nullptr, items,
                      counter, L.gate, L.strides);
 }
 
-template <typename E>
+// E: intermediate and MFMA operand type (fp32 operands run as split bf16
+// pairs); I: input and output type (fp16 inputs take the fp32 kernels,
+// widened exactly on load).
+template <typename E, typename I>
 static hipError_t launch_staged_t(const ChunkLaunch& L) {
   hipStream_t st = (hipStream_t)L.stream;
   mark(L, 0);
@@ -1373,8 +1399,8 @@ static hipError_t launch_staged_t(const ChunkLaunch& L) {
   mark(L, 1);
   if (L.max_chunks > 0 && T > 0) {
     if (!L.fuse_prep)
-      hipLaunchKernelGGL(prep_kernel<E>, dim3((unsigned)L.max_chunks, L.hqk), dim3(256), 0, st,
-                         (const E*)L.q, (const E*)L.k, (const E*)L.g, (const int4*)L.table,
+      hipLaunchKernelGGL((prep_kernel<E, I>), dim3((unsigned)L.max_chunks, L.hqk), dim3(256), 0,
+                         st, (const I*)L.q, (const I*)L.k, (const I*)L.g, (const int4*)L.table,
                          L.hqk, L.hv, L.use_l2, (E*)L.qg, (E*)L.kg_t, L.decay, L.gate,
                          L.strides);
     mark(L, 2);
@@ -1386,14 +1412,14 @@ static hipError_t launch_staged_t(const ChunkLaunch& L) {
     int* wy_counter = reinterpret_cast<int*>((char*)L.zero + 1024);
     if (L.gate.a_log) {
       if (L.fuse_prep)
-        launch_wy<E, true, true>(L, grid, items, wy_counter);
+        launch_wy<E, true, true, I>(L, grid, items, wy_counter);
       else
-        launch_wy<E, false, true>(L, grid, items, wy_counter);
+        launch_wy<E, false, true, I>(L, grid, items, wy_counter);
     } else {
       if (L.fuse_prep)
-        launch_wy<E, true, false>(L, grid, items, wy_counter);
+        launch_wy<E, true, false, I>(L, grid, items, wy_counter);
       else
-        launch_wy<E, false, false>(L, grid, items, wy_counter);
+        launch_wy<E, false, false, I>(L, grid, items, wy_counter);
     }
   } else {
     mark(L, 2);
@@ -1405,8 +1431,10 @@ static hipError_t launch_staged_t(const ChunkLaunch& L) {
   wa.cu = L.cu; wa.dense_len = dense_len; wa.T = T; wa.offs = L.chunk_offsets;
   wa.N = N; wa.hv = L.hv; wa.scale = L.scale;
   wa.init = L.init; wa.fin = L.fin; wa.state_bf16 = L.state_bf16;
-  wa.cache = (float*)L.cache; wa.slot_stride = L.slot_stride; wa.slots = L.slots;
-  wa.has_init = L.has_init; wa.num_slots = L.num_slots; wa.out = (E*)L.out;
+  wa.cache = L.cache; wa.slot_stride = L.slot_stride; wa.slots = L.slots;
+  wa.has_init = L.has_init; wa.num_slots = L.num_slots;
+  wa.out = std::is_same<I, _Float16>::value ? nullptr : (E*)L.out;
+  wa.out16 = std::is_same<I, _Float16>::value ? (_Float16*)L.out : nullptr;
   wa.units = N * L.hv; wa.max_chunks = (int)L.max_chunks; wa.groups = L.groups;
   wa.scan = L.scan; wa.zero = (const uint4*)L.zero;
   wa.ckpt = L.ckpt; wa.ckpt_off = L.ckpt_off; wa.ckpt_idx = L.ckpt_idx;
@@ -1432,7 +1460,11 @@ void launch_chunk_table(const ChunkLaunch& L) {
 }
 
 hipError_t launch_chunk_staged(const ChunkLaunch& L) {
-  return L.dtype == 0 ? launch_staged_t<float>(L) : launch_staged_t<bf16>(L);
+  switch (L.dtype) {
+    case 0: return launch_staged_t<float, float>(L);
+    case 1: return launch_staged_t<bf16, bf16>(L);
+    default: return launch_staged_t<float, _Float16>(L);
+  }
 }
 
 }  // namespace kda

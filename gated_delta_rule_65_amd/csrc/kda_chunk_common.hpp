@@ -103,7 +103,11 @@ __device__ __forceinline__ FragS frag_row(const float* p) {
 template <typename E> struct RawRows;
 template <> struct RawRows<bf16> { uint4 r[4]; };
 template <> struct RawRows<float> { float4 r[4][2]; };
+template <> struct RawRows<_Float16> { uint4 r[4]; };
 __device__ __forceinline__ void raw_row(const bf16* p, RawRows<bf16>& x, int it) {
+  x.r[it] = *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void raw_row(const _Float16* p, RawRows<_Float16>& x, int it) {
   x.r[it] = *reinterpret_cast<const uint4*>(p);
 }
 __device__ __forceinline__ void raw_row(const float* p, RawRows<float>& x, int it) {
@@ -116,6 +120,14 @@ __device__ __forceinline__ void raw_vals(const RawRows<bf16>& x, int it, float* 
   for (int d = 0; d < 4; ++d) {
     o[2 * d] = __uint_as_float(w[d] << 16);
     o[2 * d + 1] = __uint_as_float(w[d] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void raw_vals(const RawRows<_Float16>& x, int it, float* o) {
+  const uint32_t w[4] = {x.r[it].x, x.r[it].y, x.r[it].z, x.r[it].w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    o[2 * d] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[d] & 0xffffu));
+    o[2 * d + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[d] >> 16));
   }
 }
 __device__ __forceinline__ void raw_vals(const RawRows<float>& x, int it, float* o) {
@@ -157,6 +169,17 @@ __device__ __forceinline__ bf16x4_t raw_column(const RawRows<bf16>& x, int e) {
     b[it] = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu);
   }
   return __builtin_bit_cast(bf16x4_t, make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16)));
+}
+// fp16 inputs feed fp32 tiles: the column is widened (exactly).
+__device__ __forceinline__ float4 raw_column(const RawRows<_Float16>& x, int e) {
+  float c[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    float o[8];
+    raw_vals(x, it, o);
+    c[it] = o[e];
+  }
+  return make_float4(c[0], c[1], c[2], c[3]);
 }
 __device__ __forceinline__ float4 raw_column(const RawRows<float>& x, int e) {
   float c[4];
@@ -221,12 +244,13 @@ struct WalkArgs {
   const void* init;  // dense initial / final states: fp32, or bf16 with state_bf16
   void* fin;
   int state_bf16;
-  float* cache;
+  void* cache;          // paged pool: fp32, or bf16 with state_bf16
   int64_t slot_stride;  // elements between paged state slots
   const int32_t* slots;
   const uint8_t* has_init;
   int num_slots;
   E* out;
+  _Float16* out16;  // fp16 output instead of `out` (fp16 inputs on the fp32 path), or NULL
   int nvb, units, max_chunks, groups;
   float* scan;  // group planes (g, n, h): P [k][j], B [v][k], H_in [v][k]
   const uint4* zero;
@@ -259,6 +283,13 @@ __device__ __forceinline__ void plane_store4(void* p, size_t off, bool bf, const
   }
 }
 // Plane (n, h) of a dense [N, hv, 128, 128] state array of either storage.
+// The plane of value head h in slot `slot` of a paged pool (fp32 or bf16).
+__device__ __forceinline__ void* pool_plane(void* cache, int64_t slot_stride, int slot, int h,
+                                            bool bf) {
+  const size_t off = (size_t)slot * slot_stride + (size_t)h * PLANE;
+  return bf ? (void*)(reinterpret_cast<bf16*>(cache) + off)
+            : (void*)(reinterpret_cast<float*>(cache) + off);
+}
 __device__ __forceinline__ const void* dense_plane(const void* base, size_t plane, bool bf) {
   return bf ? (const void*)(reinterpret_cast<const bf16*>(base) + plane * PLANE)
             : (const void*)(reinterpret_cast<const float*>(base) + plane * PLANE);
@@ -298,7 +329,8 @@ __global__ __launch_bounds__(64) void compose_kernel(const WalkArgs<E> a) {
   if (a.cache) {
     const int slot = a.slots[n];
     if (slot < 0 || slot >= a.num_slots) return;
-    if (a.has_init[n]) src = a.cache + (size_t)slot * a.slot_stride + (size_t)h * PLANE;
+    src_bf = a.state_bf16 != 0;
+    if (a.has_init[n]) src = pool_plane(a.cache, a.slot_stride, slot, h, src_bf);
   } else if (a.init) {
     src_bf = a.state_bf16 != 0;
     src = dense_plane(a.init, (size_t)n * hv + h, src_bf);

@@ -69,7 +69,7 @@ struct ChunkLaunch {
   const void* init;           // dense initial state or NULL (fp32, or bf16 with state_bf16)
   void* fin;                  // dense final state or NULL (same storage)
   int state_bf16;
-  void* cache;                // paged state (fp32) or NULL
+  void* cache;                // paged state (fp32, or bf16 with state_bf16) or NULL
   const int32_t* slots;
   const uint8_t* has_init;
   int num_slots;

@@ -102,5 +102,10 @@ __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float
   const bf16x4_t v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
   *reinterpret_cast<bf16x4_t*>(p) = v;
 }
+__device__ __forceinline__ void store4(_Float16* p, float a, float b, float c, float d) {
+  typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+  const f16x4_t v = {(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d};
+  *reinterpret_cast<f16x4_t*>(p) = v;
+}
 
 }  // namespace kda

@@ -56,7 +56,7 @@ struct OnchipArgs {
   const void* init;  // dense initial / final states: fp32, or bf16 with state_bf16
   void* fin;
   int state_bf16;
-  float* cache;  // paged fp32 pool
+  void* cache;  // paged pool: fp32, or bf16 with state_bf16
   int64_t slot_stride;
   const int32_t* slots;
   const uint8_t* has_init;
@@ -240,7 +240,7 @@ onchip_kernel(
   const int cpg = (nch_all + G - 1) / G;
   const int jc0 = min(nch_all, g * cpg), jc1 = min(nch_all, jc0 + cpg);
 
-  float* row = nullptr;  // paged cache row of this (sequence, head)
+  void* row = nullptr;  // paged pool plane of this (sequence, head)
   if (a.cache) {
     const int slot = a.slots[n];
     if (slot < 0 || slot >= a.num_slots) {
@@ -254,24 +254,25 @@ onchip_kernel(
       }
       return;
     }
-    row = a.cache + (size_t)slot * a.slot_stride + (size_t)h * PLANE;
+    row = pool_plane(a.cache, a.slot_stride, slot, h, a.state_bf16 != 0);
   }
-  const bool dense_bf = !a.cache && a.state_bf16;
+  // state in (src) and out (dst): fp32, or bf16 (dense states or the pool)
+  const bool state_bf = a.state_bf16 != 0;
   const void* src = nullptr;
   void* dst = nullptr;
   bool src_bf = false, dst_bf = false;
   const size_t unit_plane = (size_t)n * hv + h;
   if (MODE == 0) {
-    src = a.cache ? (a.has_init[n] ? (const void*)row : nullptr)
-                  : (a.init ? dense_plane(a.init, unit_plane, dense_bf) : nullptr);
-    dst = a.cache ? (void*)row : (a.fin ? dense_plane(a.fin, unit_plane, dense_bf) : nullptr);
-    src_bf = dst_bf = dense_bf;
+    src = a.cache ? (a.has_init[n] ? row : nullptr)
+                  : (a.init ? dense_plane(a.init, unit_plane, state_bf) : nullptr);
+    dst = a.cache ? row : (a.fin ? dense_plane(a.fin, unit_plane, state_bf) : nullptr);
+    src_bf = dst_bf = state_bf;
   } else if (MODE == 2) {
     src = scan_plane(a.scan, g, n, h, a.N, hv, 2);
     const int g_last = nch_all > 0 ? (nch_all - 1) / cpg : 0;
     if (g == g_last) {
-      dst = a.cache ? (void*)row : (a.fin ? dense_plane(a.fin, unit_plane, dense_bf) : nullptr);
-      dst_bf = dense_bf;
+      dst = a.cache ? row : (a.fin ? dense_plane(a.fin, unit_plane, state_bf) : nullptr);
+      dst_bf = state_bf;
     }
   }
   int ck_step = -1;
@@ -863,7 +864,7 @@ static void launch_onchip_t(const ChunkLaunch& L, const OnchipArgs& oa) {
   memset(&wa, 0, sizeof(wa));
   wa.cu = L.cu; wa.dense_len = a.dense_len; wa.T = a.T; wa.offs = L.chunk_offsets;
   wa.N = a.N; wa.hv = a.hv; wa.init = L.init; wa.state_bf16 = L.state_bf16;
-  wa.cache = (float*)L.cache; wa.slot_stride = L.slot_stride; wa.slots = L.slots;
+  wa.cache = L.cache; wa.slot_stride = L.slot_stride; wa.slots = L.slots;
   wa.has_init = L.has_init; wa.num_slots = L.num_slots; wa.units = a.units;
   wa.max_chunks = a.max_chunks; wa.groups = G; wa.scan = L.scan;
   hipLaunchKernelGGL((compose_kernel<bf16>), dim3((unsigned)(a.units * 8)), dim3(64), 0, st, wa);
@@ -890,7 +891,7 @@ hipError_t launch_chunk_onchip(const ChunkLaunch& L) {
   a.N = N; a.hqk = L.hqk; a.hv = L.hv; a.max_chunks = (int)L.max_chunks;
   a.groups = L.groups; a.units = N * L.hv; a.use_l2 = L.use_l2; a.scale = L.scale;
   a.init = L.init; a.fin = L.fin; a.state_bf16 = L.state_bf16;
-  a.cache = (float*)L.cache; a.slot_stride = L.slot_stride; a.slots = L.slots;
+  a.cache = L.cache; a.slot_stride = L.slot_stride; a.slots = L.slots;
   a.has_init = L.has_init; a.num_slots = L.num_slots; a.out = (bf16*)L.out;
   a.scan = L.scan; a.ckpt = L.ckpt; a.ckpt_off = L.ckpt_off; a.ckpt_idx = L.ckpt_idx;
   a.ckpt_rows = L.ckpt_rows;

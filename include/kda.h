@@ -67,7 +67,8 @@ extern "C" {
 typedef enum kda_dtype {
   KDA_F32 = 0,   /* fp32 inputs; MFMA operands carried as split bf16 pairs */
   KDA_BF16 = 1,  /* bf16 inputs; bf16 MFMA with fp32 accumulation */
-  KDA_F16 = 2    /* fp16 inputs (decode only) */
+  KDA_F16 = 2    /* fp16 inputs; the chunked forward runs them on its fp32
+                    kernels (widened exactly, split MFMA operands) */
 } kda_dtype;
 
 typedef enum kda_status {
@@ -106,7 +107,7 @@ typedef struct kda_chunk_args {
   const void *v;               /* (device) [T_tot, Hv, 128] dtype */
   const void *g;               /* (device) [T_tot, Hv, 128] dtype, log-decay <= 0 */
   const void *beta;            /* (device) [T_tot, Hv] dtype, logits */
-  int32_t dtype;               /* kda_dtype: KDA_F32 or KDA_BF16 */
+  int32_t dtype;               /* kda_dtype: KDA_F32, KDA_BF16 or KDA_F16 */
   int32_t num_seqs;            /* N >= 0 */
   int64_t total_tokens;        /* T_tot >= 0; KDA_ERR_UNSUPPORTED above 2^31 - 1, or when
                                   (T_tot / 64 + num_seqs) * hv is */
@@ -163,11 +164,11 @@ typedef struct kda_chunk_args {
   const int32_t *checkpoint_offsets;       /* (device) [N]; with checkpoint_state */
   const int32_t *checkpoint_state_indices; /* (device) [N] or NULL */
   int32_t checkpoint_rows;
-  /* Storage of initial_state / final_state: KDA_F32 (0) or the input dtype
-     (chunk_kda's rule on page "mate.kda": the states are fp32 or of q's
-     dtype, both alike).  A bf16 initial state is widened exactly; the final
-     state is rounded to nearest even.  The paged state_cache and the
-     checkpoint rows are always fp32 (page "vllm.models.kimi_k3.amd.ops.kda_chunk"). */
+  /* Storage of initial_state / final_state, or of the paged state_cache:
+     KDA_F32 (0) or the input dtype (chunk_kda's rule on page "mate.kda": the
+     states are fp32 or of q's dtype, both alike), and not fp16
+     (KDA_ERR_UNSUPPORTED).  A bf16 start state is widened exactly; the final
+     state is rounded to nearest even.  The checkpoint rows are always fp32. */
   int32_t state_dtype;
   /* Input strides (optional), in elements between consecutive tokens of
      q, k, v, g and beta; 0 means dense (hqk*128 for q and k, hv*128 for v
@@ -266,7 +267,8 @@ kda_status kda_chunk_fwd_noalloc(const kda_chunk_args *a);
  * (P): the last axis is stored in MFMA fragment order: inside each block of
  * 32 elements, position 8 g + j holds element 4 g + j for j < 4 and
  * 16 + 4 g + (j - 4) for j >= 4.  Token axes of a short chunk are zero past
- * its length.  Element type: bf16 for KDA_BF16 inputs, fp32 for KDA_F32.
+ * its length.  Element type: bf16 for KDA_BF16 inputs, fp32 for KDA_F32 and
+ * KDA_F16 inputs.
  */
 typedef struct kda_ws_layout {
   size_t chunk_offsets, zero, table, qg, kg_t, decay, w, u, aqk, scan, total;

@@ -102,7 +102,6 @@ def test_onchip_workspace_holds_only_the_table_and_scan_planes(lib):
 @pytest.mark.parametrize("field,value,status", [
     ("hv", 3, B.KDA_ERR_SHAPE),            # GVA divisibility
     ("hqk", 0, B.KDA_ERR_SHAPE),
-    ("dtype", 2, B.KDA_ERR_DTYPE),         # fp16 chunk path not served
     ("dtype", 9, B.KDA_ERR_DTYPE),
     ("num_seqs", -1, B.KDA_ERR_SHAPE),
     ("total_tokens", 255, B.KDA_ERR_SHAPE),  # dense: not a multiple of num_seqs
@@ -201,7 +200,7 @@ def test_binding_shape_checks_raise_like_chunk_kda():
     with pytest.raises(ValueError, match="beta"):
         B.chunk_kda(q, q, v, v, cpu((1, 64, 2)))
     with pytest.raises(TypeError):
-        B.chunk_kda(q.half(), q.half(), v.half(), v.half(), beta.half())
+        B.chunk_kda(q.double(), q.double(), v.double(), v.double(), beta.double())
     with pytest.raises(TypeError):
         B.chunk_kda(q, q, v.float(), v, beta)
     with pytest.raises(ValueError, match="4D"):
@@ -330,12 +329,23 @@ def test_multi_token_decode_checks(lib, fields, status):
 
 
 def test_state_dtype_checks(lib):
-    # chunk: the states are fp32 or of the input dtype; the paged chunk state is fp32
+    # chunk: the states (dense or paged) are fp32 or of the input dtype, never fp16
     assert ws_size(lib, chunk_args(state_dtype=2))[0] == B.KDA_ERR_DTYPE   # f16 with bf16 input
     assert ws_size(lib, chunk_args(state_dtype=1))[0] == B.KDA_OK
     a = chunk_args(state_dtype=1, state_cache=FAKE, state_indices=FAKE, has_initial_state=FAKE,
                    num_slots=4)
-    assert ws_size(lib, a)[0] == B.KDA_ERR_UNSUPPORTED
+    assert ws_size(lib, a)[0] == B.KDA_OK                                  # bf16 pool
+    a = chunk_args(dtype=0, state_dtype=1, state_cache=FAKE, state_indices=FAKE,
+                   has_initial_state=FAKE, num_slots=4)
+    assert ws_size(lib, a)[0] == B.KDA_ERR_DTYPE                           # bf16 pool, fp32 in
+    assert ws_size(lib, chunk_args(dtype=2))[0] == B.KDA_OK                # fp16 inputs
+    assert ws_size(lib, chunk_args(dtype=2, state_dtype=2))[0] == B.KDA_ERR_UNSUPPORTED
+    assert ws_size(lib, chunk_args(dtype=2, path=B.PATH_ONCHIP))[0] == B.KDA_ERR_UNSUPPORTED
+    # fp16 inputs keep fp32 intermediates: the same layout as fp32 inputs
+    l16, l32 = B.WsLayout(), B.WsLayout()
+    assert lib.kda_chunk_ws_layout(ctypes.byref(chunk_args(dtype=2)), ctypes.byref(l16)) == B.KDA_OK
+    assert lib.kda_chunk_ws_layout(ctypes.byref(chunk_args(dtype=0)), ctypes.byref(l32)) == B.KDA_OK
+    assert l16.total == l32.total and l16.aqk == l32.aqk
     # decode: fp32 or bf16 cache
     assert lib.kda_decode(ctypes.byref(decode_args(state_dtype=2))) == B.KDA_ERR_DTYPE
 
@@ -346,6 +356,13 @@ def test_binding_state_dtype_rules():
     beta = cpu((1, 64, 4))
     with pytest.raises(TypeError, match="initial_state"):
         B.chunk_kda(q, q, v, v, beta, initial_state=cpu((1, 4, 128, 128), torch.float16))
+    q16, v16, b16 = q.half(), v.half(), beta.half()
+    with pytest.raises(TypeError, match="initial_state"):   # fp16 inputs: fp32 states only
+        B.chunk_kda(q16, q16, v16, v16, b16, initial_state=cpu((1, 4, 128, 128), torch.float16))
+    with pytest.raises(TypeError, match="state_cache"):
+        B.chunk_kda(q16, q16, v16, v16, b16, state_cache=cpu((3, 4, 128, 128), torch.float16),
+                    state_indices=torch.zeros(1, dtype=torch.int32),
+                    has_initial_state=torch.zeros(1, dtype=torch.uint8))
     with pytest.raises(TypeError, match="same dtype"):
         B.chunk_kda(q, q, v, v, beta, initial_state=cpu((1, 4, 128, 128)),
                     output_final_state=True, final_state=cpu((1, 4, 128, 128), torch.float32))

@@ -855,3 +855,102 @@ def test_mixed_configurations_match_oracle(i):
     assert rel(out.float().cpu().numpy(), o_ref, b.cu_seqlens) < t_
     got = cache.cpu()[b.state_indices.long()] if cfg["paged"] else fin.cpu()
     assert rel(got.numpy(), s_ref) < t_
+
+
+# ------------------------------------------------ fp16 inputs, bf16 paged pool
+
+FP16_CASES = [
+    # (name, lengths, hqk, hv, g_scale, groups)
+    ("ragged", [1, 63, 64, 65, 200, 7], 1, 2, 5.0, 0),
+    ("gva", [130, 77], 2, 8, 5.0, 0),
+    ("weak_decay_scan", [3000], 1, 2, 0.01, 4),
+]
+
+
+@pytest.mark.parametrize("case", FP16_CASES, ids=[c[0] for c in FP16_CASES])
+def test_fp16_inputs(case):
+    """fp16 inputs run on the fp32 kernels (widened exactly, split MFMA
+    operands): outputs are stored in fp16 (the 1e-2 bar of 16-bit outputs), the
+    fp32 final states keep the fp32 bar (1e-4)."""
+    name, lengths, hqk, hv, gs, groups = case
+    b = inputs.make_chunk(lengths, hqk, hv, dtype=torch.float16, g_scale=gs, seed=130,
+                          init=True)
+    say("fp16", name)
+    q, k, v, g, beta = gpu(b)
+    out, fin = chunk_kda(q, k, v, g, beta, scale=b.scale, initial_state=b.initial_state.to(DEV),
+                         output_final_state=True, cu_seqlens=b.cu_seqlens.to(DEV),
+                         groups=groups)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.float16 and fin.dtype == torch.float32
+    o_ref, s_ref = oracle_dense(b)
+    cu = b.cu_seqlens.numpy()
+    assert report("out", out.float().cpu().numpy(), o_ref, cu) < 1e-2
+    assert report("state", fin.cpu().numpy(), s_ref) < 1e-4
+    assert report("first 64", first_rows(out.float().cpu().numpy(), cu),
+                  first_rows(o_ref, cu), first_cu(cu)) < 1e-2
+
+
+def test_fp16_paged_pool_with_gate_parameters():
+    lengths = [90, 0, 64, 131]
+    hv = 4
+    b = inputs.make_chunk(lengths, 2, hv, dtype=torch.float16, seed=131, paged_slots=9)
+    b.has_initial_state = torch.tensor([1, 1, 0, 1], dtype=torch.uint8)
+    gen = torch.Generator().manual_seed(132)
+    b.g = torch.randn(b.g.shape, generator=gen).to(torch.float16)  # raw gate ~ N(0, 1)
+    a_log = (torch.rand(hv, generator=gen) * 2 - 1).float()
+    dt_bias = torch.randn(hv, 128, generator=gen).float()
+    say("fp16 paged gate")
+    q, k, v, g, beta = gpu(b)
+    cache = b.state_cache.to(DEV)
+    out = chunk_kda(q, k, v, g, beta, scale=b.scale, cu_seqlens=b.cu_seqlens.to(DEV),
+                    state_cache=cache, state_indices=b.state_indices.to(DEV),
+                    has_initial_state=b.has_initial_state.to(DEV), A_log=a_log.to(DEV),
+                    dt_bias=dt_bias.to(DEV))
+    torch.cuda.synchronize()
+    idx = b.state_indices.long()
+    s0 = b.state_cache[idx].clone()
+    s0[2] = 0.0
+    o_ref, s_ref = oracle.recurrence(b.q, b.k, b.v, b.g, b.beta, cu_seqlens=b.cu_seqlens,
+                                     scale=b.scale, initial_state=s0, A_log=a_log,
+                                     dt_bias=dt_bias)
+    assert report("out", out.float().cpu().numpy(), o_ref, b.cu_seqlens.numpy()) < 1e-2
+    got = cache.cpu()
+    assert report("state", got[idx].numpy(), s_ref) < 1e-4
+    others = torch.ones(9, dtype=torch.bool)
+    others[idx] = False
+    assert torch.equal(got[others], b.state_cache[others])
+
+
+@pytest.mark.parametrize("groups", [1, 4])
+def test_bf16_paged_pool(groups):
+    """A bf16 state pool (chunk_kda's states may take q's dtype): each row is
+    widened exactly as the start state and the final state is rounded to
+    nearest even; a zero-length sequence passes its row through bit for bit,
+    rows of other slots are untouched."""
+    lengths = [900, 0, 64, 1300]
+    b = inputs.make_chunk(lengths, 2, 4, dtype=torch.bfloat16, g_scale=0.5, seed=133,
+                          paged_slots=9)
+    b.has_initial_state = torch.tensor([1, 1, 0, 1], dtype=torch.uint8)
+    pool = (b.state_cache * 25.0).to(torch.bfloat16)
+    say("bf16 pool", groups)
+    q, k, v, g, beta = gpu(b)
+    cache = pool.to(DEV)
+    out = chunk_kda(q, k, v, g, beta, scale=b.scale, cu_seqlens=b.cu_seqlens.to(DEV),
+                    state_cache=cache, state_indices=b.state_indices.to(DEV),
+                    has_initial_state=b.has_initial_state.to(DEV), groups=groups)
+    torch.cuda.synchronize()
+    idx = b.state_indices.long()
+    s0 = pool[idx].float()
+    s0[2] = 0.0
+    o_ref, s_ref = oracle.recurrence(b.q, b.k, b.v, b.g, b.beta, cu_seqlens=b.cu_seqlens,
+                                     scale=b.scale, initial_state=s0)
+    assert report("out", out.float().cpu().numpy(), o_ref, b.cu_seqlens.numpy()) < 1e-2
+    got = cache.cpu()
+    assert got.dtype == torch.bfloat16
+    live = [0, 2, 3]
+    assert report("state", got[idx[live]].float().numpy(),
+                  oracle.round_bf16(s_ref[live])) < 1e-2
+    assert torch.equal(got[idx[1]], pool[idx[1]])
+    others = torch.ones(9, dtype=torch.bool)
+    others[idx] = False
+    assert torch.equal(got[others], pool[others])
