@@ -24,12 +24,31 @@ FLAGS = [
 ]
 
 
+def _spilling_kernels(remarks: str):
+    """(kernel, bytes per lane) for every kernel the compiler's resource
+    remarks report with private scratch (register spills)."""
+    out, name = [], None
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:")[1].split()[0]
+        elif "ScratchSize [bytes/lane]:" in line and name:
+            n = int(line.split("ScratchSize [bytes/lane]:")[1].split()[0])
+            if n:
+                out.append((name, n))
+    return out
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+    # every kernel keeps its working set in registers and LDS: a spill to
+    # scratch is a build error, not a silent slowdown
+    spills = _spilling_kernels(r.stderr)
+    if spills:
+        raise RuntimeError(f"{src}: kernels spill to scratch: {spills}")
     return obj
 
 

@@ -1032,9 +1032,14 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
         const char* kb = (const char*)(a.kg_t + ((size_t)c * hv + h) * D * C);
         const char* db = (const char*)(a.decay + ((size_t)c * hv + h) * D);
         const char* ub = (const char*)(a.u_t + (((size_t)c * hv + h) * D + v0) * C);
+        // the lane's line indices from an opaque copy of the lane id: hoisted
+        // out of the loop, the per-branch line addresses would stay live
+        // across it (and spill)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int k = 0; k < KW; ++k) {
-          const int f = 64 * LW * k + 64 * dwave + lane;
+          const int f = 64 * LW * k + 64 * dwave + ln;
           const char* p = nullptr;
           if (f < per) {
             const int i = vb * per + f;

@@ -608,3 +608,16 @@ def test_binding_verify_and_commit_checks():
         B.kda_commit(cache, idx, torch.tensor([1, 2]), corr, kg[:, :, :3])
     with pytest.raises(ValueError):   # accepted counts shape
         B.kda_commit(cache, idx, torch.tensor([1]), corr, kg)
+
+
+def test_build_rejects_kernels_that_spill():
+    """The build parses the compiler's resource remarks and fails on any kernel
+    with private scratch (a register spill)."""
+    from gated_delta_rule_65_amd import build
+    remarks = "\n".join([
+        "x.hip:1:1: remark: Function Name: kern_a [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:9:1: remark: Function Name: kern_b [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:9:1: remark:     ScratchSize [bytes/lane]: 12 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert build._spilling_kernels(remarks) == [("kern_b", 12)]
