@@ -10,7 +10,10 @@ tokens/s: 131072 tokens over the mean wall time of a step.
 
 After the timed region, each with HIP events on the library's stream:
   * K more calls with the library's stage events: the per-kernel breakdown
-    of the headline workload and ``roofline`` (its dominant kernel);
+    of the headline workload (``kernels``: one row per kernel launch, each
+    with its algorithmic flops and bytes and its roofline bound, HBM when its
+    arithmetic intensity is below the ridge point of 312.5 flop/B, MFMA
+    above) and ``roofline``, the row of its longest kernel;
   * the chunk path as a whole (all kernels of a call) against the bf16 MFMA
     peak: ``roofline_chunk_path``;
   * the other prefill workloads, each timed alone (``legs``): the dense
@@ -66,12 +69,14 @@ def chunk_lengths(lengths):
     return out
 
 
-def chunk_work(lengths, hqk, hv, es, state_in, state_out):
-    """Algorithmic flops and bytes per kernel for one chunked forward."""
+def chunk_work(lengths, hqk, hv, es, state_in, state_out, groups=1):
+    """Algorithmic flops and bytes per kernel for one chunked forward (groups:
+    the chunk groups of the walk's group scan, 1 for the plain walk)."""
     T = sum(lengths)
     chunks = chunk_lengths(lengths)
     nch = len(chunks)
     N = len(lengths)
+    plane = 128 * 128 * 4
     prep_b = (2 * T * hqk + T * hv) * 128 * es + T * hv * 128 * es + nch * hv * 128 * (64 * es + 4)
     wy_b = (2 * T * hqk + 2 * T * hv) * 128 * es + T * hv * es + T * hv * (2 * 128 + 64) * es
     walk_b = (T * hv * (3 * 128 + 64) * es + nch * hv * 128 * (64 * es + 4)
@@ -79,12 +84,48 @@ def chunk_work(lengths, hqk, hv, es, state_in, state_out):
     # prep folded into WY: the inputs once, all six intermediates out
     intra_b = ((2 * T * hqk + 2 * T * hv) * 128 * es + T * hv * es
                + T * hv * (2 * 128 + 64) * es + nch * hv * 128 * (2 * 64 * es + 4))
+    wyf = hv * sum(wy_flops(L) for L in chunks)
+    wkf = hv * sum(walk_flops(L) for L in chunks)
+    G = max(1, groups)
+    planes = G * N * hv * plane
+    # pass one walks every group but the last: its chunks, per sequence
+    p1_chunks, p1_T = [], 0
+    for n_ in lengths:
+        cl = chunk_lengths([n_])
+        cpg = -(-len(cl) // G) if cl else 0
+        keep = cl[:min(len(cl), (G - 1) * cpg)]
+        p1_chunks += keep
+        p1_T += sum(keep)
+    # group scan.  Pass one reads w, kg_t, u_t and decay and writes a group's
+    # transfer and partial state; compose reads those and the start states and
+    # writes each group's start state; pass two is the plain walk from them.
+    # Work: pass one walks the 128 value and the 128 transfer columns without
+    # outputs (w S and kg^T U for both), compose G - 1 products of 128^3 per
+    # (sequence, head).
+    p1_b = (p1_T * hv * 128 * es + len(p1_chunks) * hv * 128 * (2 * 64 * es + 4)
+            + 2 * planes * (G - 1) // G)
+    p1_f = 2 * hv * sum(4 * L * K * V + K * V for L in p1_chunks)
+    cmp_b = 2 * planes + (state_in * N * hv * plane) + planes
+    cmp_f = 2.0 * (G - 1) * N * hv * (2 * K * K * V)
+    p2_b = walk_b + planes
+    # on-chip path: inputs once per pass, outputs and states; nothing else
+    in_b = (2 * T * hqk + 2 * T * hv) * 128 * es + T * hv * es
+    oc_b = in_b + T * hv * 128 * es + (state_in + state_out) * N * hv * plane
+    oc1_b = ((2 * p1_T * hv + p1_T * hqk) * 128 * es + p1_T * hv * es
+             + 2 * planes * (G - 1) // G)
     return dict(
         tokens=T,
         prep=dict(bytes=prep_b, flops=0.0),
-        intra=dict(bytes=intra_b, flops=hv * sum(wy_flops(L) for L in chunks)),
-        wy=dict(bytes=wy_b, flops=hv * sum(wy_flops(L) for L in chunks)),
-        walk=dict(bytes=walk_b, flops=hv * sum(walk_flops(L) for L in chunks)),
+        intra=dict(bytes=intra_b, flops=wyf),
+        wy=dict(bytes=wy_b, flops=wyf),
+        walk=dict(bytes=walk_b, flops=wkf),
+        pass_one=dict(bytes=p1_b, flops=p1_f),
+        compose=dict(bytes=cmp_b, flops=cmp_f),
+        pass_two=dict(bytes=p2_b, flops=wkf),
+        onchip=dict(bytes=oc_b, flops=wyf + wkf),
+        onchip_pass_one=dict(bytes=oc1_b,
+                             flops=hv * sum(wy_flops(L) for L in p1_chunks) + p1_f),
+        onchip_pass_two=dict(bytes=oc_b + planes, flops=wyf + wkf),
         table=dict(bytes=4 * (2 * N + 1), flops=0.0),
     )
 
@@ -139,18 +180,33 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str):
-    """Counter-derived HBM bytes per launch (profiles/traffic.json), or None
-    when absent or taken from a different kernel source."""
+def load_traffic(workload: str, row: str):
+    """Counter-derived HBM bytes per launch of kernel row `row` on `workload`
+    (profiles/traffic.json), or None when absent or taken from a different
+    kernel source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    rec = t.get("kernels", {}).get(kernel)
-    if not rec or rec.get("source_hash") != source_hash():
+    if t.get("source_hash") != source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    rec = t.get("workloads", {}).get(workload, {}).get(row)
+    return None if not rec else rec.get("bytes_per_launch")
+
+
+def roofline_of(flops, nbytes, ms):
+    """The roofline bound of a kernel from its arithmetic intensity against
+    the ridge point (bf16 MFMA peak / HBM peak = 312.5 flop per byte), and
+    the achieved rate against that bound's peak."""
+    s = ms / 1e3
+    if nbytes and flops / nbytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        gbs = nbytes / s / 1e9
+        return dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(gbs / PEAK_HBM_GBS, 4))
+    tf = flops / s / 1e12
+    return dict(bound="mfma", achieved=round(tf, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                frac=round(tf / PEAK_BF16_TFLOPS, 4))
 
 
 def cpu_model():
@@ -377,11 +433,6 @@ def next_rows(dev):
 
 
 STAGES = ["table", "prep", "wy", "walk", "compose", "pass2"]
-# kernel names per stage, by plan (the chunk-table kernel is its own stage)
-KERNEL_OF = {"table": "chunk_offsets_kernel", "prep": "prep_kernel", "wy": "wy_kernel",
-             "walk": "walk_kernel", "compose": "compose_kernel", "pass2": "walk_kernel"}
-
-
 class ChunkCase:
     """One prefill workload resident in HBM with preallocated outputs and
     workspace; call() queues one kda_chunk_fwd on the current stream."""
@@ -402,7 +453,7 @@ class ChunkCase:
             (b.num_seqs, self.hv, 128, 128), device=dev, dtype=torch.float32)
         self.max_seqlen = max(self.lengths)
         self.path = {"auto": B.PATH_AUTO, "staged": B.PATH_STAGED,
-                     "fused": B.PATH_FUSED}[args.path]
+                     "fused": B.PATH_FUSED, "onchip": B.PATH_ONCHIP}[args.path]
         self.kw = dict(scale=b.scale, cu_seqlens=b.cu_seqlens, max_seqlen=self.max_seqlen,
                        groups=args.groups, walk_waves=args.walk_waves, path=self.path,
                        output=self.out)
@@ -415,11 +466,13 @@ class ChunkCase:
         self.plan = B.chunk_plan(b.q, b.k, b.v, b.g, b.beta, cu_seqlens=b.cu_seqlens,
                                  initial_state=None if self.paged else b.initial_state,
                                  output_final_state=not self.paged, groups=args.groups,
-                                 walk_waves=args.walk_waves, max_seqlen=self.max_seqlen)
+                                 walk_waves=args.walk_waves, max_seqlen=self.max_seqlen,
+                                 path=self.path)
         nbytes = B.chunk_workspace_bytes(b.q, b.k, b.v, b.g, b.beta, **self._ws_kw())
         self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
         es = 2 if b.q.dtype == torch.bfloat16 else 4
-        self.work = chunk_work(self.lengths, self.hqk, self.hv, es, True, True)
+        self.work = chunk_work(self.lengths, self.hqk, self.hv, es, True, True,
+                               groups=self.plan[0])
         self.flops = self.work["wy"]["flops"] + self.work["walk"]["flops"]
 
     def _ws_kw(self):
@@ -478,42 +531,56 @@ def stage_breakdown(ev, case, n):
 
 
 def kernel_rows(case, per):
-    """Per-kernel figures of one chunked forward from its stage times."""
+    """One row per kernel launch of a chunked forward, from its stage times:
+    algorithmic work, time, and the roofline bound with the achieved rate."""
     w = case.work
+    onchip = case.path == case.B.PATH_ONCHIP
     fused_prep = case.path != case.B.PATH_STAGED
     groups = case.plan[0]
     rows = {}
+
+    def row(name, kernel, key, ms, note=None):
+        if ms <= 0:
+            return
+        r = dict(kernel=kernel, ms=round(ms, 4), algorithmic_flops=w[key]["flops"],
+                 algorithmic_bytes=w[key]["bytes"])
+        r.update(roofline_of(w[key]["flops"], w[key]["bytes"], ms))
+        s_ = ms / 1e3
+        r["tflops"] = round(w[key]["flops"] / s_ / 1e12, 2)
+        r["gb_s"] = round(w[key]["bytes"] / s_ / 1e9, 1)
+        if note:
+            r["note"] = note
+        rows[name] = r
+
     if per["table"] > 0:
-        rows["table"] = dict(kernel=KERNEL_OF["table"], ms=round(per["table"], 4))
-    if not fused_prep and per["prep"] > 0:
-        s = per["prep"] / 1e3
-        rows["prep"] = dict(kernel="prep_kernel", ms=round(per["prep"], 4), bound="hbm",
-                            gb_s=round(w["prep"]["bytes"] / s / 1e9, 1),
-                            frac=round(w["prep"]["bytes"] / s / 1e9 / PEAK_HBM_GBS, 4),
-                            algorithmic_bytes=w["prep"]["bytes"])
-    if per["wy"] > 0:
-        wk = "intra" if fused_prep else "wy"
-        s = per["wy"] / 1e3
-        rows["wy"] = dict(kernel="wy_kernel", ms=round(per["wy"], 4), bound="mfma",
-                          tflops=round(w[wk]["flops"] / s / 1e12, 2),
-                          frac=round(w[wk]["flops"] / s / 1e12 / PEAK_BF16_TFLOPS, 4),
-                          gb_s=round(w[wk]["bytes"] / s / 1e9, 1),
-                          algorithmic_flops=w[wk]["flops"], algorithmic_bytes=w[wk]["bytes"])
-        if fused_prep:
-            rows["wy"]["note"] = "prep folded in (reads q, k, v, g, beta; writes all intermediates)"
-    walk_ms = per["walk"] + per["compose"] + per["pass2"]
-    if walk_ms > 0:
-        s = walk_ms / 1e3
-        rows["walk"] = dict(kernel="walk_kernel", ms=round(walk_ms, 4), bound="mfma",
-                            tflops=round(w["walk"]["flops"] / s / 1e12, 2),
-                            frac=round(w["walk"]["flops"] / s / 1e12 / PEAK_BF16_TFLOPS, 4),
-                            algorithmic_flops=w["walk"]["flops"],
-                            algorithmic_bytes=w["walk"]["bytes"])
+        rows["table"] = dict(kernel="chunk_offsets_kernel", ms=round(per["table"], 4))
+    if onchip:
         if groups > 1:
-            rows["walk"]["note"] = (f"group scan, G = {groups}: pass one "
-                                    f"{per['walk']:.4f} ms, compose {per['compose']:.4f} ms, "
-                                    f"pass two {per['pass2']:.4f} ms; algorithmic flops "
-                                    "are the plain walk's (pass one is scan overhead)")
+            row("pass_one", "onchip_kernel<1>", "onchip_pass_one", per["walk"],
+                "group scan pass one: the intra-chunk stage and the walk of the value and "
+                "transfer columns, per chunk, on chip")
+            row("compose", "compose_kernel", "compose", per["compose"])
+            row("pass_two", "onchip_kernel<2>", "onchip_pass_two", per["pass2"],
+                "group scan pass two: the intra-chunk stage and the walk, on chip")
+        else:
+            row("walk", "onchip_kernel<0>", "onchip", per["walk"],
+                "the intra-chunk stage and the walk, per chunk, on chip")
+        return rows
+    if not fused_prep:
+        row("prep", "prep_kernel", "prep", per["prep"])
+    row("wy", "wy_kernel", "intra" if fused_prep else "wy", per["wy"],
+        "prep folded in (reads q, k, v, g, beta; writes all intermediates)"
+        if fused_prep else None)
+    if groups > 1:
+        row("pass_one", "walk_kernel<1>", "pass_one", per["walk"],
+            f"group scan (G = {groups}) pass one: each group walked from zero and from the "
+            "identity (value and transfer columns), no outputs")
+        row("compose", "compose_kernel", "compose", per["compose"])
+        row("pass_two", "walk_kernel<2>", "pass_two", per["pass2"],
+            f"group scan (G = {groups}) pass two: the plain walk from the composed start "
+            "states")
+    else:
+        row("walk", "walk_kernel<0>", "walk", per["walk"])
     return rows
 
 
@@ -540,8 +607,9 @@ def main():
     ap.add_argument("--groups", type=int, default=0, help="chunk groups (0 = auto)")
     ap.add_argument("--walk-waves", type=int, default=0,
                     help="waves per walk workgroup: 0 = auto, 2, 4 or 8")
-    ap.add_argument("--path", choices=["auto", "staged", "fused"], default="auto",
-                    help="chunk path: prep as its own kernel (staged) or folded into WY")
+    ap.add_argument("--path", choices=["auto", "staged", "fused", "onchip"], default="auto",
+                    help="chunk path: prep as its own kernel (staged), folded into WY "
+                         "(fused), or the intra-chunk stage inside the walk (onchip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-legs", action="store_true",
                     help="skip the other prefill workloads and the decode")
@@ -595,24 +663,25 @@ def main():
     # event-timed launch duration)
     dom = max((k for k in kernels if k != "table"), key=lambda k: kernels[k]["ms"])
     kd = kernels[dom]
-    if kd["bound"] == "hbm":
-        roof = dict(bound="hbm", achieved=kd["gb_s"], peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=kd["frac"], kernel=kd["kernel"],
-                    algorithmic_bytes=kd["algorithmic_bytes"])
-    else:
-        roof = dict(bound="mfma", achieved=kd["tflops"], peak=PEAK_BF16_TFLOPS,
-                    unit="TFLOP/s", frac=kd["frac"], kernel=kd["kernel"],
-                    algorithmic_flops=kd["algorithmic_flops"])
-    roof["traffic"] = load_traffic(kd["kernel"]) if case.plan[0] <= 1 or dom != "walk" else None
+    roof = {k: kd[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    roof.update(kernel=kd["kernel"], algorithmic_bytes=kd["algorithmic_bytes"],
+                algorithmic_flops=kd["algorithmic_flops"])
+    roof["traffic"] = load_traffic(args.workload, dom)
     roof["launch_ms"] = kd["ms"]
     if "note" in kd:
         roof["note"] = kd["note"]
     cs = call_ms / 1e3
+    min_b = case.work["onchip"]["bytes"]
     roof_path = dict(bound="mfma", achieved=round(case.flops / cs / 1e12, 2),
                      peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                      frac=round(case.flops / cs / 1e12 / PEAK_BF16_TFLOPS, 4),
                      kernel="whole chunked forward (every kernel of one call)",
-                     algorithmic_flops=case.flops, launch_ms=round(call_ms, 4))
+                     algorithmic_flops=case.flops, launch_ms=round(call_ms, 4),
+                     min_bytes=min_b,
+                     min_bytes_gb_s=round(min_b / cs / 1e9, 1),
+                     min_bytes_hbm_frac=round(min_b / cs / 1e9 / PEAK_HBM_GBS, 4),
+                     note="min_bytes: inputs, outputs and states only, the HBM floor of a "
+                          "path that keeps every intermediate on chip")
     wl = inputs.WORKLOADS[args.workload]
     config = dict(workload=args.workload, B=len(case.lengths), T=max(case.lengths),
                   tokens=case.T, hqk=case.hqk, hv=case.hv, head_dim=128, chunk=64,
@@ -687,7 +756,7 @@ def main():
         res["roofline_decode"] = dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS,
                                       unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4),
                                       kernel="decode_kernel", algorithmic_bytes=dw["bytes"],
-                                      traffic=load_traffic("decode_kernel"),
+                                      traffic=load_traffic("decode_paged", "decode"),
                                       launch_ms=round(dec_ms, 4),
                                       note="launched after a dense-prefill chunked forward")
         del dense, db

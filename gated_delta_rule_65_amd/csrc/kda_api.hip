@@ -232,7 +232,8 @@ WalkPlan plan_walk(const kda_chunk_args* a) {
         cost = std::max(std::ceil((double)(units * nvb) / cap) * nc, chain) * step_cost[wi];
       } else {
         const double cpg = std::ceil(nc / G);
-        const double r1 = std::ceil((double)(units * G * 2 * nvb) / cap);
+        // pass one walks every group but the last
+        const double r1 = std::ceil((double)(units * (G - 1) * 2 * nvb) / cap);
         const double r2 = std::ceil((double)(units * G * nvb) / cap);
         // the group chains (pass one and pass two) have a floor as well
         cost = std::max((0.8 * r1 + r2) * cpg, 1.8 * std::ceil(chain / G)) * step_cost[wi] + G;
@@ -288,8 +289,8 @@ WalkPlan plan_onchip(const kda_chunk_args* a) {
       cost = std::max(walk((double)units, nc, 2, 1.3), chain);
     } else {
       const double cpg = std::ceil(nc / G);
-      cost = walk((double)units * G, cpg, 1, 1.0) * 1.1 + walk((double)units * G, cpg, 2, 1.3) +
-             0.25 * G;
+      cost = walk((double)units * (G - 1), cpg, 1, 1.0) * 1.1 +
+             walk((double)units * G, cpg, 2, 1.3) + 0.25 * G;
       cost = std::max(cost, 2.1 * std::ceil(chain / G));
     }
     if (cost < best_cost * 0.999) {

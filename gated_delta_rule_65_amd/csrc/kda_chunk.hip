@@ -782,7 +782,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
 //         zero; the first nvb column blocks are the 128 value columns (with
 //         u: the group's partial state B_g), the next nvb blocks are 128
 //         transfer columns started at the identity with u = 0 (the group
-//         transfer P_g = prod_c (diag(d_c) - kg_c^T w_c)).  No outputs.
+//         transfer P_g = prod_c (diag(d_c) - kg_c^T w_c)).  No outputs.  The
+//         last group is left out: no later group starts from its transfer.
 // MODE 2: group pass two.  Group g is walked from its composed start state
 //         H_in(g); outputs for its tokens, the final state from the group
 //         that holds the sequence's last chunk.
@@ -818,8 +819,10 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
   const int id = blockIdx.x;
   const int blk = id / (8 * ncb), rem = id - blk * 8 * ncb;
   const int cb = rem >> 3, ug = blk * 8 + (rem & 7);
-  if (ug >= a.units * G) return;
-  const int unit = ug / G, g = ug - unit * G;
+  // pass one leaves out the last group: compose never reads its transfer
+  const int GW = MODE == 1 ? G - 1 : G;  // groups this launch walks
+  if (ug >= a.units * GW) return;
+  const int unit = ug / GW, g = ug - unit * GW;
   const int hv = a.hv;
   const int n = unit / hv, h = unit - n * hv;
   const bool tcols = MODE == 1 && cb >= a.nvb;  // transfer columns of pass one
@@ -1368,11 +1371,12 @@ static void launch_walk(const ChunkLaunch& L, const WalkArgs<E>& wa) {
     mark(L, 6);
     return;
   }
-  const int ug = units * G;
-  hipLaunchKernelGGL((walk_kernel<E, NW, 1, LW>), dim3((unsigned)(((ug + 7) / 8) * 8 * 2 * nvb)),
+  const int ug = units * G, ug1 = units * (G - 1);  // pass one: all groups but the last
+  hipLaunchKernelGGL((walk_kernel<E, NW, 1, LW>), dim3((unsigned)(((ug1 + 7) / 8) * 8 * 2 * nvb)),
                      block, 0, st, wa);
   mark(L, 4);
-  hipLaunchKernelGGL((compose_kernel<E>), dim3((unsigned)(units * 8)), dim3(64), 0, st, wa);
+  hipLaunchKernelGGL((compose_kernel<E>), dim3((unsigned)(((units + 7) / 8) * 64)), dim3(64), 0,
+                     st, wa);
   mark(L, 5);
   hipLaunchKernelGGL((walk_kernel<E, NW, 2, LW>), dim3((unsigned)(((ug + 7) / 8) * 8 * nvb)),
                      block, 0, st, wa);

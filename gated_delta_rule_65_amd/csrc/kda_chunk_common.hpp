@@ -314,7 +314,11 @@ __device__ __forceinline__ float* scan_plane(float* scan, int g, int n, int h, i
 // composition close to fp32 however many groups there are.
 template <typename E>
 __global__ __launch_bounds__(64) void compose_kernel(const WalkArgs<E> a) {
-  const int unit = blockIdx.x >> 3, rb = blockIdx.x & 7;
+  // The 8 column-block workgroups of a (sequence, head) get ids with equal
+  // id % 8, so they run on one XCD and read each group's transfer through its
+  // L2 (blocks of 64 ids hold 8 units).
+  const int id = blockIdx.x;
+  const int unit = (id >> 6) * 8 + (id & 7), rb = (id >> 3) & 7;
   if (unit >= a.units) return;
   const int hv = a.hv;
   const int n = unit / hv, h = unit - n * hv;

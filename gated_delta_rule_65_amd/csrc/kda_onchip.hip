@@ -210,8 +210,10 @@ onchip_kernel(
   // one query/key head among them) share an XCD and its L2.
   const int G = MODE == 0 ? 1 : a.groups;
   const int chain = (int)(blockIdx.x & 7) * a.per_xcd + (int)(blockIdx.x >> 3);
-  if (chain >= a.units * G) return;
-  const int unit = chain / G, g = chain - unit * G;
+  // pass one leaves out the last group: compose never reads its transfer
+  const int GW = MODE == 1 ? G - 1 : G;  // groups this launch walks
+  if (chain >= a.units * GW) return;
+  const int unit = chain / GW, g = chain - unit * GW;
   const int hv = a.hv;
   const int n = unit / hv, h = unit - n * hv;
   const int hq = h / (hv / a.hqk);
@@ -858,7 +860,10 @@ static void launch_onchip_t(const ChunkLaunch& L, const OnchipArgs& oa) {
     mark_ev(L, 6);
     return;
   }
-  hipLaunchKernelGGL((onchip_kernel<1, GATE>), grid, block, 0, st, a);
+  OnchipArgs a1 = a;  // pass one: all groups but the last
+  a1.per_xcd = (oa.units * (G - 1) + 7) / 8;
+  hipLaunchKernelGGL((onchip_kernel<1, GATE>), dim3((unsigned)(8 * a1.per_xcd)), block, 0, st,
+                     a1);
   mark_ev(L, 4);
   WalkArgs<bf16> wa;
   memset(&wa, 0, sizeof(wa));
@@ -867,7 +872,8 @@ static void launch_onchip_t(const ChunkLaunch& L, const OnchipArgs& oa) {
   wa.cache = L.cache; wa.slot_stride = L.slot_stride; wa.slots = L.slots;
   wa.has_init = L.has_init; wa.num_slots = L.num_slots; wa.units = a.units;
   wa.max_chunks = a.max_chunks; wa.groups = G; wa.scan = L.scan;
-  hipLaunchKernelGGL((compose_kernel<bf16>), dim3((unsigned)(a.units * 8)), dim3(64), 0, st, wa);
+  hipLaunchKernelGGL((compose_kernel<bf16>), dim3((unsigned)(((a.units + 7) / 8) * 64)), dim3(64),
+                     0, st, wa);
   mark_ev(L, 5);
   hipLaunchKernelGGL((onchip_kernel<2, GATE>), grid, block, 0, st, a);
   mark_ev(L, 6);

@@ -261,7 +261,8 @@ kda_status kda_chunk_fwd_noalloc(const kda_chunk_args *a);
  *   scan           fp32 [G, N, Hv, 3, 128, 128] when the walk runs as a
  *                  group scan (G = groups > 1), else empty: per chunk group,
  *                  the transfer (plane 0, [k][j]), the partial state from zero
- *                  and the group's start state (planes 1 and 2, [v][k])
+ *                  and the group's start state (planes 1 and 2, [v][k]); the
+ *                  last group's planes 0 and 1 are not written (unused)
  * groups and walk_waves report the launch plan that kda_chunk_fwd takes for
  * these arguments (the chosen values when the arguments leave them at 0).
  * (P): the last axis is stored in MFMA fragment order: inside each block of
