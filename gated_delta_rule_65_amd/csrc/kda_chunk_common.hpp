@@ -313,7 +313,8 @@ __device__ __forceinline__ float* scan_plane(float* scan, int g, int n, int h, i
 // operands split into hi + lo bf16 pairs (three products), keeping the
 // composition close to fp32 however many groups there are.
 template <typename E>
-__global__ __launch_bounds__(64) void compose_kernel(const WalkArgs<E> a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void compose_kernel(
+    const WalkArgs<E> a) {
   // The 8 column-block workgroups of a (sequence, head) get ids with equal
   // id % 8, so they run on one XCD and read each group's transfer through its
   // L2 (blocks of 64 ids hold 8 units).
@@ -360,6 +361,19 @@ __global__ __launch_bounds__(64) void compose_kernel(const WalkArgs<E> a) {
     if (min(nch_all, g * cpg) >= min(nch_all, g * cpg + cpg)) continue;
     const float* P = scan_plane(a.scan, g, n, h, a.N, hv, 0);
     const float* Bp = scan_plane(a.scan, g, n, h, a.N, hv, 1);
+    // every load of the step first (one memory round trip per group, not one
+    // per row block; the wave has the registers), then the products
+    float4 pr[8][4][2], b4[8];
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      const float* prow = P + (size_t)(16 * kb + l16) * D;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        pr[kb][s][0] = *reinterpret_cast<const float4*>(prow + 32 * s + 4 * gq);
+        pr[kb][s][1] = *reinterpret_cast<const float4*>(prow + 32 * s + 16 + 4 * gq);
+      }
+      b4[kb] = *reinterpret_cast<const float4*>(Bp + (size_t)vcol * D + 16 * kb + 4 * gq);
+    }
     FragS Hf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -369,12 +383,13 @@ __global__ __launch_bounds__(64) void compose_kernel(const WalkArgs<E> a) {
     }
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
-      const float4 b4 = *reinterpret_cast<const float4*>(Bp + (size_t)vcol * D + 16 * kb + 4 * gq);
-      f32x4_t acc = {b4.x, b4.y, b4.z, b4.w};
-      const float* prow = P + (size_t)(16 * kb + l16) * D;
+      f32x4_t acc = {b4[kb].x, b4[kb].y, b4[kb].z, b4[kb].w};
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        mma(acc, frag_from(prow + 32 * s + 4 * gq, prow + 32 * s + 16 + 4 * gq), Hf[s]);
+      for (int s = 0; s < 4; ++s) {
+        const float x[8] = {pr[kb][s][0].x, pr[kb][s][0].y, pr[kb][s][0].z, pr[kb][s][0].w,
+                            pr[kb][s][1].x, pr[kb][s][1].y, pr[kb][s][1].z, pr[kb][s][1].w};
+        mma(acc, make_frag<true>(x), Hf[s]);
+      }
       S[kb] = acc;
     }
   }
