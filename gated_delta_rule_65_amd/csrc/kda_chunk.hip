@@ -1117,6 +1117,13 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
     if (LW == 0) __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA of chunk jc has landed
     lds_barrier();  // ... and every other wave's (loaders: their LDS writes)
     const bool more = LW == 0 && STAGES == 2 && jc + 1 < jc1;
+    // Eight-wave walks (one workgroup per chain, HBM-bound): the whole next
+    // chunk's DMA goes out at the top of the step, for the most lead time.
+    constexpr bool EARLY = NW == 8 && STAGES == 2 && LW == 0;
+    if (EARLY && more) {
+      issue_wq(jc + 1, nxt);
+      issue_rest(jc + 1, nxt);
+    }
     const uint4* tW = cur + OFF_W;
     const uint4* tQ = cur + OFF_Q;
     const uint4* tA = cur + OFF_A;
@@ -1171,7 +1178,7 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         if (s < 3) load_k(s + 1, (s + 1) & 1);
-        if (more) {
+        if (more && !EARLY) {
 #pragma unroll
           for (int m = 0; m < (NDMA + 3) / 4; ++m) {
             const int mm = ((NDMA + 3) / 4) * s + m;
@@ -1207,7 +1214,7 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
           if (OUT) mma(O[ta], Hf[s], frag_f32<P128>(tQ, 16 * ta + l16, 4 * s + gq));
         }
     }
-    if (more) issue_rest(jc + 1, nxt);
+    if (more && !EARLY) issue_rest(jc + 1, nxt);
     // U = u - w S  (C layout: col v, rows t = 16 ta + 4 gq + r)
     Frag<SPLIT> Uf[2];
 #pragma unroll
