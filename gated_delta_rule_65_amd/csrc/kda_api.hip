@@ -232,11 +232,22 @@ WalkPlan plan_walk(const kda_chunk_args* a) {
         cost = std::max(std::ceil((double)(units * nvb) / cap) * nc, chain) * step_cost[wi];
       } else {
         const double cpg = std::ceil(nc / G);
-        // pass one walks every group but the last
-        const double r1 = std::ceil((double)(units * (G - 1) * 2 * nvb) / cap);
         const double r2 = std::ceil((double)(units * G * nvb) / cap);
+        // pass one walks every group but the last.  bf16: one sixteen-wave
+        // workgroup per group (both column sets; its step measured at 0.5 -
+        // 0.8 of an eight-wave pass-two step); fp32: value and transfer
+        // workgroups of the pass-two width.
+        // Compose takes about four eight-wave steps per group with bf16.
+        double p1, comp;
+        if (a->dtype == KDA_BF16) {
+          p1 = 0.8 * std::ceil((double)(units * (G - 1)) / cap) * step_cost[2] / step_cost[wi];
+          comp = 4.0 * G;
+        } else {
+          p1 = 0.8 * std::ceil((double)(units * (G - 1) * 2 * nvb) / cap);
+          comp = G;
+        }
         // the group chains (pass one and pass two) have a floor as well
-        cost = std::max((0.8 * r1 + r2) * cpg, 1.8 * std::ceil(chain / G)) * step_cost[wi] + G;
+        cost = std::max((p1 + r2) * cpg, 1.8 * std::ceil(chain / G)) * step_cost[wi] + comp;
       }
       if (cost < best_cost * 0.999) {
         best_cost = cost;

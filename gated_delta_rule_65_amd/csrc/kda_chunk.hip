@@ -802,10 +802,20 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
   constexpr bool OUT = MODE != 1;
   constexpr int NT = 64 * NW;
   constexpr int BV = 16 * NW;
+  // FUSED1: pass one with the value columns (waves 0-7) and the transfer
+  // columns (waves 8-15) of a group in one sixteen-wave workgroup, so the
+  // group's K-side tiles are fetched once (two workgroups fetch them twice,
+  // and drift too far apart for L2 to catch the second read).
+  constexpr bool FUSED1 = MODE == 1 && NW == 16;
+  static_assert(NW != 16 || (MODE == 1 && LW == 0 && !std::is_same<E, float>::value),
+                "sixteen waves: bf16 pass one only");
+  constexpr int BVU = FUSED1 ? D : BV;  // u_t rows in a stage (value columns)
   constexpr int EPP = 16 / (int)sizeof(E);  // elements per 16-byte piece
   constexpr int P128 = D / EPP, P64 = C / EPP;
-  constexpr int OFF_W = 0, OFF_Q = OFF_W + C * P128, OFF_A = OFF_Q + C * P128;
-  constexpr int OFF_K = OFF_A + C * P64, OFF_U = OFF_K + D * P64, OFF_D = OFF_U + BV * P64;
+  // (qg and aqk only feed the outputs: pass one's stages leave them out)
+  constexpr int OFF_W = 0, OFF_Q = OFF_W + C * P128, OFF_A = OFF_Q + (OUT ? C * P128 : 0);
+  constexpr int OFF_K = OFF_A + (OUT ? C * P64 : 0), OFF_U = OFF_K + D * P64;
+  constexpr int OFF_D = OFF_U + BVU * P64;
   constexpr int STAGE = OFF_D + 64;
   // two distinct arrays (not one indexed ring) so that the compiler can tell
   // the stage being filled from the stage being read
@@ -815,7 +825,7 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
   // The column blocks of one (sequence, head, group) get ids with equal
   // id % 8, so they land on one XCD and share its L2 for the K-side tiles.
   const int G = MODE == 0 ? 1 : a.groups;
-  const int ncb = MODE == 1 ? 2 * a.nvb : a.nvb;
+  const int ncb = MODE == 1 ? (FUSED1 ? 1 : 2 * a.nvb) : a.nvb;
   const int id = blockIdx.x;
   const int blk = id / (8 * ncb), rem = id - blk * 8 * ncb;
   const int cb = rem >> 3, ug = blk * 8 + (rem & 7);
@@ -825,17 +835,18 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
   const int unit = ug / GW, g = ug - unit * GW;
   const int hv = a.hv;
   const int n = unit / hv, h = unit - n * hv;
-  const bool tcols = MODE == 1 && cb >= a.nvb;  // transfer columns of pass one
-  const int vb = tcols ? cb - a.nvb : cb;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // transfer columns of pass one (per wave in the sixteen-wave form)
+  const bool tcols = FUSED1 ? wave >= 8 : (MODE == 1 && cb >= a.nvb);
+  const int vb = FUSED1 ? 0 : (tcols ? cb - a.nvb : cb);
   static_assert(LW == 0 || STAGES == 2, "loader waves serve the two-stage ring");
   const bool loader = LW > 0 && wave >= NW;  // wave-uniform role
   constexpr int DW = LW > 0 ? LW : NW;         // waves that issue the DMA
   const int dwave = LW > 0 ? wave - NW : wave;
   const int l16 = lane & 15, gq = lane >> 4;
   const int v0 = vb * BV;                  // first column of the block
-  const int vl = 16 * wave + l16;          // this lane's C-tile column inside the block
+  const int vl = 16 * (FUSED1 ? wave & 7 : wave) + l16;  // this lane's column in the block
   const int vcol = v0 + vl;
   const SeqSpan sp = seq_span(a.cu, n, a.dense_len, a.T);
 
@@ -933,7 +944,7 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
     const size_t rowb = (size_t)hv * D * sizeof(E);
     dma_tile<C, P128, DW, true>(base + OFF_W, a.w + ((size_t)t0 * hv + h) * D, rowb, L, zero,
                                 dwave, lane);
-    if (OUT)
+    if constexpr (OUT)
       dma_tile<C, P128, DW, true>(base + OFF_Q, a.qg + ((size_t)t0 * hv + h) * D, rowb, L, zero,
                                   dwave, lane);
   };
@@ -941,14 +952,14 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
     const int c = c_first + jc;
     const int t0 = sp.bos + C * jc;
     const int L = min(C, sp.eos - t0);
-    if (OUT)
+    if constexpr (OUT)
       dma_tile<C, P64, DW, true>(base + OFF_A, a.aqk + ((size_t)t0 * hv + h) * C,
                                  (size_t)hv * C * sizeof(E), L, zero, dwave, lane);
     dma_tile<D, P64, DW, false>(base + OFF_K, a.kg_t + ((size_t)c * hv + h) * D * C,
                                 C * sizeof(E), D, zero, dwave, lane);
-    if (!tcols)
-      dma_tile<BV, P64, DW, false>(base + OFF_U, a.u_t + (((size_t)c * hv + h) * D + v0) * C,
-                                   C * sizeof(E), BV, zero, dwave, lane);
+    if (FUSED1 || !tcols)
+      dma_tile<BVU, P64, DW, false>(base + OFF_U, a.u_t + (((size_t)c * hv + h) * D + v0) * C,
+                                    C * sizeof(E), BVU, zero, dwave, lane);
     if (dwave == DW - 1) {
       // decay: 32 pieces, lanes 32..63 fill the pad from the zero page
       const char* gp = lane < 32 ? (const char*)(a.decay + ((size_t)c * hv + h) * D) + 16 * lane
@@ -1119,7 +1130,7 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
     const bool more = LW == 0 && STAGES == 2 && jc + 1 < jc1;
     // Eight-wave walks (one workgroup per chain, HBM-bound): the whole next
     // chunk's DMA goes out at the top of the step, for the most lead time.
-    constexpr bool EARLY = NW == 8 && STAGES == 2 && LW == 0;
+    constexpr bool EARLY = NW >= 8 && STAGES == 2 && LW == 0;
     if (EARLY && more) {
       issue_wq(jc + 1, nxt);
       issue_rest(jc + 1, nxt);
@@ -1232,6 +1243,21 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
       // are read up front (A_qk is lower: t < 32 needs i < 32 only); the
       // schedule is pinned so the reads go out together and the products
       // follow as they land, instead of each product waiting on its own read.
+      if constexpr (FUSED1) {
+        // sixteen waves (128 VGPRs): the fragments stream in per row block
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+          const FragB k0 = frag_bf16<P64>(tK, 16 * kb + l16, gq);
+          const FragB k1 = frag_bf16<P64>(tK, 16 * kb + l16, 4 + gq);
+          const float4 d4 = *reinterpret_cast<const float4*>(sD + 16 * kb + 4 * gq);
+          S[kb][0] *= d4.x;
+          S[kb][1] *= d4.y;
+          S[kb][2] *= d4.z;
+          S[kb][3] *= d4.w;
+          mma(S[kb], k0, Uf[0]);
+          mma(S[kb], k1, Uf[1]);
+        }
+      } else {
       FragB fa[4][2], fk[8][2];
       float4 dk[8];
       if (OUT) {
@@ -1272,6 +1298,7 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
       for (int kb = 0; kb < 8; ++kb) {
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // decay
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // kg^T U
+      }
       }
     } else {
       if (OUT) {
@@ -1379,8 +1406,16 @@ static void launch_walk(const ChunkLaunch& L, const WalkArgs<E>& wa) {
     return;
   }
   const int ug = units * G, ug1 = units * (G - 1);  // pass one: all groups but the last
-  hipLaunchKernelGGL((walk_kernel<E, NW, 1, LW>), dim3((unsigned)(((ug1 + 7) / 8) * 8 * 2 * nvb)),
-                     block, 0, st, wa);
+  if constexpr (!std::is_same<E, float>::value) {
+    // one sixteen-wave workgroup per group: value and transfer columns together
+    WalkArgs<E> w1 = wa;
+    w1.nvb = 1;
+    hipLaunchKernelGGL((walk_kernel<E, 16, 1, 0>), dim3((unsigned)(((ug1 + 7) / 8) * 8)),
+                       dim3(1024), 0, st, w1);
+  } else {
+    hipLaunchKernelGGL((walk_kernel<E, NW, 1, LW>),
+                       dim3((unsigned)(((ug1 + 7) / 8) * 8 * 2 * nvb)), block, 0, st, wa);
+  }
   mark(L, 4);
   hipLaunchKernelGGL((compose_kernel<E>), dim3((unsigned)(((units + 7) / 8) * 64)), dim3(64), 0,
                      st, wa);
