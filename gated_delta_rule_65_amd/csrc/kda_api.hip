@@ -6,6 +6,7 @@
 #include <cmath>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <initializer_list>
@@ -407,6 +408,51 @@ KDA_API kda_status kda_chunk_ws_layout(const kda_chunk_args* a, kda_ws_layout* l
 
 namespace {
 
+// KDA_LOG=1 in the environment: one line per chunked-forward call on stderr
+// with the launch plan (path, chunk groups, walk width and grids, workspace).
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = getenv("KDA_LOG");
+    return e && e[0] && strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+void log_plan(const char* entry, const kda_chunk_args* a, const kda_ws_layout& W) {
+  if (!log_enabled()) return;
+  static const char* const names[4] = {"auto", "staged", "fused", "onchip"};
+  const int32_t p = path_of(a);
+  const long long units = (long long)a->num_seqs * a->hv;
+  const int G = W.groups, nw = W.walk_waves;
+  if (p == KDA_PATH_ONCHIP) {
+    fprintf(stderr,
+            "kda: %s path=onchip seqs=%d hv=%d tokens=%lld chunks=%lld groups=%d "
+            "chains=%lld (4-wave workgroups) workspace=%zu B\n",
+            entry, a->num_seqs, a->hv, (long long)a->total_tokens, (long long)W.max_chunks, G,
+            units * G, W.total);
+    return;
+  }
+  // Column blocks per (sequence, head) and walk workgroups per pass: 16
+  // state columns per compute wave; bf16 pass one walks both column sets in
+  // one sixteen-wave workgroup.
+  // Grids round the (sequence, head[, group]) count up to a multiple of 8.
+  auto r8 = [](long long x) { return (x + 7) / 8 * 8; };
+  const int bv = 16 * nw, blocks = KDA_HEAD_DIM / bv;
+  const long long walk_wgs = r8(units * G) * blocks;
+  char scan[160] = "";
+  if (G > 1) {
+    const bool bf = a->dtype == KDA_BF16;
+    const long long p1 = bf ? r8(units * (G - 1)) : r8(units * (G - 1)) * 2 * blocks;
+    snprintf(scan, sizeof scan, " pass_one_wgs=%lld (%d waves) compose_wgs=%lld", p1,
+             bf ? 16 : nw, r8(units) * 8);
+  }
+  fprintf(stderr,
+          "kda: %s path=%s seqs=%d hv=%d tokens=%lld chunks=%lld groups=%d walk_waves=%d "
+          "BV=%d walk_wgs=%lld%s wy_wgs=2/CU (persistent) workspace=%zu B\n",
+          entry, names[p], a->num_seqs, a->hv, (long long)a->total_tokens,
+          (long long)W.max_chunks, G, nw, bv, walk_wgs, scan, W.total);
+}
+
 // The chunked forward over an already checked argument set and a workspace
 // of at least W.total bytes.
 kda_status run_chunk(const kda_chunk_args* a, const kda_ws_layout& W, char* ws) {
@@ -498,6 +544,7 @@ KDA_API kda_status kda_chunk_fwd(const kda_chunk_args* a) {
   if (a->workspace_bytes < W.total || (W.total > 0 && a->workspace == nullptr))
     return fail(KDA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", W.total,
                 a->workspace_bytes);
+  log_plan("chunk_fwd", a, W);
   return run_chunk(a, W, (char*)a->workspace);
 }
 
@@ -511,6 +558,7 @@ KDA_API kda_status kda_chunk_fwd_noalloc(const kda_chunk_args* a) {
                 "this call needs %zu bytes of workspace, beyond the %zu-byte static scratch",
                 W.total, SCRATCH_BYTES);
   if (a->num_seqs == 0) return ok();
+  log_plan("chunk_fwd_noalloc", a, W);
   char* ws = nullptr;
   s = scratch_of_current_device(&ws);
   if (s != KDA_OK) return s;

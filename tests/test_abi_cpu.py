@@ -621,3 +621,41 @@ def test_build_rejects_kernels_that_spill():
         "x.hip:9:1: remark:     ScratchSize [bytes/lane]: 12 [-Rpass-analysis=kernel-resource-usage]",
     ])
     assert build._spilling_kernels(remarks) == [("kern_b", 12)]
+
+
+LOG_SCRIPT = r"""
+import ctypes, sys
+sys.path.insert(0, {root!r})
+from gated_delta_rule_65_amd import binding as B
+lib = B.load_library()
+a = B.ChunkArgs()
+a.struct_size = ctypes.sizeof(B.ChunkArgs)
+a.dtype, a.num_seqs, a.total_tokens, a.hqk, a.hv = 1, 0, 0, 2, 4
+a.scale, a.use_qk_l2norm = 128 ** -0.5, 1
+fake = ctypes.c_void_p(0x1000)
+for f in ("q", "k", "v", "g", "beta", "out"):
+    setattr(a, f, fake)
+n = ctypes.c_size_t(0)
+assert lib.kda_chunk_fwd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0
+a.workspace, a.workspace_bytes = fake, n.value
+sys.exit(lib.kda_chunk_fwd(ctypes.byref(a)))   # empty batch: nothing is queued
+"""
+
+
+@pytest.mark.parametrize("value", ["1", None])
+def test_kda_log_prints_the_launch_plan(value):
+    env = dict(os.environ)
+    env.pop("KDA_LOG", None)
+    if value is not None:
+        env["KDA_LOG"] = value
+    r = subprocess.run(["python", "-c", LOG_SCRIPT.format(root=ROOT)], env=env,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    lines = [l for l in r.stderr.splitlines() if l.startswith("kda: ")]
+    if value is None:
+        assert lines == []
+    else:
+        assert len(lines) == 1, r.stderr
+        for field in ("chunk_fwd", "path=fused", "groups=1", "walk_waves=", "BV=",
+                      "walk_wgs=", "workspace="):
+            assert field in lines[0], lines[0]
