@@ -349,6 +349,26 @@ __global__ __launch_bounds__(256) void prep_kernel(const I* __restrict__ q,
 //
 // With PREP the kernel also writes the prep outputs (qg, kg_t, decay), so the
 // inputs are read from HBM once for the whole intra-chunk stage.
+// One token's qg row from the 16 lanes of a row group (lane j: channels
+// 8 j .. 8 j + 7), stored in fragment order.  A lane's channels fall on two
+// runs of 4 packed positions; lanes j and j ^ 2 (one DPP quad) swap a run so
+// that each lane holds 8 consecutive positions, and the row leaves as sixteen
+// 16-byte pieces that fill whole 64-byte segments.
+__device__ __forceinline__ void qg_row_store(bf16* row, const float (&x)[8], int j) {
+  const uint4 u = __builtin_bit_cast(uint4, pack8(x));
+  const bool up = (j & 2) != 0;  // lanes 2, 3 of the quad keep their second run
+  const uint32_t s0 = up ? u.x : u.z, s1 = up ? u.y : u.w;
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s0, 0x4E, 0xF, 0xF, true);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s1, 0x4E, 0xF, 0xF, true);
+  const uint4 o = up ? make_uint4(r0, r1, u.z, u.w) : make_uint4(u.x, u.y, r0, r1);
+  *reinterpret_cast<uint4*>(row + 32 * (j >> 2) + 16 * (j & 1) + 8 * ((j >> 1) & 1)) = o;
+}
+__device__ __forceinline__ void qg_row_store(float* row, const float (&x)[8], int j) {
+  float* dst = row + 32 * (j >> 2);
+  store4(dst + pack32(8 * (j & 3)), x[0], x[1], x[2], x[3]);
+  store4(dst + pack32(8 * (j & 3) + 4), x[4], x[5], x[6], x[7]);
+}
+
 template <typename E, bool PREP, bool GATE, typename I>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void wy_kernel(
     const I* __restrict__ q, const I* __restrict__ k, const I* __restrict__ v,
@@ -536,23 +556,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
       store8(QL + t * ST + 8 * j, xq);
       store8(KL + t * ST + 8 * j, xl);
       store8(KR + t * ST + 8 * j, xr);
-      if (PREP && t < L) {
-        // qg in fragment order: channels 8 j .. 8 j + 3 and 8 j + 4 .. 8 j + 7
-        // are two runs of 4 consecutive packed positions
-        E* dst = qg + ((size_t)(p.t0 + t) * hv + h) * D + 32 * (j >> 2);
-        store4(dst + pack32(8 * (j & 3)), xg[0], xg[1], xg[2], xg[3]);
-        store4(dst + pack32(8 * (j & 3) + 4), xg[4], xg[5], xg[6], xg[7]);
-      }
+      // (the row group's 16 lanes share t, so a quad is uniformly in or out)
+      if (PREP && t < L) qg_row_store(qg + ((size_t)(p.t0 + t) * hv + h) * D, xg, j);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) col4(kgp[e], G[0][e], G[1][e], G[2][e], G[3][e]);
     if (PREP) {
       // kg_t[c][h][key channel][packed t]: this thread's 4 consecutive tokens
       // are 4 consecutive packed positions (zero past L)
-      E* kdst = kg_t + ((size_t)c * hv + h) * D * C + packed_index(4 * rg);
+      if constexpr (!SPLIT) {
+        // staged in R3 (A_kk's region, free until phase 1) as [128][64]
+        // with 16-byte pieces XOR-swizzled by (row >> 3) & 7, and stored
+        // from there in whole 16-byte pieces after the barrier
+        const int pos = packed_index(4 * rg);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        store4(kdst + (size_t)(8 * j + e) * C, kx[0][e], kx[1][e], kx[2][e], kx[3][e]);
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * j + e;
+          col4(*reinterpret_cast<bf16x4_t*>(smem + R3 + r * 128 +
+                                            (((pos >> 3) ^ (r >> 3 & 7)) << 4) + 2 * (pos & 7)),
+               kx[0][e], kx[1][e], kx[2][e], kx[3][e]);
+        }
+      } else {
+        E* kdst = kg_t + ((size_t)c * hv + h) * D * C + packed_index(4 * rg);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          store4(kdst + (size_t)(8 * j + e) * C, kx[0][e], kx[1][e], kx[2][e], kx[3][e]);
+      }
       if (tid < 16) {
         float dv[8];
 #pragma unroll
@@ -571,12 +600,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   const int nitem = s_next;
   ChunkPos np;
   const bool nok = nitem < items && locate_chunk(nitem / hv, table, np);
+  if constexpr (PREP && !SPLIT) {
+    // the item's kg_t (16 KB, contiguous in memory) leaves the staging tile
+    // in whole rows: piece tid + 256 m is row (tid + 256 m) / 8, piece tid % 8
+    E* kdst = kg_t + ((size_t)c * hv + h) * D * C;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int r = (tid >> 3) + 32 * m, pc = tid & 7;
+      *reinterpret_cast<uint4*>(kdst + (size_t)r * C + 8 * pc) =
+          *reinterpret_cast<const uint4*>(smem + R3 + r * 128 + ((pc ^ (r >> 3 & 7)) << 4));
+    }
+    lds_barrier();  // R3 becomes A_kk
+  }
 
   // ---- phase 1: couplings, transposed tiles (rows i from KR, columns t from L).
-  //      Each wave takes a fixed set of (row block a, column block b) pairs
-  //      and writes the strictly upper blocks of A_qk as zeros.
+  //      Each wave takes a fixed set of units (row block a, column blocks
+  //      2 m and 2 m + 1): a lane's A_qk values of the two blocks are 8
+  //      consecutive packed positions, stored as one 16-byte piece; blocks
+  //      above the diagonal are stored as zeros.
   {
-    auto pair = [&](const int a, const int b) {
+    auto pair = [&](const int a, const int b, float (&aq)[4]) {
       const int t = 16 * a + l16;
       const int i = 16 * b + l16;
       const float* eab = sE + (a * (a - 1) / 2 + b) * D;
@@ -601,31 +644,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
         mma(accq, R, Lq);
       }
       const int i0 = 16 * b + 4 * gq;
-      float ak[4], aq[4];
+      float ak[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         ak[r] = (i0 + r < t) ? acck[r] * sB[t] : 0.f;
         aq[r] = (i0 + r <= t) ? accq[r] : 0.f;
       }
       store4(sA + t * SA + i0, ak[0], ak[1], ak[2], ak[3]);
-      if (t < L)
-        store4(aqk + ((size_t)(p.t0 + t) * hv + h) * C + packed_index(i0), aq[0], aq[1], aq[2],
-               aq[3]);
     };
-    auto zero = [&](const int a, const int b) {
+    auto unit = [&](const int a, const int m) {
+      float aq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      float lo[4], hi[4];
+      if (2 * m <= a) {
+        pair(a, 2 * m, lo);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) aq[r] = lo[r];
+      }
+      if (2 * m + 1 <= a) {
+        pair(a, 2 * m + 1, hi);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) aq[4 + r] = hi[r];
+      }
       const int t = 16 * a + l16;
-      if (t < L)
-        store4(aqk + ((size_t)(p.t0 + t) * hv + h) * C + packed_index(16 * b + 4 * gq), 0.f,
-               0.f, 0.f, 0.f);
+      if (t < L) store8(aqk + ((size_t)(p.t0 + t) * hv + h) * C + 32 * m + 8 * gq, aq);
     };
+    // ten block products over the four waves (3 / 2 / 3 / 2)
     if (wv == 0) {
-      pair(3, 3); pair(3, 2); pair(3, 1);
+      unit(3, 1); unit(0, 0);
     } else if (wv == 1) {
-      pair(3, 0); pair(2, 2); pair(2, 1);
+      unit(3, 0); unit(1, 1);
     } else if (wv == 2) {
-      pair(2, 0); pair(1, 1); zero(0, 1); zero(0, 2); zero(0, 3);
+      unit(2, 0); unit(2, 1);
     } else {
-      pair(1, 0); pair(0, 0); zero(1, 2); zero(1, 3); zero(2, 3);
+      unit(1, 0); unit(0, 1);
     }
   }
   // the next item's raw rows load during phases 2 and 3.  Without a next
