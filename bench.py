@@ -572,7 +572,9 @@ def kernel_rows(case, per):
         "prep folded in (reads q, k, v, g, beta; writes all intermediates)"
         if fused_prep else None)
     if groups > 1:
-        row("pass_one", "walk_kernel<1>", "pass_one", per["walk"],
+        bf16 = str(case.b.q.dtype) == "torch.bfloat16"
+        row("pass_one", "pass_one_kernel" if bf16 else "walk_kernel<1>", "pass_one",
+            per["walk"],
             f"group scan (G = {groups}) pass one: each group walked from zero and from the "
             "identity (value and transfer columns), no outputs")
         row("compose", "compose_kernel", "compose", per["compose"])

@@ -234,10 +234,10 @@ WalkPlan plan_walk(const kda_chunk_args* a) {
       } else {
         const double cpg = std::ceil(nc / G);
         const double r2 = std::ceil((double)(units * G * nvb) / cap);
-        // pass one walks every group but the last.  bf16: one sixteen-wave
-        // workgroup per group (both column sets; its step measured at 0.5 -
-        // 0.8 of an eight-wave pass-two step); fp32: value and transfer
-        // workgroups of the pass-two width.
+        // pass one walks every group but the last.  bf16: one eight-wave
+        // workgroup per group (both column sets, 32 columns a wave; its step
+        // measured at 0.5 - 0.8 of an eight-wave pass-two step); fp32: value
+        // and transfer workgroups of the pass-two width.
         // Compose takes about four eight-wave steps per group with bf16.
         double p1, comp;
         if (a->dtype == KDA_BF16) {
@@ -434,17 +434,17 @@ void log_plan(const char* entry, const kda_chunk_args* a, const kda_ws_layout& W
   }
   // Column blocks per (sequence, head) and walk workgroups per pass: 16
   // state columns per compute wave; bf16 pass one walks both column sets in
-  // one sixteen-wave workgroup.
-  // Grids round the (sequence, head[, group]) count up to a multiple of 8.
+  // one eight-wave workgroup per group.  Other grids round the (sequence,
+  // head[, group]) count up to a multiple of 8.
   auto r8 = [](long long x) { return (x + 7) / 8 * 8; };
   const int bv = 16 * nw, blocks = KDA_HEAD_DIM / bv;
   const long long walk_wgs = r8(units * G) * blocks;
   char scan[160] = "";
   if (G > 1) {
     const bool bf = a->dtype == KDA_BF16;
-    const long long p1 = bf ? r8(units * (G - 1)) : r8(units * (G - 1)) * 2 * blocks;
+    const long long p1 = bf ? units * (G - 1) : r8(units * (G - 1)) * 2 * blocks;
     snprintf(scan, sizeof scan, " pass_one_wgs=%lld (%d waves) compose_wgs=%lld", p1,
-             bf ? 16 : nw, r8(units) * 8);
+             bf ? 8 : nw, r8(units) * 8);
   }
   fprintf(stderr,
           "kda: %s path=%s seqs=%d hv=%d tokens=%lld chunks=%lld groups=%d walk_waves=%d "

@@ -853,20 +853,12 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
   constexpr bool OUT = MODE != 1;
   constexpr int NT = 64 * NW;
   constexpr int BV = 16 * NW;
-  // FUSED1: pass one with the value columns (waves 0-7) and the transfer
-  // columns (waves 8-15) of a group in one sixteen-wave workgroup, so the
-  // group's K-side tiles are fetched once (two workgroups fetch them twice,
-  // and drift too far apart for L2 to catch the second read).
-  constexpr bool FUSED1 = MODE == 1 && NW == 16;
-  static_assert(NW != 16 || (MODE == 1 && LW == 0 && !std::is_same<E, float>::value),
-                "sixteen waves: bf16 pass one only");
-  constexpr int BVU = FUSED1 ? D : BV;  // u_t rows in a stage (value columns)
   constexpr int EPP = 16 / (int)sizeof(E);  // elements per 16-byte piece
   constexpr int P128 = D / EPP, P64 = C / EPP;
   // (qg and aqk only feed the outputs: pass one's stages leave them out)
   constexpr int OFF_W = 0, OFF_Q = OFF_W + C * P128, OFF_A = OFF_Q + (OUT ? C * P128 : 0);
   constexpr int OFF_K = OFF_A + (OUT ? C * P64 : 0), OFF_U = OFF_K + D * P64;
-  constexpr int OFF_D = OFF_U + BVU * P64;
+  constexpr int OFF_D = OFF_U + BV * P64;
   constexpr int STAGE = OFF_D + 64;
   // two distinct arrays (not one indexed ring) so that the compiler can tell
   // the stage being filled from the stage being read
@@ -876,7 +868,7 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
   // The column blocks of one (sequence, head, group) get ids with equal
   // id % 8, so they land on one XCD and share its L2 for the K-side tiles.
   const int G = MODE == 0 ? 1 : a.groups;
-  const int ncb = MODE == 1 ? (FUSED1 ? 1 : 2 * a.nvb) : a.nvb;
+  const int ncb = MODE == 1 ? 2 * a.nvb : a.nvb;
   const int id = blockIdx.x;
   const int blk = id / (8 * ncb), rem = id - blk * 8 * ncb;
   const int cb = rem >> 3, ug = blk * 8 + (rem & 7);
@@ -888,16 +880,16 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
   const int n = unit / hv, h = unit - n * hv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // transfer columns of pass one (per wave in the sixteen-wave form)
-  const bool tcols = FUSED1 ? wave >= 8 : (MODE == 1 && cb >= a.nvb);
-  const int vb = FUSED1 ? 0 : (tcols ? cb - a.nvb : cb);
+  // transfer columns of pass one (fp32 operands: a workgroup of their own)
+  const bool tcols = MODE == 1 && cb >= a.nvb;
+  const int vb = tcols ? cb - a.nvb : cb;
   static_assert(LW == 0 || STAGES == 2, "loader waves serve the two-stage ring");
   const bool loader = LW > 0 && wave >= NW;  // wave-uniform role
   constexpr int DW = LW > 0 ? LW : NW;         // waves that issue the DMA
   const int dwave = LW > 0 ? wave - NW : wave;
   const int l16 = lane & 15, gq = lane >> 4;
   const int v0 = vb * BV;                  // first column of the block
-  const int vl = 16 * (FUSED1 ? wave & 7 : wave) + l16;  // this lane's column in the block
+  const int vl = 16 * wave + l16;  // this lane's column in the block
   const int vcol = v0 + vl;
   const SeqSpan sp = seq_span(a.cu, n, a.dense_len, a.T);
 
@@ -1008,9 +1000,9 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
                                  (size_t)hv * C * sizeof(E), L, zero, dwave, lane);
     dma_tile<D, P64, DW, false>(base + OFF_K, a.kg_t + ((size_t)c * hv + h) * D * C,
                                 C * sizeof(E), D, zero, dwave, lane);
-    if (FUSED1 || !tcols)
-      dma_tile<BVU, P64, DW, false>(base + OFF_U, a.u_t + (((size_t)c * hv + h) * D + v0) * C,
-                                    C * sizeof(E), BVU, zero, dwave, lane);
+    if (!tcols)
+      dma_tile<BV, P64, DW, false>(base + OFF_U, a.u_t + (((size_t)c * hv + h) * D + v0) * C,
+                                   C * sizeof(E), BV, zero, dwave, lane);
     if (dwave == DW - 1) {
       // decay: 32 pieces, lanes 32..63 fill the pad from the zero page
       const char* gp = lane < 32 ? (const char*)(a.decay + ((size_t)c * hv + h) * D) + 16 * lane
@@ -1294,21 +1286,6 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
       // are read up front (A_qk is lower: t < 32 needs i < 32 only); the
       // schedule is pinned so the reads go out together and the products
       // follow as they land, instead of each product waiting on its own read.
-      if constexpr (FUSED1) {
-        // sixteen waves (128 VGPRs): the fragments stream in per row block
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-          const FragB k0 = frag_bf16<P64>(tK, 16 * kb + l16, gq);
-          const FragB k1 = frag_bf16<P64>(tK, 16 * kb + l16, 4 + gq);
-          const float4 d4 = *reinterpret_cast<const float4*>(sD + 16 * kb + 4 * gq);
-          S[kb][0] *= d4.x;
-          S[kb][1] *= d4.y;
-          S[kb][2] *= d4.z;
-          S[kb][3] *= d4.w;
-          mma(S[kb], k0, Uf[0]);
-          mma(S[kb], k1, Uf[1]);
-        }
-      } else {
       FragB fa[4][2], fk[8][2];
       float4 dk[8];
       if (OUT) {
@@ -1349,7 +1326,6 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
       for (int kb = 0; kb < 8; ++kb) {
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // decay
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // kg^T U
-      }
       }
     } else {
       if (OUT) {
@@ -1429,6 +1405,189 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
   }
 }
 
+// Group pass one with bf16 operands: one workgroup of eight waves per
+// (group, sequence, head) for every group but the last.  Waves 0-3 carry the
+// 128 value columns (walked from zero with u: the group's partial state B_g),
+// waves 4-7 the 128 transfer columns (from the identity with u = 0: the
+// transfer P_g).  Each wave holds two 16-column blocks of the state, so every
+// w and kg_t fragment it reads from LDS feeds two products: a chunk step
+// reads the shared tiles 8 times from LDS where sixteen waves of one block
+// each read them 16 times, and LDS bandwidth is what bounds this pure read
+// stream.  The K-side tiles (w, kg_t, the 128 u_t rows, decay) arrive by LDS
+// DMA into a two-stage ring; the next chunk's DMA goes out at the top of each
+// step.
+template <typename E>
+__global__ __launch_bounds__(512) void pass_one_kernel(const WalkArgs<E> a) {
+  static_assert(!std::is_same<E, float>::value, "bf16 operands");
+  constexpr int NW = 8;
+  constexpr int EPP = 16 / (int)sizeof(E);
+  constexpr int P128 = D / EPP, P64 = C / EPP;
+  constexpr int OFF_W = 0, OFF_K = OFF_W + C * P128, OFF_U = OFF_K + D * P64;
+  constexpr int OFF_D = OFF_U + D * P64, STAGE = OFF_D + 64;
+  __shared__ uint4 smemA[STAGE];
+  __shared__ uint4 smemB[STAGE];
+
+  const int G = a.groups, GW = G - 1;  // the last group is not walked
+  const int ug = blockIdx.x;
+  if (ug >= a.units * GW) return;
+  const int unit = ug / GW, g = ug - unit * GW;
+  const int hv = a.hv;
+  const int n = unit / hv, h = unit - n * hv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool tcols = wave >= 4;
+  const int l16 = lane & 15, gq = lane >> 4;
+  const int col0 = 32 * (wave & 3) + l16;  // this lane's columns: col0 and col0 + 16
+  const SeqSpan sp = seq_span(a.cu, n, a.dense_len, a.T);
+  const int c_first = a.offs[n];
+  const int nch_all = max(0, min(a.offs[n + 1], a.max_chunks) - c_first);
+  const int cpg = (nch_all + G - 1) / G;
+  const int jc0 = min(nch_all, g * cpg), jc1 = min(nch_all, jc0 + cpg);
+
+  // state slices: S[b][kb][r] = S[k = 16 kb + 4 gq + r][column col0 + 16 b]
+  f32x4_t S[2][8];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      const int k0 = 16 * kb + 4 * gq, col = col0 + 16 * b;
+      S[b][kb] = tcols ? f32x4_t{k0 == col ? 1.f : 0.f, k0 + 1 == col ? 1.f : 0.f,
+                                 k0 + 2 == col ? 1.f : 0.f, k0 + 3 == col ? 1.f : 0.f}
+                       : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+  const uint4* zero = a.zero;
+  auto issue = [&](int jc, uint4* base) {
+    const int c = c_first + jc;
+    const int t0 = sp.bos + C * jc;
+    const int L = min(C, sp.eos - t0);
+    dma_tile<C, P128, NW, true>(base + OFF_W, a.w + ((size_t)t0 * hv + h) * D,
+                                (size_t)hv * D * sizeof(E), L, zero, wave, lane);
+    dma_tile<D, P64, NW, false>(base + OFF_K, a.kg_t + ((size_t)c * hv + h) * D * C,
+                                C * sizeof(E), D, zero, wave, lane);
+    dma_tile<D, P64, NW, false>(base + OFF_U, a.u_t + ((size_t)c * hv + h) * D * C,
+                                C * sizeof(E), D, zero, wave, lane);
+    if (wave == NW - 1) {
+      // decay: 32 pieces, lanes 32..63 fill the pad from the zero page
+      const char* gp = lane < 32 ? (const char*)(a.decay + ((size_t)c * hv + h) * D) + 16 * lane
+                                 : (const char*)zero;
+      __builtin_amdgcn_global_load_lds(gp, (lds_vptr)(base + OFF_D), 16, 0, 0);
+    }
+  };
+  if (jc0 < jc1) issue(jc0, smemA);
+
+  auto body = [&](int jc, const uint4* cur, uint4* nxt) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMA of chunk jc has landed
+    lds_barrier();                  // ... and every other wave's
+    if (jc + 1 < jc1) issue(jc + 1, nxt);
+    const uint4* tW = cur + OFF_W;
+    const uint4* tK = cur + OFF_K;
+    const uint4* tU = cur + OFF_U;
+    const float* sD = reinterpret_cast<const float*>(cur + OFF_D);
+
+    // the state blocks as MFMA operands (K = key channel, perm32 order)
+    FragB Hf[2][4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const float x[8] = {S[b][2 * s][0],     S[b][2 * s][1],     S[b][2 * s][2],
+                            S[b][2 * s][3],     S[b][2 * s + 1][0], S[b][2 * s + 1][1],
+                            S[b][2 * s + 1][2], S[b][2 * s + 1][3]};
+        Hf[b][s] = make_frag<false>(x);
+      }
+    // HW_b = w S_b (rows t, cols v); each w fragment feeds both blocks
+    f32x4_t HW[2][4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int ta = 0; ta < 4; ++ta) HW[b][ta] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    FragB fw[2][4];
+    auto load_w = [&](int s, int buf) {
+#pragma unroll
+      for (int ta = 0; ta < 4; ++ta) fw[buf][ta] = frag_bf16<P128>(tW, 16 * ta + l16, 4 * s + gq);
+    };
+    load_w(0, 0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s < 3) load_w(s + 1, (s + 1) & 1);
+#pragma unroll
+      for (int ta = 0; ta < 4; ++ta) {
+        mma(HW[0][ta], fw[s & 1][ta], Hf[0][s]);
+        mma(HW[1][ta], fw[s & 1][ta], Hf[1][s]);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    // U_b = u_b - HW_b (C layout: col v, rows t = 16 ta + 4 gq + r); u = 0
+    // for the transfer columns
+    FragB Uf[2][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float uv[2][8];
+      if (!tcols) {
+        unit_vals<P64>(tU, col0 + 16 * b, gq, false, uv[0]);
+        unit_vals<P64>(tU, col0 + 16 * b, 4 + gq, false, uv[1]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) uv[0][e] = uv[1][e] = 0.f;
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        float x[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[r] = uv[s2][r] - HW[b][2 * s2][r];
+          x[4 + r] = uv[s2][4 + r] - HW[b][2 * s2 + 1][r];
+        }
+        Uf[b][s2] = make_frag<false>(x);
+      }
+    }
+    // S_b <- diag(d) S_b + kg^T U_b (rows k, cols v, K = t); each kg^T
+    // fragment feeds both blocks
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      const FragB k0 = frag_bf16<P64>(tK, 16 * kb + l16, gq);
+      const FragB k1 = frag_bf16<P64>(tK, 16 * kb + l16, 4 + gq);
+      const float4 d4 = *reinterpret_cast<const float4*>(sD + 16 * kb + 4 * gq);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        S[b][kb][0] *= d4.x;
+        S[b][kb][1] *= d4.y;
+        S[b][kb][2] *= d4.z;
+        S[b][kb][3] *= d4.w;
+        mma(S[b][kb], k0, Uf[b][0]);
+        mma(S[b][kb], k1, Uf[b][1]);
+      }
+    }
+  };
+  for (int jc = jc0; jc < jc1; jc += 2) {
+    body(jc, smemA, smemB);
+    if (jc + 1 < jc1) body(jc + 1, smemB, smemA);
+  }
+  // transfer: P[k][j] row-major (plane 0); partial state: V-first [v][k] (plane 1)
+  float* dst = scan_plane(a.scan, g, n, h, a.N, hv, tcols ? 0 : 1);
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int col = col0 + 16 * b;
+    if (tcols) {
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(size_t)(16 * kb + 4 * gq + r) * D + col] = S[b][kb][r];
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb)
+        plane_store4(dst, (size_t)col * D + 16 * kb + 4 * gq, false, S[b][kb]);
+    }
+  }
+}
+
 static void mark(const ChunkLaunch& L, int i) {
   if (i < L.num_events && L.events[i]) (void)hipEventRecord((hipEvent_t)L.events[i], (hipStream_t)L.stream);
 }
@@ -1458,11 +1617,8 @@ static void launch_walk(const ChunkLaunch& L, const WalkArgs<E>& wa) {
   }
   const int ug = units * G, ug1 = units * (G - 1);  // pass one: all groups but the last
   if constexpr (!std::is_same<E, float>::value) {
-    // one sixteen-wave workgroup per group: value and transfer columns together
-    WalkArgs<E> w1 = wa;
-    w1.nvb = 1;
-    hipLaunchKernelGGL((walk_kernel<E, 16, 1, 0>), dim3((unsigned)(((ug1 + 7) / 8) * 8)),
-                       dim3(1024), 0, st, w1);
+    // one eight-wave workgroup per group: value and transfer columns together
+    hipLaunchKernelGGL((pass_one_kernel<E>), dim3((unsigned)ug1), dim3(512), 0, st, wa);
   } else {
     hipLaunchKernelGGL((walk_kernel<E, NW, 1, LW>),
                        dim3((unsigned)(((ug1 + 7) / 8) * 8 * 2 * nvb)), block, 0, st, wa);
