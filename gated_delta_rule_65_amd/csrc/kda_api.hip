@@ -228,9 +228,20 @@ WalkPlan plan_walk(const kda_chunk_args* a) {
     if (a->walk_waves > 0 && nw != a->walk_waves) continue;
     for (int G = 1; G <= 64; G *= 2) {
       if (a->groups > 0 && G != a->groups) continue;
+      // The group scan fills CUs that the (sequence, head) chains leave
+      // idle; with a chain per CU or more it only adds pass one and the
+      // compose (measured on the varlen GVA batch, 768 chains: G = 2 took
+      // 1.03 ms against 0.89 for the plain walk).
+      if (G > 1 && a->groups <= 0 && units >= cap) continue;
       double cost;
       if (G == 1) {
-        cost = std::max(std::ceil((double)(units * nvb) / cap) * nc, chain) * step_cost[wi];
+        // With more workgroups than fit at once every CU is busy, and a
+        // four-wave bf16 step then costs about as much as an eight-wave one
+        // (measured on the varlen GVA batch: 2.0, against 1.45 on the dense
+        // prefill, whose four-wave walk leaves half the CUs idle).
+        const double rounds = std::ceil((double)(units * nvb) / cap);
+        const double c = (a->dtype == KDA_BF16 && nw == 4 && rounds > 1) ? 2.0 : step_cost[wi];
+        cost = std::max(rounds * nc, chain) * c;
       } else {
         const double cpg = std::ceil(nc / G);
         const double r2 = std::ceil((double)(units * G * nvb) / cap);
