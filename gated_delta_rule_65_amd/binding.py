@@ -548,8 +548,9 @@ def chunk_stages(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=No
     """Run the chunk path (PATH_STAGED: prep as its own kernel; PATH_FUSED:
     prep folded into WY) and return its intermediates as raw views of the
     workspace (layouts and the packed fragment order as kda.h documents them):
-    chunk_offsets, qg, kg_t, decay, w, u_t, aqk, plus out and the final
-    state.  For tests and tools."""
+    chunk_offsets, order (the sequences longest first), nch_max (the longest
+    sequence's chunk count), qg, kg_t, decay, w, u_t, aqk, plus out and the
+    final state.  For tests and tools."""
     p = _prepare_chunk(q, k, v, g, beta, scale, initial_state, True, cu_seqlens,
                        use_qk_l2norm_in_kernel, None, None, None, None, None)
     keep = {}
@@ -573,6 +574,8 @@ def chunk_stages(q, k, v, g, beta, cu_seqlens=None, scale=None, initial_state=No
     return dict(
         out=p["out"], final_state=p["fin"],
         chunk_offsets=view(lay.chunk_offsets, (N + 1,), torch.int32, 4),
+        order=view(lay.chunk_offsets + 4 * (N + 1), (N,), torch.int32, 4),
+        nch_max=view(lay.zero + 1040, (1,), torch.int32, 4),
         qg=view(lay.qg, (T, H, D), dt, es),
         kg_t=view(lay.kg_t, (mc, H, D, CHUNK), dt, es),
         decay=view(lay.decay, (mc, H, D), torch.float32, 4),

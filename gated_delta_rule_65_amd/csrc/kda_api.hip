@@ -342,9 +342,9 @@ kda_status layout_of(const kda_chunk_args* a, kda_ws_layout* L) {
   L->groups = plan.groups;
   L->walk_waves = plan.waves;
   L->chunk_offsets = off;
-  off = align_up(off + sizeof(int32_t) * ((size_t)a->num_seqs + 1), 256);
+  off = align_up(off + sizeof(int32_t) * (2 * (size_t)a->num_seqs + 1), 256);  // + the order
   L->zero = off;
-  off = align_up(off + 1024 + 256, 256);  // zero page, then the WY work counter
+  off = align_up(off + 1024 + 256, 256);  // zero page, WY work counter, longest chunk count
   L->table = off;
   off = align_up(off + 16 * (size_t)mc, 256);
   if (onchip) {

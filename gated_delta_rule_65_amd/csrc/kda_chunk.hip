@@ -46,18 +46,25 @@ __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* cu, 
                                                              int dense_len, int T,
                                                              int32_t* offs, int4* table,
                                                              int max_chunks, uint4* zero) {
-  __shared__ int32_t wsum[16];
+  __shared__ int32_t wsum[16], wmax[16], ccount[64];
   __shared__ int32_t soffs[OFFS_LDS + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid < 65) zero[tid] = make_uint4(0, 0, 0, 0);  // the zero page the walk DMAs from,
                                                      // then the WY work counter
   const int per = (N + 1023) / 1024;
   const int s0 = min(N, tid * per), s1 = min(N, s0 + per);
-  int sum = 0;
+  int sum = 0, longest = 0;
   for (int n = s0; n < s1; ++n) {
     const SeqSpan s = seq_span(cu, n, dense_len, T);
-    sum += (s.eos - s.bos + C - 1) / C;
+    const int nc = (s.eos - s.bos + C - 1) / C;
+    sum += nc;
+    longest = max(longest, nc);
   }
+  // the longest sequence's chunk count (the group scan's group length comes
+  // from it), capped at the chunk bound like every walk's own count
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) longest = max(longest, __shfl_xor(longest, off));
+  if (lane == 0) wmax[wave] = longest;
   // inclusive scan inside the wave, then across the 16 wave totals
   int incl = sum;
 #pragma unroll
@@ -77,6 +84,12 @@ __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* cu, 
     wsum[tid] = x;  // inclusive over waves
   }
   __syncthreads();
+  if (tid == 0) {
+    int m = 0;
+    for (int w = 0; w < 16; ++w) m = max(m, wmax[w]);
+    reinterpret_cast<int32_t*>(reinterpret_cast<char*>(zero) + KDA_NCH_MAX_OFFSET)[0] =
+        min(m, max_chunks);
+  }
   const int run0 = (wave > 0 ? wsum[wave - 1] : 0) + incl - sum;  // exclusive
   const int total = wsum[15];
   const bool in_lds = N <= OFFS_LDS;
@@ -95,6 +108,39 @@ __global__ __launch_bounds__(1024) void chunk_offsets_kernel(const int32_t* cu, 
     }
   }
   if (tid == 1023) offs[N] = total;
+  {
+    // The sequences in decreasing chunk count, after offs[N]: a counting
+    // sort over quarter-octave classes (ties in any order), so that the
+    // walks, whose workgroups start in index order, begin with the longest
+    // chains and the short ones fill in around them.
+    auto cls = [](int nc) {
+      if (nc <= 0) return 0;
+      const int e = 31 - __clz(nc);
+      const int f = e >= 2 ? (nc >> (e - 2)) & 3 : (nc << (2 - e)) & 3;
+      return min(63, 4 * e + f + 1);
+    };
+    for (int i = tid; i < 64; i += 1024) ccount[i] = 0;
+    __syncthreads();
+    for (int n = s0; n < s1; ++n) {
+      const SeqSpan s = seq_span(cu, n, dense_len, T);
+      atomicAdd(&ccount[cls((s.eos - s.bos + C - 1) / C)], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int run = 0;
+      for (int c = 63; c >= 0; --c) {
+        const int k = ccount[c];
+        ccount[c] = run;
+        run += k;
+      }
+    }
+    __syncthreads();
+    int32_t* order = offs + N + 1;
+    for (int n = s0; n < s1; ++n) {
+      const SeqSpan s = seq_span(cu, n, dense_len, T);
+      order[atomicAdd(&ccount[cls((s.eos - s.bos + C - 1) / C)], 1)] = n;
+    }
+  }
   if (in_lds) {
     if (tid == 0) soffs[N] = total;
     __syncthreads();
@@ -877,7 +923,8 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
   if (ug >= a.units * GW) return;
   const int unit = ug / GW, g = ug - unit * GW;
   const int hv = a.hv;
-  const int n = unit / hv, h = unit - n * hv;
+  // (sequence, head) in longest-first order: unit / hv indexes the order
+  const int n = a.order[unit / hv], h = unit - (unit / hv) * hv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // transfer columns of pass one (fp32 operands: a workgroup of their own)
@@ -897,8 +944,15 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
   const int c_first = a.offs[n];
   // a malformed cu_seqlens could claim chunks past the bound; never read them
   const int nch_all = max(0, min(a.offs[n + 1], a.max_chunks) - c_first);
-  const int cpg = (nch_all + G - 1) / G;
+  const int cpg = MODE == 0 ? max(1, nch_all) : group_chunks(a.nch_max, G);
   const int jc0 = min(nch_all, g * cpg), jc1 = min(nch_all, jc0 + cpg);
+  // Groups past the one holding the sequence's last chunk are empty: pass
+  // one writes nothing for them (compose stops at that group), pass two has
+  // neither tokens nor the final state to write.  (Group 0 of an empty
+  // sequence is that group: its pass two writes the final state.)
+  const int g_last = nch_all > 0 ? (nch_all - 1) / cpg : 0;
+  if (MODE == 1 && jc0 >= jc1) return;
+  if (MODE == 2 && g > g_last) return;
 
   void* row = nullptr;  // paged pool plane of this (sequence, head)
   if (a.cache) {
@@ -938,7 +992,6 @@ __global__ __launch_bounds__(64 * (NW + LW)) void walk_kernel(const WalkArgs<E> 
     // the group holding the sequence's last chunk writes the final state
     // (group 0 for an empty sequence: its start state is an exact copy), so
     // the final state is the walk's own, as is a checkpoint at the end
-    const int g_last = nch_all > 0 ? (nch_all - 1) / cpg : 0;
     if (g == g_last) {
       dst = a.cache ? row : (a.fin ? dense_plane(a.fin, unit_plane, state_bf) : nullptr);
       dst_bf = state_bf;
@@ -1432,7 +1485,8 @@ __global__ __launch_bounds__(512) void pass_one_kernel(const WalkArgs<E> a) {
   if (ug >= a.units * GW) return;
   const int unit = ug / GW, g = ug - unit * GW;
   const int hv = a.hv;
-  const int n = unit / hv, h = unit - n * hv;
+  // (sequence, head) in longest-first order: unit / hv indexes the order
+  const int n = a.order[unit / hv], h = unit - (unit / hv) * hv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool tcols = wave >= 4;
@@ -1441,8 +1495,9 @@ __global__ __launch_bounds__(512) void pass_one_kernel(const WalkArgs<E> a) {
   const SeqSpan sp = seq_span(a.cu, n, a.dense_len, a.T);
   const int c_first = a.offs[n];
   const int nch_all = max(0, min(a.offs[n + 1], a.max_chunks) - c_first);
-  const int cpg = (nch_all + G - 1) / G;
+  const int cpg = group_chunks(a.nch_max, G);
   const int jc0 = min(nch_all, g * cpg), jc1 = min(nch_all, jc0 + cpg);
+  if (jc0 >= jc1) return;  // an empty group: compose does not read its planes
 
   // state slices: S[b][kb][r] = S[k = 16 kb + 4 gq + r][column col0 + 16 b]
   f32x4_t S[2][8];
@@ -1695,6 +1750,8 @@ static hipError_t launch_staged_t(const ChunkLaunch& L) {
   wa.out16 = std::is_same<I, _Float16>::value ? (_Float16*)L.out : nullptr;
   wa.units = N * L.hv; wa.max_chunks = (int)L.max_chunks; wa.groups = L.groups;
   wa.scan = L.scan; wa.zero = (const uint4*)L.zero;
+  wa.nch_max = reinterpret_cast<const int32_t*>((const char*)L.zero + KDA_NCH_MAX_OFFSET);
+  wa.order = L.chunk_offsets + N + 1;
   wa.ckpt = L.ckpt; wa.ckpt_off = L.ckpt_off; wa.ckpt_idx = L.ckpt_idx;
   wa.ckpt_rows = L.ckpt_rows;
   wa.nvb = D / (16 * L.walk_waves);

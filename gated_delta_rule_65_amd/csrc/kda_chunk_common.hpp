@@ -253,6 +253,8 @@ struct WalkArgs {
   _Float16* out16;  // fp16 output instead of `out` (fp16 inputs on the fp32 path), or NULL
   int nvb, units, max_chunks, groups;
   float* scan;  // group planes (g, n, h): P [k][j], B [v][k], H_in [v][k]
+  const int32_t* nch_max;  // chunks of the batch's longest sequence (device)
+  const int32_t* order;    // [N] sequences in decreasing chunk count (device)
   const uint4* zero;
   float* ckpt;  // mid-prefill snapshots [rows, hv, 128, 128] or NULL
   const int32_t *ckpt_off, *ckpt_idx;
@@ -260,6 +262,20 @@ struct WalkArgs {
 };
 
 constexpr size_t PLANE = (size_t)D * D;
+
+// Workspace bytes after the zero page (1 KiB of zeros, then the WY work
+// counter) where the chunk-table kernel leaves the longest sequence's chunk
+// count.
+constexpr int KDA_NCH_MAX_OFFSET = 1040;
+
+// Chunks per group of the group scan.  One length for the whole batch, from
+// its longest sequence (the chunk-table kernel leaves that count beside the
+// zero page): the longest sequences split into G groups, shorter ones into
+// fewer (one when they fit a group), so the scan adds pass-one work only
+// where it shortens the longest chains.
+__device__ __forceinline__ int group_chunks(const int32_t* nch_max, int G) {
+  return max(1, (*nch_max + G - 1) / G);
+}
 
 // Four values (elements off .. off + 3) of an fp32 or bf16 state plane; bf16
 // is widened exactly on load and rounded to nearest even on store.
@@ -326,9 +342,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int lane = threadIdx.x, l16 = lane & 15, gq = lane >> 4;
   const int vcol = 16 * rb + l16;
   const int G = a.groups;
-  // the walk's split of the sequence's chunks into groups
+  // the walk's split of the sequence's chunks into groups; the groups after
+  // the one holding its last chunk are empty and walk nothing
   const int nch_all = max(0, min(a.offs[n + 1], a.max_chunks) - a.offs[n]);
-  const int cpg = (nch_all + G - 1) / G;
+  const int cpg = group_chunks(a.nch_max, G);
+  const int g_last = nch_all > 0 ? (nch_all - 1) / cpg : 0;
   const void* src = nullptr;
   bool src_bf = false;
   if (a.cache) {
@@ -349,13 +367,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       S[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   }
-  for (int g = 0; g < G; ++g) {
+  for (int g = 0; g <= g_last; ++g) {
     float* hin = scan_plane(a.scan, g, n, h, a.N, hv, 2);
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb)
       *reinterpret_cast<float4*>(hin + (size_t)vcol * D + 16 * kb + 4 * gq) =
           make_float4(S[kb][0], S[kb][1], S[kb][2], S[kb][3]);
-    if (g == G - 1) break;
+    if (g == g_last) break;
     // an empty group's transfer is exactly the identity and its B zero: the
     // state passes on bit for bit (a zero-length sequence keeps its state)
     if (min(nch_all, g * cpg) >= min(nch_all, g * cpg + cpg)) continue;

@@ -63,6 +63,7 @@ struct OnchipArgs {
   int num_slots;
   bf16* out;
   float* scan;  // group planes (g, n, h): P [k][j], B [v][k], H_in [v][k]
+  const int32_t* nch_max;  // chunks of the batch's longest sequence (device)
   float* ckpt;
   const int32_t *ckpt_off, *ckpt_idx;
   int ckpt_rows;
@@ -239,8 +240,12 @@ onchip_kernel(
 
   const int c_first = a.offs[n];
   const int nch_all = max(0, min(a.offs[n + 1], a.max_chunks) - c_first);
-  const int cpg = (nch_all + G - 1) / G;
+  const int cpg = MODE == 0 ? max(1, nch_all) : group_chunks(a.nch_max, G);
   const int jc0 = min(nch_all, g * cpg), jc1 = min(nch_all, jc0 + cpg);
+  // groups past the one holding the last chunk are empty (see the staged walk)
+  const int g_last = nch_all > 0 ? (nch_all - 1) / cpg : 0;
+  if (MODE == 1 && jc0 >= jc1) return;
+  if (MODE == 2 && g > g_last) return;
 
   void* row = nullptr;  // paged pool plane of this (sequence, head)
   if (a.cache) {
@@ -271,7 +276,6 @@ onchip_kernel(
     src_bf = dst_bf = state_bf;
   } else if (MODE == 2) {
     src = scan_plane(a.scan, g, n, h, a.N, hv, 2);
-    const int g_last = nch_all > 0 ? (nch_all - 1) / cpg : 0;
     if (g == g_last) {
       dst = a.cache ? row : (a.fin ? dense_plane(a.fin, unit_plane, state_bf) : nullptr);
       dst_bf = state_bf;
@@ -871,7 +875,7 @@ static void launch_onchip_t(const ChunkLaunch& L, const OnchipArgs& oa) {
   wa.N = a.N; wa.hv = a.hv; wa.init = L.init; wa.state_bf16 = L.state_bf16;
   wa.cache = L.cache; wa.slot_stride = L.slot_stride; wa.slots = L.slots;
   wa.has_init = L.has_init; wa.num_slots = L.num_slots; wa.units = a.units;
-  wa.max_chunks = a.max_chunks; wa.groups = G; wa.scan = L.scan;
+  wa.max_chunks = a.max_chunks; wa.groups = G; wa.scan = L.scan; wa.nch_max = a.nch_max;
   hipLaunchKernelGGL((compose_kernel<bf16>), dim3((unsigned)(((a.units + 7) / 8) * 64)), dim3(64),
                      0, st, wa);
   mark_ev(L, 5);
@@ -900,6 +904,7 @@ hipError_t launch_chunk_onchip(const ChunkLaunch& L) {
   a.cache = L.cache; a.slot_stride = L.slot_stride; a.slots = L.slots;
   a.has_init = L.has_init; a.num_slots = L.num_slots; a.out = (bf16*)L.out;
   a.scan = L.scan; a.ckpt = L.ckpt; a.ckpt_off = L.ckpt_off; a.ckpt_idx = L.ckpt_idx;
+  a.nch_max = reinterpret_cast<const int32_t*>((const char*)L.zero + KDA_NCH_MAX_OFFSET);
   a.ckpt_rows = L.ckpt_rows;
   if (L.gate.a_log)
     launch_onchip_t<true>(L, a);

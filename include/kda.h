@@ -246,9 +246,13 @@ kda_status kda_chunk_fwd_noalloc(const kda_chunk_args *a);
  * and tools.  Offsets are in bytes from the workspace base; "chunks" is the
  * bound n_chunks_max = total_tokens / 64 + num_seqs used for sizing.  G is the
  * inclusive in-chunk cumulative log-decay, b = sigmoid(beta).
- *   chunk_offsets  int32 [N + 1]: first chunk index of each sequence
+ *   chunk_offsets  int32 [N + 1]: first chunk index of each sequence, then
+ *                  int32 [N]: the sequences in decreasing chunk count (in
+ *                  quarter-octave classes; the walks start the longest
+ *                  chains first)
  *   zero           1 KiB of zeros (source of the rows past a short chunk),
- *                  then a work counter of the WY kernel (int32)
+ *                  then a work counter of the WY kernel (int32) and, at
+ *                  byte 1040, the longest sequence's chunk count (int32)
  *   table          int32x4 [chunks]: (sequence, first token, length, 0) per
  *                  chunk, length 0 past the last chunk
  *   qg             [T_tot, Hv, 128]  qn * exp(G)                        (P)

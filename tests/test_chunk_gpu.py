@@ -775,6 +775,23 @@ def test_group_scan_keeps_empty_sequences_and_end_checkpoints_exact(groups):
 
 # ------------------------------------------------------------- chunk table
 
+def chunk_class(nc):
+    """Quarter-octave class of a chunk count: 0 for none, else
+    4 floor(log2 nc) + the two bits after the leading one, plus 1 (capped
+    at 63); the walks start sequences in decreasing class."""
+    if nc <= 0:
+        return 0
+    e = nc.bit_length() - 1
+    f = (nc >> (e - 2)) & 3 if e >= 2 else (nc << (2 - e)) & 3
+    return min(63, 4 * e + f + 1)
+
+
+def test_chunk_class_orders_counts():
+    assert [chunk_class(n) for n in (0, 1, 2, 3, 4, 5, 6, 7, 8)] == [0, 1, 5, 7, 9, 10, 11, 12, 13]
+    cls = [chunk_class(n) for n in range(1, 5000)]
+    assert all(a <= b for a, b in zip(cls, cls[1:]))
+
+
 @pytest.mark.parametrize("n_seqs,max_len,init", [(2000, 200, True), (9000, 3, False)])
 def test_chunk_table_for_many_sequences(n_seqs, max_len, init):
     """Thousands of sequences (some empty): the chunk offsets are the prefix
@@ -793,6 +810,13 @@ def test_chunk_table_for_many_sequences(n_seqs, max_len, init):
     counts = torch.tensor([(L + 63) // 64 for L in lengths])
     want = torch.cat([torch.zeros(1, dtype=torch.long), counts.cumsum(0)])
     assert torch.equal(st["chunk_offsets"].cpu().long(), want)
+    # the walk order: every sequence once, chunk counts non-increasing by
+    # quarter-octave class; and the longest count
+    order = st["order"].cpu().long()
+    assert sorted(order.tolist()) == list(range(n_seqs))
+    cls = [chunk_class(int(counts[n])) for n in order.tolist()]
+    assert all(a >= b for a, b in zip(cls, cls[1:]))
+    assert int(st["nch_max"].cpu()[0]) == int(counts.max())
     o_ref, s_ref = oracle_dense(b)
     assert rel(st["out"].float().cpu().numpy(), o_ref, b.cu_seqlens) < 1e-2
     assert rel(st["final_state"].cpu().numpy(), s_ref) < 1e-2
