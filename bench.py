@@ -454,21 +454,34 @@ class ChunkCase:
         self.max_seqlen = max(self.lengths)
         self.path = {"auto": B.PATH_AUTO, "staged": B.PATH_STAGED,
                      "fused": B.PATH_FUSED, "onchip": B.PATH_ONCHIP}[args.path]
-        self.kw = dict(scale=b.scale, cu_seqlens=b.cu_seqlens, max_seqlen=self.max_seqlen,
-                       groups=args.groups, walk_waves=args.walk_waves, path=self.path,
-                       output=self.out)
+        # A dense workload (B sequences of T tokens) is passed as chunk_kda's
+        # [B, T, H, 128] tensors without cu_seqlens, as a caller holds it; the
+        # varlen batch as [S, H, 128] with cu_seqlens.
+        self.dense = wl["kind"] == "chunk"
+        if self.dense:
+            nb, tl = wl["B"], wl["T"]
+            d4 = lambda x: x.view(nb, tl, *x.shape[1:])
+            self.inputs = tuple(d4(x) for x in (b.q, b.k, b.v, b.g, b.beta))
+            self.kw = dict(scale=b.scale, output=d4(self.out))
+        else:
+            self.inputs = (b.q, b.k, b.v, b.g, b.beta)
+            self.kw = dict(scale=b.scale, cu_seqlens=b.cu_seqlens, max_seqlen=self.max_seqlen,
+                           output=self.out)
+        self.kw.update(groups=args.groups, walk_waves=args.walk_waves, path=self.path)
         if self.paged:
             self.kw.update(state_cache=b.state_cache, state_indices=b.state_indices,
                            has_initial_state=b.has_initial_state)
         else:
             self.kw.update(initial_state=b.initial_state, output_final_state=True,
                            final_state=self.fin)
-        self.plan = B.chunk_plan(b.q, b.k, b.v, b.g, b.beta, cu_seqlens=b.cu_seqlens,
+        self.plan = B.chunk_plan(*self.inputs,
+                                 cu_seqlens=None if self.dense else b.cu_seqlens,
                                  initial_state=None if self.paged else b.initial_state,
                                  output_final_state=not self.paged, groups=args.groups,
-                                 walk_waves=args.walk_waves, max_seqlen=self.max_seqlen,
+                                 walk_waves=args.walk_waves,
+                                 max_seqlen=None if self.dense else self.max_seqlen,
                                  path=self.path)
-        nbytes = B.chunk_workspace_bytes(b.q, b.k, b.v, b.g, b.beta, **self._ws_kw())
+        nbytes = B.chunk_workspace_bytes(*self.inputs, **self._ws_kw())
         self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
         es = 2 if b.q.dtype == torch.bfloat16 else 4
         self.work = chunk_work(self.lengths, self.hqk, self.hv, es, True, True,
@@ -482,9 +495,7 @@ class ChunkCase:
         return kw
 
     def call(self, events=None):
-        b = self.b
-        self.B.chunk_kda(b.q, b.k, b.v, b.g, b.beta, workspace=self.ws, stage_events=events,
-                         **self.kw)
+        self.B.chunk_kda(*self.inputs, workspace=self.ws, stage_events=events, **self.kw)
 
     def cpu_batch(self):
         from gated_delta_rule_65_amd import inputs

@@ -126,17 +126,29 @@ def test_no_l2norm_custom_scale():
     assert rel(out, o_ref, b.cu_seqlens) < 1e-4 and rel(fin, s_ref) < 1e-4
 
 
-def test_dense_4d_input_matches_varlen():
-    b = inputs.make_chunk([96, 96], 2, 2, seed=8, init=True)
+@pytest.mark.parametrize("nb,T,hqk,hv,dt,groups", [
+    (2, 96, 2, 2, torch.bfloat16, 0),     # ragged last chunk
+    (3, 1000, 1, 4, torch.bfloat16, 3),   # GVA, forced group scan
+    (1, 4160, 2, 2, torch.bfloat16, 0),   # one sequence: the planner's group scan
+    (2, 200, 1, 2, torch.float32, 2),     # fp32 operands
+], ids=["ragged", "gva_scan", "single", "fp32_scan"])
+def test_dense_4d_input_matches_varlen(nb, T, hqk, hv, dt, groups):
+    """A dense batch given as [B, T, H, 128] (no cu_seqlens) equals the same
+    batch given in varlen form, bit for bit, and the oracle."""
+    b = inputs.make_chunk([T] * nb, hqk, hv, dtype=dt, seed=8 + T, init=True)
     q, k, v, g, beta = gpu(b)
-    out4, fin4 = chunk_kda(q.view(2, 96, 2, 128), k.view(2, 96, 2, 128),
-                             v.view(2, 96, 2, 128), g.view(2, 96, 2, 128),
-                             beta.view(2, 96, 2), scale=b.scale,
-                             initial_state=b.initial_state.to(DEV), output_final_state=True)
+    d4 = lambda x, h: x.view(nb, T, h, 128)
+    out4, fin4 = chunk_kda(d4(q, hqk), d4(k, hqk), d4(v, hv), d4(g, hv), beta.view(nb, T, hv),
+                           scale=b.scale, initial_state=b.initial_state.to(DEV),
+                           output_final_state=True, groups=groups)
     out, fin = chunk_kda(q, k, v, g, beta, scale=b.scale,
-                           initial_state=b.initial_state.to(DEV), output_final_state=True,
-                           cu_seqlens=b.cu_seqlens.to(DEV))
+                         initial_state=b.initial_state.to(DEV), output_final_state=True,
+                         cu_seqlens=b.cu_seqlens.to(DEV), groups=groups)
+    torch.cuda.synchronize()
     assert torch.equal(out4.view_as(out), out) and torch.equal(fin4, fin)
+    o_ref, s_ref = oracle_dense(b)
+    assert rel(out.float().cpu().numpy(), o_ref, b.cu_seqlens) < tol(dt)
+    assert rel(fin.cpu().numpy(), s_ref) < tol(dt)
 
 
 # ------------------------------------------------------- stage intermediates
