@@ -17,12 +17,14 @@
 //
 // Exponent range.  Per-step g lies in [-5, 0], so G spans up to 460 (log2
 // units) across a chunk and 2^(-G_i) alone would overflow fp32.  The WY
-// kernel therefore evaluates 2^(G_t - G_i) through a reference token m_a in
-// the middle of each 16-token block a of the row index t:
-//   2^(G_t - G_i) = 2^(G_t - G_ma) * 2^(G_ma - G_i)
-// For i in an earlier block both factors are <= 1; inside block a both
-// exponents stay within 8 steps (<= 58 in log2 units), which fp32 and bf16
-// hold.  Products for i > t may be large but finite and are masked away.
+// kernel therefore evaluates 2^(G_t - G_i) through a reference token m_a =
+// 16 a + 7 of each 16-token block a (t in block a, i in block b):
+//   2^(G_t - G_i) = 2^(G_t - G_ma) * 2^(G_ma - G_mb) * 2^(G_mb - G_i)
+// The outer factors span at most 8 steps each (within 2^(+-58), finite in
+// fp32 and bf16); the middle one (b < a) is <= 1, at least 2^-115.4 for
+// adjacent blocks with g >= -5, and rounds to zero only for blocks two or
+// more apart whose true coupling is then below 2^-21.  Products for i > t may
+// be large but finite and are masked away.
 #include <algorithm>
 #include <type_traits>
 
