@@ -854,7 +854,7 @@ def _mixed_case(i):
                 waves=[0, 2, 4, 8][r(4)], seed=2000 + i)
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(24))
 def test_mixed_configurations_match_oracle(i):
     cfg = _mixed_case(i)
     say("mixed", i, cfg)
