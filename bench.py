@@ -679,7 +679,10 @@ def main():
     roof = {k: kd[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
     roof.update(kernel=kd["kernel"], algorithmic_bytes=kd["algorithmic_bytes"],
                 algorithmic_flops=kd["algorithmic_flops"])
-    roof["traffic"] = load_traffic(args.workload, dom)
+    # (counters are recorded per workload for the default path, and under
+    # "workload@path" for the others: the kernels and their rows differ)
+    tkey = args.workload if args.path == "auto" else f"{args.workload}@{args.path}"
+    roof["traffic"] = load_traffic(tkey, dom)
     roof["launch_ms"] = kd["ms"]
     if "note" in kd:
         roof["note"] = kd["note"]
