@@ -378,11 +378,23 @@ def check_workload(out, o_ref, fin, s_ref, cu, t_=1e-2):
     assert e_o < t_ and e_s < t_ and f_o < t_, (e_o, e_s, f_o)
 
 
+def run_batched(batch, nb, tl):
+    """The call bench.py times for a dense workload: [B, T, H, 128] tensors,
+    no cu_seqlens, the library's own plan; returns varlen-shaped results."""
+    q, k, v, g, beta = gpu(batch)
+    d4 = lambda x: x.view(nb, tl, *x.shape[1:])
+    out, fin = chunk_kda(d4(q), d4(k), d4(v), d4(g), d4(beta), scale=batch.scale,
+                         initial_state=batch.initial_state.to(DEV), output_final_state=True)
+    torch.cuda.synchronize()
+    return out.reshape(nb * tl, *out.shape[2:]).float().cpu().numpy(), fin.cpu().numpy()
+
+
 def test_dense_prefill_workload():
-    """B=4, T=4096, H=16, bf16, fp32 initial state: every output and state."""
+    """B=4, T=4096, H=16, bf16, fp32 initial state, as bench.py calls it:
+    every output and state."""
     b = inputs.make_workload("dense_prefill")
     say("dense_prefill")
-    out, fin = run_dense_state(b)
+    out, fin = run_batched(b, 4, 4096)
     o_ref, s_ref = oracle_dense(b)
     check_workload(out, o_ref, fin, s_ref, b.cu_seqlens)
 
@@ -408,11 +420,11 @@ def test_varlen_gva_paged_workload():
 
 
 def test_long_single_workload():
-    """B=1, T=131072, H=32, slow decay: every output and final state of all
-    32 heads."""
+    """B=1, T=131072, H=32, slow decay, as bench.py calls it: every output
+    and final state of all 32 heads."""
     b = inputs.make_workload("long_single")
     say("long_single")
-    out, fin = run_dense_state(b)
+    out, fin = run_batched(b, 1, 131072)
     o_ref, s_ref = oracle_dense(b)
     check_workload(out, o_ref, fin, s_ref, b.cu_seqlens)
 
