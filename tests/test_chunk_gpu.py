@@ -8,6 +8,8 @@ intermediates (qg, kg_t, decay, w, u, aqk) are checked against the oracle's
 chunked form at the same bars.  Exactness cases (zero write strength with no
 decay, overwrite with orthonormal keys) are checked bit for bit.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -1002,3 +1004,65 @@ def test_bf16_paged_pool(groups):
     others = torch.ones(9, dtype=torch.bool)
     others[idx] = False
     assert torch.equal(got[others], pool[others])
+
+
+# ------------------------------------------- randomised stress (opt-in)
+
+def _stress_case(i):
+    """Case i of a wider seeded family than the mixed configurations: up to
+    120 sequences with log-uniform lengths up to 3000 tokens (some empty), GVA
+    1 / 2 / 4, bf16 / fp16 / fp32, gate parameters, paged pools, G up to 16,
+    every walk width and path."""
+    gen = torch.Generator().manual_seed(190000 + i)
+    r = lambda n: int(torch.randint(0, n, (1,), generator=gen))
+    n_seqs = 1 + r([40, 120][r(2)])
+    lengths = [0 if r(8) == 0 else int(np.exp(np.log(3000) * float(torch.rand(1, generator=gen))))
+               for _ in range(n_seqs)]
+    if sum(lengths) == 0:
+        lengths[0] = 100
+    hqk = [1, 2, 4][r(3)]
+    hv = hqk * [1, 2, 4][r(3)]
+    dtype = [torch.bfloat16, torch.bfloat16, torch.float32, torch.float16][r(4)]
+    paths = [B.PATH_AUTO, B.PATH_STAGED] + ([B.PATH_ONCHIP] if dtype == torch.bfloat16 else [])
+    return dict(lengths=lengths, hqk=hqk, hv=hv, dtype=dtype, gate=r(3) == 0, paged=bool(r(2)),
+                groups=[0, 0, 1, 2, 3, 5, 8, 16][r(8)], waves=[0, 0, 2, 4, 8][r(5)],
+                path=paths[r(len(paths))], seed=195000 + i)
+
+
+@pytest.mark.parametrize("i", range(int(os.environ.get("KDA_STRESS", "0"))))
+def test_random_configurations_match_oracle(i):
+    """Opt-in (KDA_STRESS=<cases>): outputs and final states of seeded random
+    configurations against the oracle at the usual bars, per unit."""
+    cfg = _stress_case(i)
+    say("stress", i, {k: v for k, v in cfg.items() if k != "lengths"}, len(cfg["lengths"]))
+    b = inputs.make_chunk(cfg["lengths"], cfg["hqk"], cfg["hv"], dtype=cfg["dtype"], g_scale=0.5,
+                          seed=cfg["seed"], init=not cfg["paged"],
+                          paged_slots=len(cfg["lengths"]) + 3 if cfg["paged"] else 0)
+    hv = cfg["hv"]
+    gk = {}
+    if cfg["gate"]:
+        gg = torch.Generator().manual_seed(cfg["seed"])
+        gk = dict(A_log=torch.randn(hv, generator=gg) * 0.3,
+                  dt_bias=torch.randn(hv, 128, generator=gg) * 0.5)
+    q, k, v, g, beta = gpu(b)
+    kw = dict(scale=b.scale, cu_seqlens=b.cu_seqlens.to(DEV), groups=cfg["groups"],
+              walk_waves=cfg["waves"], path=cfg["path"],
+              **{k_: v_.to(DEV) for k_, v_ in gk.items()})
+    if cfg["paged"]:
+        cache = b.state_cache.to(DEV)
+        out = B.chunk_kda(q, k, v, g, beta, state_cache=cache,
+                          state_indices=b.state_indices.to(DEV),
+                          has_initial_state=b.has_initial_state.to(DEV), **kw)
+        s0 = b.state_cache[b.state_indices.long()] * b.has_initial_state.view(-1, 1, 1, 1).float()
+    else:
+        out, fin = B.chunk_kda(q, k, v, g, beta, initial_state=b.initial_state.to(DEV),
+                               output_final_state=True, **kw)
+        s0 = b.initial_state
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.recurrence(b.q, b.k, b.v, b.g, b.beta, cu_seqlens=b.cu_seqlens,
+                                     scale=b.scale, initial_state=s0,
+                                     **{k_: v_.double() for k_, v_ in gk.items()})
+    t_ = tol(cfg["dtype"])
+    assert rel(out.float().cpu().numpy(), o_ref, b.cu_seqlens) < t_
+    got = cache.cpu()[b.state_indices.long()] if cfg["paged"] else fin.cpu()
+    assert rel(got.float().numpy(), s_ref) < t_
