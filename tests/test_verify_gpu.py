@@ -11,6 +11,8 @@ of a rounding boundary: 1e-2.  The kg records are copies of the raw inputs
 and are compared bit for bit; record rows and cache slots a call must not
 touch are checked unchanged.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -268,3 +270,26 @@ def test_padded_pool_slots():
     torch.cuda.synchronize()
     assert torch.equal(out, out2) and torch.equal(corr, corr2)
     assert torch.equal(pool.cpu(), dense.cpu())
+
+
+@pytest.mark.parametrize("i", range(int(os.environ.get("KDA_STRESS", "0"))))
+def test_random_verify_and_commit_match_the_oracle(i):
+    """Opt-in (KDA_STRESS=<cases>): seeded random windows (1..8), request
+    counts (up to 300, some empty, some null slots), GVA, input dtypes, bf16
+    pools and gate parameters; outputs, records and committed states against
+    the oracle."""
+    gen = torch.Generator().manual_seed(290000 + i)
+    r = lambda n: int(torch.randint(0, n, (1,), generator=gen))
+    window = 1 + r(8)
+    n = 1 + r(300)
+    lengths = [r(window + 1) for _ in range(n)]
+    hqk = [1, 2, 4, 8][r(4)]
+    hv = hqk * [1, 2, 4][r(3)]
+    dt = [torch.bfloat16, torch.float32, torch.float16][r(3)]
+    state_dt = torch.bfloat16 if dt == torch.bfloat16 and r(2) else torch.float32
+    null = tuple(q for q in range(n) if r(10) == 0)
+    gate = gate_params(hv, 299000 + i) if r(3) == 0 else None
+    b = inputs.make_verify(lengths, window, hqk, hv, n + r(16), dtype=dt, seed=295000 + i,
+                           null=null)
+    res = run(b, window, state_dt=state_dt, gate=gate)
+    check(b, res, dt, state_dt, window)
