@@ -6,6 +6,8 @@ updated cache rows are held to 1e-5 (the only error is fp32 arithmetic).  Each
 bar holds over the whole tensor and for the worst unit: every (request, token,
 head) output row, every state plane (tests/parity.py).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -371,6 +373,58 @@ def test_mixed_decode_configurations_match_oracle(i):
     torch.cuda.synchronize()
     ro, rc = oracle.decode_multi(q, k, v, g, beta, cache, idx, acc, state_bf16=state_bf16,
                                  **{k_: v_.double() for k_, v_ in gk.items()})
+    t_ = 1e-4 if dtype == torch.float32 and not state_bf16 else 1e-2
+    assert rel(out.float().cpu().numpy(), ro) < t_
+    assert rel(cd.cpu().float().numpy(), rc) < t_
+
+
+@pytest.mark.parametrize("i", range(int(os.environ.get("KDA_STRESS", "0"))))
+def test_random_decode_configurations_match_oracle(i):
+    """Opt-in (KDA_STRESS=<cases>): seeded random single-token ([N, H, 128])
+    and multi-token ([B, T, H, 128]) decodes over request counts up to 64,
+    GVA, input dtypes, fp32 or bf16 pools, null slots, accepted-token counts
+    and gate parameters, against the oracle."""
+    gen = torch.Generator().manual_seed(310000 + i)
+    r = lambda n: int(torch.randint(0, n, (1,), generator=gen))
+    Bn, T = 1 + r(64), 1 + r(8)
+    single = T == 1 and bool(r(2))
+    hqk = [1, 2, 4, 8][r(4)]
+    hv = min(16, hqk * [1, 2, 4][r(3)])
+    dtype = [torch.bfloat16, torch.float16, torch.float32][r(3)]
+    state_bf16 = bool(r(2))
+    slots = Bn * T + r(32)
+    print("random decode", i, Bn, T, single, hqk, hv, dtype, state_bf16, flush=True)
+    q, k, v, g, beta, cache = spec_case(Bn, T, hqk, hv, slots, dtype, seed=320000 + i)
+    if state_bf16:
+        cache = cache.to(torch.bfloat16)
+    idx = torch.randperm(slots, generator=gen)[:Bn * T].to(torch.int32).reshape(Bn, T)
+    for b_ in range(Bn):
+        if r(8) == 0:
+            idx[b_, r(T)] = -1
+    acc = None if single or r(3) == 0 else \
+        torch.randint(1, T + 1, (Bn,), generator=gen).to(torch.int32)
+    gk = {}
+    if r(3) == 0:
+        gk = dict(A_log=torch.randn(hv, generator=gen) * 0.3,
+                  dt_bias=torch.randn(hv, 128, generator=gen) * 0.5,
+                  lower_bound=-float(1 + r(5)))
+    cd = cache.to(DEV)
+    dev = {k_: (v_.to(DEV) if isinstance(v_, torch.Tensor) else v_) for k_, v_ in gk.items()}
+    ref = {k_: (v_.double() if isinstance(v_, torch.Tensor) else v_) for k_, v_ in gk.items()}
+    if single:
+        flat = [t[:, 0].contiguous() for t in (q, k, v, g, beta)]
+        out = B.kda_decode(*(t.to(DEV) for t in flat), cd, idx[:, 0].contiguous().to(DEV),
+                           **dev)
+        torch.cuda.synchronize()
+        ro, rc = oracle.decode_multi(q, k, v, g, beta, cache, idx, None,
+                                     state_bf16=state_bf16, **ref)
+        ro = ro[:, 0]
+    else:
+        out = B.kda_decode(*(t.to(DEV) for t in (q, k, v, g, beta)), cd, idx.to(DEV),
+                           num_accepted_tokens=None if acc is None else acc.to(DEV), **dev)
+        torch.cuda.synchronize()
+        ro, rc = oracle.decode_multi(q, k, v, g, beta, cache, idx, acc,
+                                     state_bf16=state_bf16, **ref)
     t_ = 1e-4 if dtype == torch.float32 and not state_bf16 else 1e-2
     assert rel(out.float().cpu().numpy(), ro) < t_
     assert rel(cd.cpu().float().numpy(), rc) < t_
