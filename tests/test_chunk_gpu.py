@@ -8,13 +8,12 @@ intermediates (qg, kg_t, decay, w, u, aqk) are checked against the oracle's
 chunked form at the same bars.  Exactness cases (zero write strength with no
 decay, overwrite with orthonormal keys) are checked bit for bit.
 """
-import os
-
 import numpy as np
 import pytest
 import torch
 
 import oracle
+import stress
 from oracle import forms
 from gated_delta_rule_65_amd import binding as B
 from gated_delta_rule_65_amd import inputs
@@ -1029,7 +1028,7 @@ def _stress_case(i):
                 path=paths[r(len(paths))], seed=195000 + i)
 
 
-@pytest.mark.parametrize("i", range(int(os.environ.get("KDA_STRESS", "0"))))
+@pytest.mark.parametrize("i", stress.cases())
 def test_random_configurations_match_oracle(i):
     """Opt-in (KDA_STRESS=<cases>): outputs and final states of seeded random
     configurations against the oracle at the usual bars, per unit."""

@@ -6,14 +6,13 @@ updated cache rows are held to 1e-5 (the only error is fp32 arithmetic).  Each
 bar holds over the whole tensor and for the worst unit: every (request, token,
 head) output row, every state plane (tests/parity.py).
 """
-import os
-
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import parity
+import stress
 from gated_delta_rule_65_amd import binding as B
 from gated_delta_rule_65_amd import inputs
 
@@ -378,7 +377,7 @@ def test_mixed_decode_configurations_match_oracle(i):
     assert rel(cd.cpu().float().numpy(), rc) < t_
 
 
-@pytest.mark.parametrize("i", range(int(os.environ.get("KDA_STRESS", "0"))))
+@pytest.mark.parametrize("i", stress.cases())
 def test_random_decode_configurations_match_oracle(i):
     """Opt-in (KDA_STRESS=<cases>): seeded random single-token ([N, H, 128])
     and multi-token ([B, T, H, 128]) decodes over request counts up to 64,

@@ -11,14 +11,13 @@ of a rounding boundary: 1e-2.  The kg records are copies of the raw inputs
 and are compared bit for bit; record rows and cache slots a call must not
 touch are checked unchanged.
 """
-import os
-
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import parity
+import stress
 from gated_delta_rule_65_amd import binding as B
 from gated_delta_rule_65_amd import inputs
 
@@ -272,7 +271,7 @@ def test_padded_pool_slots():
     assert torch.equal(pool.cpu(), dense.cpu())
 
 
-@pytest.mark.parametrize("i", range(int(os.environ.get("KDA_STRESS", "0"))))
+@pytest.mark.parametrize("i", stress.cases())
 def test_random_verify_and_commit_match_the_oracle(i):
     """Opt-in (KDA_STRESS=<cases>): seeded random windows (1..8), request
     counts (up to 300, some empty, some null slots), GVA, input dtypes, bf16
