@@ -3,6 +3,7 @@
 // planes, the walk arguments and the group-compose kernel.
 #pragma once
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "kda_common.hpp"
@@ -415,16 +416,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 
 // --------------------------------------------------------------------- launch
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device, cached per device (relaxed atomics:
+// host threads may launch concurrently, and they all store the same value).
 inline int cu_count() {
-  static int cache[64];
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     n = 256;
-  if (dev < 64) cache[dev] = n;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
